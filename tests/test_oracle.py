@@ -1,0 +1,112 @@
+"""CPU tests of the oracle against its pins (no GPU needed)."""
+
+import os
+import shutil
+
+import numpy as np
+import pytest
+
+import oracle
+import oracle_pins as pins
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return oracle.load()
+
+
+@pytest.mark.parametrize("pin", pins.PINS, ids=lambda f: f.__name__)
+def test_pin(lib, pin):
+    pin(lib)
+
+
+def test_invariants(lib):
+    """Background is 0; flipping or transposing the input permutes the output;
+    adding background never increases a value; the distance is 1-Lipschitz per
+    axis step (|d(p) - d(q)| <= s_k for axis neighbours)."""
+    rng = np.random.default_rng([42, 1010])
+    for t in range(10):
+        shape = tuple(int(x) for x in rng.integers(5, 60, 2))
+        samp = (1.0, 1.0) if t % 2 == 0 else (2.0, 0.5)
+        mask = (rng.random(shape) >= 0.05).astype(np.uint8)
+        mask[0, 0] = 0
+        sq, _ = oracle.edt(mask, samp, False, lib)
+        assert (sq[mask == 0] == 0).all()
+        sqf, _ = oracle.edt(mask[::-1, ::-1].copy(), samp, False, lib)
+        np.testing.assert_array_equal(sqf, sq[::-1, ::-1])
+        sqt, _ = oracle.edt(mask.T.copy(), samp[::-1], False, lib)
+        np.testing.assert_array_equal(sqt, sq.T)
+        more = mask.copy()
+        more[rng.integers(0, shape[0]), rng.integers(0, shape[1])] = 0
+        sqm, _ = oracle.edt(more, samp, False, lib)
+        assert (sqm <= sq).all()
+        d = np.sqrt(sq)
+        assert (np.abs(np.diff(d, axis=0)) <= samp[0] + 1e-12).all()
+        assert (np.abs(np.diff(d, axis=1)) <= samp[1] + 1e-12).all()
+
+
+def test_batch_equals_single(lib):
+    from workloads import ellipsoids_3d_batch, rng_for
+    vols = ellipsoids_3d_batch(rng_for("c4", 7), 3, 16, 2, 4, 2.0, 6.0)
+    vols[1] = 1  # one volume without background
+    sq, feat = oracle.edt_batch(vols, None, True, lib)
+    for b in range(3):
+        s, f = oracle.edt(vols[b], None, True, lib)
+        np.testing.assert_array_equal(sq[b], s)
+        np.testing.assert_array_equal(feat[b], f)
+    assert (feat[1][..., 0] == -1).all()
+
+
+# Planted mistakes: each replaces one piece of oracle_edt.c in a temporary copy.
+# A useful set of pins must fail for every one of them.
+MUTANTS = {
+    "transposed_operands_in_dominance":
+        ("return (Y[b] - Y[a]) * (double)(c - b) >= (Y[c] - Y[b]) * (double)(b - a);",
+         "return (Y[b] - Y[a]) * (double)(b - a) >= (Y[c] - Y[b]) * (double)(c - b);"),
+    "reversed_dominance":
+        ("return (Y[b] - Y[a]) * (double)(c - b) >= (Y[c] - Y[b]) * (double)(b - a);",
+         "return (Y[b] - Y[a]) * (double)(c - b) <= (Y[c] - Y[b]) * (double)(b - a);"),
+    "dropped_square_in_lifting":
+        ("Y[j] = f[j] + s2 * (double)j * (double)j;", "Y[j] = f[j] + s2 * (double)j;"),
+    "dropped_spacing_in_query":
+        ("2.0 * s2 * (double)q * (double)(stack[m + 1] - stack[m]) >",
+         "2.0 * (double)q * (double)(stack[m + 1] - stack[m]) >"),
+    "dropped_column_term_in_query":
+        ("out[q] = s2 * (double)(q - j) * (double)(q - j) + f[j];",
+         "out[q] = s2 * (double)(q - j) * (double)(q - j);"),
+    "wrong_choice_between_up_and_down":
+        ("if (up >= 0 && (next < 0 || i - up <= next - i)) g = up;",
+         "if (up >= 0 && (next < 0 || i - up >= next - i)) g = up;"),
+    "virtual_background_wrong_side":
+        ("double d = s2[0] * (double)(coord[0] + 1) * (double)(coord[0] + 1);",
+         "double d = s2[0] * (double)(coord[0] - 1) * (double)(coord[0] - 1);"),
+    "spacing_of_wrong_axis":
+        ("envelope_1d((int)nk, s2[ax], fl, Y, stack, owner, outl);",
+         "envelope_1d((int)nk, s2[0], fl, Y, stack, owner, outl);"),
+    "query_stops_one_early":
+        ("while (m + 1 < k &&", "while (m + 2 < k &&"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_mistake_is_caught(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(oracle._SRC).read()
+    assert src.count(old) == 1, f"mutation site for {name} not unique/found"
+    mdir = tmp_path / "mutant"
+    mdir.mkdir()
+    shutil.copy(os.path.join(os.path.dirname(oracle._SRC), "oracle_edt.h"), mdir)
+    (mdir / "oracle_edt.c").write_text(src.replace(old, new))
+    so = str(mdir / "libmutant.so")
+    oracle.build(str(mdir / "oracle_edt.c"), so)
+    mlib = oracle.load(so)
+    failed = []
+    for pin in pins.PINS:
+        try:
+            if pin is pins.pin_brute_random:
+                pin(mlib, count=60)
+            else:
+                pin(mlib)
+        except AssertionError:
+            failed.append(pin.__name__)
+    assert failed, f"no pin caught the planted mistake {name}"
