@@ -1,0 +1,241 @@
+#!/usr/bin/env python3
+"""Benchmark of the exact EDT hot path on one MI355X.
+
+One step = one complete transform (every pass of the path) of one synthetic
+workload already resident in HBM.  Prints ONE JSON line:
+
+  value        whole-job throughput, Gpixel/s (elements per second / 1e9)
+  roofline     the dominant kernel's algorithmic HBM bytes per launch / its mean
+               duration (HIP events on the launch stream), against 8 TB/s
+  cpu_baseline the CPU oracle (single thread) on a bounded sample of the same
+               workload, same units
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c3]
+                       [--no-cpu-baseline] [--check]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "EDT Gpixel/s at 1 GPU + achieved HBM GB/s fraction of peak"
+HBM_PEAK_GBS = 8000.0   # MI355X HBM3E peak, GB/s
+
+WORKLOADS = {
+    "c1": "2D 512x512 uint8, background i.i.d. Bernoulli(0.01), isotropic; "
+          "outputs int32 sqdist + float32 dist + int32 index",
+    "c2a": "2D 4096x4096 uint8, foreground = union of 300 disks (r ~ U[8,400]); "
+           "outputs sqdist + dist + index",
+    "c2b": "2D 4096x4096 uint8, single background pixel; outputs sqdist + dist + index",
+    "c3": "2D 16384x16384 uint8, background i.i.d. Bernoulli(1e-4), isotropic; "
+          "outputs int32 sqdist + float32 dist",
+    "c4": "3D batch 16 x 128^3 uint8, foreground = union of 5-20 ellipsoids per volume, "
+          "isotropic; output float32 dist",
+    "c5": "3D 512^3 uint8, background Bernoulli(1e-3) + 64-voxel background slab, "
+          "sampling (2.5,1,1); outputs float32 dist + int32 index",
+}
+OUTPUTS = {
+    "c1": ("sqdist", "dist", "indices"),
+    "c2a": ("sqdist", "dist", "indices"),
+    "c2b": ("sqdist", "dist", "indices"),
+    "c3": ("sqdist", "dist"),
+    "c4": ("dist",),
+    "c5": ("dist", "indices"),
+}
+
+
+def algorithmic_bytes(kernel: str, shape, n_out: int) -> int:
+    """Bytes a kernel must move through HBM by the per-element byte model:
+    every input it needs read once and every output written once, at the
+    narrowest exact width (mask 1 B, axis-0 coordinate 2 B, packed coordinate
+    pair 4 B, each requested output 4 B)."""
+    n = int(np.prod(shape))
+    if len(shape) == 2:
+        n0, M, B = shape[0], shape[1], 1
+    else:
+        B, n0, M = shape[0], shape[1], shape[2] * shape[3]
+    nseg = (n0 + 63) // 64
+    summ = B * nseg * M * 2 * 2          # first + last, uint16 each
+    if kernel == "axis0_summary":
+        return n + summ
+    if kernel == "axis0_scan":
+        return 2 * summ
+    if kernel == "axis0_resolve":
+        return n + summ + 2 * n
+    if kernel == "envelope_rows_2d":
+        return 2 * n + 4 * n * n_out
+    if kernel == "envelope_cols_3d":
+        return 2 * n + 4 * n
+    if kernel == "envelope_rows_3d":
+        return 4 * n + 4 * n * n_out
+    raise KeyError(kernel)
+
+
+def cpu_baseline(name, mask, sampling):
+    """Time the oracle (single thread, as written) on a bounded sample."""
+    import oracle
+    if mask.ndim == 2:
+        rows = mask.shape[0]
+        budget = 40_000_000           # elements: a few seconds of oracle time
+        take = max(1, min(rows, budget // mask.shape[1]))
+        sample = np.ascontiguousarray(mask[:take])
+        if not (sample == 0).any():
+            sample = np.ascontiguousarray(mask)
+            take = rows
+        t0 = time.perf_counter()
+        oracle.edt(sample, sampling, features=False)
+        dt = time.perf_counter() - t0
+        desc = f"oracle on rows [0,{take}) of the {mask.shape[0]}x{mask.shape[1]} mask"
+        n = sample.size
+    else:
+        vols = mask.shape[0]
+        budget = 40_000_000
+        per = int(np.prod(mask.shape[1:]))
+        take = max(1, min(vols, budget // per))
+        sample = mask[:take]
+        t0 = time.perf_counter()
+        oracle.edt_batch(sample, sampling, features=("indices" in OUTPUTS[name]))
+        dt = time.perf_counter() - t0
+        desc = f"oracle on {take} of {vols} volumes of {mask.shape[1:]}"
+        n = sample.size
+    return {"value": n / dt / 1e9, "unit": "Gpixel/s", "cores": 1, "kind": "oracle",
+            "sample": desc, "seconds": round(dt, 3),
+            "cpu": platform.processor() or platform.machine()}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="c3", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--check", action="store_true", help="also compare with the oracle")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build measures one GPU only (the transform of one "
+              "workload runs on a single MI355X); run with --gpus 1", file=sys.stderr)
+        return 2
+
+    import torch
+    from exact_euclidean_distance_amd import alloc_workspace, edt2d, edt3d, workspace_size_2d, \
+        workspace_size_3d
+    from workloads import make_config
+
+    if not torch.cuda.is_available():
+        print("bench.py: no HIP device", file=sys.stderr)
+        return 1
+    dev = torch.device("cuda:0")
+    name = args.config
+    print(f"[bench] generating {name}", file=sys.stderr, flush=True)
+    mask_np, sampling, _ = make_config(name)
+    shape = mask_np.shape
+    n = int(np.prod(shape))
+    want = OUTPUTS[name]
+    mask = torch.from_numpy(mask_np).to(dev)
+    sq = torch.empty(shape, dtype=torch.int32, device=dev) if "sqdist" in want else None
+    ds = torch.empty(shape, dtype=torch.float32, device=dev) if "dist" in want else None
+    ix = torch.empty(shape, dtype=torch.int32, device=dev) if "indices" in want else None
+    if len(shape) == 2:
+        ws = alloc_workspace(workspace_size_2d(*shape), dev)
+        fn = edt2d
+    else:
+        ws = alloc_workspace(workspace_size_3d(*shape), dev)
+        fn = edt3d
+    stream = torch.cuda.current_stream()
+
+    def step(timed=False):
+        return fn(mask, sampling, sqdist=sq, dist=ds, indices=ix, return_distances=ds is not None,
+                  workspace=ws, stream=stream, timed=timed)
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / max(1, args.steps)
+
+    # per-kernel durations: HIP events recorded by the library around each launch
+    per = {}
+    for _ in range(max(3, args.steps)):
+        _, times = step(timed=True)
+        for k, t in times:
+            per.setdefault(k, []).append(t)
+    kernels = []
+    n_out = len(want)
+    for k, ts in per.items():
+        avg = float(np.mean(ts))
+        b = algorithmic_bytes(k, shape, n_out)
+        kernels.append({"name": k, "ms": round(avg, 4), "alg_bytes": b,
+                        "GBps": round(b / (avg * 1e-3) / 1e9, 1)})
+    dom = max(kernels, key=lambda r: r["ms"])
+    achieved = dom["alg_bytes"] / (dom["ms"] * 1e-3) / 1e9
+
+    if args.check:
+        import oracle
+        sys.path.insert(0, os.path.join(ROOT, "tests"))
+        from gpu_check import compare
+        print("[bench] parity check against the oracle", file=sys.stderr, flush=True)
+        if len(shape) == 2:
+            ref, _ = oracle.edt(mask_np, sampling, features=False)
+        else:
+            ref, _ = oracle.edt_batch(mask_np, sampling, features=False)
+        compare(mask_np, sampling, ref,
+                None if sq is None else sq.cpu().numpy(),
+                None if ds is None else ds.cpu().numpy(),
+                None if ix is None else ix.cpu().numpy(), batch=(len(shape) == 4))
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(name, mask_np, sampling)
+
+    total_bytes = sum(k["alg_bytes"] for k in kernels)
+    line = {
+        "metric": METRIC,
+        "value": round(n / (ms * 1e-3) / 1e9, 3),
+        "unit": "Gpixel/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f64",
+        "data": "synthetic",
+        "config": {"workload": f"{name}: {WORKLOADS[name]}", "shape": list(shape),
+                   "sampling": list(sampling) if sampling else None, "outputs": list(want)},
+        "roofline": {"bound": "hbm", "kernel": dom["name"], "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+        "path_GBps": round(total_bytes / (ms * 1e-3) / 1e9, 1),
+        "kernels": kernels,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,147 @@
+"""Thin Python binding of the C ABI: argument marshalling only.
+
+PyTorch provides device memory and the current HIP stream; every step of the
+transform runs in the library's kernels.  The keywords follow TorchMorph's
+SciPy-compatible distance-transform interface (``sampling``,
+``return_distances`` / ``return_indices``, preallocated outputs).
+"""
+
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+import torch
+
+from . import _lib
+from ._lib import EDTError
+
+
+@dataclass
+class EDTResult:
+    sqdist: Optional[torch.Tensor]   # int32, exact squared distances
+    dist: Optional[torch.Tensor]     # float32 distances
+    indices: Optional[torch.Tensor]  # int32 flat index of the nearest background (per image)
+
+
+def workspace_size_2d(H: int, W: int) -> int:
+    return int(_lib.load().edt2d_workspace_size(H, W))
+
+
+def workspace_size_3d(B: int, D: int, H: int, W: int) -> int:
+    return int(_lib.load().edt3d_workspace_size(B, D, H, W))
+
+
+def alloc_workspace(nbytes: int, device) -> torch.Tensor:
+    """A device byte buffer; torch allocations are at least 256-byte aligned."""
+    return torch.empty(max(1, nbytes), dtype=torch.uint8, device=device)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check_mask(mask: torch.Tensor, ndim: Sequence[int]):
+    if not isinstance(mask, torch.Tensor):
+        raise TypeError("mask must be a torch.Tensor")
+    if mask.dtype != torch.uint8:
+        raise TypeError("mask must be uint8 (0 = background)")
+    if not mask.is_cuda:
+        raise ValueError("mask must be a device (HIP) tensor")
+    if mask.dim() not in ndim:
+        raise ValueError(f"mask must have {ndim} dimensions, got {mask.dim()}")
+    if not mask.is_contiguous():
+        raise ValueError("mask must be C-contiguous")
+
+
+def _out(t, shape, dtype, device, want):
+    if t is not None:
+        if t.dtype != dtype or tuple(t.shape) != tuple(shape) or not t.is_contiguous() or t.device != device:
+            raise ValueError(f"preallocated output must be contiguous {dtype} of shape {tuple(shape)}")
+        return t
+    if want:
+        return torch.empty(shape, dtype=dtype, device=device)
+    return None
+
+
+def _sampling(sampling, n):
+    if sampling is None:
+        return None
+    vals = [float(s) for s in sampling]
+    if len(vals) != n:
+        raise ValueError(f"sampling needs {n} values")
+    return (ctypes.c_float * n)(*vals)
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def edt2d(mask: torch.Tensor, sampling=None, *, return_distances: bool = True,
+          return_sqdist: bool = False, return_indices: bool = False,
+          dist=None, sqdist=None, indices=None, workspace=None, stream=None,
+          timed: bool = False):
+    """Exact EDT of one (H, W) uint8 mask.  Returns :class:`EDTResult` (and the
+    per-kernel times in ms when ``timed``)."""
+    _check_mask(mask, (2,))
+    H, W = mask.shape
+    dev = mask.device
+    sq = _out(sqdist, (H, W), torch.int32, dev, return_sqdist)
+    ds = _out(dist, (H, W), torch.float32, dev, return_distances)
+    ix = _out(indices, (H, W), torch.int32, dev, return_indices)
+    lib = _lib.load()
+    need = int(lib.edt2d_workspace_size(H, W))
+    if workspace is None:
+        workspace = alloc_workspace(need, dev)
+    samp = _sampling(sampling, 2)
+    args = [_ptr(mask), H, W, samp, _ptr(sq), _ptr(ds), _ptr(ix), _ptr(workspace),
+            workspace.numel() * workspace.element_size(), _stream(stream)]
+    if not timed:
+        st = lib.edt2d_u8(*args)
+        if st != 0:
+            raise EDTError(st, "edt2d_u8")
+        return EDTResult(sq, ds, ix)
+    ms = (ctypes.c_float * 8)()
+    names = (ctypes.c_char_p * 8)()
+    cnt = ctypes.c_int32(0)
+    st = lib.edt2d_u8_timed(*args, ms, names, 8, ctypes.byref(cnt))
+    if st != 0:
+        raise EDTError(st, "edt2d_u8_timed")
+    return EDTResult(sq, ds, ix), [(names[i].decode(), ms[i]) for i in range(cnt.value)]
+
+
+def edt3d(mask: torch.Tensor, sampling=None, *, return_distances: bool = True,
+          return_sqdist: bool = False, return_indices: bool = False,
+          dist=None, sqdist=None, indices=None, workspace=None, stream=None,
+          timed: bool = False):
+    """Exact EDT of a batch of volumes, mask (B, D, H, W) or (D, H, W) uint8.
+    Indices are flat within each volume."""
+    _check_mask(mask, (3, 4))
+    m4 = mask if mask.dim() == 4 else mask.unsqueeze(0)
+    B, D, H, W = m4.shape
+    shape = tuple(mask.shape)
+    dev = mask.device
+    sq = _out(sqdist, shape, torch.int32, dev, return_sqdist)
+    ds = _out(dist, shape, torch.float32, dev, return_distances)
+    ix = _out(indices, shape, torch.int32, dev, return_indices)
+    lib = _lib.load()
+    need = int(lib.edt3d_workspace_size(B, D, H, W))
+    if workspace is None:
+        workspace = alloc_workspace(need, dev)
+    samp = _sampling(sampling, 3)
+    args = [_ptr(m4), B, D, H, W, samp, _ptr(sq), _ptr(ds), _ptr(ix), _ptr(workspace),
+            workspace.numel() * workspace.element_size(), _stream(stream)]
+    if not timed:
+        st = lib.edt3d_u8_batched(*args)
+        if st != 0:
+            raise EDTError(st, "edt3d_u8_batched")
+        return EDTResult(sq, ds, ix)
+    ms = (ctypes.c_float * 8)()
+    names = (ctypes.c_char_p * 8)()
+    cnt = ctypes.c_int32(0)
+    st = lib.edt3d_u8_batched_timed(*args, ms, names, 8, ctypes.byref(cnt))
+    if st != 0:
+        raise EDTError(st, "edt3d_u8_batched_timed")
+    return EDTResult(sq, ds, ix), [(names[i].decode(), ms[i]) for i in range(cnt.value)]

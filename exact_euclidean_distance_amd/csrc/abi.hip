@@ -1,0 +1,252 @@
+// abi.hip -- host planner and C ABI of libedt_mi355x.so (declared in include/edt.h).
+//
+// Argument conventions are resolved here and only here (as TorchMorph keeps
+// argument handling in one validation layer); every check runs before the
+// first HIP call, so a rejected call touches no buffer.  The planner carves
+// the caller's workspace and enqueues the passes on the caller's stream:
+//   2-D:  axis-0 scan (3 kernels) -> row envelope + epilogue
+//   3-D:  axis-0 scan (3 kernels) -> axis-1 envelope -> axis-2 envelope + epilogue
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/edt.h"
+#include "kernels.h"
+
+namespace {
+
+constexpr int32_t kMaxExtent = 65535;
+constexpr int32_t kMaxW2D = 32768;
+constexpr int32_t kMaxH3D = 1024;
+constexpr int32_t kMaxW3D = 16384;
+constexpr size_t kAlign = 256;
+
+size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct Layout {
+    size_t c0 = 0, c01 = 0, first = 0, last = 0, total = 0;
+};
+
+bool shape2d_ok(int32_t H, int32_t W) {
+    if (H < 1 || W < 1 || H > kMaxExtent || W > kMaxExtent) return false;
+    if (W > kMaxW2D) return false;
+    if ((int64_t)H * W > INT32_MAX) return false;
+    return edt::rows_lds_bytes(W, 2) != 0;
+}
+
+bool shape3d_ok(int32_t B, int32_t D, int32_t H, int32_t W) {
+    if (B < 1 || D < 1 || H < 1 || W < 1) return false;
+    if (B > kMaxExtent || D > kMaxExtent || H > kMaxExtent || W > kMaxExtent) return false;
+    if (H > kMaxH3D || W > kMaxW3D) return false;
+    if ((int64_t)D * H * W > INT32_MAX) return false;
+    return edt::rows_lds_bytes(W, 4) != 0;
+}
+
+Layout layout2d(int32_t H, int32_t W) {
+    Layout L;
+    const size_t n = (size_t)H * W;
+    const size_t nseg = (size_t)(H + edt::kSegRows - 1) / edt::kSegRows;
+    L.c0 = 0;
+    L.first = round_up(n * 2);
+    L.last = L.first + round_up(nseg * W * 2);
+    L.total = L.last + round_up(nseg * W * 2);
+    return L;
+}
+
+Layout layout3d(int32_t B, int32_t D, int32_t H, int32_t W) {
+    Layout L;
+    const size_t n = (size_t)B * D * H * W;
+    const size_t nseg = (size_t)(D + edt::kSegRows - 1) / edt::kSegRows;
+    const size_t summ = (size_t)B * nseg * H * W * 2;
+    L.c0 = 0;
+    L.c01 = round_up(n * 2);
+    L.first = L.c01 + round_up(n * 4);
+    L.last = L.first + round_up(summ);
+    L.total = L.last + round_up(summ);
+    return L;
+}
+
+// Returns EDT_OK and the squared spacings, or the error for bad spacing.
+edt_status read_sampling(const float* sampling, int ndim, double* s2, bool* unit) {
+    *unit = true;
+    for (int k = 0; k < ndim; ++k) {
+        double s = 1.0;
+        if (sampling) {
+            const float f = sampling[k];
+            if (!(f > 0.0f) || !isfinite(f)) return EDT_ERR_INVALID_ARGUMENT;
+            s = (double)f;
+        }
+        if (s != 1.0) *unit = false;
+        s2[k] = s * s;
+    }
+    return EDT_OK;
+}
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+    if (!a || !b || na == 0 || nb == 0) return false;
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return x < y + nb && y < x + na;
+}
+
+// Common checks on outputs and workspace; n = total element count.
+edt_status check_buffers(const uint8_t* mask, size_t n, int32_t* sqdist, float* dist,
+                         int32_t* indices, void* ws, size_t ws_bytes, size_t ws_need) {
+    if (!mask) return EDT_ERR_INVALID_ARGUMENT;
+    if (!sqdist && !dist && !indices) return EDT_ERR_INVALID_ARGUMENT;
+    if (((uintptr_t)sqdist & 3) || ((uintptr_t)dist & 3) || ((uintptr_t)indices & 3))
+        return EDT_ERR_INVALID_ARGUMENT;
+    if (!ws || ((uintptr_t)ws & (kAlign - 1))) return EDT_ERR_INVALID_ARGUMENT;
+    if (ws_bytes < ws_need) return EDT_ERR_WORKSPACE_TOO_SMALL;
+    const void* bufs[5] = {mask, sqdist, dist, indices, ws};
+    const size_t sizes[5] = {n, sqdist ? n * 4 : 0, dist ? n * 4 : 0, indices ? n * 4 : 0, ws_need};
+    for (int i = 0; i < 5; ++i)
+        for (int j = i + 1; j < 5; ++j)
+            if (overlap(bufs[i], sizes[i], bufs[j], sizes[j])) return EDT_ERR_INVALID_ARGUMENT;
+    return EDT_OK;
+}
+
+edt_status run2d(const uint8_t* mask, int32_t H, int32_t W, const float* sampling,
+                 int32_t* sqdist, float* dist, int32_t* indices, void* ws, size_t ws_bytes,
+                 hipStream_t stream, edt::KernelTimer* tm) {
+    if (H < 1 || W < 1) return EDT_ERR_INVALID_ARGUMENT;
+    if (!shape2d_ok(H, W)) return EDT_ERR_UNSUPPORTED_SHAPE;
+    double s2[2];
+    bool unit;
+    edt_status st = read_sampling(sampling, 2, s2, &unit);
+    if (st != EDT_OK) return st;
+    if (sqdist && !unit) return EDT_ERR_INVALID_ARGUMENT;
+    if (sqdist && (double)H * H + (double)W * W > (double)INT32_MAX) return EDT_ERR_UNSUPPORTED_SHAPE;
+    const Layout L = layout2d(H, W);
+    st = check_buffers(mask, (size_t)H * W, sqdist, dist, indices, ws, ws_bytes, L.total);
+    if (st != EDT_OK) return st;
+
+    char* base = static_cast<char*>(ws);
+    uint16_t* c0 = reinterpret_cast<uint16_t*>(base + L.c0);
+    uint16_t* first = reinterpret_cast<uint16_t*>(base + L.first);
+    uint16_t* last = reinterpret_cast<uint16_t*>(base + L.last);
+    if (edt::launch_axis0(mask, 1, H, W, first, last, c0, stream, tm) != hipSuccess) return EDT_ERR_HIP;
+    if (edt::launch_rows_2d(c0, H, W, s2[0], s2[1], sqdist, dist, indices, stream, tm) != hipSuccess)
+        return EDT_ERR_HIP;
+    return EDT_OK;
+}
+
+edt_status run3d(const uint8_t* mask, int32_t B, int32_t D, int32_t H, int32_t W,
+                 const float* sampling, int32_t* sqdist, float* dist, int32_t* indices,
+                 void* ws, size_t ws_bytes, hipStream_t stream, edt::KernelTimer* tm) {
+    if (B < 1 || D < 1 || H < 1 || W < 1) return EDT_ERR_INVALID_ARGUMENT;
+    if (!shape3d_ok(B, D, H, W)) return EDT_ERR_UNSUPPORTED_SHAPE;
+    double s2[3];
+    bool unit;
+    edt_status st = read_sampling(sampling, 3, s2, &unit);
+    if (st != EDT_OK) return st;
+    if (sqdist && !unit) return EDT_ERR_INVALID_ARGUMENT;
+    if (sqdist && (double)D * D + (double)H * H + (double)W * W > (double)INT32_MAX)
+        return EDT_ERR_UNSUPPORTED_SHAPE;
+    const Layout L = layout3d(B, D, H, W);
+    st = check_buffers(mask, (size_t)B * D * H * W, sqdist, dist, indices, ws, ws_bytes, L.total);
+    if (st != EDT_OK) return st;
+
+    char* base = static_cast<char*>(ws);
+    uint16_t* c0 = reinterpret_cast<uint16_t*>(base + L.c0);
+    uint32_t* c01 = reinterpret_cast<uint32_t*>(base + L.c01);
+    uint16_t* first = reinterpret_cast<uint16_t*>(base + L.first);
+    uint16_t* last = reinterpret_cast<uint16_t*>(base + L.last);
+    if (edt::launch_axis0(mask, B, D, (int64_t)H * W, first, last, c0, stream, tm) != hipSuccess)
+        return EDT_ERR_HIP;
+    if (edt::launch_cols_3d(c0, B, D, H, W, s2[0], s2[1], c01, stream, tm) != hipSuccess)
+        return EDT_ERR_HIP;
+    if (edt::launch_rows_3d(c01, B, D, H, W, s2[0], s2[1], s2[2], sqdist, dist, indices, stream, tm) !=
+        hipSuccess)
+        return EDT_ERR_HIP;
+    return EDT_OK;
+}
+
+edt_status finish_timed(edt_status st, edt::KernelTimer& tm, hipStream_t stream, float* kernel_ms,
+                        const char** kernel_names, int32_t* count) {
+    if (st == EDT_OK && hipStreamSynchronize(stream) != hipSuccess) st = EDT_ERR_HIP;
+    for (int i = 0; i < tm.n; ++i) {
+        float ms = 0.0f;
+        if (st == EDT_OK && hipEventElapsedTime(&ms, tm.ev[2 * i], tm.ev[2 * i + 1]) != hipSuccess)
+            st = EDT_ERR_HIP;
+        if (st == EDT_OK) {
+            kernel_ms[i] = ms;
+            if (kernel_names) kernel_names[i] = tm.name[i];
+        }
+    }
+    for (int i = 0; i < tm.created; ++i) {
+        (void)hipEventDestroy(tm.ev[2 * i]);
+        (void)hipEventDestroy(tm.ev[2 * i + 1]);
+    }
+    if (st == EDT_OK && !tm.ok) st = EDT_ERR_INVALID_ARGUMENT;
+    if (count) *count = (st == EDT_OK) ? tm.n : 0;
+    return st;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t edt2d_workspace_size(int32_t H, int32_t W) {
+    if (!shape2d_ok(H, W)) return 0;
+    return layout2d(H, W).total;
+}
+
+size_t edt3d_workspace_size(int32_t B, int32_t D, int32_t H, int32_t W) {
+    if (!shape3d_ok(B, D, H, W)) return 0;
+    return layout3d(B, D, H, W).total;
+}
+
+edt_status edt2d_u8(const uint8_t* mask, int32_t H, int32_t W, const float* sampling,
+                    int32_t* sqdist, float* dist, int32_t* indices, void* workspace,
+                    size_t workspace_bytes, hipStream_t stream) {
+    return run2d(mask, H, W, sampling, sqdist, dist, indices, workspace, workspace_bytes, stream,
+                 nullptr);
+}
+
+edt_status edt3d_u8_batched(const uint8_t* mask, int32_t B, int32_t D, int32_t H, int32_t W,
+                            const float* sampling, int32_t* sqdist, float* dist, int32_t* indices,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    return run3d(mask, B, D, H, W, sampling, sqdist, dist, indices, workspace, workspace_bytes,
+                 stream, nullptr);
+}
+
+edt_status edt2d_u8_timed(const uint8_t* mask, int32_t H, int32_t W, const float* sampling,
+                          int32_t* sqdist, float* dist, int32_t* indices, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream, float* kernel_ms,
+                          const char** kernel_names, int32_t capacity, int32_t* count) {
+    if (!kernel_ms || capacity < 1) return EDT_ERR_INVALID_ARGUMENT;
+    edt::KernelTimer tm;
+    tm.capacity = capacity;
+    edt_status st = run2d(mask, H, W, sampling, sqdist, dist, indices, workspace, workspace_bytes,
+                          stream, &tm);
+    return finish_timed(st, tm, stream, kernel_ms, kernel_names, count);
+}
+
+edt_status edt3d_u8_batched_timed(const uint8_t* mask, int32_t B, int32_t D, int32_t H,
+                                  int32_t W, const float* sampling, int32_t* sqdist, float* dist,
+                                  int32_t* indices, void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream, float* kernel_ms, const char** kernel_names,
+                                  int32_t capacity, int32_t* count) {
+    if (!kernel_ms || capacity < 1) return EDT_ERR_INVALID_ARGUMENT;
+    edt::KernelTimer tm;
+    tm.capacity = capacity;
+    edt_status st = run3d(mask, B, D, H, W, sampling, sqdist, dist, indices, workspace,
+                          workspace_bytes, stream, &tm);
+    return finish_timed(st, tm, stream, kernel_ms, kernel_names, count);
+}
+
+const char* edt_status_string(edt_status status) {
+    switch (status) {
+        case EDT_OK: return "EDT_OK";
+        case EDT_ERR_INVALID_ARGUMENT: return "EDT_ERR_INVALID_ARGUMENT";
+        case EDT_ERR_UNSUPPORTED_SHAPE: return "EDT_ERR_UNSUPPORTED_SHAPE";
+        case EDT_ERR_WORKSPACE_TOO_SMALL: return "EDT_ERR_WORKSPACE_TOO_SMALL";
+        case EDT_ERR_HIP: return "EDT_ERR_HIP";
+    }
+    return "EDT_ERR_UNKNOWN";
+}
+
+const char* edt_version(void) { return "0.1.0"; }
+
+}  // extern "C"

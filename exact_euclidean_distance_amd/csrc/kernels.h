@@ -1,0 +1,55 @@
+// kernels.h -- internal launch interface between the host planner (abi.hip)
+// and the gfx950 kernels (kernels.hip).  Not part of the public C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace edt {
+
+constexpr uint16_t kNone16 = 0xFFFFu;
+constexpr uint32_t kNone32 = 0xFFFFFFFFu;
+constexpr int kSegRows = 64;   // rows per segment of the axis-0 scan
+
+// Records a HIP event pair around each kernel when non-null (measurement only).
+struct KernelTimer {
+    static constexpr int kMax = 8;
+    hipEvent_t ev[2 * kMax];
+    const char* name[kMax];
+    int n = 0;         // completed event pairs
+    int created = 0;   // event pairs created (destroy all of them)
+    int capacity = 0;
+    bool ok = true;
+    hipError_t begin(const char* kname, hipStream_t s);
+    hipError_t end(hipStream_t s);
+};
+
+// Axis-0 pass: for every line along axis 0 (B images of n0 x M elements), the
+// axis-0 coordinate of the nearest background element on that line (kNone16 if
+// the line has none).  first/last: workspace of B * nseg * M uint16 each.
+hipError_t launch_axis0(const uint8_t* mask, int B, int n0, int64_t M,
+                        uint16_t* first, uint16_t* last, uint16_t* c0,
+                        hipStream_t s, KernelTimer* tm);
+
+// Envelope pass along the last axis of a 2-D image (lines = rows of length W).
+hipError_t launch_rows_2d(const uint16_t* c0, int H, int W, double s2_0, double s2_1,
+                          int32_t* sqdist, float* dist, int32_t* indices,
+                          hipStream_t s, KernelTimer* tm);
+
+// Envelope pass along axis 1 of B volumes (lines of length H at fixed (d, w));
+// writes the packed nearest coordinates (axis0 << 16 | axis1), kNone32 if none.
+hipError_t launch_cols_3d(const uint16_t* c0, int B, int D, int H, int W,
+                          double s2_0, double s2_1, uint32_t* c01,
+                          hipStream_t s, KernelTimer* tm);
+
+// Envelope pass along axis 2 of B volumes (lines of length W) with the epilogue.
+hipError_t launch_rows_3d(const uint32_t* c01, int B, int D, int H, int W,
+                          double s2_0, double s2_1, double s2_2,
+                          int32_t* sqdist, float* dist, int32_t* indices,
+                          hipStream_t s, KernelTimer* tm);
+
+// Dynamic LDS each envelope launch needs (0 if the line is too long).
+size_t rows_lds_bytes(int L, int value_bytes);
+size_t cols_lds_bytes(int H);
+
+}  // namespace edt

@@ -1,0 +1,131 @@
+/*
+ * edt.h -- exact Euclidean distance transform for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libedt_mi355x.so.  Plain pointers and sizes only.
+ *
+ * The transform ("GPU-Based Parallel Euclidean Distance Transform Algorithm",
+ * Mathematics 14(4), §1 Introduction): every element of a binary image gets
+ * the Euclidean distance to its nearest background element and, on request,
+ * the index of that element (the discrete Voronoi / feature transform).  It is
+ * computed exactly by the separable lower-envelope-of-parabolas method
+ * (TorchMorph, the paragraph on the separable lower-envelope EDT): one
+ * nearest-background scan along axis 0, then one lower-envelope pass per
+ * remaining axis.  Keyword semantics (grid spacing `sampling`, distances
+ * and/or indices, caller-preallocated outputs) follow TorchMorph's
+ * SciPy-compatible distance-transform interface.
+ *
+ * Conventions shared by every entry point
+ *   mask       device pointer, uint8, C-contiguous; 0 = background, any other
+ *              value = foreground.  Any alignment.
+ *   sampling   HOST pointer to one positive float per axis (axis order of the
+ *              array), or NULL for unit spacing.  sampling[k] scales axis k.
+ *   sqdist     device int32 [N] or NULL: exact squared distance.  Only with
+ *              unit spacing (sampling NULL or all 1.0f).
+ *   dist       device float [N] or NULL: sqrt of the squared distance,
+ *              rounded to float32 (error <= 1 ulp of the float32 result).
+ *   indices    device int32 [N] or NULL: row-major flat index, within the same
+ *              image/volume, of a nearest background element.  Where several
+ *              are equally near, any one of them may be returned.
+ *   At least one of sqdist / dist / indices must be non-NULL.  Outputs are
+ *   4-byte aligned, C-contiguous, and alias neither the mask, each other, nor
+ *   the workspace.
+ *   workspace  device buffer of at least *_workspace_size() bytes, 256-byte
+ *              aligned, owned by the caller; its contents on entry do not
+ *              matter and on return are unspecified.
+ *   stream     HIP stream the kernels are enqueued on (NULL = default stream).
+ *              The call returns after enqueueing; it never synchronizes.
+ *
+ * No background.  An image/volume without any background element is handled
+ * with a virtual background element at coordinates (-1, 0, ..., 0), the
+ * convention SciPy follows (TorchMorph defers to it): its squared distance is
+ * s0^2 (p0+1)^2 + sum_k sk^2 pk^2 and its index is -(n1 * ... * n_{d-1}).
+ *
+ * Ownership and threading.  The library allocates no device memory and keeps
+ * no state between calls; concurrent calls with distinct buffers are safe.
+ *
+ * Errors.  Argument errors are detected on the host before any HIP call and
+ * return without touching any buffer.  EDT_ERR_HIP means a kernel launch was
+ * rejected (hipGetLastError after the launch); outputs are then unspecified.
+ *
+ * Limits.  Every extent in [1, 65535]; elements per image/volume <= 2^31-1;
+ * when sqdist is requested the largest possible squared distance
+ * (sum of extent^2) must fit in int32.  The lower envelope of a line is kept in
+ * LDS, which bounds the line lengths of the envelope passes:
+ *   2-D: W <= 32768;  3-D: H <= 1024 and W <= 16384.
+ * Shapes beyond the limits return EDT_ERR_UNSUPPORTED_SHAPE.
+ */
+#ifndef EDT_MI355X_H
+#define EDT_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* hipStream_t;
+
+typedef enum edt_status {
+    EDT_OK = 0,
+    EDT_ERR_INVALID_ARGUMENT = 1,    /* NULL mask, no output, bad spacing, sqdist with
+                                        non-unit spacing, misaligned output/workspace */
+    EDT_ERR_UNSUPPORTED_SHAPE = 2,   /* extent or element count beyond the limits */
+    EDT_ERR_WORKSPACE_TOO_SMALL = 3, /* workspace_bytes < *_workspace_size(...) */
+    EDT_ERR_HIP = 4                  /* a kernel launch failed */
+} edt_status;
+
+/* Bytes of workspace edt2d_u8 needs for an H x W image (0 if the shape is
+   outside the limits). */
+size_t edt2d_workspace_size(int32_t H, int32_t W);
+
+/* 2-D transform of one H x W image (row-major, axis 0 = rows).  sampling is
+   {s_rows, s_cols} or NULL. */
+edt_status edt2d_u8(const uint8_t* mask, int32_t H, int32_t W,
+                    const float* sampling,
+                    int32_t* sqdist, float* dist, int32_t* indices,
+                    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace edt3d_u8_batched needs for B volumes of D x H x W. */
+size_t edt3d_workspace_size(int32_t B, int32_t D, int32_t H, int32_t W);
+
+/* 3-D transform of B independent volumes, each D x H x W, stored back to back
+   ([B][D][H][W]).  sampling is {s_D, s_H, s_W} or NULL.  indices are flat
+   within each volume (d*H*W + h*W + w). */
+edt_status edt3d_u8_batched(const uint8_t* mask, int32_t B, int32_t D, int32_t H, int32_t W,
+                            const float* sampling,
+                            int32_t* sqdist, float* dist, int32_t* indices,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Same as edt2d_u8 / edt3d_u8_batched, for measurement: records a HIP event
+   pair around every kernel it enqueues, waits for the stream, and returns each
+   kernel's duration in milliseconds (launch order) in kernel_ms[0..*count) and
+   its name in kernel_names[] (static strings; may be NULL).  Fails with
+   EDT_ERR_INVALID_ARGUMENT if capacity is smaller than the number of kernels
+   (at most 8).  Results are identical to the untimed call. */
+edt_status edt2d_u8_timed(const uint8_t* mask, int32_t H, int32_t W,
+                          const float* sampling,
+                          int32_t* sqdist, float* dist, int32_t* indices,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream,
+                          float* kernel_ms, const char** kernel_names,
+                          int32_t capacity, int32_t* count);
+
+edt_status edt3d_u8_batched_timed(const uint8_t* mask, int32_t B, int32_t D, int32_t H,
+                                  int32_t W, const float* sampling,
+                                  int32_t* sqdist, float* dist, int32_t* indices,
+                                  void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream, float* kernel_ms,
+                                  const char** kernel_names, int32_t capacity,
+                                  int32_t* count);
+
+/* Human-readable name of a status code (static string). */
+const char* edt_status_string(edt_status status);
+
+/* Library version, as "major.minor.patch". */
+const char* edt_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EDT_MI355X_H */

@@ -1,0 +1,121 @@
+"""CPU tests of the C ABI boundary: the library loads, exports every symbol the
+header declares, and rejects bad arguments on the host before any HIP call
+(so these run without a GPU; the pointers below are never dereferenced)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from exact_euclidean_distance_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "edt.h")
+
+OK, INVALID, SHAPE, SMALL, HIP = 0, 1, 2, 3, 4
+# fake, aligned device addresses in disjoint ranges (never dereferenced)
+MASK, SQ, DIST, IDX, WS = 0x10000000, 0x20000000, 0x30000000, 0x40000000, 0x50000000
+BIG = 1 << 40
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(edt\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == set(_lib.EXPORTS), names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for code, name in _lib.STATUS.items():
+        assert lib.edt_status_string(code).decode() == name
+    assert lib.edt_version().decode().count(".") == 2
+
+
+def test_workspace_sizes(lib):
+    assert lib.edt2d_workspace_size(512, 512) >= 512 * 512 * 2
+    assert lib.edt3d_workspace_size(16, 128, 128, 128) >= 16 * 128 ** 3 * 6
+    assert lib.edt2d_workspace_size(0, 5) == 0
+    assert lib.edt2d_workspace_size(5, 40000) == 0
+    assert lib.edt2d_workspace_size(70000, 5) == 0
+    assert lib.edt3d_workspace_size(1, 8, 2000, 8) == 0
+    assert lib.edt3d_workspace_size(1, 8, 8, 20000) == 0
+    assert lib.edt3d_workspace_size(1, 65535, 1024, 64) == 0    # > 2^31-1 elements
+
+
+def call2d(lib, mask=MASK, H=64, W=64, sampling=None, sq=SQ, dist=DIST, idx=IDX, ws=WS,
+           ws_bytes=BIG):
+    samp = None if sampling is None else (ctypes.c_float * 2)(*sampling)
+    return lib.edt2d_u8(mask, H, W, samp, sq, dist, idx, ws, ws_bytes, None)
+
+
+def call3d(lib, mask=MASK, B=2, D=8, H=8, W=8, sampling=None, sq=SQ, dist=DIST, idx=IDX, ws=WS,
+           ws_bytes=BIG):
+    samp = None if sampling is None else (ctypes.c_float * 3)(*sampling)
+    return lib.edt3d_u8_batched(mask, B, D, H, W, samp, sq, dist, idx, ws, ws_bytes, None)
+
+
+def test_2d_argument_errors(lib):
+    assert call2d(lib, mask=None) == INVALID
+    assert call2d(lib, H=0) == INVALID
+    assert call2d(lib, W=-3) == INVALID
+    assert call2d(lib, H=70000) == SHAPE
+    assert call2d(lib, W=40000) == SHAPE
+    assert call2d(lib, H=65535, W=32768) == SHAPE           # > 2^31-1 elements
+    assert call2d(lib, sq=None, dist=None, idx=None) == INVALID
+    assert call2d(lib, sampling=(2.0, 1.0)) == INVALID      # sqdist needs unit spacing
+    assert call2d(lib, sampling=(0.0, 1.0), sq=None) == INVALID
+    assert call2d(lib, sampling=(-1.0, 1.0), sq=None) == INVALID
+    assert call2d(lib, sampling=(float("nan"), 1.0), sq=None) == INVALID
+    assert call2d(lib, sampling=(float("inf"), 1.0), sq=None) == INVALID
+    assert call2d(lib, ws=None) == INVALID
+    assert call2d(lib, ws=WS + 16) == INVALID               # workspace not 256-byte aligned
+    assert call2d(lib, ws_bytes=lib.edt2d_workspace_size(64, 64) - 1) == SMALL
+    assert call2d(lib, sq=SQ + 2) == INVALID                # misaligned output
+    assert call2d(lib, dist=WS + 256) == INVALID            # output inside the workspace
+    assert call2d(lib, idx=SQ) == INVALID                   # outputs alias each other
+    assert call2d(lib, sq=MASK) == INVALID                  # output aliases the mask
+    assert call2d(lib, H=50000, W=50000, sampling=None, dist=None, idx=None) == SHAPE
+
+
+def test_3d_argument_errors(lib):
+    assert call3d(lib, mask=None) == INVALID
+    assert call3d(lib, B=0) == INVALID
+    assert call3d(lib, D=0) == INVALID
+    assert call3d(lib, H=2000) == SHAPE
+    assert call3d(lib, W=20000) == SHAPE
+    assert call3d(lib, D=70000) == SHAPE
+    assert call3d(lib, sq=None, dist=None, idx=None) == INVALID
+    assert call3d(lib, sampling=(2.5, 1.0, 1.0)) == INVALID
+    assert call3d(lib, sampling=(2.5, 0.0, 1.0), sq=None) == INVALID
+    assert call3d(lib, ws=None) == INVALID
+    assert call3d(lib, ws_bytes=lib.edt3d_workspace_size(2, 8, 8, 8) - 1) == SMALL
+    assert call3d(lib, idx=IDX + 1) == INVALID
+    assert call3d(lib, dist=WS) == INVALID
+
+
+def test_timed_entry_rejects_without_buffer(lib):
+    cnt = ctypes.c_int32(0)
+    st = lib.edt2d_u8_timed(MASK, 8, 8, None, SQ, DIST, IDX, WS, BIG, None,
+                            None, None, 8, ctypes.byref(cnt))
+    assert st == INVALID
+
+
+def test_python_binding_refuses_cpu_tensors():
+    import torch
+    from exact_euclidean_distance_amd import edt2d
+    with pytest.raises(ValueError):
+        edt2d(torch.zeros((4, 4), dtype=torch.uint8))
+    with pytest.raises(TypeError):
+        edt2d(torch.zeros((4, 4), dtype=torch.float32))

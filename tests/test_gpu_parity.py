@@ -1,0 +1,221 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Integer squared distances must match bit for bit (unit spacing); float32
+distances within 1e-6 relative (unit spacing) / 1e-5 (anisotropic); every
+returned index must attain the oracle's minimum exactly (ties are legal).
+Outputs are poisoned before each call so unwritten elements are caught.
+"""
+
+import os
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from gpu_check import compare
+from golden_io import load as load_golden, names as golden_names
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch_dev():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    from exact_euclidean_distance_amd import _lib
+    _lib.load()
+    return torch, torch.device("cuda:0")
+
+
+def _say(msg):
+    sys.stdout.write(msg + "\n")
+    sys.stdout.flush()
+
+
+def run_gpu(torch_dev, mask, sampling=None, want=("sqdist", "dist", "indices"), offset=0):
+    """Run the transform on ``mask`` (2-D, or 4-D batch of volumes); returns
+    numpy outputs.  ``offset`` > 0 places the mask at a misaligned address."""
+    torch, dev = torch_dev
+    from exact_euclidean_distance_amd import edt2d, edt3d
+    flat = torch.from_numpy(np.ascontiguousarray(mask).reshape(-1))
+    if offset:
+        buf = torch.empty(flat.numel() + offset, dtype=torch.uint8, device=dev)
+        buf[offset:].copy_(flat)
+        m = buf[offset:].view(mask.shape)
+    else:
+        m = flat.to(dev).view(mask.shape)
+    shape = mask.shape
+    sq = torch.full(shape, -7, dtype=torch.int32, device=dev) if "sqdist" in want else None
+    ds = torch.full(shape, float("nan"), dtype=torch.float32, device=dev) if "dist" in want else None
+    ix = torch.full(shape, -7, dtype=torch.int32, device=dev) if "indices" in want else None
+    fn = edt2d if mask.ndim == 2 else edt3d
+    fn(m, sampling, sqdist=sq, dist=ds, indices=ix, return_distances=ds is not None)
+    torch.cuda.synchronize()
+    out = {}
+    for k, t in (("sqdist", sq), ("dist", ds), ("indices", ix)):
+        if t is not None:
+            out[k] = t.cpu().numpy()
+    return out
+
+
+def check(torch_dev, mask, sampling=None, want=None, offset=0, ref=None):
+    iso = sampling is None or all(float(s) == 1.0 for s in sampling)
+    if want is None:
+        want = ("sqdist", "dist", "indices") if iso else ("dist", "indices")
+    out = run_gpu(torch_dev, mask, sampling, want, offset)
+    if ref is None:
+        if mask.ndim == 2:
+            ref, _ = oracle.edt(mask, sampling, features=False)
+        else:
+            ref, _ = oracle.edt_batch(mask, sampling, features=False)
+    compare(mask, sampling, ref, out.get("sqdist"), out.get("dist"), out.get("indices"),
+            batch=(mask.ndim == 4))
+    return out
+
+
+# ---------------------------------------------------------------- small cases
+
+SHAPES_2D = [(1, 1), (1, 37), (37, 1), (2, 2), (63, 65), (64, 64), (65, 130), (200, 333),
+             (129, 1031), (3, 4100), (700, 7), (130, 257)]
+
+
+@pytest.mark.parametrize("shape", SHAPES_2D)
+def test_random_2d(torch_dev, shape):
+    rng = np.random.default_rng([42, 3000, shape[0], shape[1]])
+    for p in (0.001, 0.05, 0.5, 0.97):
+        mask = (rng.random(shape) >= p).astype(np.uint8)
+        if not (mask == 0).any():
+            mask.reshape(-1)[rng.integers(0, mask.size)] = 0
+        _say(f"2d {shape} p={p}")
+        check(torch_dev, mask)
+        check(torch_dev, mask, (2.5, 1.0))
+        check(torch_dev, mask, (1.0, 0.75))
+
+
+SHAPES_3D = [(1, 1, 1, 1), (2, 5, 7, 9), (1, 1, 33, 70), (1, 70, 1, 33), (1, 66, 40, 1),
+             (3, 40, 33, 65), (1, 130, 65, 100), (2, 9, 520, 17), (1, 5, 17, 600)]
+
+
+@pytest.mark.parametrize("shape", SHAPES_3D)
+def test_random_3d(torch_dev, shape):
+    rng = np.random.default_rng([42, 3001, *shape])
+    for p in (0.002, 0.1, 0.9):
+        mask = (rng.random(shape) >= p).astype(np.uint8)
+        for b in range(shape[0]):
+            if not (mask[b] == 0).any():
+                mask[b].reshape(-1)[0] = 0
+        _say(f"3d {shape} p={p}")
+        check(torch_dev, mask)
+        check(torch_dev, mask, (2.5, 1.0, 1.0))
+        check(torch_dev, mask, (1.0, 2.0, 0.5))
+
+
+@pytest.mark.parametrize("name", golden_names())
+def test_golden_fixtures(torch_dev, name):
+    g = load_golden(name)
+    mask = g["mask"]
+    if mask.ndim == 3:
+        mask = mask[None]
+        ref = g["sqdist"][None]
+    elif mask.ndim == 2:
+        ref = g["sqdist"]
+    else:
+        pytest.skip("1-D fixture")
+    check(torch_dev, mask, g["sampling"], ref=ref)
+
+
+# ---------------------------------------------------------------- edge cases
+
+def test_edge_cases_2d(torch_dev):
+    rng = np.random.default_rng([42, 3002])
+    # all background / no background (virtual element at (-1, 0))
+    check(torch_dev, np.zeros((70, 90), np.uint8))
+    check(torch_dev, np.ones((70, 90), np.uint8))
+    check(torch_dev, np.ones((3, 4), np.uint8), (2.0, 1.0))
+    # a single background pixel: closed form
+    mask = np.ones((300, 500), np.uint8)
+    mask[299, 0] = 0
+    out = check(torch_dev, mask)
+    yy, xx = np.indices(mask.shape)
+    np.testing.assert_array_equal(out["sqdist"], (yy - 299) ** 2 + xx ** 2)
+    assert (out["indices"] == 299 * 500).all()
+    # one full background row: every candidate on every envelope
+    mask = np.ones((257, 1500), np.uint8)
+    mask[100] = 0
+    check(torch_dev, mask)
+    # misaligned mask address and widths not a multiple of 4 / 16
+    for shape in [(100, 64), (100, 36), (90, 33)]:
+        mask = (rng.random(shape) >= 0.05).astype(np.uint8)
+        mask[0, 0] = 0
+        check(torch_dev, mask, offset=1)
+        check(torch_dev, mask, offset=4)
+    # longest supported row
+    mask = (rng.random((5, 32768)) >= 0.001).astype(np.uint8)
+    mask[2, 5] = 0
+    check(torch_dev, mask)
+    # background only in the last row / first column
+    mask = np.ones((1000, 300), np.uint8)
+    mask[-1, -1] = 0
+    mask[0, 0] = 0
+    check(torch_dev, mask)
+
+
+def test_edge_cases_3d(torch_dev):
+    rng = np.random.default_rng([42, 3003])
+    mask = (rng.random((3, 20, 30, 40)) >= 0.01).astype(np.uint8)
+    mask[1] = 1       # a volume without background inside a batch
+    mask[0, 0, 0, 0] = 0
+    mask[2, 19, 29, 39] = 0
+    check(torch_dev, mask)
+    check(torch_dev, mask, (2.5, 1.0, 1.0))
+    # longest supported middle line (K=64 column layout) and last line
+    mask = (rng.random((1, 3, 1024, 70)) >= 0.002).astype(np.uint8)
+    mask[0, 1, 5, 5] = 0
+    check(torch_dev, mask)
+    mask = (rng.random((1, 2, 3, 16384)) >= 0.001).astype(np.uint8)
+    mask[0, 1, 1, 1] = 0
+    check(torch_dev, mask)
+    # full background plane across axis 1 (all envelopes full)
+    mask = np.ones((2, 30, 50, 70), np.uint8)
+    mask[:, :, 17, :] = 0
+    check(torch_dev, mask)
+
+
+def test_repeat_is_bit_identical(torch_dev):
+    from workloads import make_config
+    mask, _, _ = make_config("c1")
+    a = run_gpu(torch_dev, mask)
+    b = run_gpu(torch_dev, mask)
+    for k in a:
+        np.testing.assert_array_equal(a[k], b[k])
+
+
+# ---------------------------------------------------------------- full sizes
+
+# outputs as timed by bench.py for each workload
+BENCH_OUTPUTS = {
+    "c1": ("sqdist", "dist", "indices"),
+    "c2a": ("sqdist", "dist", "indices"),
+    "c2b": ("sqdist", "dist", "indices"),
+    "c3": ("sqdist", "dist"),
+    "c4": ("dist",),
+    "c5": ("dist", "indices"),
+}
+
+
+@pytest.mark.parametrize("name", ["c1", "c2a", "c2b", "c4", "c5", "c3"])
+def test_full_size_config(torch_dev, name):
+    from workloads import make_config
+    _say(f"config {name}: generating")
+    mask, sampling, meta = make_config(name)
+    _say(f"config {name}: GPU + oracle {mask.shape}")
+    out = check(torch_dev, mask, sampling, want=BENCH_OUTPUTS[name])
+    if name == "c2b":
+        r0, c0 = meta["bg"]
+        yy, xx = np.indices(mask.shape)
+        np.testing.assert_array_equal(out["sqdist"], (yy - r0) ** 2 + (xx - c0) ** 2)
+        assert (out["indices"] == r0 * mask.shape[1] + c0).all()
+    if name == "c4":
+        # the timed call returns distances only; a second call checks sqdist exactly
+        check(torch_dev, mask, sampling, want=("sqdist", "indices"))

@@ -1,0 +1,156 @@
+"""CPU checks of the envelope algorithm the kernels run.
+
+tests/host_model/host_model.cpp compiles the device helpers of
+exact_euclidean_distance_amd/csrc/envelope.h as host C++ and drives them in the
+kernels' phase order (chunk envelopes -> merge tree -> first owned chunk ->
+walk).  Here that model is checked against the definition of a 1-D pass
+(brute force over all candidates) and, composed into full transforms, against
+the oracle.  No GPU is needed.
+"""
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "host_model", "host_model.cpp")
+
+
+@pytest.fixture(scope="module")
+def model(tmp_path_factory):
+    out = str(tmp_path_factory.mktemp("host_model") / "host_model.so")
+    subprocess.run(["g++", "-O2", "-std=c++17", "-fPIC", "-shared", "-o", out, SRC], check=True)
+    lib = ctypes.CDLL(out)
+    lib.model_envelope_lines.restype = ctypes.c_int
+    lib.model_envelope_lines.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+                                         ctypes.c_double, ctypes.c_int, ctypes.c_int,
+                                         ctypes.c_void_p]
+
+    def run(fb, s2l, K, G):
+        fb = np.ascontiguousarray(fb, np.float64)
+        nl, L = fb.shape
+        own = np.empty((nl, L), np.int32)
+        rc = lib.model_envelope_lines(fb.ctypes.data, nl, L, s2l, K, G, own.ctypes.data)
+        assert rc == 0
+        return own
+
+    return run
+
+
+def _brute_lines(fb, s2l):
+    L = fb.shape[1]
+    q = np.arange(L, dtype=np.float64)
+    vals = s2l * (q[:, None] - q[None, :]) ** 2 + fb[:, None, :]   # [line][q][j]
+    return vals.min(-1)
+
+
+def _value_at(fb, own, s2l):
+    q = np.arange(fb.shape[1])
+    sel = np.take_along_axis(fb, np.maximum(own, 0), 1)
+    v = s2l * (q[None, :] - own).astype(np.float64) ** 2 + sel
+    return np.where(own < 0, np.inf, v)
+
+
+def _layouts(L):
+    out = []
+    for K in (32, 64):
+        g0 = -(-L // K)
+        p2 = 1 << max(0, (g0 - 1).bit_length())
+        out += [(K, g0), (K, p2), (K, g0 + 3)]
+    return out
+
+
+@pytest.mark.parametrize("L", [1, 2, 31, 32, 33, 64, 100, 257, 1000, 4096])
+def test_lines_match_definition(model, L):
+    rng = np.random.default_rng([42, 2000, L])
+    nl = 24
+    fb = np.empty((nl, L))
+    for i in range(nl):
+        kind = i % 6
+        if kind == 0:      # squared column distances, some columns without background
+            g = rng.integers(0, 3 * L + 1, L).astype(np.float64)
+            fb[i] = g * g
+            fb[i][rng.random(L) < 0.3] = np.inf
+        elif kind == 1:    # all equal: every candidate on the envelope
+            fb[i] = float(rng.integers(0, 50)) ** 2
+        elif kind == 2:    # a single candidate
+            fb[i] = np.inf
+            fb[i][rng.integers(0, L)] = float(rng.integers(0, 100))
+        elif kind == 3:    # no candidate
+            fb[i] = np.inf
+        elif kind == 4:    # deep dip at the end: long removal cascades at junctions
+            fb[i] = float(L) ** 2
+            fb[i][-1] = 0.0
+        else:              # random small integers (many ties)
+            fb[i] = rng.integers(0, 4, L).astype(np.float64)
+    for s2l in (1.0, 6.25):
+        ref = _brute_lines(fb, s2l)
+        for K, G in _layouts(L):
+            own = model(fb, s2l, K, G)
+            got = _value_at(fb, own, s2l)
+            np.testing.assert_array_equal(got, ref, err_msg=f"L={L} K={K} G={G} s2={s2l}")
+            has = np.isfinite(fb)
+            ok = own >= 0
+            assert (ok == has.any(1)[:, None]).all()
+            assert np.isfinite(np.take_along_axis(fb, np.maximum(own, 0), 1)[ok]).all()
+
+
+def _axis0_nearest(mask):
+    """Nearest background along axis 0 (the smaller coordinate on ties); -1 if none."""
+    n0 = mask.shape[0]
+    i = np.arange(n0).reshape((n0,) + (1,) * (mask.ndim - 1))
+    big = 1 << 30
+    up = np.maximum.accumulate(np.where(mask == 0, i, -1), axis=0)
+    dn = np.flip(np.minimum.accumulate(np.flip(np.where(mask == 0, i, big), 0), axis=0), 0)
+    use_up = (up >= 0) & ((dn >= big) | (i - up <= dn - i))
+    g = np.where(use_up, up, np.where(dn < big, dn, -1))
+    return g
+
+
+def _model_edt(model, mask, sampling, K):
+    """Full transform composed from the model: axis-0 nearest, then one
+    envelope pass per further axis (values are squared distances so far)."""
+    s2 = np.ones(mask.ndim) if sampling is None else np.asarray(sampling, np.float64) ** 2
+    g = _axis0_nearest(mask)
+    i = np.arange(mask.shape[0]).reshape((mask.shape[0],) + (1,) * (mask.ndim - 1))
+    F = np.where(g >= 0, s2[0] * (i - g).astype(np.float64) ** 2, np.inf)
+    for ax in range(1, mask.ndim):
+        Fm = np.moveaxis(F, ax, -1)
+        shp = Fm.shape
+        fb = Fm.reshape(-1, shp[-1])
+        L = shp[-1]
+        G = -(-L // K)
+        own = model(fb, s2[ax], K, G)
+        F = np.moveaxis(_value_at(fb, own, s2[ax]).reshape(shp), -1, ax)
+    return F
+
+
+@pytest.mark.parametrize("K", [32, 64])
+def test_model_transform_matches_oracle(model, K):
+    rng = np.random.default_rng([42, 2001, K])
+    cases = []
+    for t in range(16):
+        shape = tuple(int(x) for x in rng.integers(1, 200, 2))
+        mask = (rng.random(shape) >= [1e-3, 0.01, 0.2, 0.9][t % 4]).astype(np.uint8)
+        cases.append((mask, [None, (2.5, 1.0)][t % 2]))
+    full_row = np.ones((150, 300), np.uint8)
+    full_row[77] = 0
+    cases.append((full_row, None))
+    single = np.ones((130, 170), np.uint8)
+    single[3, 160] = 0
+    cases.append((single, None))
+    for t in range(6):
+        shape = tuple(int(x) for x in rng.integers(1, 40, 3))
+        mask = (rng.random(shape) >= [0.001, 0.05, 0.5][t % 3]).astype(np.uint8)
+        cases.append((mask, [None, (2.5, 1.0, 1.0)][t % 2]))
+    for mask, samp in cases:
+        if not (mask == 0).any():
+            mask.reshape(-1)[0] = 0
+        ref, _ = oracle.edt(mask, samp, False)
+        got = _model_edt(model, mask, samp, K)
+        np.testing.assert_array_equal(got, ref, err_msg=f"shape {mask.shape} sampling {samp}")
