@@ -3,6 +3,15 @@
 // (inside the kernels) and as host C++ (the test-only host model in
 // tests/host_model, which drives the same functions in the kernels' phase order
 // on the CPU).
+//
+// Geometry ("GPU-Based Parallel Euclidean Distance Transform Algorithm", §3.3,
+// Figures 4 and 5; TorchMorph, the separable lower-envelope paragraph).  Along
+// one line every candidate j carries the parabola pi_j(q) = s^2 (q - j)^2 + F_j,
+// F_j being the squared distance already accumulated over the earlier axes.
+// With the lifted height Y_j = F_j + s^2 j^2, two parabolas a < b cross at
+// x(a,b) = (Y_b - Y_a) / (2 s^2 (b - a)), where the bisector of their background
+// elements meets the line.  pi_b(q) < pi_a(q) exactly when
+// Y_b - Y_a < 2 s^2 q (b - a).
 #pragma once
 
 #include <math.h>
@@ -16,8 +25,8 @@
 
 namespace edt {
 
-template <int K> struct MaskOf;
-template <> struct MaskOf<32> { using T = uint32_t; };
+// Bit mask of the surviving positions of one chunk of K positions.
+template <int K> struct MaskOf { using T = uint32_t; };
 template <> struct MaskOf<64> { using T = uint64_t; };
 
 EDT_HD inline int low_bit(uint32_t m) { return __builtin_ctz(m); }
@@ -25,20 +34,19 @@ EDT_HD inline int low_bit(uint64_t m) { return __builtin_ctzll(m); }
 EDT_HD inline int high_bit(uint32_t m) { return 31 - __builtin_clz(m); }
 EDT_HD inline int high_bit(uint64_t m) { return 63 - __builtin_clzll(m); }
 
-// bits strictly below bit i
+// bits strictly below bit i (0 <= i < width)
 template <class M> EDT_HD inline M bits_below(int i) { return (M(1) << i) - M(1); }
-// bits strictly above bit i (i <= width-1)
+// bits strictly above bit i (0 <= i < width)
 template <class M> EDT_HD inline M bits_above(int i) { return ~((M(2) << i) - M(1)); }
 
-// Middle member b of a < b < c leaves the envelope iff x(a,b) >= x(b,c).
+// Middle member b of a < b < c leaves the envelope iff x(a,b) >= x(b,c)
+// (a collinear middle point is dropped).
 EDT_HD inline bool dominated(int a, double Ya, int b, double Yb, int c, double Yc) {
     return (Yb - Ya) * (double)(c - b) >= (Yc - Yb) * (double)(b - a);
 }
 
 // --------------------------------------------------------------------------
-// Envelope machinery shared by both pass layouts.
-//
-// A line of length L is cut into G chunks of K positions.  One lane builds the
+// A line of length L is cut into chunks of K positions.  One lane builds the
 // lower envelope of its chunk with the insertion sweep of PR-EDT Algorithm 1
 // (insert by increasing coordinate, drop the members the new one dominates);
 // the stack is a K-bit mask of surviving positions, so it needs no storage
@@ -49,26 +57,22 @@ EDT_HD inline bool dominated(int a, double Ya, int b, double Yb, int c, double Y
 // Every merged chain stays locally convex, hence is the envelope of its union.
 // --------------------------------------------------------------------------
 
-// View of one line: chunk masks and parabola heights Y.  Implemented by the
-// two layouts below.
+// View of one line: chunk masks, parabola heights Y and the search for
+// non-empty chunks (last_nonempty / first_nonempty over a half-open chunk
+// range, -1 if none; mark_empty when a chunk loses its last member).
+// Implemented by the kernels' LDS layouts and by the host model.
 template <class View, class Mask, int K>
 struct Chain {
     View& v;
     EDT_HD Chain(View& vv) : v(vv) {}
 
     EDT_HD int last_in(int c0, int c1) {  // largest member in chunks [c0, c1)
-        for (int c = c1 - 1; c >= c0; --c) {
-            const Mask m = v.mask(c);
-            if (m) return c * K + high_bit(m);
-        }
-        return -1;
+        const int c = v.last_nonempty(c0, c1);
+        return c < 0 ? -1 : c * K + high_bit(v.mask(c));
     }
     EDT_HD int first_in(int c0, int c1) {  // smallest member in chunks [c0, c1)
-        for (int c = c0; c < c1; ++c) {
-            const Mask m = v.mask(c);
-            if (m) return c * K + low_bit(m);
-        }
-        return -1;
+        const int c = v.first_nonempty(c0, c1);
+        return c < 0 ? -1 : c * K + low_bit(v.mask(c));
     }
     EDT_HD int prev_member(int pos, int c_lo) {  // largest member < pos, chunks >= c_lo
         const int c = pos / K;
@@ -84,7 +88,9 @@ struct Chain {
     }
     EDT_HD void remove(int pos) {
         const int c = pos / K;
-        v.set_mask(c, v.mask(c) & ~(Mask(1) << (pos % K)));
+        const Mask m = v.mask(c) & ~(Mask(1) << (pos % K));
+        v.set_mask(c, m);
+        if (!m) v.mark_empty(c);
     }
 
     // Merge the envelopes of chunks [cl, cm) and [cm, cr).
@@ -116,21 +122,47 @@ struct Chain {
     }
 };
 
-// Local envelope of chunk g by the insertion sweep; returns the member mask.
-// Y(pos) re-reads a member's height after a removal exposes it.
-template <class Mask, int K, class ValAt, class IsValid, class HeightOf>
-EDT_HD inline Mask build_chunk(int g, int L, ValAt val_at, IsValid valid,
-                                            HeightOf height) {
+// Non-empty chunk search over an occupancy bit set (bit c of word c / 64 set
+// when chunk c has a member), for views that keep one.
+template <class Words>
+EDT_HD inline int occ_last(const Words& occ, int lo, int hi) {  // largest set bit in [lo, hi)
+    for (int w = (hi - 1) >> 6; hi > lo && w >= (lo >> 6); --w) {
+        uint64_t bits = occ(w);
+        const int top = hi - 64 * w;                  // bits below top
+        if (top < 64) bits &= (uint64_t(1) << top) - 1;
+        const int bot = lo - 64 * w;                  // bits from bot up
+        if (bot > 0) bits &= ~((uint64_t(1) << bot) - 1);
+        if (bits) return 64 * w + high_bit(bits);
+    }
+    return -1;
+}
+template <class Words>
+EDT_HD inline int occ_first(const Words& occ, int lo, int hi) {  // smallest set bit in [lo, hi)
+    for (int w = lo >> 6; lo < hi && w <= ((hi - 1) >> 6); ++w) {
+        uint64_t bits = occ(w);
+        const int top = hi - 64 * w;
+        if (top < 64) bits &= (uint64_t(1) << top) - 1;
+        const int bot = lo - 64 * w;
+        if (bot > 0) bits &= ~((uint64_t(1) << bot) - 1);
+        if (bits) return 64 * w + low_bit(bits);
+    }
+    return -1;
+}
+
+// Local envelope of one chunk by the insertion sweep, over the candidate
+// positions base + t for the set bits t of cand (increasing order); returns the
+// member mask.  val_at(t) reads the stored value of position base + t and
+// height(v, p) is its lifted height Y_p.
+template <class Mask, class ValAt, class HeightOf>
+EDT_HD inline Mask build_chunk(int base, Mask cand, ValAt val_at, HeightOf height) {
     Mask m = 0;
     int top = -1, sec = -1;
     double Ytop = 0.0, Ysec = 0.0;
-    const int base = g * K;
-    for (int t = 0; t < K; ++t) {
+    while (cand) {
+        const int t = low_bit(cand);
+        cand &= cand - 1;
         const int p = base + t;
-        if (p >= L) break;
-        const auto v = val_at(t);
-        if (!valid(v)) continue;
-        const double Y = height(v, p);
+        const double Y = height(val_at(t), p);
         while (sec >= 0 && dominated(sec, Ysec, top, Ytop, p, Y)) {
             m &= ~(Mask(1) << (top - base));
             top = sec; Ytop = Ysec;
@@ -149,48 +181,54 @@ EDT_HD inline Mask build_chunk(int g, int L, ValAt val_at, IsValid valid,
     return m;
 }
 
-// First position at which member v is strictly nearer than its predecessor u
-// on the line: floor(x(u,v)) + 1.  float64 division of integers below 2^53 with
-// a denominator below 2^17 cannot round across an integer, so this is exact for
-// unit spacing.
-EDT_HD inline double start_after(int u, double Yu, int v, double Yv, double s2l) {
-    return floor((Yv - Yu) / (2.0 * s2l * (double)(v - u))) + 1.0;
+// Candidate bound.  If U bounds the final squared distance of every position
+// of a line, a candidate with F_j > U owns no position (its parabola stays
+// above U everywhere) and can be left out without changing any result.  A
+// valid U is the largest, over the chunks of K positions, of
+//   min( Fmin(c) + s^2 (K-1)^2,  Fmin(c +- 1) + s^2 (2K-1)^2 )
+// where Fmin(c) is the smallest F of chunk c: every position of chunk c lies
+// within K-1 of its own chunk's minimiser and within 2K-1 of a neighbour's.
+EDT_HD inline double chunk_bound(double fmin_self, double fmin_prev, double fmin_next, double s2l,
+                                 int K) {
+    const double near = s2l * (double)(K - 1) * (double)(K - 1);
+    const double far = s2l * (double)(2 * K - 1) * (double)(2 * K - 1);
+    double b = fmin_self + near;
+    if (fmin_prev + far < b) b = fmin_prev + far;
+    if (fmin_next + far < b) b = fmin_next + far;
+    return b;
 }
 
-
-// Index of the first chunk (of K positions, G chunks in the line) whose first
-// position member v owns, given its predecessor u on the merged envelope
-// (u < 0: none, v owns from the start); G if v owns no chunk start.
-EDT_HD inline int first_owned_chunk(int u, double Yu, int v, double Yv, double s2l, int K, int G) {
-    if (u < 0) return 0;
-    const double st = start_after(u, Yu, v, Yv, s2l);
-    if (st <= 0.0) return 0;
-    if (st > (double)G * K) return G;
-    return (int)ceil(st / (double)K);
+// Smallest float32 >= x (x >= 0): bounds stored as float32 stay upper bounds.
+EDT_HD inline float round_up_float(double x) {
+    float f = (float)x;
+    if ((double)f < x) f = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, f) + 1u);
+    return f;
 }
 
-// Owner of every position of chunk g, starting from the owner v of its first
-// position: the next member w takes over at the first q where it is strictly
-// nearer (ties stay with the smaller coordinate), the query of the line's 1-D
-// Voronoi diagram (PR-EDT §3.4).  emit(t, owner) for t in [0, K), q < L.
-template <class NextOf, class HeightOf, class Emit>
-EDT_HD inline void walk_chunk(int g, int K, int L, int v, double s2l, NextOf next_of,
-                              HeightOf Y, Emit emit) {
-    double Yv = Y(v);
-    int w = next_of(v);
-    double Yw = w >= 0 ? Y(w) : 0.0;
-    const double two_s2 = 2.0 * s2l;
-    for (int t = 0; t < K; ++t) {
-        const int q = g * K + t;
-        if (q >= L) break;
-        while (w >= 0 && (Yw - Yv) < two_s2 * (double)q * (double)(w - v)) {
-            v = w;
-            Yv = Yw;
-            w = next_of(v);
-            if (w >= 0) Yw = Y(w);
-        }
-        emit(t, v);
-    }
+// Approximate float32 quotient (a reciprocal estimate on the GPU).
+EDT_HD inline float approx_div(float a, float b) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    return a * __builtin_amdgcn_rcpf(b);
+#else
+    return a / b;
+#endif
+}
+
+// Smallest integer c >= 0 with A < B c (B > 0), or cap if it is cap or more.
+// The estimate comes from a float32 quotient; the result is then fixed with
+// exact float64 products (exact whenever heights and spacings are integers or
+// short dyadic fractions), so no float64 division is needed.
+EDT_HD inline int first_index_beating(double A, double B, int cap) {
+    if (A < 0.0) return 0;
+    const float ratio = approx_div((float)A, (float)B);
+    // The float32 quotient is within a relative 1e-6 of A / B, so a quotient of
+    // cap + 2 or more puts the answer at cap or beyond.
+    if (!(ratio < (float)cap + 2.0f)) return cap;
+    int c = (int)floorf(ratio) + 1;
+    if (c > cap) c = cap;
+    while (c > 0 && A < B * (double)(c - 1)) --c;
+    while (c < cap && !(A < B * (double)c)) ++c;
+    return c;
 }
 
 }  // namespace edt

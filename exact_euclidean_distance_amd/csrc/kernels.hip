@@ -293,446 +293,606 @@ hipError_t launch_axis0(const uint8_t* mask, int B, int n0, int64_t M, uint16_t*
 }
 
 // --------------------------------------------------------------------------
+// Envelope passes.
+//
+// Every lane owns one chunk of K consecutive positions of one line.  Chunk
+// values sit in LDS at slot * CS + t (t < K), slot being the lane's thread
+// index; CS = K + pad makes the 32-bit word stride between slots odd, so when
+// every lane reads position t of its own chunk the reads fall in distinct
+// banks.  The owner marks use the same slot layout with 16-bit entries.  Per
+// slot there are also the member mask, a 32-bit word (chunk minimum, then
+// chunk-level owner marks) and two 16-bit scan words (last member + 1, first
+// member).
+//
+// Phases of one line (all lanes of the line together):
+//   1. chunk minima of F and the line's candidate bound U (see chunk_bound);
+//   2. local envelope of every chunk's candidates with F <= U;
+//   3. merge tree of the chunk envelopes;
+//   4. every member v computes the interval [st, en) of positions it owns and,
+//      if it is non-empty, writes v + 1 at position st (intervals are disjoint,
+//      so every mark has one writer);
+//   5. each lane scans its chunk: the owner of position q is the latest mark at
+//      or before q, so the outputs follow without any per-position search.
+// --------------------------------------------------------------------------
+
+template <class Val, int K>
+struct Slots {
+    static constexpr int CS = sizeof(Val) == 2 ? K + 2 : K + 1;   // value stride
+    static constexpr int CM = K + 2;                               // mark stride (16-bit)
+    using Mask = typename MaskOf<K>::T;
+    // Occupancy words: ceil(Gp / 64) per line of Gp chunks.
+    static int occ_words(int nslots, int Gp) { return (nslots / Gp) * ((Gp + 63) / 64); }
+    // The per-line bound words share the storage of the two 16-bit scan arrays,
+    // which are not live until later (lines per block <= slots).
+    static size_t bytes(int nslots, int Gp) {
+        return align16((size_t)nslots * CS * sizeof(Val)) + align16((size_t)nslots * CM * 2) +
+               align16((size_t)nslots * sizeof(Mask)) + align16((size_t)nslots * 4) +
+               2 * align16((size_t)nslots * 2) + align16((size_t)occ_words(nslots, Gp) * 8);
+    }
+};
+
+constexpr uint16_t kNoFirst = 0xFFFFu;   // "no member" in the first-member scan
+
+// LDS carve-up shared by both layouts.
+template <class Val, int K>
+struct SlotArrays {
+    using Mask = typename MaskOf<K>::T;
+    Val* val;
+    uint16_t* mark;   // per position: owner + 1 of the interval starting there, else 0
+    Mask* mask;
+    int* own;         // chunk minimum of F (float32 bits), then chunk-level owner marks
+    uint16_t* last;   // last member + 1 (0: none), then prefix maximum
+    uint16_t* first;  // first member (kNoFirst: none), then suffix minimum
+    unsigned* bound;  // per line: the candidate bound U (float32 bits); shares
+                      // the storage of last/first, used before they are written
+    uint64_t* occ;    // per line: bit c set while chunk c has a member
+    __device__ SlotArrays(unsigned char* smem, int nslots) {
+        size_t off = 0;
+        val = reinterpret_cast<Val*>(smem);
+        off += align16((size_t)nslots * Slots<Val, K>::CS * sizeof(Val));
+        mark = reinterpret_cast<uint16_t*>(smem + off);
+        off += align16((size_t)nslots * Slots<Val, K>::CM * 2);
+        mask = reinterpret_cast<Mask*>(smem + off);
+        off += align16((size_t)nslots * sizeof(Mask));
+        own = reinterpret_cast<int*>(smem + off);
+        off += align16((size_t)nslots * 4);
+        last = reinterpret_cast<uint16_t*>(smem + off);
+        off += align16((size_t)nslots * 2);
+        first = reinterpret_cast<uint16_t*>(smem + off);
+        off += align16((size_t)nslots * 2);
+        bound = reinterpret_cast<unsigned*>(last);
+        occ = reinterpret_cast<uint64_t*>(smem + off);
+    }
+};
+
+// One line as seen by the envelope helpers: chunk c of the line lives in slot
+// slot0 + c * gs; occ points at the line's occupancy words.
+template <class Val, int K, class FOf>
+struct LineView {
+    using Mask = typename MaskOf<K>::T;
+    static constexpr int CS = Slots<Val, K>::CS;
+    const Val* vals;
+    Mask* masks;
+    uint64_t* occ;
+    int slot0, gs;
+    double s2l;
+    FOf fof;
+    __device__ int last_nonempty(int lo, int hi) const {
+        return occ_last([&](int w) { return occ[w]; }, lo, hi);
+    }
+    __device__ int first_nonempty(int lo, int hi) const {
+        return occ_first([&](int w) { return occ[w]; }, lo, hi);
+    }
+    __device__ void mark_empty(int c) { atomicAnd(&occ[c >> 6], ~(uint64_t(1) << (c & 63))); }
+    __device__ int slot(int c) const { return slot0 + c * gs; }
+    __device__ Val val(int pos) const {
+        return vals[slot((unsigned)pos / K) * CS + ((unsigned)pos % K)];
+    }
+    __device__ double f(int pos) const { return fof(val(pos)); }
+    __device__ double Y(int pos) const { return f(pos) + s2l * (double)pos * (double)pos; }
+    __device__ Mask mask(int c) const { return masks[slot(c)]; }
+    __device__ void set_mask(int c, Mask m) { masks[slot(c)] = m; }
+};
+
+// Inclusive scans over the Gp chunks of every line (slot step gs), in LDS:
+// prefix maximum of a[], and (when b is non-null) suffix minimum of b[].
+// Every thread of the block calls it; it ends with a barrier.
+template <class T>
+__device__ void line_scans(T* a, uint16_t* b, int myslot, int g, int gs, int Gp) {
+    for (int d = 1; d < Gp; d <<= 1) {
+        __syncthreads();
+        const T x = (g >= d) ? a[myslot - d * gs] : T(0);
+        const uint16_t y = (b && g + d < Gp) ? b[myslot + d * gs] : kNoFirst;
+        __syncthreads();
+        if (x > a[myslot]) a[myslot] = x;
+        if (b && y < b[myslot]) b[myslot] = y;
+    }
+    __syncthreads();
+}
+
+// Phases 1-4 for the lane's chunk g of its line (local line index lslot).
+// Fills the line's owner marks and returns owner + 1 of the position just
+// before the chunk (0: no owner yet).  Every thread of the block must call it
+// (it contains barriers).
+template <int K, class Val, class View, class IsValid, class FOfVal>
+__device__ int resolve_line(View& view, SlotArrays<Val, K>& sa, const Val* mychunk,
+                            uint16_t* mymarks, int g, int Gp, int L, bool active, int myslot,
+                            int gs, int lslot, IsValid valid, FOfVal fval) {
+    using Mask = typename MaskOf<K>::T;
+    constexpr int CM = Slots<Val, K>::CM;
+    const int base = g * K;
+    const int n = active ? min(K, L - base) : 0;
+    const int G = (L + K - 1) / K;
+    const double s2l = view.s2l;
+
+    // 1. chunk minimum of F and its first minimiser, then the line's
+    //    candidate bound.  The minimiser (+1, 0: none) is published in the mask
+    //    slot, which the local envelope overwrites only after the second barrier.
+    double fmin = __builtin_huge_val();
+    int amin = -1;
+#pragma unroll 8
+    for (int t = 0; t < n; ++t) {
+        const Val v = mychunk[t];
+        const double f = fval(v);
+        if (valid(v) && f < fmin) { fmin = f; amin = t; }
+    }
+    const float fmin_up = round_up_float(fmin);
+    sa.own[myslot] = __float_as_int(fmin_up);
+    sa.mask[myslot] = (Mask)(amin < 0 ? 0 : base + amin + 1);
+    if (g == 0) sa.bound[lslot] = 0u;
+    if ((g & 63) == 0) view.occ[g >> 6] = 0ull;
+    __syncthreads();
+    int aprev = -1, anext = -1;
+    if (n > 0) {
+        const double prev = g > 0 ? (double)__int_as_float(sa.own[myslot - gs]) : __builtin_huge_val();
+        const double next = g + 1 < G ? (double)__int_as_float(sa.own[myslot + gs]) : __builtin_huge_val();
+        const float b = round_up_float(chunk_bound((double)fmin_up, prev, next, s2l, K));
+        atomicMax(&sa.bound[lslot], __float_as_uint(b));
+        if (g > 0) aprev = (int)sa.mask[myslot - gs] - 1;
+        if (g + 1 < G) anext = (int)sa.mask[myslot + gs] - 1;
+    }
+    __syncthreads();
+    const double U = (double)__uint_as_float(sa.bound[lslot]);
+
+    // 2. local envelope of the chunk's candidates that can still own a
+    //    position: F <= U, and not dominated by the nearest chunk minimisers on
+    //    either side (both are candidates, so a dominated candidate is no
+    //    vertex of the envelope).
+    const int acur = amin < 0 ? -1 : base + amin;
+    const double Yprev = aprev >= 0 ? view.Y(aprev) : 0.0;
+    const double Ycur = acur >= 0 ? view.Y(acur) : 0.0;
+    const double Ynext = anext >= 0 ? view.Y(anext) : 0.0;
+    Mask cand = 0;
+#pragma unroll 8
+    for (int t = 0; t < n; ++t) {
+        const Val v = mychunk[t];
+        const double f = fval(v);
+        const int p = base + t;
+        const double Yp = f + s2l * (double)p * (double)p;
+        const int lo = acur >= 0 && acur < p ? acur : aprev;
+        const double Ylo = acur >= 0 && acur < p ? Ycur : Yprev;
+        const int hi = acur > p ? acur : anext;
+        const double Yhi = acur > p ? Ycur : Ynext;
+        const bool gone = lo >= 0 && hi >= 0 && dominated(lo, Ylo, p, Yp, hi, Yhi);
+        if (valid(v) && f <= U && !gone) cand |= Mask(1) << t;
+    }
+    Mask m = build_chunk<Mask>(base, cand, [&](int t) { return mychunk[t]; },
+                               [&](Val v, int p) { return fval(v) + s2l * (double)p * (double)p; });
+    sa.mask[myslot] = m;
+    if (m) atomicOr(&view.occ[g >> 6], uint64_t(1) << (g & 63));
+
+    // 3. merge tree
+    for (int h = 1; h < Gp; h <<= 1) {
+        __syncthreads();
+        if (active && (g & (2 * h - 1)) == h) {
+            Chain<View, Mask, K> ch(view);
+            ch.junction(g - h, g, min(g + h, Gp));
+        }
+    }
+    __syncthreads();
+
+    // last member up to each chunk, first member from each chunk on; clear marks
+    m = sa.mask[myslot];
+    sa.last[myslot] = m ? (uint16_t)(base + high_bit(m) + 1) : (uint16_t)0;
+    sa.first[myslot] = m ? (uint16_t)(base + low_bit(m)) : kNoFirst;
+    sa.own[myslot] = 0;
+#pragma unroll
+    for (int t = 0; t < K; t += 2) *reinterpret_cast<uint32_t*>(mymarks + t) = 0u;
+    line_scans(sa.last, sa.first, myslot, g, gs, Gp);
+
+    // 4. owned intervals of the members: v owns [st, en), st against its
+    //    predecessor u, en where its successor w takes over
+    if (m) {
+        Mask mm = m;
+        const int u = g > 0 ? (int)sa.last[myslot - gs] - 1 : -1;
+        int v = base + low_bit(mm);
+        mm &= mm - 1;
+        double Yv = view.Y(v);
+        int st = 0;
+        if (u >= 0) st = first_index_beating(Yv - view.Y(u), 2.0 * s2l * (double)(v - u), L);
+        for (;;) {
+            int w;
+            if (mm) {
+                w = base + low_bit(mm);
+            } else {
+                const uint16_t nf = g + 1 < Gp ? sa.first[myslot + gs] : kNoFirst;
+                w = nf == kNoFirst ? -1 : (int)nf;
+            }
+            int en = L;
+            double Yw = 0.0;
+            if (w >= 0) {
+                Yw = view.Y(w);
+                en = first_index_beating(Yw - Yv, 2.0 * s2l * (double)(w - v), L);
+            }
+            if (st < en) {   // st < L follows from en <= L
+                const int cs = (unsigned)st / K;
+                sa.mark[(size_t)view.slot(cs) * CM + ((unsigned)st % K)] = (uint16_t)(v + 1);
+                atomicMax(&sa.own[view.slot(cs)], v + 1);
+            }
+            if (!mm) break;
+            mm &= mm - 1;
+            v = w;
+            Yv = Yw;
+            st = en;
+        }
+    }
+    line_scans(sa.own, (uint16_t*)nullptr, myslot, g, gs, Gp);
+    return g > 0 ? sa.own[myslot - gs] : 0;
+}
+
+// --------------------------------------------------------------------------
 // Row layout: lines contiguous in memory (the last axis).  A work-group holds
-// LPW lines; lane g of a line owns chunk g.  LDS per chunk: its K values plus a
-// one-word pad (so chunk reads at stride K are bank-conflict free), its K owner
-// slots, and a few words of chunk metadata.  The final owner of every position
-// is written to LDS and the epilogue then streams the outputs coalesced.
+// LPW lines; lane g of a line owns chunk g.  The line is loaded with 16-byte
+// coalesced reads, and each lane writes its own chunk's outputs with 16-byte
+// stores (chunks are 4-aligned), so no LDS staging of outputs is needed.
 // --------------------------------------------------------------------------
 
 struct Geo2D {          // rows of an H x W image; value = axis-0 coordinate
+    using Val = uint16_t;
     double s2a, s2l;    // squared spacing of axis 0 and along the row
     int W;
-    using Val = uint16_t;
+    struct Line { int row; };
+    __device__ Line line(int64_t ln) const { return Line{(int)ln}; }
     __device__ static bool valid(uint16_t v) { return v != kNone16; }
-    __device__ double baseF(int64_t line, uint16_t v) const {
-        const double t = (double)((int)line - (int)v);
+    __device__ double f(const Line& l, uint16_t v) const {
+        const double t = (double)(l.row - (int)v);
         return s2a * t * t;
     }
-    __device__ int32_t index(int64_t line, uint16_t v, int pos) const { return (int32_t)v * W + pos; }
-    __device__ double virtF(int64_t line, int q) const {
-        const double t = (double)(line + 1);
-        return s2a * t * t + s2l * (double)q * (double)q;
+    __device__ int32_t index(const Line&, uint16_t v, int pos) const { return (int32_t)v * W + pos; }
+    __device__ double virt_f(const Line& l) const {
+        const double t = (double)(l.row + 1);
+        return s2a * t * t;
     }
     __device__ int32_t virt_index() const { return -W; }
 };
 
 struct Geo3D {          // rows along W of B x D x H x W volumes; value = packed (axis0, axis1)
+    using Val = uint32_t;
     double s2a, s2b, s2l;
     int D, H, W;
-    using Val = uint32_t;
+    struct Line { int d, h; };
+    __device__ Line line(int64_t ln) const {
+        const int64_t dh = ln % ((int64_t)D * H);
+        return Line{(int)(dh / H), (int)(dh % H)};
+    }
     __device__ static bool valid(uint32_t v) { return v != kNone32; }
-    __device__ double baseF(int64_t line, uint32_t v) const {
-        const int h = (int)(line % H);
-        const int d = (int)((line / H) % D);
-        const double t0 = (double)(d - (int)(v >> 16));
-        const double t1 = (double)(h - (int)(v & 0xFFFFu));
+    __device__ double f(const Line& l, uint32_t v) const {
+        const double t0 = (double)(l.d - (int)(v >> 16));
+        const double t1 = (double)(l.h - (int)(v & 0xFFFFu));
         return s2a * t0 * t0 + s2b * t1 * t1;
     }
-    __device__ int32_t index(int64_t line, uint32_t v, int pos) const {
+    __device__ int32_t index(const Line&, uint32_t v, int pos) const {
         return ((int32_t)(v >> 16) * H + (int32_t)(v & 0xFFFFu)) * W + pos;
     }
-    __device__ double virtF(int64_t line, int q) const {
-        const int h = (int)(line % H);
-        const int d = (int)((line / H) % D);
-        const double t0 = (double)(d + 1);
-        return s2a * t0 * t0 + s2b * (double)h * (double)h + s2l * (double)q * (double)q;
+    __device__ double virt_f(const Line& l) const {
+        const double t0 = (double)(l.d + 1);
+        return s2a * t0 * t0 + s2b * (double)l.h * (double)l.h;
     }
     __device__ int32_t virt_index() const { return -(H * W); }
 };
 
-template <class Val, int K>
-struct RowLayout {
-    static constexpr int kPadV = 4 / (int)sizeof(Val);
-    static constexpr int kVStride = K + kPadV;   // Val units per chunk
-    static constexpr int kOStride = K + 2;       // uint16 units per chunk
-    using Mask = typename MaskOf<K>::T;
-    static size_t bytes(int nchunks) {
-        return align16((size_t)nchunks * kVStride * sizeof(Val)) +
-               align16((size_t)nchunks * kOStride * sizeof(uint16_t)) +
-               align16((size_t)nchunks * sizeof(Mask)) + 3 * align16((size_t)nchunks * 4);
-    }
-};
+template <int BYTES> struct RawVec;
+template <> struct RawVec<16> { using T = uint4; };
+template <> struct RawVec<8> { using T = uint2; };
+template <> struct RawVec<4> { using T = uint32_t; };
+template <> struct RawVec<2> { using T = uint16_t; };
 
-template <class Geo, int K>
-struct RowView {
-    using Val = typename Geo::Val;
-    using Lay = RowLayout<Val, K>;
-    using Mask = typename Lay::Mask;
-    const Val* sval;   // this line's first chunk
-    Mask* scm;         // this line's first chunk mask
-    const Geo& geo;
-    int64_t line;
-    __device__ Mask mask(int c) const { return scm[c]; }
-    __device__ void set_mask(int c, Mask m) { scm[c] = m; }
-    __device__ Val val(int pos) const { return sval[(pos / K) * Lay::kVStride + pos % K]; }
-    __device__ double Y(int pos) const {
-        return geo.baseF(line, val(pos)) + geo.s2l * (double)pos * (double)pos;
+// Load one line of L values (L % VW == 0) into its chunk slots: lane g of the
+// line reads pieces g, g + Gp, ... of VW values each.
+template <class Val, int K, int VW>
+__device__ inline void load_row_line(const Val* __restrict__ src, int L, int g, int Gp, Val* dst) {
+    constexpr int CS = Slots<Val, K>::CS;
+    constexpr int NP = K / VW;               // pieces per lane at most (Gp * K >= L)
+    constexpr int NB = NP < 16 ? NP : 16;    // loads kept in flight per batch
+    using V = typename RawVec<VW * (int)sizeof(Val)>::T;
+    const int PL = L / VW;
+#pragma unroll
+    for (int i0 = 0; i0 < NP; i0 += NB) {
+        V buf[NB];
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+            const int k = g + (i0 + i) * Gp;
+            if (k < PL) buf[i] = reinterpret_cast<const V*>(src)[k];
+        }
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+            const int k = g + (i0 + i) * Gp;
+            if (k < PL) {
+                const int p = k * VW;
+                Val* d = dst + ((unsigned)p / K) * CS + ((unsigned)p % K);
+                if constexpr (VW * sizeof(Val) == 16) {
+                    uint32_t* d32 = reinterpret_cast<uint32_t*>(d);   // 4-byte aligned (CS even for uint16)
+                    d32[0] = buf[i].x; d32[1] = buf[i].y; d32[2] = buf[i].z; d32[3] = buf[i].w;
+                } else {
+                    d[0] = buf[i];
+                }
+            }
+        }
     }
-};
+}
 
-template <class Geo, int K>
+template <class Geo, int K, int VW>
 __global__ __launch_bounds__(1024) void k_envelope_rows(const typename Geo::Val* __restrict__ in,
-                                                        int L, int64_t nlines, int G, int LPW,
+                                                        int L, int64_t nlines, int Gp, int LPW,
                                                         Geo geo, int32_t* __restrict__ sqdist,
                                                         float* __restrict__ dist,
-                                                        int32_t* __restrict__ indices) {
+                                                        int32_t* __restrict__ indices, int vec_out) {
     using Val = typename Geo::Val;
-    using Lay = RowLayout<Val, K>;
-    using Mask = typename Lay::Mask;
+    constexpr int CS = Slots<Val, K>::CS;
+    constexpr int CM = Slots<Val, K>::CM;
     extern __shared__ __align__(16) unsigned char smem[];
-    const int nchunks = G * LPW;
-    Val* sval = reinterpret_cast<Val*>(smem);
-    size_t off = align16((size_t)nchunks * Lay::kVStride * sizeof(Val));
-    uint16_t* sown = reinterpret_cast<uint16_t*>(smem + off);
-    off += align16((size_t)nchunks * Lay::kOStride * sizeof(uint16_t));
-    Mask* scm = reinterpret_cast<Mask*>(smem + off);
-    off += align16((size_t)nchunks * sizeof(Mask));
-    int* sA = reinterpret_cast<int*>(smem + off);       // last member, then prefix max
-    off += align16((size_t)nchunks * 4);
-    int* sB = reinterpret_cast<int*>(smem + off);       // first member, then suffix min
-    off += align16((size_t)nchunks * 4);
-    unsigned* sslot = reinterpret_cast<unsigned*>(smem + off);
+    SlotArrays<Val, K> sa(smem, Gp * LPW);
 
     const int tid = threadIdx.x;
-    const int nthr = blockDim.x;
-    const int g = tid % G;
-    const int r = tid / G;
-    const int c = tid;                      // chunk index within the work-group
-    const int64_t line0 = (int64_t)blockIdx.x * LPW;
-    const int nl = (int)min((int64_t)LPW, nlines - line0);
-    const bool active = r < nl;
-    const int64_t line = line0 + r;
+    const int g = tid & (Gp - 1);
+    const int r = tid / Gp;
+    const int slot0 = r * Gp;
+    const int64_t line = (int64_t)blockIdx.x * LPW + r;
+    const bool active = line < nlines;
 
-    // ---- load the work-group's lines (contiguous in memory) into LDS ----
-    {
-        const Val* src = in + line0 * (int64_t)L;
-        const int64_t nelem = (int64_t)nl * L;
-        int rr = tid / L, p = tid % L;
-        for (int64_t e = tid; e < nelem; e += nthr) {
-            sval[(rr * G + p / K) * Lay::kVStride + p % K] = src[e];
-            p += nthr;
-            while (p >= L) { p -= L; ++rr; }
-        }
-    }
+    if (active) load_row_line<Val, K, VW>(in + line * (int64_t)L, L, g, Gp, sa.val + (size_t)slot0 * CS);
     __syncthreads();
 
-    RowView<Geo, K> view{sval + (size_t)r * G * Lay::kVStride, scm + (size_t)r * G, geo, line};
+    const typename Geo::Line gl = geo.line(active ? line : 0);
+    auto fof = [&](Val v) { return geo.f(gl, v); };
+    LineView<Val, K, decltype(fof)> view{sa.val, sa.mask, sa.occ + (size_t)r * ((Gp + 63) / 64),
+                                         slot0, 1, geo.s2l, fof};
+    uint16_t* mymarks = sa.mark + (size_t)tid * CM;
+    int o = resolve_line<K>(view, sa, sa.val + (size_t)tid * CS, mymarks, g, Gp, L, active, tid, 1,
+                            r, [](Val v) { return Geo::valid(v); }, fof);
 
-    // ---- local envelope of every chunk ----
-    Mask m = 0;
-    if (active) {
-        const Val* cv = sval + (size_t)c * Lay::kVStride;
-        m = build_chunk<Mask, K>(
-            g, L, [&](int t) { return cv[t]; }, [](Val v) { return Geo::valid(v); },
-            [&](Val v, int p) { return geo.baseF(line, v) + geo.s2l * (double)p * (double)p; });
-    }
-    scm[c] = m;
-
-    // ---- merge tree ----
-    for (int h = 1; h < G; h <<= 1) {
-        __syncthreads();
-        if (active && (g & (2 * h - 1)) == h) {
-            Chain<RowView<Geo, K>, Mask, K> ch(view);
-            ch.junction(g - h, g, min(g + h, G));
-        }
-    }
-    __syncthreads();
-
-    // ---- per line: last member up to each chunk, first member from each chunk ----
-    {
-        const Mask mm = active ? scm[c] : Mask(0);
-        sA[c] = mm ? g * K + high_bit(mm) : -1;
-        sB[c] = mm ? g * K + low_bit(mm) : INT_MAX;
-    }
-    for (int d = 1; d < G; d <<= 1) {
-        __syncthreads();
-        const int a = (g >= d) ? sA[c - d] : -1;
-        const int bb = (g + d < G) ? sB[c + d] : INT_MAX;
-        __syncthreads();
-        sA[c] = max(sA[c], a);
-        sB[c] = min(sB[c], bb);
-    }
-    sslot[c] = 0u;
-    __syncthreads();
-
-    // ---- every member marks the first chunk whose first position it owns ----
-    if (active) {
-        Mask mm = scm[c];
-        int u = (g > 0) ? sA[c - 1] : -1;
-        double Yu = u >= 0 ? view.Y(u) : 0.0;
-        while (mm) {
-            const int vpos = g * K + low_bit(mm);
-            mm &= mm - 1;
-            const double Yv = view.Y(vpos);
-            const int sc = first_owned_chunk(u, Yu, vpos, Yv, geo.s2l, K, G);
-            if (sc < G) atomicMax(&sslot[r * G + sc], (unsigned)(vpos + 1));
-            u = vpos;
-            Yu = Yv;
-        }
-    }
-    for (int d = 1; d < G; d <<= 1) {
-        __syncthreads();
-        const unsigned a = (g >= d) ? sslot[c - d] : 0u;
-        __syncthreads();
-        sslot[c] = max(sslot[c], a);
-    }
-    __syncthreads();
-
-    // ---- walk the chunk's positions, recording each position's owner ----
-    if (active) {
-        uint16_t* own = sown + (size_t)c * Lay::kOStride;
-        int v = (int)sslot[c] - 1;
-        if (v < 0) {
-            for (int t = 0; t < K; ++t) own[t] = kNone16;
+    // 5. outputs of the chunk
+    const int base = g * K;
+    const int n = active ? min(K, L - base) : 0;
+    if (n <= 0) return;   // no barrier follows
+    const double s2l = geo.s2l;
+    const double fvirt = geo.virt_f(gl);
+    const int32_t ivirt = geo.virt_index();
+    const int64_t obase = line * (int64_t)L + base;
+    int32_t osq[4];
+    float od[4];
+    int32_t oix[4];
+    auto one = [&](int j, int t) {
+        const int mk = mymarks[t];
+        o = mk > o ? mk : o;
+        const int ow = o - 1;
+        const Val vo = view.val(ow < 0 ? 0 : ow);
+        const double q = (double)(base + t);
+        const double dq = (double)(base + t - ow);
+        const double F = ow < 0 ? fvirt + s2l * q * q : fof(vo) + s2l * dq * dq;
+        osq[j] = sqdist ? (int32_t)F : 0;
+        od[j] = __builtin_amdgcn_sqrtf((float)F);
+        oix[j] = ow < 0 ? ivirt : geo.index(gl, vo, ow);
+    };
+    for (int t0 = 0; t0 < n; t0 += 4) {
+        const int cnt = min(4, n - t0);
+        if (cnt == 4) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) one(j, t0 + j);
         } else {
-            auto next_of = [&](int pos) -> int {
-                const int cc = pos / K;
-                const Mask nm = scm[r * G + cc] & bits_above<Mask>(pos % K);
-                if (nm) return cc * K + low_bit(nm);
-                const int nf = (cc + 1 < G) ? sB[r * G + cc + 1] : INT_MAX;
-                return nf == INT_MAX ? -1 : nf;
-            };
-            walk_chunk(g, K, L, v, geo.s2l, next_of, [&](int pos) { return view.Y(pos); },
-                       [&](int t, int o) { own[t] = (uint16_t)o; });
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (j < cnt) one(j, t0 + j);
         }
-    }
-    __syncthreads();
-
-    // ---- epilogue: distances and indices, streamed coalesced ----
-    {
-        const int64_t nelem = (int64_t)nl * L;
-        int rr = tid / L, p = tid % L;
-        for (int64_t e = tid; e < nelem; e += nthr) {
-            const int64_t ln = line0 + rr;
-            const int o = sown[(rr * G + p / K) * Lay::kOStride + p % K];
-            double F;
-            int32_t ix;
-            if (o == kNone16) {
-                F = geo.virtF(ln, p);
-                ix = geo.virt_index();
-            } else {
-                const Val v = sval[(rr * G + o / K) * Lay::kVStride + o % K];
-                const double t = (double)(p - o);
-                F = geo.baseF(ln, v) + geo.s2l * t * t;
-                ix = geo.index(ln, v, o);
+        const int64_t ob = obase + t0;
+        if (vec_out && cnt == 4) {
+            if (sqdist) *reinterpret_cast<int4*>(sqdist + ob) = make_int4(osq[0], osq[1], osq[2], osq[3]);
+            if (dist) *reinterpret_cast<float4*>(dist + ob) = make_float4(od[0], od[1], od[2], od[3]);
+            if (indices) *reinterpret_cast<int4*>(indices + ob) = make_int4(oix[0], oix[1], oix[2], oix[3]);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if (j < cnt) {
+                    if (sqdist) sqdist[ob + j] = osq[j];
+                    if (dist) dist[ob + j] = od[j];
+                    if (indices) indices[ob + j] = oix[j];
+                }
             }
-            const int64_t go = line0 * (int64_t)L + e;
-            if (sqdist) sqdist[go] = (int32_t)F;
-            if (dist) dist[go] = sqrtf((float)F);
-            if (indices) indices[go] = ix;
-            p += nthr;
-            while (p >= L) { p -= L; ++rr; }
         }
     }
 }
 
 struct RowPlan {
-    int K, G, LPW;
+    int K, Gp, LPW, VW;
     size_t lds;
 };
 
+// Chunk size: 32 positions for 16-bit values, 16 for 32-bit values (their
+// larger slots would otherwise leave too few lanes resident per CU).  Lines
+// shorter than a block share it, up to 256 threads.
 static RowPlan plan_rows(int L, int value_bytes) {
     RowPlan p{};
-    p.K = (L <= 8192) ? 32 : 64;
-    int chunks = (L + p.K - 1) / p.K;
-    p.G = 1;
-    while (p.G < chunks) p.G <<= 1;
-    p.LPW = p.G >= 256 ? 1 : 256 / p.G;
-    const int nch = p.G * p.LPW;
-    if (value_bytes == 2)
-        p.lds = p.K == 32 ? RowLayout<uint16_t, 32>::bytes(nch) : RowLayout<uint16_t, 64>::bytes(nch);
-    else
-        p.lds = p.K == 32 ? RowLayout<uint32_t, 32>::bytes(nch) : RowLayout<uint32_t, 64>::bytes(nch);
+    p.K = value_bytes == 2 ? 32 : 16;
+    const int chunks = (L + p.K - 1) / p.K;
+    p.Gp = 1;
+    while (p.Gp < chunks) p.Gp <<= 1;
+    p.LPW = p.Gp >= 256 ? 1 : 256 / p.Gp;
+    const int nslots = p.Gp * p.LPW;
+    const int vw16 = 16 / value_bytes;
+    p.VW = (L % vw16 == 0) ? vw16 : 1;
+    p.lds = value_bytes == 2 ? Slots<uint16_t, 32>::bytes(nslots, p.Gp) : Slots<uint32_t, 16>::bytes(nslots, p.Gp);
     return p;
 }
 
 size_t rows_lds_bytes(int L, int value_bytes) {
-    RowPlan p = plan_rows(L, value_bytes);
-    if (p.G > 1024) return 0;
+    const RowPlan p = plan_rows(L, value_bytes);
+    if (p.Gp > 1024 || p.lds > 160 * 1024) return 0;
     return p.lds;
 }
 
-template <class Geo, int K>
+template <class Geo, int K, int VW>
 static hipError_t launch_rows_t(const typename Geo::Val* in, int L, int64_t nlines, const RowPlan& p,
                                 const Geo& geo, int32_t* sqdist, float* dist, int32_t* indices,
                                 hipStream_t s, KernelTimer* tm, const char* kname) {
     static bool attr_done = false;
     if (!attr_done) {
-        allow_large_lds((const void*)k_envelope_rows<Geo, K>);
+        allow_large_lds((const void*)k_envelope_rows<Geo, K, VW>);
         attr_done = true;
     }
     const int64_t nblocks = (nlines + p.LPW - 1) / p.LPW;
+    const bool aligned16 = (((uintptr_t)sqdist | (uintptr_t)dist | (uintptr_t)indices) & 15) == 0;
+    const int vec_out = (L % 4 == 0 && aligned16) ? 1 : 0;
     EDT_LAUNCH(tm, kname, s,
-               hipLaunchKernelGGL((k_envelope_rows<Geo, K>), dim3((unsigned)nblocks),
-                                  dim3(p.G * p.LPW), p.lds, s, in, L, nlines, p.G, p.LPW, geo,
-                                  sqdist, dist, indices));
+               hipLaunchKernelGGL((k_envelope_rows<Geo, K, VW>), dim3((unsigned)nblocks),
+                                  dim3(p.Gp * p.LPW), p.lds, s, in, L, nlines, p.Gp, p.LPW, geo,
+                                  sqdist, dist, indices, vec_out));
     return hipSuccess;
+}
+
+template <class Geo, int K>
+static hipError_t launch_rows_any(const typename Geo::Val* in, int L, int64_t nlines, const Geo& geo,
+                                  int32_t* sqdist, float* dist, int32_t* indices, hipStream_t s,
+                                  KernelTimer* tm, const char* kname) {
+    constexpr int VB = (int)sizeof(typename Geo::Val);
+    constexpr int V16 = 16 / VB;
+    const RowPlan p = plan_rows(L, VB);
+    if (p.VW == V16) return launch_rows_t<Geo, K, V16>(in, L, nlines, p, geo, sqdist, dist, indices, s, tm, kname);
+    return launch_rows_t<Geo, K, 1>(in, L, nlines, p, geo, sqdist, dist, indices, s, tm, kname);
 }
 
 hipError_t launch_rows_2d(const uint16_t* c0, int H, int W, double s2_0, double s2_1,
                           int32_t* sqdist, float* dist, int32_t* indices, hipStream_t s,
                           KernelTimer* tm) {
-    const RowPlan p = plan_rows(W, 2);
     Geo2D geo{s2_0, s2_1, W};
-    if (p.K == 32)
-        return launch_rows_t<Geo2D, 32>(c0, W, H, p, geo, sqdist, dist, indices, s, tm, "envelope_rows_2d");
-    return launch_rows_t<Geo2D, 64>(c0, W, H, p, geo, sqdist, dist, indices, s, tm, "envelope_rows_2d");
+    return launch_rows_any<Geo2D, 32>(c0, W, H, geo, sqdist, dist, indices, s, tm, "envelope_rows_2d");
 }
 
 hipError_t launch_rows_3d(const uint32_t* c01, int B, int D, int H, int W, double s2_0,
                           double s2_1, double s2_2, int32_t* sqdist, float* dist,
                           int32_t* indices, hipStream_t s, KernelTimer* tm) {
-    const RowPlan p = plan_rows(W, 4);
     Geo3D geo{s2_0, s2_1, s2_2, D, H, W};
     const int64_t nlines = (int64_t)B * D * H;
-    if (p.K == 32)
-        return launch_rows_t<Geo3D, 32>(c01, W, nlines, p, geo, sqdist, dist, indices, s, tm, "envelope_rows_3d");
-    return launch_rows_t<Geo3D, 64>(c01, W, nlines, p, geo, sqdist, dist, indices, s, tm, "envelope_rows_3d");
+    return launch_rows_any<Geo3D, 16>(c01, W, nlines, geo, sqdist, dist, indices, s, tm, "envelope_rows_3d");
 }
 
 // --------------------------------------------------------------------------
 // Column layout: the middle axis of a volume, lines strided by W.  A
-// work-group takes 64 neighbouring lines (lane x = line, so every LDS row and
-// every global access is 64 consecutive elements) and G = ceil(H/K) waves
-// (wave g = chunk g of all 64 lines).  Outputs go straight from the walk to
-// memory: at each step the 64 lanes of a wave write 64 consecutive words.
+// work-group takes TW neighbouring lines (lane x = line) and Gp chunk groups
+// (chunk g of all TW lines), so every global load and store moves TW
+// consecutive elements.  Each lane loads its own chunk.
 // --------------------------------------------------------------------------
 
-template <int K>
-struct ColView {
-    using Mask = typename MaskOf<K>::T;
-    const uint16_t* sval;  // [H][64]
-    Mask* scm;             // [G][64]
-    int x, d;
-    double s2a, s2l;
-    __device__ Mask mask(int c) const { return scm[c * 64 + x]; }
-    __device__ void set_mask(int c, Mask m) { scm[c * 64 + x] = m; }
-    __device__ double Y(int pos) const {
-        const double t = (double)(d - (int)sval[pos * 64 + x]);
-        return s2a * t * t + s2l * (double)pos * (double)pos;
-    }
+struct ColPlan {
+    int K, TW, Gp;
+    size_t lds;
 };
 
-size_t cols_lds_bytes(int H) {
-    const int K = H <= 512 ? 32 : 64;
-    const int G = (H + K - 1) / K;
-    const size_t mb = K == 32 ? 4 : 8;
-    return align16((size_t)H * 64 * 2) + align16((size_t)G * 64 * mb) + align16((size_t)G * 64 * 4);
+// H <= 512: chunks of 32 and 64 lines per block; H <= 1024: chunks of 64 and
+// 32 lines per block (LDS holds TW lines of values and marks).
+static ColPlan plan_cols(int H) {
+    ColPlan p{};
+    p.K = H <= 512 ? 32 : 64;
+    p.TW = H <= 512 ? 64 : 32;
+    p.Gp = 1;
+    while (p.Gp * p.K < H) p.Gp <<= 1;
+    p.lds = p.K == 32 ? Slots<uint16_t, 32>::bytes(p.Gp * p.TW, p.Gp) : Slots<uint16_t, 64>::bytes(p.Gp * p.TW, p.Gp);
+    return p;
 }
 
-template <int K>
+size_t cols_lds_bytes(int H) {
+    const ColPlan p = plan_cols(H);
+    return (p.Gp * p.TW > 1024 || p.lds > 160 * 1024) ? 0 : p.lds;
+}
+
+template <int K, int TW>
 __global__ __launch_bounds__(1024) void k_envelope_cols(const uint16_t* __restrict__ c0,
                                                         uint32_t* __restrict__ out, int D, int H,
-                                                        int W, int G, double s2a, double s2l) {
-    using Mask = typename MaskOf<K>::T;
+                                                        int W, int Gp, double s2a, double s2l) {
+    constexpr int CS = Slots<uint16_t, K>::CS;
+    constexpr int CM = Slots<uint16_t, K>::CM;
     extern __shared__ __align__(16) unsigned char smem[];
-    uint16_t* sval = reinterpret_cast<uint16_t*>(smem);
-    size_t off = align16((size_t)H * 64 * 2);
-    Mask* scm = reinterpret_cast<Mask*>(smem + off);
-    off += align16((size_t)G * 64 * sizeof(Mask));
-    unsigned* sslot = reinterpret_cast<unsigned*>(smem + off);
+    SlotArrays<uint16_t, K> sa(smem, Gp * TW);
 
     const int x = threadIdx.x;
     const int g = threadIdx.y;
-    const int tiles = (W + 63) / 64;
+    const int tid = g * TW + x;
+    const int tiles = (W + TW - 1) / TW;
     const int64_t plane = blockIdx.x / tiles;
-    const int w0 = (blockIdx.x % tiles) * 64;
+    const int w0 = (int)(blockIdx.x % tiles) * TW;
     const bool active = (w0 + x) < W;
     const int d = (int)(plane % D);
+    const int base = g * K;
+    const int n = active ? min(K, H - base) : 0;
 
-    const uint16_t* src = c0 + plane * (int64_t)H * W + w0 + x;
-    for (int h = g; h < H; h += G) sval[h * 64 + x] = active ? src[(int64_t)h * W] : kNone16;
-    __syncthreads();
-
-    ColView<K> view{sval, scm, x, d, s2a, s2l};
-    Mask m = 0;
-    if (active) {
-        m = build_chunk<Mask, K>(
-            g, H, [&](int t) { return sval[(g * K + t) * 64 + x]; },
-            [](uint16_t v) { return v != kNone16; },
-            [&](uint16_t v, int p) {
-                const double t = (double)(d - (int)v);
-                return s2a * t * t + s2l * (double)p * (double)p;
-            });
-    }
-    scm[g * 64 + x] = m;
-
-    for (int h = 1; h < G; h <<= 1) {
-        __syncthreads();
-        if (active && (g & (2 * h - 1)) == h) {
-            Chain<ColView<K>, Mask, K> ch(view);
-            ch.junction(g - h, g, min(g + h, G));
+    // own chunk: rows base .. base + n - 1 of column w0 + x (all loads issued
+    // before any is used; rows past the end read row n - 1 and are discarded)
+    uint16_t* mine = sa.val + (size_t)tid * CS;
+    if (n > 0) {
+        const uint16_t* src = c0 + plane * (int64_t)H * W + (int64_t)base * W + w0 + x;
+        uint16_t buf[K];
+#pragma unroll
+        for (int t = 0; t < K; ++t) buf[t] = src[(int64_t)min(t, n - 1) * W];
+#pragma unroll
+        for (int t = 0; t < K; t += 2) {
+            const uint32_t lo = t < n ? buf[t] : kNone16;
+            const uint32_t hi = t + 1 < n ? buf[t + 1] : kNone16;
+            *reinterpret_cast<uint32_t*>(mine + t) = lo | (hi << 16);
         }
     }
-    sslot[g * 64 + x] = 0u;
-    __syncthreads();
 
-    Chain<ColView<K>, Mask, K> ch(view);
-    if (active) {
-        Mask mm = scm[g * 64 + x];
-        int u = ch.last_in(0, g);
-        double Yu = u >= 0 ? view.Y(u) : 0.0;
-        while (mm) {
-            const int vpos = g * K + low_bit(mm);
-            mm &= mm - 1;
-            const double Yv = view.Y(vpos);
-            const int sc = first_owned_chunk(u, Yu, vpos, Yv, s2l, K, G);
-            if (sc < G) atomicMax(&sslot[sc * 64 + x], (unsigned)(vpos + 1));
-            u = vpos;
-            Yu = Yv;
-        }
-    }
-    __syncthreads();
+    auto fof = [&](uint16_t v) {
+        const double t = (double)(d - (int)v);
+        return s2a * t * t;
+    };
+    LineView<uint16_t, K, decltype(fof)> view{sa.val, sa.mask, sa.occ + x, x, TW, s2l, fof};
+    uint16_t* mymarks = sa.mark + (size_t)tid * CM;
+    int o = resolve_line<K>(view, sa, mine, mymarks, g, Gp, H, active, tid, TW, x,
+                            [](uint16_t v) { return v != kNone16; }, fof);
 
-    if (active) {
-        unsigned best = 0;
-        for (int cc = 0; cc <= g; ++cc) best = max(best, sslot[cc * 64 + x]);
-        int v = (int)best - 1;
-        uint32_t* dst = out + plane * (int64_t)H * W + w0 + x;
-        if (v < 0) {
-            for (int t = 0; t < K; ++t) {
-                const int q = g * K + t;
-                if (q >= H) break;
-                dst[(int64_t)q * W] = kNone32;
-            }
-        } else {
-            walk_chunk(g, K, H, v, s2l, [&](int pos) { return ch.next_member(pos, G); },
-                       [&](int pos) { return view.Y(pos); },
-                       [&](int t, int o) {
-                           dst[(int64_t)(g * K + t) * W] = ((uint32_t)sval[o * 64 + x] << 16) | (uint32_t)o;
-                       });
-        }
+    if (n <= 0) return;   // no barrier follows
+    uint32_t* dst = out + plane * (int64_t)H * W + (int64_t)base * W + w0 + x;
+#pragma unroll 4
+    for (int t = 0; t < n; ++t) {
+        const int mk = mymarks[t];
+        o = mk > o ? mk : o;
+        const int ow = o - 1;
+        const uint32_t hi = (uint32_t)view.val(ow < 0 ? 0 : ow) << 16;
+        dst[(int64_t)t * W] = ow < 0 ? kNone32 : (hi | (uint32_t)ow);
     }
+}
+
+template <int K, int TW>
+static hipError_t launch_cols_t(const uint16_t* c0, int B, int D, int H, int W, double s2_0,
+                                double s2_1, uint32_t* c01, const ColPlan& p, hipStream_t s,
+                                KernelTimer* tm) {
+    static bool attr = false;
+    if (!attr) {
+        allow_large_lds((const void*)k_envelope_cols<K, TW>);
+        attr = true;
+    }
+    const int tiles = (W + TW - 1) / TW;
+    const int64_t nblocks = (int64_t)B * D * tiles;
+    EDT_LAUNCH(tm, "envelope_cols_3d", s,
+               hipLaunchKernelGGL((k_envelope_cols<K, TW>), dim3((unsigned)nblocks), dim3(TW, p.Gp),
+                                  p.lds, s, c0, c01, D, H, W, p.Gp, s2_0, s2_1));
+    return hipSuccess;
 }
 
 hipError_t launch_cols_3d(const uint16_t* c0, int B, int D, int H, int W, double s2_0,
                           double s2_1, uint32_t* c01, hipStream_t s, KernelTimer* tm) {
-    const int K = H <= 512 ? 32 : 64;
-    const int G = (H + K - 1) / K;
-    const size_t lds = cols_lds_bytes(H);
-    const int tiles = (W + 63) / 64;
-    const int64_t nblocks = (int64_t)B * D * tiles;
-    if (K == 32) {
-        static bool attr = false;
-        if (!attr) {
-            allow_large_lds((const void*)k_envelope_cols<32>);
-            attr = true;
-        }
-        EDT_LAUNCH(tm, "envelope_cols_3d", s,
-                   hipLaunchKernelGGL(k_envelope_cols<32>, dim3((unsigned)nblocks), dim3(64, G), lds, s,
-                                      c0, c01, D, H, W, G, s2_0, s2_1));
-    } else {
-        static bool attr = false;
-        if (!attr) {
-            allow_large_lds((const void*)k_envelope_cols<64>);
-            attr = true;
-        }
-        EDT_LAUNCH(tm, "envelope_cols_3d", s,
-                   hipLaunchKernelGGL(k_envelope_cols<64>, dim3((unsigned)nblocks), dim3(64, G), lds, s,
-                                      c0, c01, D, H, W, G, s2_0, s2_1));
-    }
-    return hipSuccess;
+    const ColPlan p = plan_cols(H);
+    if (p.K == 32) return launch_cols_t<32, 64>(c0, B, D, H, W, s2_0, s2_1, c01, p, s, tm);
+    return launch_cols_t<64, 32>(c0, B, D, H, W, s2_0, s2_1, c01, p, s, tm);
 }
 
 }  // namespace edt

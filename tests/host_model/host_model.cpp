@@ -2,7 +2,7 @@
 // exact_euclidean_distance_amd/csrc/envelope.h.
 //
 // Runs, for one line at a time, the same functions the envelope kernels run
-// (build_chunk, Chain::junction, first_owned_chunk, walk_chunk) in the same
+// (chunk_bound, build_chunk, Chain::junction, first_index_beating) in the same
 // phase order as the kernels, with plain arrays in place of LDS, so the CPU
 // test-suite can check the algorithm against the definition.  Not part of the
 // library.
@@ -21,23 +21,68 @@ struct LineView {
     using Mask = typename edt::MaskOf<K>::T;
     const double* fb;
     Mask* masks;
+    uint64_t* occ;
     double s2l;
+    int last_nonempty(int lo, int hi) const {
+        return edt::occ_last([&](int w) { return occ[w]; }, lo, hi);
+    }
+    int first_nonempty(int lo, int hi) const {
+        return edt::occ_first([&](int w) { return occ[w]; }, lo, hi);
+    }
+    void mark_empty(int c) { occ[c >> 6] &= ~(uint64_t(1) << (c & 63)); }
     Mask mask(int c) const { return masks[c]; }
     void set_mask(int c, Mask m) { masks[c] = m; }
     double Y(int pos) const { return fb[pos] + s2l * (double)pos * (double)pos; }
 };
 
+// G chunk slots of K positions (G * K >= L; slots past the line stay empty).
 template <int K>
 int run_line(const double* fb, int L, double s2l, int G, int32_t* owner) {
     using Mask = typename edt::MaskOf<K>::T;
     if ((int64_t)G * K < L) return -1;
+    const int Greal = (L + K - 1) / K;
     std::vector<Mask> masks(G, 0);
-    LineView<K> view{fb, masks.data(), s2l};
-    // phase 1: local envelopes
+    std::vector<uint64_t> occ((G + 63) / 64, 0);
+    LineView<K> view{fb, masks.data(), occ.data(), s2l};
+    // phase 0: chunk minima of F, their first minimisers, and the candidate
+    // bound U (float32, rounded up)
+    std::vector<float> fmin(G, INFINITY);
+    std::vector<int> amin(G, -1);
+    for (int g = 0; g < Greal; ++g) {
+        double mn = INFINITY;
+        for (int p = g * K; p < L && p < (g + 1) * K; ++p)
+            if (isfinite(fb[p]) && fb[p] < mn) { mn = fb[p]; amin[g] = p; }
+        fmin[g] = edt::round_up_float(mn);
+    }
+    float U = 0.0f;
+    for (int g = 0; g < Greal; ++g) {
+        const double prev = g > 0 ? (double)fmin[g - 1] : INFINITY;
+        const double next = g + 1 < Greal ? (double)fmin[g + 1] : INFINITY;
+        const float b = edt::round_up_float(edt::chunk_bound(fmin[g], prev, next, s2l, K));
+        if (b > U) U = b;
+    }
+    // phase 1: local envelopes of the candidates with F <= U that are not
+    // dominated by the nearest chunk minimisers on either side
     for (int g = 0; g < G; ++g) {
-        masks[g] = edt::build_chunk<Mask, K>(
-            g, L, [&](int t) { return fb[g * K + t]; }, [](double v) { return isfinite(v) != 0; },
+        const int base = g * K;
+        const int n = L - base < K ? L - base : K;
+        const int acur = g < Greal ? amin[g] : -1;
+        const int aprev = g > 0 && g - 1 < Greal ? amin[g - 1] : -1;
+        const int anext = g + 1 < Greal ? amin[g + 1] : -1;
+        Mask cand = 0;
+        for (int t = 0; t < n; ++t) {
+            const int p = base + t;
+            if (!isfinite(fb[p]) || !(fb[p] <= (double)U)) continue;
+            const int lo = acur >= 0 && acur < p ? acur : aprev;
+            const int hi = acur > p ? acur : anext;
+            if (lo >= 0 && hi >= 0 && edt::dominated(lo, view.Y(lo), p, view.Y(p), hi, view.Y(hi)))
+                continue;
+            cand |= Mask(1) << t;
+        }
+        masks[g] = edt::build_chunk<Mask>(
+            base, cand, [&](int t) { return fb[base + t]; },
             [&](double v, int p) { return v + s2l * (double)p * (double)p; });
+        if (masks[g]) occ[g >> 6] |= uint64_t(1) << (g & 63);
     }
     // phase 2: merge tree, one level at a time
     for (int h = 1; h < G; h <<= 1) {
@@ -48,32 +93,29 @@ int run_line(const double* fb, int L, double s2l, int G, int32_t* owner) {
             }
         }
     }
-    // phase 3: first owned chunk of every member, prefix maximum
-    std::vector<unsigned> slot(G, 0u);
+    // phase 3: every member v owns [st, en): st where it beats its
+    // predecessor, en where its successor takes over; a non-empty interval
+    // marks v + 1 at st (one writer per mark)
     edt::Chain<LineView<K>, Mask, K> ch(view);
-    for (int g = 0; g < G; ++g) {
-        Mask mm = masks[g];
-        int u = ch.last_in(0, g);
-        double Yu = u >= 0 ? view.Y(u) : 0.0;
-        while (mm) {
-            const int v = g * K + edt::low_bit(mm);
-            mm &= mm - 1;
-            const double Yv = view.Y(v);
-            const int sc = edt::first_owned_chunk(u, Yu, v, Yv, s2l, K, G);
-            if (sc < G && slot[sc] < (unsigned)(v + 1)) slot[sc] = (unsigned)(v + 1);
-            u = v;
-            Yu = Yv;
-        }
+    std::vector<int> mark(L, 0);
+    int u = -1;
+    double Yu = 0.0;
+    for (int v = ch.first_in(0, G); v >= 0;) {
+        const double Yv = view.Y(v);
+        const int st = u < 0 ? 0 : edt::first_index_beating(Yv - Yu, 2.0 * s2l * (double)(v - u), L);
+        const int w = ch.next_member(v, G);
+        int en = L;
+        if (w >= 0) en = edt::first_index_beating(view.Y(w) - Yv, 2.0 * s2l * (double)(w - v), L);
+        if (st < en) mark[st] = v + 1;
+        u = v;
+        Yu = Yv;
+        v = w;
     }
-    for (int g = 1; g < G; ++g) if (slot[g] < slot[g - 1]) slot[g] = slot[g - 1];
-    // phase 4: walk
-    for (int g = 0; g < G; ++g) {
-        const int v = (int)slot[g] - 1;
-        for (int t = 0; t < K && g * K + t < L; ++t) owner[g * K + t] = -1;
-        if (v < 0) continue;
-        edt::walk_chunk(g, K, L, v, s2l, [&](int pos) { return ch.next_member(pos, G); },
-                        [&](int pos) { return view.Y(pos); },
-                        [&](int t, int o) { owner[g * K + t] = o; });
+    // phase 4: the owner of q is the latest mark at or before q
+    int o = 0;
+    for (int q = 0; q < L; ++q) {
+        if (mark[q] > o) o = mark[q];
+        owner[q] = o - 1;
     }
     return 0;
 }
@@ -82,6 +124,8 @@ int run_line(const double* fb, int L, double s2l, int G, int32_t* owner) {
 
 extern "C" int model_envelope_line(const double* fb, int L, double s2l, int K, int G,
                                    int32_t* owner) {
+    if (K == 8) return run_line<8>(fb, L, s2l, G, owner);
+    if (K == 16) return run_line<16>(fb, L, s2l, G, owner);
     if (K == 32) return run_line<32>(fb, L, s2l, G, owner);
     if (K == 64) return run_line<64>(fb, L, s2l, G, owner);
     return -1;

@@ -58,7 +58,7 @@ def _value_at(fb, own, s2l):
 
 def _layouts(L):
     out = []
-    for K in (32, 64):
+    for K in (8, 16, 32, 64):
         g0 = -(-L // K)
         p2 = 1 << max(0, (g0 - 1).bit_length())
         out += [(K, g0), (K, p2), (K, g0 + 3)]
@@ -130,7 +130,7 @@ def _model_edt(model, mask, sampling, K):
     return F
 
 
-@pytest.mark.parametrize("K", [32, 64])
+@pytest.mark.parametrize("K", [8, 16, 32, 64])
 def test_model_transform_matches_oracle(model, K):
     rng = np.random.default_rng([42, 2001, K])
     cases = []
