@@ -2,21 +2,33 @@
 """Benchmark of the exact EDT hot path on one MI355X.
 
 One step = one complete transform (every pass of the path) of one synthetic
-workload already resident in HBM.  Prints ONE JSON line:
+workload already resident in HBM.  The default workload is the 512^3 volume
+with spacing (2.5, 1, 1) and distances + indices: the one configuration that
+runs all three passes (axis-0 scan, middle-axis envelope, last-axis envelope
+with the epilogue).  Prints ONE JSON line:
 
   value        whole-job throughput, Gpixel/s (elements per second / 1e9)
   roofline     the dominant kernel's algorithmic HBM bytes per launch / its mean
-               duration (HIP events on the launch stream), against 8 TB/s
+               duration (HIP events on the launch stream), against 8 TB/s; the
+               measured HBM traffic of that kernel comes from the committed
+               rocprofv3 counter summary (profiles/traffic_<config>.json) and is
+               null when the kernel sources changed since it was taken
   cpu_baseline the CPU oracle (single thread) on a bounded sample of the same
-               workload, same units
+               workload, same unit
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c3]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c5]
                        [--no-cpu-baseline] [--check]
+       python bench.py --probe-copy           (copy kernel for counter calibration)
+       python bench.py --summarize-traffic FETCH WRITE COPY_FETCH COPY_WRITE --config c5
+                       (rocprofv3 --pmc output directories -> profiles/traffic_<config>.json)
 """
 
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
 import platform
@@ -30,6 +42,12 @@ sys.path.insert(0, ROOT)
 
 METRIC = "EDT Gpixel/s at 1 GPU + achieved HBM GB/s fraction of peak"
 HBM_PEAK_GBS = 8000.0   # MI355X HBM3E peak, GB/s
+DEFAULT_CONFIG = "c5"
+COPY_PROBE_BYTES = 1 << 30   # float32 elements read (and as many written) by the copy probe
+KERNEL_SOURCES = ("exact_euclidean_distance_amd/csrc/kernels.hip",
+                  "exact_euclidean_distance_amd/csrc/envelope.h",
+                  "exact_euclidean_distance_amd/csrc/kernels.h",
+                  "exact_euclidean_distance_amd/csrc/abi.hip")
 
 WORKLOADS = {
     "c1": "2D 512x512 uint8, background i.i.d. Bernoulli(0.01), isotropic; "
@@ -58,7 +76,7 @@ def algorithmic_bytes(kernel: str, shape, n_out: int) -> int:
     """Bytes a kernel must move through HBM by the per-element byte model:
     every input it needs read once and every output written once, at the
     narrowest exact width (mask 1 B, axis-0 coordinate 2 B, packed coordinate
-    pair 4 B, each requested output 4 B)."""
+    pair 4 B, each requested output 4 B; segment summaries 2 B each)."""
     n = int(np.prod(shape))
     if len(shape) == 2:
         n0, M, B = shape[0], shape[1], 1
@@ -81,35 +99,159 @@ def algorithmic_bytes(kernel: str, shape, n_out: int) -> int:
     raise KeyError(kernel)
 
 
-def cpu_baseline(name, mask, sampling):
-    """Time the oracle (single thread, as written) on a bounded sample."""
+def sources_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+# rocprofv3 kernel names -> the names the timed entry points report
+KERNEL_KEYS = (("k_axis0_summary", "axis0_summary"), ("k_axis0_scan", "axis0_scan"),
+               ("k_axis0_resolve", "axis0_resolve"), ("k_envelope_cols", "envelope_cols_3d"),
+               ("Geo3D", "envelope_rows_3d"), ("Geo2D", "envelope_rows_2d"))
+
+
+def _kernel_key(name: str):
+    for pat, key in KERNEL_KEYS:
+        if pat in name:
+            return key
+    return None
+
+
+def _pmc_per_dispatch(run_dir: str, counter: str):
+    """Mean value of one counter per dispatch, per kernel, from a rocprofv3
+    --pmc --output-format csv directory."""
+    files = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise FileNotFoundError(f"no counter_collection.csv under {run_dir}")
+    acc = {}
+    for path in files:
+        with open(path) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] != counter:
+                    continue
+                acc.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return {k: float(np.mean(v)) for k, v in acc.items()}
+
+
+def summarize_traffic(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, config):
+    """Write profiles/traffic_<config>.json: per-kernel HBM bytes per dispatch
+    from FETCH_SIZE / WRITE_SIZE (KiB), each scaled by the same counter's
+    reading for the copy probe divided by the bytes it is known to move."""
+    fetch = _pmc_per_dispatch(fetch_dir, "FETCH_SIZE")
+    write = _pmc_per_dispatch(write_dir, "WRITE_SIZE")
+    cf = _pmc_per_dispatch(copy_fetch_dir, "FETCH_SIZE")
+    cw = _pmc_per_dispatch(copy_write_dir, "WRITE_SIZE")
+    # the copy probe is the largest dispatch of its run
+    copy_fetch_kib = max(cf.values())
+    copy_write_kib = max(cw.values())
+    f_fetch = copy_fetch_kib * 1024.0 / COPY_PROBE_BYTES
+    f_write = copy_write_kib * 1024.0 / COPY_PROBE_BYTES
+    kernels = {}
+    for name, kib in fetch.items():
+        key = _kernel_key(name)
+        if key is None:
+            continue
+        wkib = write.get(name, 0.0)
+        kernels[key] = {
+            "rocprof_name": name,
+            "FETCH_SIZE_KiB": round(kib, 1), "WRITE_SIZE_KiB": round(wkib, 1),
+            "hbm_bytes": int(kib * 1024.0 / f_fetch + wkib * 1024.0 / f_write),
+        }
+    out = {"config": config, "sources_sha256_16": sources_hash(),
+           "copy_probe_bytes_each_way": COPY_PROBE_BYTES,
+           "copy_probe_FETCH_SIZE_KiB": round(copy_fetch_kib, 1),
+           "copy_probe_WRITE_SIZE_KiB": round(copy_write_kib, 1),
+           "scale_fetch": round(f_fetch, 5), "scale_write": round(f_write, 5),
+           "kernels": kernels}
+    path = os.path.join(ROOT, "profiles", f"traffic_{config}.json")
+    with open(path, "w") as fh:
+        json.dump(out, fh, indent=1)
+        fh.write("\n")
+    print(json.dumps(out, indent=1))
+    return 0
+
+
+def measured_traffic(config: str, kernel: str):
+    path = os.path.join(ROOT, "profiles", f"traffic_{config}.json")
+    try:
+        with open(path) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if t.get("sources_sha256_16") != sources_hash():
+        return None
+    k = t.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("hbm_bytes")
+
+
+def probe_copy():
+    """A plain elementwise kernel of known size (reads and writes
+    COPY_PROBE_BYTES each) for calibrating FETCH_SIZE / WRITE_SIZE."""
+    import torch
+    dev = torch.device("cuda:0")
+    a = torch.ones(COPY_PROBE_BYTES // 4, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        torch.neg(a, out=b)
+    torch.cuda.synchronize()
+    print("copy probe done", flush=True)
+    return 0
+
+
+def cpu_baseline(name, mask, sampling, budget_s=15.0):
+    """Time the oracle (single thread, as written) on a bounded sample of the
+    same workload: whole volumes for batched 3-D, whole 3-D volumes split into
+    slabs of axis-0 planes otherwise, leading rows for 2-D; grown until about
+    budget_s seconds of oracle time."""
     import oracle
+    want_idx = "indices" in OUTPUTS[name]
     if mask.ndim == 2:
         rows = mask.shape[0]
-        budget = 40_000_000           # elements: a few seconds of oracle time
-        take = max(1, min(rows, budget // mask.shape[1]))
-        sample = np.ascontiguousarray(mask[:take])
-        if not (sample == 0).any():
-            sample = np.ascontiguousarray(mask)
-            take = rows
-        t0 = time.perf_counter()
-        oracle.edt(sample, sampling, features=False)
-        dt = time.perf_counter() - t0
+        take = max(1, min(rows, 2_000_000 // mask.shape[1]))
+        while True:
+            sample = np.ascontiguousarray(mask[:take])
+            if not (sample == 0).any():
+                sample[0, 0] = 0
+            t0 = time.perf_counter()
+            oracle.edt(sample, sampling, features=want_idx)
+            dt = time.perf_counter() - t0
+            if dt >= budget_s / 4 or take == rows:
+                break
+            take = min(rows, int(take * max(2.0, budget_s / max(dt, 1e-3) * 0.8)))
         desc = f"oracle on rows [0,{take}) of the {mask.shape[0]}x{mask.shape[1]} mask"
-        n = sample.size
     else:
-        vols = mask.shape[0]
-        budget = 40_000_000
-        per = int(np.prod(mask.shape[1:]))
-        take = max(1, min(vols, budget // per))
-        sample = mask[:take]
-        t0 = time.perf_counter()
-        oracle.edt_batch(sample, sampling, features=("indices" in OUTPUTS[name]))
-        dt = time.perf_counter() - t0
-        desc = f"oracle on {take} of {vols} volumes of {mask.shape[1:]}"
-        n = sample.size
+        vols, D = mask.shape[0], mask.shape[1]
+        if vols > 1:
+            take = 1
+            while True:
+                sample = mask[:take]
+                t0 = time.perf_counter()
+                oracle.edt_batch(sample, sampling, features=want_idx)
+                dt = time.perf_counter() - t0
+                if dt >= budget_s / 4 or take == vols:
+                    break
+                take = min(vols, int(take * max(2.0, budget_s / max(dt, 1e-3) * 0.8)))
+            desc = f"oracle on {take} of {vols} volumes of {mask.shape[1:]}"
+        else:
+            take = max(1, min(D, 8))
+            while True:
+                sample = np.ascontiguousarray(mask[0, :take])
+                if not (sample == 0).any():
+                    sample.reshape(-1)[0] = 0
+                t0 = time.perf_counter()
+                oracle.edt(sample, sampling, features=want_idx)
+                dt = time.perf_counter() - t0
+                if dt >= budget_s / 4 or take == D:
+                    break
+                take = min(D, int(take * max(2.0, budget_s / max(dt, 1e-3) * 0.8)))
+            desc = (f"oracle on axis-0 planes [0,{take}) of the {mask.shape[1:]} volume "
+                    f"(as its own volume)")
+    n = sample.size
     return {"value": n / dt / 1e9, "unit": "Gpixel/s", "cores": 1, "kind": "oracle",
-            "sample": desc, "seconds": round(dt, 3),
+            "sample": desc + (", with indices" if want_idx else ""), "seconds": round(dt, 3),
             "cpu": platform.processor() or platform.machine()}
 
 
@@ -118,15 +260,23 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", default="c3", choices=sorted(WORKLOADS))
+    ap.add_argument("--config", default=DEFAULT_CONFIG, choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--check", action="store_true", help="also compare with the oracle")
+    ap.add_argument("--probe-copy", action="store_true")
+    ap.add_argument("--summarize-traffic", nargs=4, metavar="DIR")
     args = ap.parse_args(argv)
+
+    if args.summarize_traffic:
+        return summarize_traffic(*args.summarize_traffic, args.config)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build measures one GPU only (the transform of one "
               "workload runs on a single MI355X); run with --gpus 1", file=sys.stderr)
         return 2
+
+    if args.probe_copy:
+        return probe_copy()
 
     import torch
     from exact_euclidean_distance_amd import alloc_workspace, edt2d, edt3d, workspace_size_2d, \
@@ -175,7 +325,8 @@ def main(argv=None):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / max(1, args.steps)
 
-    # per-kernel durations: HIP events recorded by the library around each launch
+    # per-kernel durations: HIP events recorded by the library around each
+    # launch, on the stream the kernels run on
     per = {}
     for _ in range(max(3, args.steps)):
         _, times = step(timed=True)
@@ -211,6 +362,7 @@ def main(argv=None):
         cpu = cpu_baseline(name, mask_np, sampling)
 
     total_bytes = sum(k["alg_bytes"] for k in kernels)
+    traffic = measured_traffic(name, dom["name"])
     line = {
         "metric": METRIC,
         "value": round(n / (ms * 1e-3) / 1e9, 3),
@@ -228,7 +380,7 @@ def main(argv=None):
                    "sampling": list(sampling) if sampling else None, "outputs": list(want)},
         "roofline": {"bound": "hbm", "kernel": dom["name"], "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic},
         "path_GBps": round(total_bytes / (ms * 1e-3) / 1e9, 1),
         "kernels": kernels,
         "cpu_baseline": cpu,
