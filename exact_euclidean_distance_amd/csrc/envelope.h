@@ -231,4 +231,204 @@ EDT_HD inline int first_index_beating(double A, double B, int cap) {
     return c;
 }
 
+// Up to eight 16-bit values held in four 32-bit registers; no array, so
+// nothing is placed in scratch memory whatever the index.
+struct Packed8 {
+    uint32_t w0 = 0, w1 = 0, w2 = 0, w3 = 0;
+    EDT_HD int get(int i) const {
+        const int k = i >> 1;
+        const uint32_t w = k == 0 ? w0 : k == 1 ? w1 : k == 2 ? w2 : w3;
+        return (int)((w >> ((i & 1) * 16)) & 0xFFFFu);
+    }
+    EDT_HD void set(int i, int v) {
+        const int sh = (i & 1) * 16;
+        const uint32_t keep = ~(0xFFFFu << sh), put = ((uint32_t)v & 0xFFFFu) << sh;
+        const int k = i >> 1;
+        if (k == 0) w0 = (w0 & keep) | put;
+        else if (k == 1) w1 = (w1 & keep) | put;
+        else if (k == 2) w2 = (w2 & keep) | put;
+        else w3 = (w3 & keep) | put;
+    }
+};
+
+// Owner marks of one chunk (positions [b, e], b = cK) from its local envelope
+// M and the members of other chunks that reach into it, with no merging of
+// whole lines.
+//
+// A member m < b can own a position of the chunk only if it is strictly nearer
+// at b than every member between m and b: for m < x, pi_m - pi_x grows with q,
+// so losing at b means losing on the whole chunk.  Scanning leftwards from b,
+// such members are kept while s^2 (b - m)^2 stays below the best value at b so
+// far (beyond that no member can beat it).  Symmetrically on the right at e.
+// The reaching members (at most CAP per side) and the chunk's members form a
+// short sorted sequence whose lower envelope, on [b, e], is the line's.  Its
+// members then get their owned intervals; mark(t, owner) is called at chunk
+// offset t where an interval starts (t = 0 for the owner of b).  A whole chunk
+// is passed over when a lower bound of its F plus the squared distance to its
+// nearest position is no better than the best value so far.  Returns false
+// without marking if more than CAP members reach in from one side.
+// View: Y(pos), f(pos), s2l, mask(c), last_nonempty / first_nonempty (as for
+// Chain), fmin_lb(c) (a lower bound of F over chunk c).  Needs 2 CAP + K <= 64.
+template <int K, int CAP, class View, class Mask, class Mark>
+EDT_HD inline bool chunk_owner_marks(View& v, int c, int G, int L, Mask M, Mark mark) {
+    static_assert(2 * CAP + K <= 64, "sequence index space must fit 64 bits");
+    static_assert(CAP <= 8, "reach lists hold at most eight members");
+    const int b = c * K;
+    const int n = L - b < K ? L - b : K;
+    const int e = b + n - 1;
+    const double s2 = v.s2l;
+    Chain<View, Mask, K> ch(v);
+
+    // members reaching in from the left (Lp[0] nearest) and from the right
+    Packed8 Lp, Rp;
+    int nL = 0, nR = 0;
+    double best = __builtin_huge_val();
+    if (M) {
+        const int x = b + low_bit(M);
+        const double d = (double)(x - b);
+        best = v.f(x) + s2 * d * d;
+    }
+    for (int m = ch.last_in(0, c), seen = -1; m >= 0;) {
+        const int cm = m / K;
+        if (cm != seen) {   // entering chunk cm: pass over it if it cannot win
+            seen = cm;
+            const double dn = (double)(b - (cm * K + K - 1));
+            if (!(s2 * dn * dn < best)) break;
+            if (!(v.fmin_lb(cm) + s2 * dn * dn < best)) {
+                m = ch.last_in(0, cm);
+                continue;
+            }
+        }
+        const double d = (double)(b - m);
+        const double dd = s2 * d * d;
+        if (!(dd < best)) break;
+        const double p = v.f(m) + dd;
+        if (p < best) {
+            if (nL == CAP) return false;
+            Lp.set(nL, m);
+            ++nL;
+            best = p;
+        }
+        m = ch.prev_member(m, 0);
+    }
+    best = __builtin_huge_val();
+    if (M) {
+        const int x = b + high_bit(M);
+        const double d = (double)(e - x);
+        best = v.f(x) + s2 * d * d;
+    }
+    for (int m = ch.first_in(c + 1, G), seen = -1; m >= 0;) {
+        const int cm = m / K;
+        if (cm != seen) {   // entering chunk cm: pass over it if it cannot win
+            seen = cm;
+            const double dn = (double)(cm * K - e);
+            if (!(s2 * dn * dn < best)) break;
+            if (!(v.fmin_lb(cm) + s2 * dn * dn < best)) {
+                m = ch.first_in(cm + 1, G);
+                continue;
+            }
+        }
+        const double d = (double)(m - e);
+        const double dd = s2 * d * d;
+        if (!(dd < best)) break;
+        const double p = v.f(m) + dd;
+        if (p < best) {
+            if (nR == CAP) return false;
+            Rp.set(nR, m);
+            ++nR;
+            best = p;
+        }
+        m = ch.next_member(m, G);
+    }
+
+    // Sequence index space: [0, nL) the left members in increasing position,
+    // [CAP, CAP + K) the chunk's positions, [CAP + K, CAP + K + nR) the right
+    // members in increasing position.
+    auto pos_of = [&](int i) -> int {
+        if (i < CAP) return Lp.get(nL - 1 - i);
+        if (i < CAP + K) return b + (i - CAP);
+        return Rp.get(i - CAP - K);
+    };
+    auto in_chunk = [&](int i) { return i >= CAP && i < CAP + K; };
+
+    // lower envelope of the sequence (insertion sweep; the chunk's own members
+    // are already convex, so once two of them lead the stack the rest of them
+    // are appended without tests)
+    uint64_t alive = 0;
+    int top = -1, sec = -1;
+    double Ytop = 0.0, Ysec = 0.0;
+    auto insert = [&](int i) {
+        const int p = pos_of(i);
+        const double Y = v.Y(p);
+        while (sec >= 0 && dominated(pos_of(sec), Ysec, pos_of(top), Ytop, p, Y)) {
+            alive &= ~(uint64_t(1) << top);
+            top = sec;
+            Ytop = Ysec;
+            const uint64_t below = alive & ((uint64_t(1) << top) - 1);
+            if (below) {
+                sec = high_bit(below);
+                Ysec = v.Y(pos_of(sec));
+            } else {
+                sec = -1;
+            }
+        }
+        alive |= uint64_t(1) << i;
+        sec = top;
+        Ysec = Ytop;
+        top = i;
+        Ytop = Y;
+    };
+    for (int i = 0; i < nL; ++i) insert(i);
+    Mask rest = M;
+    while (rest) {
+        if (top >= 0 && sec >= 0 && in_chunk(top) && in_chunk(sec)) {
+            // append the remaining chunk members
+            const int t_last = high_bit(rest);
+            alive |= (uint64_t)rest << CAP;
+            if (rest & (rest - 1)) {
+                const Mask below = rest & ~(Mask(1) << t_last);
+                sec = CAP + high_bit(below);
+            } else {
+                sec = top;
+            }
+            top = CAP + t_last;
+            Ytop = v.Y(pos_of(top));
+            Ysec = v.Y(pos_of(sec));
+            break;
+        }
+        const int t = low_bit(rest);
+        rest &= rest - 1;
+        insert(CAP + t);
+    }
+    for (int i = 0; i < nR; ++i) insert(CAP + K + i);
+
+    // owned intervals: member i owns [st, en), st where it is strictly nearer
+    // than its predecessor, en where its successor is; clipped to [b, e]
+    if (!alive) return true;
+    int i = low_bit(alive);
+    int pi = pos_of(i);
+    double Yi = v.Y(pi);
+    int st = b;
+    for (;;) {
+        const uint64_t after = alive & ~((uint64_t(2) << i) - 1);
+        int en = e + 1;
+        int j = -1, pj = 0;
+        double Yj = 0.0;
+        if (after) {
+            j = low_bit(after);
+            pj = pos_of(j);
+            Yj = v.Y(pj);
+            en = first_index_beating(Yj - Yi, 2.0 * s2 * (double)(pj - pi), e + 1);
+        }
+        const int lo = st > b ? st : b;
+        if (lo < en) mark(lo - b, pi);
+        if (j < 0 || en > e) break;
+        i = j;
+        pi = pj;
+        Yi = Yj;
+        st = en;
+    }
+    return true;
+}
+
 }  // namespace edt

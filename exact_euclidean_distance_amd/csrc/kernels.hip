@@ -305,13 +305,15 @@ hipError_t launch_axis0(const uint8_t* mask, int B, int n0, int64_t M, uint16_t*
 // member).
 //
 // Phases of one line (all lanes of the line together):
-//   1. chunk minima of F and the line's candidate bound U (see chunk_bound);
-//   2. local envelope of every chunk's candidates with F <= U;
-//   3. merge tree of the chunk envelopes;
-//   4. every member v computes the interval [st, en) of positions it owns and,
-//      if it is non-empty, writes v + 1 at position st (intervals are disjoint,
-//      so every mark has one writer);
-//   5. each lane scans its chunk: the owner of position q is the latest mark at
+//   1. chunk minima of F and the line's candidate bound U (see chunk_bound),
+//      then the candidates a nearest chunk minimiser pair dominates are dropped;
+//   2. local envelope of every chunk's remaining candidates;
+//   3. each lane resolves its chunk alone from its own envelope and the few
+//      members of other chunks that reach into it (chunk_owner_marks), writing
+//      owner + 1 where each owned interval starts; if a chunk has more reaching
+//      members than fit, the block instead merges whole lines (merge tree,
+//      every member marking the start of its interval, a chunk-level scan);
+//   4. each lane scans its chunk: the owner of position q is the latest mark at
 //      or before q, so the outputs follow without any per-position search.
 // --------------------------------------------------------------------------
 
@@ -321,17 +323,18 @@ struct Slots {
     static constexpr int CM = K + 2;                               // mark stride (16-bit)
     using Mask = typename MaskOf<K>::T;
     // Occupancy words: ceil(Gp / 64) per line of Gp chunks.
-    static int occ_words(int nslots, int Gp) { return (nslots / Gp) * ((Gp + 63) / 64); }
+    __host__ __device__ static int occ_words(int nslots, int Gp) { return (nslots / Gp) * ((Gp + 63) / 64); }
     // The per-line bound words share the storage of the two 16-bit scan arrays,
     // which are not live until later (lines per block <= slots).
     static size_t bytes(int nslots, int Gp) {
         return align16((size_t)nslots * CS * sizeof(Val)) + align16((size_t)nslots * CM * 2) +
                align16((size_t)nslots * sizeof(Mask)) + align16((size_t)nslots * 4) +
-               2 * align16((size_t)nslots * 2) + align16((size_t)occ_words(nslots, Gp) * 8);
+               2 * align16((size_t)nslots * 2) + align16((size_t)occ_words(nslots, Gp) * 8) + 16;
     }
 };
 
 constexpr uint16_t kNoFirst = 0xFFFFu;   // "no member" in the first-member scan
+constexpr int kReach = 8;                // reaching members kept per chunk side
 
 // LDS carve-up shared by both layouts.
 template <class Val, int K>
@@ -346,7 +349,8 @@ struct SlotArrays {
     unsigned* bound;  // per line: the candidate bound U (float32 bits); shares
                       // the storage of last/first, used before they are written
     uint64_t* occ;    // per line: bit c set while chunk c has a member
-    __device__ SlotArrays(unsigned char* smem, int nslots) {
+    unsigned* flag;   // per block: some chunk needs the whole-line merge
+    __device__ SlotArrays(unsigned char* smem, int nslots, int Gp) {
         size_t off = 0;
         val = reinterpret_cast<Val*>(smem);
         off += align16((size_t)nslots * Slots<Val, K>::CS * sizeof(Val));
@@ -362,6 +366,8 @@ struct SlotArrays {
         off += align16((size_t)nslots * 2);
         bound = reinterpret_cast<unsigned*>(last);
         occ = reinterpret_cast<uint64_t*>(smem + off);
+        off += align16((size_t)Slots<Val, K>::occ_words(nslots, Gp) * 8);
+        flag = reinterpret_cast<unsigned*>(smem + off);
     }
 };
 
@@ -374,9 +380,15 @@ struct LineView {
     const Val* vals;
     Mask* masks;
     uint64_t* occ;
+    const int* own;   // chunk minima of F as float32 bits, rounded up
     int slot0, gs;
     double s2l;
     FOf fof;
+    // a lower bound of F over chunk c: its float32 minimum is within one float32
+    // step above the exact one
+    __device__ double fmin_lb(int c) const {
+        return (double)__int_as_float(own[slot(c)]) * (1.0 - 0x1p-22);
+    }
     __device__ int last_nonempty(int lo, int hi) const {
         return occ_last([&](int w) { return occ[w]; }, lo, hi);
     }
@@ -411,11 +423,11 @@ __device__ void line_scans(T* a, uint16_t* b, int myslot, int g, int gs, int Gp)
 }
 
 // Phases 1-4 for the lane's chunk g of its line (local line index lslot).
-// Fills the line's owner marks and returns owner + 1 of the position just
-// before the chunk (0: no owner yet).  Every thread of the block must call it
-// (it contains barriers).
+// Fills the owner marks of the lane's chunk: the owner of a position is the
+// largest mark at or before it within the chunk.  Every thread of the block
+// must call it (it contains barriers).
 template <int K, class Val, class View, class IsValid, class FOfVal>
-__device__ int resolve_line(View& view, SlotArrays<Val, K>& sa, const Val* mychunk,
+__device__ void resolve_line(View& view, SlotArrays<Val, K>& sa, const Val* mychunk,
                             uint16_t* mymarks, int g, int Gp, int L, bool active, int myslot,
                             int gs, int lslot, IsValid valid, FOfVal fval) {
     using Mask = typename MaskOf<K>::T;
@@ -441,6 +453,7 @@ __device__ int resolve_line(View& view, SlotArrays<Val, K>& sa, const Val* mychu
     sa.mask[myslot] = (Mask)(amin < 0 ? 0 : base + amin + 1);
     if (g == 0) sa.bound[lslot] = 0u;
     if ((g & 63) == 0) view.occ[g >> 6] = 0ull;
+    if (myslot == 0) *sa.flag = 0u;
     __syncthreads();
     int aprev = -1, anext = -1;
     if (n > 0) {
@@ -481,7 +494,26 @@ __device__ int resolve_line(View& view, SlotArrays<Val, K>& sa, const Val* mychu
     sa.mask[myslot] = m;
     if (m) atomicOr(&view.occ[g >> 6], uint64_t(1) << (g & 63));
 
-    // 3. merge tree
+    __syncthreads();
+
+    // 3. owners of the chunk from its own envelope and the members of other
+    //    chunks that reach into it (chunk_owner_marks); only if some chunk of
+    //    the block has more reaching members than the lists hold does the
+    //    block merge whole lines instead
+    bool ok = false;
+    if constexpr (2 * kReach + K <= 64) {
+#pragma unroll
+        for (int t = 0; t < K; t += 2) *reinterpret_cast<uint32_t*>(mymarks + t) = 0u;
+        ok = true;
+        if (n > 0)
+            ok = chunk_owner_marks<K, kReach>(view, g, G, L, m,
+                                              [&](int t, int o) { mymarks[t] = (uint16_t)(o + 1); });
+    }
+    if (!ok) atomicOr(sa.flag, 1u);
+    __syncthreads();
+    if (*sa.flag == 0u) return;
+
+    // 4. fallback: merge tree of the chunk envelopes over whole lines
     for (int h = 1; h < Gp; h <<= 1) {
         __syncthreads();
         if (active && (g & (2 * h - 1)) == h) {
@@ -500,8 +532,8 @@ __device__ int resolve_line(View& view, SlotArrays<Val, K>& sa, const Val* mychu
     for (int t = 0; t < K; t += 2) *reinterpret_cast<uint32_t*>(mymarks + t) = 0u;
     line_scans(sa.last, sa.first, myslot, g, gs, Gp);
 
-    // 4. owned intervals of the members: v owns [st, en), st against its
-    //    predecessor u, en where its successor w takes over
+    // owned intervals of the members: v owns [st, en), st against its
+    // predecessor u, en where its successor w takes over
     if (m) {
         Mask mm = m;
         const int u = g > 0 ? (int)sa.last[myslot - gs] - 1 : -1;
@@ -537,7 +569,9 @@ __device__ int resolve_line(View& view, SlotArrays<Val, K>& sa, const Val* mychu
         }
     }
     line_scans(sa.own, (uint16_t*)nullptr, myslot, g, gs, Gp);
-    return g > 0 ? sa.own[myslot - gs] : 0;
+    // the owner entering the chunk becomes its first mark (marks only grow)
+    const int enter = g > 0 ? sa.own[myslot - gs] : 0;
+    if (n > 0 && enter > (int)mymarks[0]) mymarks[0] = (uint16_t)enter;
 }
 
 // --------------------------------------------------------------------------
@@ -641,7 +675,7 @@ __global__ __launch_bounds__(1024) void k_envelope_rows(const typename Geo::Val*
     constexpr int CS = Slots<Val, K>::CS;
     constexpr int CM = Slots<Val, K>::CM;
     extern __shared__ __align__(16) unsigned char smem[];
-    SlotArrays<Val, K> sa(smem, Gp * LPW);
+    SlotArrays<Val, K> sa(smem, Gp * LPW, Gp);
 
     const int tid = threadIdx.x;
     const int g = tid & (Gp - 1);
@@ -656,10 +690,11 @@ __global__ __launch_bounds__(1024) void k_envelope_rows(const typename Geo::Val*
     const typename Geo::Line gl = geo.line(active ? line : 0);
     auto fof = [&](Val v) { return geo.f(gl, v); };
     LineView<Val, K, decltype(fof)> view{sa.val, sa.mask, sa.occ + (size_t)r * ((Gp + 63) / 64),
-                                         slot0, 1, geo.s2l, fof};
+                                         sa.own, slot0, 1, geo.s2l, fof};
     uint16_t* mymarks = sa.mark + (size_t)tid * CM;
-    int o = resolve_line<K>(view, sa, sa.val + (size_t)tid * CS, mymarks, g, Gp, L, active, tid, 1,
-                            r, [](Val v) { return Geo::valid(v); }, fof);
+    resolve_line<K>(view, sa, sa.val + (size_t)tid * CS, mymarks, g, Gp, L, active, tid, 1, r,
+                    [](Val v) { return Geo::valid(v); }, fof);
+    int o = 0;
 
     // 5. outputs of the chunk
     const int base = g * K;
@@ -821,7 +856,7 @@ __global__ __launch_bounds__(1024) void k_envelope_cols(const uint16_t* __restri
     constexpr int CS = Slots<uint16_t, K>::CS;
     constexpr int CM = Slots<uint16_t, K>::CM;
     extern __shared__ __align__(16) unsigned char smem[];
-    SlotArrays<uint16_t, K> sa(smem, Gp * TW);
+    SlotArrays<uint16_t, K> sa(smem, Gp * TW, Gp);
 
     const int x = threadIdx.x;
     const int g = threadIdx.y;
@@ -854,10 +889,11 @@ __global__ __launch_bounds__(1024) void k_envelope_cols(const uint16_t* __restri
         const double t = (double)(d - (int)v);
         return s2a * t * t;
     };
-    LineView<uint16_t, K, decltype(fof)> view{sa.val, sa.mask, sa.occ + x, x, TW, s2l, fof};
+    LineView<uint16_t, K, decltype(fof)> view{sa.val, sa.mask, sa.occ + x, sa.own, x, TW, s2l, fof};
     uint16_t* mymarks = sa.mark + (size_t)tid * CM;
-    int o = resolve_line<K>(view, sa, mine, mymarks, g, Gp, H, active, tid, TW, x,
-                            [](uint16_t v) { return v != kNone16; }, fof);
+    resolve_line<K>(view, sa, mine, mymarks, g, Gp, H, active, tid, TW, x,
+                    [](uint16_t v) { return v != kNone16; }, fof);
+    int o = 0;
 
     if (n <= 0) return;   // no barrier follows
     uint32_t* dst = out + plane * (int64_t)H * W + (int64_t)base * W + w0 + x;

@@ -2,7 +2,8 @@
 // exact_euclidean_distance_amd/csrc/envelope.h.
 //
 // Runs, for one line at a time, the same functions the envelope kernels run
-// (chunk_bound, build_chunk, Chain::junction, first_index_beating) in the same
+// (chunk_bound, build_chunk, chunk_owner_marks, Chain::junction,
+// first_index_beating) in the same
 // phase order as the kernels, with plain arrays in place of LDS, so the CPU
 // test-suite can check the algorithm against the definition.  Not part of the
 // library.
@@ -10,6 +11,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
 #include <vector>
 
 #include "../../exact_euclidean_distance_amd/csrc/envelope.h"
@@ -22,7 +24,9 @@ struct LineView {
     const double* fb;
     Mask* masks;
     uint64_t* occ;
+    const float* fminc;   // chunk minima of F as float32, rounded up
     double s2l;
+    double fmin_lb(int c) const { return (double)fminc[c] * (1.0 - 0x1p-22); }
     int last_nonempty(int lo, int hi) const {
         return edt::occ_last([&](int w) { return occ[w]; }, lo, hi);
     }
@@ -32,21 +36,24 @@ struct LineView {
     void mark_empty(int c) { occ[c >> 6] &= ~(uint64_t(1) << (c & 63)); }
     Mask mask(int c) const { return masks[c]; }
     void set_mask(int c, Mask m) { masks[c] = m; }
+    double f(int pos) const { return fb[pos]; }
     double Y(int pos) const { return fb[pos] + s2l * (double)pos * (double)pos; }
 };
 
 // G chunk slots of K positions (G * K >= L; slots past the line stay empty).
-template <int K>
+// CAP: members reaching into a chunk from one side before the line falls back
+// to the merge tree (0: always the merge tree).
+template <int K, int CAP>
 int run_line(const double* fb, int L, double s2l, int G, int32_t* owner) {
     using Mask = typename edt::MaskOf<K>::T;
     if ((int64_t)G * K < L) return -1;
     const int Greal = (L + K - 1) / K;
     std::vector<Mask> masks(G, 0);
     std::vector<uint64_t> occ((G + 63) / 64, 0);
-    LineView<K> view{fb, masks.data(), occ.data(), s2l};
     // phase 0: chunk minima of F, their first minimisers, and the candidate
     // bound U (float32, rounded up)
     std::vector<float> fmin(G, INFINITY);
+    LineView<K> view{fb, masks.data(), occ.data(), fmin.data(), s2l};
     std::vector<int> amin(G, -1);
     for (int g = 0; g < Greal; ++g) {
         double mn = INFINITY;
@@ -84,32 +91,45 @@ int run_line(const double* fb, int L, double s2l, int G, int32_t* owner) {
             [&](double v, int p) { return v + s2l * (double)p * (double)p; });
         if (masks[g]) occ[g >> 6] |= uint64_t(1) << (g & 63);
     }
-    // phase 2: merge tree, one level at a time
-    for (int h = 1; h < G; h <<= 1) {
-        for (int g = 0; g < G; ++g) {
-            if ((g & (2 * h - 1)) == h) {
-                edt::Chain<LineView<K>, Mask, K> ch(view);
-                ch.junction(g - h, g, g + h < G ? g + h : G);
-            }
+    std::vector<int> mark(L, 0);
+    // phase 2: owners of each chunk from its own envelope and the members of
+    // other chunks that reach into it
+    bool ok = CAP > 0;
+    if constexpr (CAP > 0) {
+        for (int g = 0; g < Greal && ok; ++g) {
+            const int base = g * K;
+            ok = edt::chunk_owner_marks<K, CAP>(view, g, Greal, L, masks[g],
+                                                [&](int t, int o) { mark[base + t] = o + 1; });
         }
     }
-    // phase 3: every member v owns [st, en): st where it beats its
-    // predecessor, en where its successor takes over; a non-empty interval
-    // marks v + 1 at st (one writer per mark)
-    edt::Chain<LineView<K>, Mask, K> ch(view);
-    std::vector<int> mark(L, 0);
-    int u = -1;
-    double Yu = 0.0;
-    for (int v = ch.first_in(0, G); v >= 0;) {
-        const double Yv = view.Y(v);
-        const int st = u < 0 ? 0 : edt::first_index_beating(Yv - Yu, 2.0 * s2l * (double)(v - u), L);
-        const int w = ch.next_member(v, G);
-        int en = L;
-        if (w >= 0) en = edt::first_index_beating(view.Y(w) - Yv, 2.0 * s2l * (double)(w - v), L);
-        if (st < en) mark[st] = v + 1;
-        u = v;
-        Yu = Yv;
-        v = w;
+    if (!ok) {
+        std::fill(mark.begin(), mark.end(), 0);
+        // phase 2': merge tree, one level at a time
+        for (int h = 1; h < G; h <<= 1) {
+            for (int g = 0; g < G; ++g) {
+                if ((g & (2 * h - 1)) == h) {
+                    edt::Chain<LineView<K>, Mask, K> ch(view);
+                    ch.junction(g - h, g, g + h < G ? g + h : G);
+                }
+            }
+        }
+        // phase 3': every member v owns [st, en): st where it beats its
+        // predecessor, en where its successor takes over; a non-empty interval
+        // marks v + 1 at st (one writer per mark)
+        edt::Chain<LineView<K>, Mask, K> ch(view);
+        int u = -1;
+        double Yu = 0.0;
+        for (int v = ch.first_in(0, G); v >= 0;) {
+            const double Yv = view.Y(v);
+            const int st = u < 0 ? 0 : edt::first_index_beating(Yv - Yu, 2.0 * s2l * (double)(v - u), L);
+            const int w = ch.next_member(v, G);
+            int en = L;
+            if (w >= 0) en = edt::first_index_beating(view.Y(w) - Yv, 2.0 * s2l * (double)(w - v), L);
+            if (st < en) mark[st] = v + 1;
+            u = v;
+            Yu = Yv;
+            v = w;
+        }
     }
     // phase 4: the owner of q is the latest mark at or before q
     int o = 0;
@@ -122,20 +142,28 @@ int run_line(const double* fb, int L, double s2l, int G, int32_t* owner) {
 
 }  // namespace
 
-extern "C" int model_envelope_line(const double* fb, int L, double s2l, int K, int G,
+template <int CAP>
+int line_k(const double* fb, int L, double s2l, int K, int G, int32_t* owner) {
+    if (K == 8) return run_line<8, CAP>(fb, L, s2l, G, owner);
+    if (K == 16) return run_line<16, CAP>(fb, L, s2l, G, owner);
+    if (K == 32) return run_line<32, CAP>(fb, L, s2l, G, owner);
+    if (K == 64) return run_line<64, (CAP > 0 ? 0 : 0)>(fb, L, s2l, G, owner);
+    return -1;
+}
+
+extern "C" int model_envelope_line(const double* fb, int L, double s2l, int K, int G, int reach,
                                    int32_t* owner) {
-    if (K == 8) return run_line<8>(fb, L, s2l, G, owner);
-    if (K == 16) return run_line<16>(fb, L, s2l, G, owner);
-    if (K == 32) return run_line<32>(fb, L, s2l, G, owner);
-    if (K == 64) return run_line<64>(fb, L, s2l, G, owner);
+    if (reach == 8) return line_k<8>(fb, L, s2l, K, G, owner);
+    if (reach == 1) return line_k<1>(fb, L, s2l, K, G, owner);
+    if (reach == 0) return line_k<0>(fb, L, s2l, K, G, owner);
     return -1;
 }
 
 // Every line of a [nlines][L] array (one call per line).
 extern "C" int model_envelope_lines(const double* fb, int64_t nlines, int L, double s2l, int K,
-                                    int G, int32_t* owner) {
+                                    int G, int reach, int32_t* owner) {
     for (int64_t i = 0; i < nlines; ++i) {
-        const int rc = model_envelope_line(fb + i * L, L, s2l, K, G, owner + i * L);
+        const int rc = model_envelope_line(fb + i * L, L, s2l, K, G, reach, owner + i * L);
         if (rc) return rc;
     }
     return 0;

@@ -9,6 +9,7 @@ the oracle.  No GPU is needed.
 """
 
 import ctypes
+import itertools
 import os
 import subprocess
 
@@ -29,13 +30,13 @@ def model(tmp_path_factory):
     lib.model_envelope_lines.restype = ctypes.c_int
     lib.model_envelope_lines.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
                                          ctypes.c_double, ctypes.c_int, ctypes.c_int,
-                                         ctypes.c_void_p]
+                                         ctypes.c_int, ctypes.c_void_p]
 
-    def run(fb, s2l, K, G):
+    def run(fb, s2l, K, G, reach=8):
         fb = np.ascontiguousarray(fb, np.float64)
         nl, L = fb.shape
         own = np.empty((nl, L), np.int32)
-        rc = lib.model_envelope_lines(fb.ctypes.data, nl, L, s2l, K, G, own.ctypes.data)
+        rc = lib.model_envelope_lines(fb.ctypes.data, nl, L, s2l, K, G, reach, own.ctypes.data)
         assert rc == 0
         return own
 
@@ -90,10 +91,10 @@ def test_lines_match_definition(model, L):
             fb[i] = rng.integers(0, 4, L).astype(np.float64)
     for s2l in (1.0, 6.25):
         ref = _brute_lines(fb, s2l)
-        for K, G in _layouts(L):
-            own = model(fb, s2l, K, G)
+        for (K, G), reach in itertools.product(_layouts(L), (8, 1, 0)):
+            own = model(fb, s2l, K, G, reach)
             got = _value_at(fb, own, s2l)
-            np.testing.assert_array_equal(got, ref, err_msg=f"L={L} K={K} G={G} s2={s2l}")
+            np.testing.assert_array_equal(got, ref, err_msg=f"L={L} K={K} G={G} s2={s2l} reach={reach}")
             has = np.isfinite(fb)
             ok = own >= 0
             assert (ok == has.any(1)[:, None]).all()
@@ -112,7 +113,7 @@ def _axis0_nearest(mask):
     return g
 
 
-def _model_edt(model, mask, sampling, K):
+def _model_edt(model, mask, sampling, K, reach=8):
     """Full transform composed from the model: axis-0 nearest, then one
     envelope pass per further axis (values are squared distances so far)."""
     s2 = np.ones(mask.ndim) if sampling is None else np.asarray(sampling, np.float64) ** 2
@@ -125,13 +126,14 @@ def _model_edt(model, mask, sampling, K):
         fb = Fm.reshape(-1, shp[-1])
         L = shp[-1]
         G = -(-L // K)
-        own = model(fb, s2[ax], K, G)
+        own = model(fb, s2[ax], K, G, reach)
         F = np.moveaxis(_value_at(fb, own, s2[ax]).reshape(shp), -1, ax)
     return F
 
 
 @pytest.mark.parametrize("K", [8, 16, 32, 64])
-def test_model_transform_matches_oracle(model, K):
+@pytest.mark.parametrize("reach", [8, 0])
+def test_model_transform_matches_oracle(model, K, reach):
     rng = np.random.default_rng([42, 2001, K])
     cases = []
     for t in range(16):
@@ -152,5 +154,5 @@ def test_model_transform_matches_oracle(model, K):
         if not (mask == 0).any():
             mask.reshape(-1)[0] = 0
         ref, _ = oracle.edt(mask, samp, False)
-        got = _model_edt(model, mask, samp, K)
+        got = _model_edt(model, mask, samp, K, reach)
         np.testing.assert_array_equal(got, ref, err_msg=f"shape {mask.shape} sampling {samp}")
