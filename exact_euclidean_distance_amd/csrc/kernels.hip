@@ -577,8 +577,10 @@ __device__ void resolve_line(View& view, SlotArrays<Val, K>& sa, const Val* mych
 // --------------------------------------------------------------------------
 // Row layout: lines contiguous in memory (the last axis).  A work-group holds
 // LPW lines; lane g of a line owns chunk g.  The line is loaded with 16-byte
-// coalesced reads, and each lane writes its own chunk's outputs with 16-byte
-// stores (chunks are 4-aligned), so no LDS staging of outputs is needed.
+// coalesced reads.  Once every chunk's owners are in LDS, lane g writes the
+// 4-position pieces g, g + Gp, ... of its line, so neighbouring lanes store
+// neighbouring 16 bytes (a lane writing its own chunk would scatter each store
+// over one cache line per lane).
 // --------------------------------------------------------------------------
 
 struct Geo2D {          // rows of an H x W image; value = axis-0 coordinate
@@ -694,55 +696,60 @@ __global__ __launch_bounds__(1024) void k_envelope_rows(const typename Geo::Val*
     uint16_t* mymarks = sa.mark + (size_t)tid * CM;
     resolve_line<K>(view, sa, sa.val + (size_t)tid * CS, mymarks, g, Gp, L, active, tid, 1, r,
                     [](Val v) { return Geo::valid(v); }, fof);
-    int o = 0;
 
-    // 5. outputs of the chunk
-    const int base = g * K;
-    const int n = active ? min(K, L - base) : 0;
-    if (n <= 0) return;   // no barrier follows
+    // 5. outputs.  mk is owner + 1 of position q (0: the line has no
+    //    background, the owner is the virtual element).
+    const int n = active ? min(K, L - g * K) : 0;
     const double s2l = geo.s2l;
     const double fvirt = geo.virt_f(gl);
     const int32_t ivirt = geo.virt_index();
-    const int64_t obase = line * (int64_t)L + base;
+    auto one = [&](int q, int mk, int32_t& osq, float& od, int32_t& oix) {
+        const int ow = mk - 1;
+        const Val vo = view.val(ow < 0 ? 0 : ow);
+        const double qq = (double)q;
+        const double dq = (double)(q - ow);
+        const double F = ow < 0 ? fvirt + s2l * qq * qq : fof(vo) + s2l * dq * dq;
+        osq = sqdist ? (int32_t)F : 0;
+        od = __builtin_amdgcn_sqrtf((float)F);
+        oix = ow < 0 ? ivirt : geo.index(gl, vo, ow);
+    };
+    const int64_t lbase = line * (int64_t)L;
     int32_t osq[4];
     float od[4];
     int32_t oix[4];
-    auto one = [&](int j, int t) {
+    auto store4 = [&](int64_t ob) {
+        if (sqdist) *reinterpret_cast<int4*>(sqdist + ob) = make_int4(osq[0], osq[1], osq[2], osq[3]);
+        if (dist) *reinterpret_cast<float4*>(dist + ob) = make_float4(od[0], od[1], od[2], od[3]);
+        if (indices) *reinterpret_cast<int4*>(indices + ob) = make_int4(oix[0], oix[1], oix[2], oix[3]);
+    };
+    // The marks of the own chunk become owners (running maximum, in place);
+    // then lane g writes the 4-position pieces g, g + Gp, ... of the line, so
+    // that neighbouring lanes store neighbouring 16-byte pieces.
+    int o = 0;
+    for (int t = 0; t < n; ++t) {
         const int mk = mymarks[t];
         o = mk > o ? mk : o;
-        const int ow = o - 1;
-        const Val vo = view.val(ow < 0 ? 0 : ow);
-        const double q = (double)(base + t);
-        const double dq = (double)(base + t - ow);
-        const double F = ow < 0 ? fvirt + s2l * q * q : fof(vo) + s2l * dq * dq;
-        osq[j] = sqdist ? (int32_t)F : 0;
-        od[j] = __builtin_amdgcn_sqrtf((float)F);
-        oix[j] = ow < 0 ? ivirt : geo.index(gl, vo, ow);
-    };
-    for (int t0 = 0; t0 < n; t0 += 4) {
-        const int cnt = min(4, n - t0);
-        if (cnt == 4) {
+        mymarks[t] = (uint16_t)o;
+    }
+    __syncthreads();
+    if (!active) return;   // no barrier follows
+    const uint16_t* marks = sa.mark + (size_t)slot0 * CM;
+    if (vec_out) {   // L % 4 == 0 and 16-byte aligned outputs
+#pragma unroll 2
+        for (int i = 0; i < K / 4; ++i) {
+            const int p = 4 * (i * Gp + g);
+            if (p >= L) break;
+            const uint16_t* om = marks + (unsigned)p / K * CM + (unsigned)p % K;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) one(j, t0 + j);
-        } else {
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                if (j < cnt) one(j, t0 + j);
+            for (int j = 0; j < 4; ++j) one(p + j, om[j], osq[j], od[j], oix[j]);
+            store4(lbase + p);
         }
-        const int64_t ob = obase + t0;
-        if (vec_out && cnt == 4) {
-            if (sqdist) *reinterpret_cast<int4*>(sqdist + ob) = make_int4(osq[0], osq[1], osq[2], osq[3]);
-            if (dist) *reinterpret_cast<float4*>(dist + ob) = make_float4(od[0], od[1], od[2], od[3]);
-            if (indices) *reinterpret_cast<int4*>(indices + ob) = make_int4(oix[0], oix[1], oix[2], oix[3]);
-        } else {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                if (j < cnt) {
-                    if (sqdist) sqdist[ob + j] = osq[j];
-                    if (dist) dist[ob + j] = od[j];
-                    if (indices) indices[ob + j] = oix[j];
-                }
-            }
+    } else {
+        for (int p = g; p < L; p += Gp) {
+            one(p, marks[(unsigned)p / K * CM + (unsigned)p % K], osq[0], od[0], oix[0]);
+            if (sqdist) sqdist[lbase + p] = osq[0];
+            if (dist) dist[lbase + p] = od[0];
+            if (indices) indices[lbase + p] = oix[0];
         }
     }
 }
