@@ -216,6 +216,16 @@ __global__ __launch_bounds__(64 * kScanQ) void k_axis0_scan(uint16_t* __restrict
     }
 }
 
+// Row at which the answer switches from the background row above (p, < 0:
+// none) to the one below (n, >= kFarRow: none): rows i with i - p <= n - i
+// keep p (the smaller coordinate wins a tie).
+constexpr int kFarRow = 1 << 20;
+__device__ __forceinline__ int switch_row(int p, int n) {
+    if (p < 0) return INT_MIN;
+    if (n >= kFarRow) return INT_MAX;
+    return ((p + n) >> 1) + 1;
+}
+
 template <int VEC>
 __global__ __launch_bounds__(256) void k_axis0_resolve(const uint8_t* __restrict__ mask, int n0,
                                                         int64_t M, int nseg,
@@ -243,22 +253,43 @@ __global__ __launch_bounds__(256) void k_axis0_resolve(const uint8_t* __restrict
     uint16_t upc[VEC], dnc[VEC];
     load_u16<VEC>(up_carry + so, upc);
     load_u16<VEC>(dn_carry + so, dnc);
+
+    // Per column: the background rows just above (prev) and at or below (next)
+    // the current row, and the row where the answer switches from one to the
+    // other; they change only when the row reaches next.
+    int prev[VEC], next[VEC], sw[VEC];
+    uint16_t pv[VEC], nv[VEC];   // prev / next as stored (kNone16: none)
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) {
+        prev[v] = upc[v] == kNone16 ? -1 : (int)upc[v];
+        next[v] = bm[v] ? i0 + __builtin_ctzll(bm[v]) : (dnc[v] == kNone16 ? kFarRow : (int)dnc[v]);
+        sw[v] = switch_row(prev[v], next[v]);
+        pv[v] = upc[v];
+        nv[v] = next[v] >= kFarRow ? kNone16 : (uint16_t)next[v];
+    }
     uint16_t* dst = c0 + (int64_t)b * n0 * M + col;
     for (int i = i0; i < i1; ++i) {
-        const int r = i - i0;
+        bool ev = false;
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) ev |= (i == next[v]);
+        if (ev) {   // a background row: it becomes prev, the following one next
+#pragma unroll
+            for (int v = 0; v < VEC; ++v) {
+                if (i == next[v]) {
+                    const int r1 = i - i0 + 1;
+                    const uint64_t rest = r1 < 64 ? bm[v] >> r1 : 0;
+                    prev[v] = i;
+                    next[v] = rest ? i + 1 + __builtin_ctzll(rest)
+                                   : (dnc[v] == kNone16 ? kFarRow : (int)dnc[v]);
+                    sw[v] = switch_row(prev[v], next[v]);
+                    pv[v] = (uint16_t)i;
+                    nv[v] = next[v] >= kFarRow ? kNone16 : (uint16_t)next[v];
+                }
+            }
+        }
         uint16_t out[VEC];
 #pragma unroll
-        for (int v = 0; v < VEC; ++v) {
-            const uint64_t below = bm[v] >> r;                        // rows >= i
-            const uint64_t above = bm[v] & ((uint64_t(2) << r) - 1);  // rows <= i
-            const int dn = below ? i + __builtin_ctzll(below)
-                                 : (dnc[v] == kNone16 ? -1 : (int)dnc[v]);
-            const int up = above ? i0 + 63 - __builtin_clzll(above)
-                                 : (upc[v] == kNone16 ? -1 : (int)upc[v]);
-            // the nearer one; the smaller coordinate on a tie
-            const int g = (up >= 0 && (dn < 0 || i - up <= dn - i)) ? up : dn;
-            out[v] = g < 0 ? kNone16 : (uint16_t)g;
-        }
+        for (int v = 0; v < VEC; ++v) out[v] = i >= sw[v] ? nv[v] : pv[v];
         store_u16<VEC>(dst + (int64_t)i * M, out);
     }
 }
@@ -282,12 +313,14 @@ hipError_t launch_axis0(const uint8_t* mask, int B, int n0, int64_t M, uint16_t*
     dim3 sgrid((unsigned)((M + 63) / 64), (unsigned)B);
     dim3 sblock(64, kScanQ);
     EDT_LAUNCH(tm, "axis0_scan", s, hipLaunchKernelGGL(k_axis0_scan, sgrid, sblock, 0, s, first, last, nseg, M));
-    if (vec == 16) {
-        EDT_LAUNCH(tm, "axis0_resolve", s, hipLaunchKernelGGL(k_axis0_resolve<16>, grid, block, 0, s, mask, n0, M, nseg, last, first, c0));
-    } else if (vec == 4) {
-        EDT_LAUNCH(tm, "axis0_resolve", s, hipLaunchKernelGGL(k_axis0_resolve<4>, grid, block, 0, s, mask, n0, M, nseg, last, first, c0));
+    // the resolve keeps per-column state in registers: 4 columns per lane
+    const int rvec = vec >= 4 ? 4 : 1;
+    const int64_t rlanes = M / rvec + (M % rvec ? 1 : 0);
+    dim3 rgrid((unsigned)((rlanes + 255) / 256), (unsigned)nseg, (unsigned)B);
+    if (rvec == 4) {
+        EDT_LAUNCH(tm, "axis0_resolve", s, hipLaunchKernelGGL(k_axis0_resolve<4>, rgrid, block, 0, s, mask, n0, M, nseg, last, first, c0));
     } else {
-        EDT_LAUNCH(tm, "axis0_resolve", s, hipLaunchKernelGGL(k_axis0_resolve<1>, grid, block, 0, s, mask, n0, M, nseg, last, first, c0));
+        EDT_LAUNCH(tm, "axis0_resolve", s, hipLaunchKernelGGL(k_axis0_resolve<1>, rgrid, block, 0, s, mask, n0, M, nseg, last, first, c0));
     }
     return hipSuccess;
 }
