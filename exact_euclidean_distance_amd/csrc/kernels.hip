@@ -300,27 +300,27 @@ hipError_t launch_axis0(const uint8_t* mask, int B, int n0, int64_t M, uint16_t*
     int vec = 1;
     if (M % 16 == 0 && ((uintptr_t)mask & 15) == 0) vec = 16;
     else if (M % 4 == 0 && ((uintptr_t)mask & 3) == 0) vec = 4;
-    const int64_t lanes = M / vec + (M % vec ? 1 : 0);
-    dim3 grid((unsigned)((lanes + 255) / 256), (unsigned)nseg, (unsigned)B);
     dim3 block(256);
-    if (vec == 16) {
-        EDT_LAUNCH(tm, "axis0_summary", s, hipLaunchKernelGGL(k_axis0_summary<16>, grid, block, 0, s, mask, n0, M, nseg, first, last));
-    } else if (vec == 4) {
-        EDT_LAUNCH(tm, "axis0_summary", s, hipLaunchKernelGGL(k_axis0_summary<4>, grid, block, 0, s, mask, n0, M, nseg, first, last));
+    auto grid_for = [&](int v) {
+        const int64_t lanes = M / v + (M % v ? 1 : 0);
+        return dim3((unsigned)((lanes + 255) / 256), (unsigned)nseg, (unsigned)B);
+    };
+    const int svec = vec;
+    if (svec == 16) {
+        EDT_LAUNCH(tm, "axis0_summary", s, hipLaunchKernelGGL(k_axis0_summary<16>, grid_for(16), block, 0, s, mask, n0, M, nseg, first, last));
+    } else if (svec == 4) {
+        EDT_LAUNCH(tm, "axis0_summary", s, hipLaunchKernelGGL(k_axis0_summary<4>, grid_for(4), block, 0, s, mask, n0, M, nseg, first, last));
     } else {
-        EDT_LAUNCH(tm, "axis0_summary", s, hipLaunchKernelGGL(k_axis0_summary<1>, grid, block, 0, s, mask, n0, M, nseg, first, last));
+        EDT_LAUNCH(tm, "axis0_summary", s, hipLaunchKernelGGL(k_axis0_summary<1>, grid_for(1), block, 0, s, mask, n0, M, nseg, first, last));
     }
     dim3 sgrid((unsigned)((M + 63) / 64), (unsigned)B);
     dim3 sblock(64, kScanQ);
     EDT_LAUNCH(tm, "axis0_scan", s, hipLaunchKernelGGL(k_axis0_scan, sgrid, sblock, 0, s, first, last, nseg, M));
     // the resolve keeps per-column state in registers: 4 columns per lane
-    const int rvec = vec >= 4 ? 4 : 1;
-    const int64_t rlanes = M / rvec + (M % rvec ? 1 : 0);
-    dim3 rgrid((unsigned)((rlanes + 255) / 256), (unsigned)nseg, (unsigned)B);
-    if (rvec == 4) {
-        EDT_LAUNCH(tm, "axis0_resolve", s, hipLaunchKernelGGL(k_axis0_resolve<4>, rgrid, block, 0, s, mask, n0, M, nseg, last, first, c0));
+    if (vec >= 4) {
+        EDT_LAUNCH(tm, "axis0_resolve", s, hipLaunchKernelGGL(k_axis0_resolve<4>, grid_for(4), block, 0, s, mask, n0, M, nseg, last, first, c0));
     } else {
-        EDT_LAUNCH(tm, "axis0_resolve", s, hipLaunchKernelGGL(k_axis0_resolve<1>, rgrid, block, 0, s, mask, n0, M, nseg, last, first, c0));
+        EDT_LAUNCH(tm, "axis0_resolve", s, hipLaunchKernelGGL(k_axis0_resolve<1>, grid_for(1), block, 0, s, mask, n0, M, nseg, last, first, c0));
     }
     return hipSuccess;
 }
@@ -473,13 +473,29 @@ __device__ void resolve_line(View& view, SlotArrays<Val, K>& sa, const Val* mych
     // 1. chunk minimum of F and its first minimiser, then the line's
     //    candidate bound.  The minimiser (+1, 0: none) is published in the mask
     //    slot, which the local envelope overwrites only after the second barrier.
+    //    F of the chunk's positions stays in registers for the candidate pass
+    //    when the chunk is short enough (+inf: no candidate there).
+    constexpr bool kKeepF = K <= 32;
+    double Fr[kKeepF ? K : 1];
+    Mask vmask = 0;   // valid positions of the chunk
     double fmin = __builtin_huge_val();
     int amin = -1;
+    if constexpr (kKeepF) {
+#pragma unroll
+        for (int t = 0; t < K; ++t) {
+            const Val v = mychunk[t];   // entries past n are stale but in bounds
+            const bool here = t < n && valid(v);
+            Fr[t] = here ? fval(v) : __builtin_huge_val();
+            if (here) vmask |= Mask(1) << t;
+            if (Fr[t] < fmin) { fmin = Fr[t]; amin = t; }
+        }
+    } else {
 #pragma unroll 8
-    for (int t = 0; t < n; ++t) {
-        const Val v = mychunk[t];
-        const double f = fval(v);
-        if (valid(v) && f < fmin) { fmin = f; amin = t; }
+        for (int t = 0; t < n; ++t) {
+            const Val v = mychunk[t];
+            const double f = fval(v);
+            if (valid(v) && f < fmin) { fmin = f; amin = t; }
+        }
     }
     const float fmin_up = round_up_float(fmin);
     sa.own[myslot] = __float_as_int(fmin_up);
@@ -509,10 +525,8 @@ __device__ void resolve_line(View& view, SlotArrays<Val, K>& sa, const Val* mych
     const double Ycur = acur >= 0 ? view.Y(acur) : 0.0;
     const double Ynext = anext >= 0 ? view.Y(anext) : 0.0;
     Mask cand = 0;
-#pragma unroll 8
-    for (int t = 0; t < n; ++t) {
-        const Val v = mychunk[t];
-        const double f = fval(v);
+    // (U may be +inf when a chunk and both its neighbours hold no candidate)
+    auto consider = [&](int t, double f, bool here) {
         const int p = base + t;
         const double Yp = f + s2l * (double)p * (double)p;
         const int lo = acur >= 0 && acur < p ? acur : aprev;
@@ -520,7 +534,17 @@ __device__ void resolve_line(View& view, SlotArrays<Val, K>& sa, const Val* mych
         const int hi = acur > p ? acur : anext;
         const double Yhi = acur > p ? Ycur : Ynext;
         const bool gone = lo >= 0 && hi >= 0 && dominated(lo, Ylo, p, Yp, hi, Yhi);
-        if (valid(v) && f <= U && !gone) cand |= Mask(1) << t;
+        if (here && f <= U && !gone) cand |= Mask(1) << t;
+    };
+    if constexpr (kKeepF) {
+#pragma unroll
+        for (int t = 0; t < K; ++t) consider(t, Fr[t], (vmask >> t) & 1);
+    } else {
+#pragma unroll 8
+        for (int t = 0; t < n; ++t) {
+            const Val v = mychunk[t];
+            consider(t, fval(v), valid(v));
+        }
     }
     Mask m = build_chunk<Mask>(base, cand, [&](int t) { return mychunk[t]; },
                                [&](Val v, int p) { return fval(v) + s2l * (double)p * (double)p; });
@@ -641,8 +665,9 @@ struct Geo3D {          // rows along W of B x D x H x W volumes; value = packed
     int D, H, W;
     struct Line { int d, h; };
     __device__ Line line(int64_t ln) const {
-        const int64_t dh = ln % ((int64_t)D * H);
-        return Line{(int)(dh / H), (int)(dh % H)};
+        const unsigned DH = (unsigned)D * (unsigned)H;   // D * H * W < 2^31
+        const unsigned dh = ln < 0x100000000ll ? (unsigned)ln % DH : (unsigned)(ln % DH);
+        return Line{(int)(dh / (unsigned)H), (int)(dh % (unsigned)H)};
     }
     __device__ static bool valid(uint32_t v) { return v != kNone32; }
     __device__ double f(const Line& l, uint32_t v) const {
