@@ -277,7 +277,6 @@ EDT_HD inline bool chunk_owner_marks(View& v, int c, int G, int L, Mask M, Mark 
     const int n = L - b < K ? L - b : K;
     const int e = b + n - 1;
     const double s2 = v.s2l;
-    Chain<View, Mask, K> ch(v);
 
     // members reaching in from the left (Lp[0] nearest) and from the right
     Packed8 Lp, Rp;
@@ -288,28 +287,29 @@ EDT_HD inline bool chunk_owner_marks(View& v, int c, int G, int L, Mask M, Mark 
         const double d = (double)(x - b);
         best = v.f(x) + s2 * d * d;
     }
-    for (int m = ch.last_in(0, c), seen = -1; m >= 0;) {
-        const int cm = m / K;
-        if (cm != seen) {   // entering chunk cm: pass over it if it cannot win
-            seen = cm;
-            const double dn = (double)(b - (cm * K + K - 1));
-            if (!(s2 * dn * dn < best)) break;
-            if (!(v.fmin_lb(cm) + s2 * dn * dn < best)) {
-                m = ch.last_in(0, cm);
-                continue;
+    for (int cc = v.last_nonempty(0, c); cc >= 0; cc = v.last_nonempty(0, cc)) {
+        const double dn = (double)(b - (cc * K + K - 1));   // to the chunk's nearest position
+        const double ddn = s2 * dn * dn;
+        if (!(ddn < best)) break;
+        if (!(v.fmin_lb(cc) + ddn < best)) continue;         // no member of it can win
+        Mask mk = v.mask(cc);
+        bool stop = false;
+        do {
+            const int t = high_bit(mk);
+            mk ^= Mask(1) << t;
+            const int m = cc * K + t;
+            const double d = (double)(b - m);
+            const double dd = s2 * d * d;
+            if (!(dd < best)) { stop = true; break; }
+            const double p = v.f(m) + dd;
+            if (p < best) {
+                if (nL == CAP) return false;
+                Lp.set(nL, m);
+                ++nL;
+                best = p;
             }
-        }
-        const double d = (double)(b - m);
-        const double dd = s2 * d * d;
-        if (!(dd < best)) break;
-        const double p = v.f(m) + dd;
-        if (p < best) {
-            if (nL == CAP) return false;
-            Lp.set(nL, m);
-            ++nL;
-            best = p;
-        }
-        m = ch.prev_member(m, 0);
+        } while (mk);
+        if (stop) break;
     }
     best = __builtin_huge_val();
     if (M) {
@@ -317,28 +317,29 @@ EDT_HD inline bool chunk_owner_marks(View& v, int c, int G, int L, Mask M, Mark 
         const double d = (double)(e - x);
         best = v.f(x) + s2 * d * d;
     }
-    for (int m = ch.first_in(c + 1, G), seen = -1; m >= 0;) {
-        const int cm = m / K;
-        if (cm != seen) {   // entering chunk cm: pass over it if it cannot win
-            seen = cm;
-            const double dn = (double)(cm * K - e);
-            if (!(s2 * dn * dn < best)) break;
-            if (!(v.fmin_lb(cm) + s2 * dn * dn < best)) {
-                m = ch.first_in(cm + 1, G);
-                continue;
+    for (int cc = v.first_nonempty(c + 1, G); cc >= 0; cc = v.first_nonempty(cc + 1, G)) {
+        const double dn = (double)(cc * K - e);
+        const double ddn = s2 * dn * dn;
+        if (!(ddn < best)) break;
+        if (!(v.fmin_lb(cc) + ddn < best)) continue;
+        Mask mk = v.mask(cc);
+        bool stop = false;
+        do {
+            const int t = low_bit(mk);
+            mk &= mk - 1;
+            const int m = cc * K + t;
+            const double d = (double)(m - e);
+            const double dd = s2 * d * d;
+            if (!(dd < best)) { stop = true; break; }
+            const double p = v.f(m) + dd;
+            if (p < best) {
+                if (nR == CAP) return false;
+                Rp.set(nR, m);
+                ++nR;
+                best = p;
             }
-        }
-        const double d = (double)(m - e);
-        const double dd = s2 * d * d;
-        if (!(dd < best)) break;
-        const double p = v.f(m) + dd;
-        if (p < best) {
-            if (nR == CAP) return false;
-            Rp.set(nR, m);
-            ++nR;
-            best = p;
-        }
-        m = ch.next_member(m, G);
+        } while (mk);
+        if (stop) break;
     }
 
     // Sequence index space: [0, nL) the left members in increasing position,
@@ -349,58 +350,64 @@ EDT_HD inline bool chunk_owner_marks(View& v, int c, int G, int L, Mask M, Mark 
         if (i < CAP + K) return b + (i - CAP);
         return Rp.get(i - CAP - K);
     };
-    auto in_chunk = [&](int i) { return i >= CAP && i < CAP + K; };
 
-    // lower envelope of the sequence (insertion sweep; the chunk's own members
-    // are already convex, so once two of them lead the stack the rest of them
-    // are appended without tests)
+    // lower envelope of the sequence (insertion sweep; the stack top and the
+    // member below it are kept with their positions and heights, and the chunk's
+    // own members, already convex, are appended without tests once two of them
+    // lead the stack)
     uint64_t alive = 0;
-    int top = -1, sec = -1;
+    int top = -1, sec = -1, ptop = 0, psec = 0;
     double Ytop = 0.0, Ysec = 0.0;
-    auto insert = [&](int i) {
-        const int p = pos_of(i);
+    auto insert = [&](int i, int p) {
         const double Y = v.Y(p);
-        while (sec >= 0 && dominated(pos_of(sec), Ysec, pos_of(top), Ytop, p, Y)) {
+        while (sec >= 0 && dominated(psec, Ysec, ptop, Ytop, p, Y)) {
             alive &= ~(uint64_t(1) << top);
             top = sec;
+            ptop = psec;
             Ytop = Ysec;
             const uint64_t below = alive & ((uint64_t(1) << top) - 1);
             if (below) {
                 sec = high_bit(below);
-                Ysec = v.Y(pos_of(sec));
+                psec = pos_of(sec);
+                Ysec = v.Y(psec);
             } else {
                 sec = -1;
             }
         }
         alive |= uint64_t(1) << i;
         sec = top;
+        psec = ptop;
         Ysec = Ytop;
         top = i;
+        ptop = p;
         Ytop = Y;
     };
-    for (int i = 0; i < nL; ++i) insert(i);
+    for (int i = 0; i < nL; ++i) insert(i, Lp.get(nL - 1 - i));
     Mask rest = M;
     while (rest) {
-        if (top >= 0 && sec >= 0 && in_chunk(top) && in_chunk(sec)) {
-            // append the remaining chunk members
-            const int t_last = high_bit(rest);
+        if (sec >= CAP) {   // top and sec are both members of the chunk
             alive |= (uint64_t)rest << CAP;
-            if (rest & (rest - 1)) {
-                const Mask below = rest & ~(Mask(1) << t_last);
+            const int t_last = high_bit(rest);
+            const Mask below = rest & ~(Mask(1) << t_last);
+            if (below) {
                 sec = CAP + high_bit(below);
+                psec = b + high_bit(below);
+                Ysec = v.Y(psec);
             } else {
                 sec = top;
+                psec = ptop;
+                Ysec = Ytop;
             }
             top = CAP + t_last;
-            Ytop = v.Y(pos_of(top));
-            Ysec = v.Y(pos_of(sec));
+            ptop = b + t_last;
+            Ytop = v.Y(ptop);
             break;
         }
         const int t = low_bit(rest);
         rest &= rest - 1;
-        insert(CAP + t);
+        insert(CAP + t, b + t);
     }
-    for (int i = 0; i < nR; ++i) insert(CAP + K + i);
+    for (int i = 0; i < nR; ++i) insert(CAP + K + i, Rp.get(i));
 
     // owned intervals: member i owns [st, en), st where it is strictly nearer
     // than its predecessor, en where its successor is; clipped to [b, e]
