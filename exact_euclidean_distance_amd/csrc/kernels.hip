@@ -406,7 +406,7 @@ struct SlotArrays {
 
 // One line as seen by the envelope helpers: chunk c of the line lives in slot
 // slot0 + c * gs; occ points at the line's occupancy words.
-template <class Val, int K, class FOf>
+template <class Val, int K, class FOf, int GS>
 struct LineView {
     using Mask = typename MaskOf<K>::T;
     static constexpr int CS = Slots<Val, K>::CS;
@@ -414,7 +414,8 @@ struct LineView {
     Mask* masks;
     uint64_t* occ;
     const int* own;   // chunk minima of F as float32 bits, rounded up
-    int slot0, gs;
+    int slot0;
+    static constexpr int gs = GS;   // slot step between neighbouring chunks
     double s2l;
     FOf fof;
     // a lower bound of F over chunk c: its float32 minimum is within one float32
@@ -462,7 +463,8 @@ __device__ void line_scans(T* a, uint16_t* b, int myslot, int g, int gs, int Gp)
 template <int K, class Val, class View, class IsValid, class FOfVal>
 __device__ void resolve_line(View& view, SlotArrays<Val, K>& sa, const Val* mychunk,
                             uint16_t* mymarks, int g, int Gp, int L, bool active, int myslot,
-                            int gs, int lslot, IsValid valid, FOfVal fval) {
+                            int lslot, IsValid valid, FOfVal fval) {
+    constexpr int gs = View::gs;
     using Mask = typename MaskOf<K>::T;
     constexpr int CM = Slots<Val, K>::CM;
     const int base = g * K;
@@ -749,10 +751,10 @@ __global__ __launch_bounds__(1024) void k_envelope_rows(const typename Geo::Val*
 
     const typename Geo::Line gl = geo.line(active ? line : 0);
     auto fof = [&](Val v) { return geo.f(gl, v); };
-    LineView<Val, K, decltype(fof)> view{sa.val, sa.mask, sa.occ + (size_t)r * ((Gp + 63) / 64),
-                                         sa.own, slot0, 1, geo.s2l, fof};
+    LineView<Val, K, decltype(fof), 1> view{sa.val, sa.mask, sa.occ + (size_t)r * ((Gp + 63) / 64),
+                                            sa.own, slot0, geo.s2l, fof};
     uint16_t* mymarks = sa.mark + (size_t)tid * CM;
-    resolve_line<K>(view, sa, sa.val + (size_t)tid * CS, mymarks, g, Gp, L, active, tid, 1, r,
+    resolve_line<K>(view, sa, sa.val + (size_t)tid * CS, mymarks, g, Gp, L, active, tid, r,
                     [](Val v) { return Geo::valid(v); }, fof);
 
     // 5. outputs.  mk is owner + 1 of position q (0: the line has no
@@ -954,9 +956,9 @@ __global__ __launch_bounds__(1024) void k_envelope_cols(const uint16_t* __restri
         const double t = (double)(d - (int)v);
         return s2a * t * t;
     };
-    LineView<uint16_t, K, decltype(fof)> view{sa.val, sa.mask, sa.occ + x, sa.own, x, TW, s2l, fof};
+    LineView<uint16_t, K, decltype(fof), TW> view{sa.val, sa.mask, sa.occ + x, sa.own, x, s2l, fof};
     uint16_t* mymarks = sa.mark + (size_t)tid * CM;
-    resolve_line<K>(view, sa, mine, mymarks, g, Gp, H, active, tid, TW, x,
+    resolve_line<K>(view, sa, mine, mymarks, g, Gp, H, active, tid, x,
                     [](uint16_t v) { return v != kNone16; }, fof);
     int o = 0;
 
