@@ -821,14 +821,16 @@ struct RowPlan {
 
 // Chunk size: 32 positions for 16-bit values, 16 for 32-bit values (their
 // larger slots would otherwise leave too few lanes resident per CU).  Lines
-// shorter than a block share it, up to 256 threads.
+// shorter than a wave share one, 64 threads per block: small blocks let the
+// phases of several blocks overlap on a CU, so one block waiting at a barrier
+// for its slowest lane leaves the SIMDs to the others.
 static RowPlan plan_rows(int L, int value_bytes) {
     RowPlan p{};
     p.K = value_bytes == 2 ? 32 : 16;
     const int chunks = (L + p.K - 1) / p.K;
     p.Gp = 1;
     while (p.Gp < chunks) p.Gp <<= 1;
-    p.LPW = p.Gp >= 256 ? 1 : 256 / p.Gp;
+    p.LPW = p.Gp >= 64 ? 1 : 64 / p.Gp;
     const int nslots = p.Gp * p.LPW;
     const int vw16 = 16 / value_bytes;
     p.VW = (L % vw16 == 0) ? vw16 : 1;
@@ -899,12 +901,13 @@ struct ColPlan {
     size_t lds;
 };
 
-// H <= 512: chunks of 32 and 64 lines per block; H <= 1024: chunks of 64 and
-// 32 lines per block (LDS holds TW lines of values and marks).
+// H <= 512: chunks of 32 and 16 lines per block; H <= 1024: chunks of 64 and
+// 32 lines per block (LDS holds TW lines of values and marks; narrower tiles
+// mean smaller blocks, more of them resident per CU).
 static ColPlan plan_cols(int H) {
     ColPlan p{};
     p.K = H <= 512 ? 32 : 64;
-    p.TW = H <= 512 ? 64 : 32;
+    p.TW = H <= 512 ? 16 : 32;
     p.Gp = 1;
     while (p.Gp * p.K < H) p.Gp <<= 1;
     p.lds = p.K == 32 ? Slots<uint16_t, 32>::bytes(p.Gp * p.TW, p.Gp) : Slots<uint16_t, 64>::bytes(p.Gp * p.TW, p.Gp);
@@ -994,7 +997,7 @@ static hipError_t launch_cols_t(const uint16_t* c0, int B, int D, int H, int W, 
 hipError_t launch_cols_3d(const uint16_t* c0, int B, int D, int H, int W, double s2_0,
                           double s2_1, uint32_t* c01, hipStream_t s, KernelTimer* tm) {
     const ColPlan p = plan_cols(H);
-    if (p.K == 32) return launch_cols_t<32, 64>(c0, B, D, H, W, s2_0, s2_1, c01, p, s, tm);
+    if (p.K == 32) return launch_cols_t<32, 16>(c0, B, D, H, W, s2_0, s2_1, c01, p, s, tm);
     return launch_cols_t<64, 32>(c0, B, D, H, W, s2_0, s2_1, c01, p, s, tm);
 }
 
