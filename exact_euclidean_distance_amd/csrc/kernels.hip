@@ -482,6 +482,7 @@ __device__ void resolve_line(View& view, SlotArrays<Val, K>& sa, const Val* mych
     Mask vmask = 0;   // valid positions of the chunk
     double fmin = __builtin_huge_val();
     int amin = -1;
+    bool allzero = true;   // every position is background itself (F = 0)
     if constexpr (kKeepF) {
 #pragma unroll
         for (int t = 0; t < K; ++t) {
@@ -489,6 +490,7 @@ __device__ void resolve_line(View& view, SlotArrays<Val, K>& sa, const Val* mych
             const bool here = t < n && valid(v);
             Fr[t] = here ? fval(v) : __builtin_huge_val();
             if (here) vmask |= Mask(1) << t;
+            if (t < n && Fr[t] != 0.0) allzero = false;
             if (Fr[t] < fmin) { fmin = Fr[t]; amin = t; }
         }
     } else {
@@ -496,9 +498,13 @@ __device__ void resolve_line(View& view, SlotArrays<Val, K>& sa, const Val* mych
         for (int t = 0; t < n; ++t) {
             const Val v = mychunk[t];
             const double f = fval(v);
+            if (!valid(v) || f != 0.0) allzero = false;
             if (valid(v) && f < fmin) { fmin = f; amin = t; }
         }
     }
+    // A chunk of background positions owns itself: F_q = 0 there, and any other
+    // candidate j is s^2 (q - j)^2 > 0 away.
+    const bool selfowned = n > 0 && allzero;
     const float fmin_up = round_up_float(fmin);
     sa.own[myslot] = __float_as_int(fmin_up);
     sa.mask[myslot] = (Mask)(amin < 0 ? 0 : base + amin + 1);
@@ -526,30 +532,35 @@ __device__ void resolve_line(View& view, SlotArrays<Val, K>& sa, const Val* mych
     const double Yprev = aprev >= 0 ? view.Y(aprev) : 0.0;
     const double Ycur = acur >= 0 ? view.Y(acur) : 0.0;
     const double Ynext = anext >= 0 ? view.Y(anext) : 0.0;
-    Mask cand = 0;
-    // (U may be +inf when a chunk and both its neighbours hold no candidate)
-    auto consider = [&](int t, double f, bool here) {
-        const int p = base + t;
-        const double Yp = f + s2l * (double)p * (double)p;
-        const int lo = acur >= 0 && acur < p ? acur : aprev;
-        const double Ylo = acur >= 0 && acur < p ? Ycur : Yprev;
-        const int hi = acur > p ? acur : anext;
-        const double Yhi = acur > p ? Ycur : Ynext;
-        const bool gone = lo >= 0 && hi >= 0 && dominated(lo, Ylo, p, Yp, hi, Yhi);
-        if (here && f <= U && !gone) cand |= Mask(1) << t;
-    };
-    if constexpr (kKeepF) {
-#pragma unroll
-        for (int t = 0; t < K; ++t) consider(t, Fr[t], (vmask >> t) & 1);
+    Mask m;
+    if (selfowned) {
+        m = n >= (int)(8 * sizeof(Mask)) ? ~Mask(0) : (Mask(1) << n) - Mask(1);   // positions 0 .. n-1
     } else {
+        Mask cand = 0;
+        // (U may be +inf when a chunk and both its neighbours hold no candidate)
+        auto consider = [&](int t, double f, bool here) {
+            const int p = base + t;
+            const double Yp = f + s2l * (double)p * (double)p;
+            const int lo = acur >= 0 && acur < p ? acur : aprev;
+            const double Ylo = acur >= 0 && acur < p ? Ycur : Yprev;
+            const int hi = acur > p ? acur : anext;
+            const double Yhi = acur > p ? Ycur : Ynext;
+            const bool gone = lo >= 0 && hi >= 0 && dominated(lo, Ylo, p, Yp, hi, Yhi);
+            if (here && f <= U && !gone) cand |= Mask(1) << t;
+        };
+        if constexpr (kKeepF) {
+#pragma unroll
+            for (int t = 0; t < K; ++t) consider(t, Fr[t], (vmask >> t) & 1);
+        } else {
 #pragma unroll 8
-        for (int t = 0; t < n; ++t) {
-            const Val v = mychunk[t];
-            consider(t, fval(v), valid(v));
+            for (int t = 0; t < n; ++t) {
+                const Val v = mychunk[t];
+                consider(t, fval(v), valid(v));
+            }
         }
+        m = build_chunk<Mask>(base, cand, [&](int t) { return mychunk[t]; },
+                              [&](Val v, int p) { return fval(v) + s2l * (double)p * (double)p; });
     }
-    Mask m = build_chunk<Mask>(base, cand, [&](int t) { return mychunk[t]; },
-                               [&](Val v, int p) { return fval(v) + s2l * (double)p * (double)p; });
     sa.mask[myslot] = m;
     if (m) atomicOr(&view.occ[g >> 6], uint64_t(1) << (g & 63));
 
@@ -564,9 +575,12 @@ __device__ void resolve_line(View& view, SlotArrays<Val, K>& sa, const Val* mych
 #pragma unroll
         for (int t = 0; t < K; t += 2) *reinterpret_cast<uint32_t*>(mymarks + t) = 0u;
         ok = true;
-        if (n > 0)
+        if (selfowned) {
+            for (int t = 0; t < n; ++t) mymarks[t] = (uint16_t)(base + t + 1);
+        } else if (n > 0) {
             ok = chunk_owner_marks<K, kReach>(view, g, G, L, m,
                                               [&](int t, int o) { mymarks[t] = (uint16_t)(o + 1); });
+        }
     }
     if (!ok) atomicOr(sa.flag, 1u);
     __syncthreads();

@@ -182,6 +182,28 @@ def test_edge_cases_3d(torch_dev):
     check(torch_dev, mask)
 
 
+def test_background_runs(torch_dev):
+    """Whole chunks of background next to foreground: such chunks own
+    themselves, and the members they offer to the neighbouring chunks must be
+    exactly their positions (a foreground pair just past a background run of
+    16 or 32 positions, nearer to the run than to the background after it)."""
+    for shape, run in (((1, 2, 3, 70), 64), ((1, 3, 40, 70), 64), ((1, 1, 33, 70), 64)):
+        mask = np.zeros(shape, np.uint8)
+        mask[..., run:run + 2] = 1
+        for samp in (None, (1.0, 2.0, 0.5), (2.5, 1.0, 1.0)):
+            check(torch_dev, mask, samp)
+    for shape, run in (((3, 4100), 4096), ((5, 200), 192), ((2, 70), 64)):
+        mask = np.zeros(shape, np.uint8)
+        mask[:, run:run + 2] = 1
+        for samp in (None, (1.0, 0.5)):
+            check(torch_dev, mask, samp)
+    # background columns (the column pass sees whole background chunks)
+    mask = np.zeros((1, 2, 70, 40), np.uint8)
+    mask[:, :, 64:66, :] = 1
+    for samp in (None, (1.0, 0.5, 1.0)):
+        check(torch_dev, mask, samp)
+
+
 def test_repeat_is_bit_identical(torch_dev):
     from workloads import make_config
     mask, _, _ = make_config("c1")
