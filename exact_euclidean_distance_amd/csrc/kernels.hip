@@ -945,9 +945,19 @@ __global__ __launch_bounds__(1024) void k_envelope_cols(const uint16_t* __restri
     const int x = threadIdx.x;
     const int g = threadIdx.y;
     const int tid = g * TW + x;
+    // Work-groups are dealt to the eight XCDs in turn.  The SH tiles that
+    // share 128-byte lines of a row go to one XCD (one L2 fetches each line
+    // once), and consecutive groups of them still go round the XCDs, so cheap
+    // and costly planes stay spread over all of them.
+    constexpr unsigned SH = TW * 2 >= 128 ? 1 : 128 / (TW * 2);
+    unsigned tile_id = blockIdx.x;
+    if (SH > 1 && blockIdx.x < gridDim.x / (8 * SH) * (8 * SH)) {
+        const unsigned xcd = blockIdx.x % 8, k = blockIdx.x / 8;
+        tile_id = ((k / SH) * 8 + xcd) * SH + k % SH;
+    }
     const int tiles = (W + TW - 1) / TW;
-    const int64_t plane = blockIdx.x / tiles;
-    const int w0 = (int)(blockIdx.x % tiles) * TW;
+    const int64_t plane = tile_id / tiles;
+    const int w0 = (int)(tile_id % tiles) * TW;
     const bool active = (w0 + x) < W;
     const int d = (int)(plane % D);
     const int base = g * K;
