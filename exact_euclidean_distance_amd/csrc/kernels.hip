@@ -667,7 +667,10 @@ struct Geo2D {          // rows of an H x W image; value = axis-0 coordinate
         const double t = (double)(l.row - (int)v);
         return s2a * t * t;
     }
-    __device__ int32_t index(const Line&, uint16_t v, int pos) const { return (int32_t)v * W + pos; }
+    // v < 2^16 and W <= 32768: a 24-bit product is exact
+    __device__ int32_t index(const Line&, uint16_t v, int pos) const {
+        return (int32_t)__umul24((unsigned)v, (unsigned)W) + pos;
+    }
     __device__ double virt_f(const Line& l) const {
         const double t = (double)(l.row + 1);
         return s2a * t * t;
@@ -679,6 +682,7 @@ struct Geo3D {          // rows along W of B x D x H x W volumes; value = packed
     using Val = uint32_t;
     double s2a, s2b, s2l;
     int D, H, W;
+    bool dh24;          // D * H < 2^24: the flat index needs only 24-bit products
     struct Line { int d, h; };
     __device__ Line line(int64_t ln) const {
         const unsigned DH = (unsigned)D * (unsigned)H;   // D * H * W < 2^31
@@ -692,7 +696,8 @@ struct Geo3D {          // rows along W of B x D x H x W volumes; value = packed
         return s2a * t0 * t0 + s2b * t1 * t1;
     }
     __device__ int32_t index(const Line&, uint32_t v, int pos) const {
-        return ((int32_t)(v >> 16) * H + (int32_t)(v & 0xFFFFu)) * W + pos;
+        const unsigned dh = __umul24(v >> 16, (unsigned)H) + (v & 0xFFFFu);   // axis 0 < 2^16, H <= 1024
+        return (int32_t)(dh24 ? __umul24(dh, (unsigned)W) : dh * (unsigned)W) + pos;
     }
     __device__ double virt_f(const Line& l) const {
         const double t0 = (double)(l.d + 1);
@@ -828,6 +833,301 @@ __global__ __launch_bounds__(1024) void k_envelope_rows(const typename Geo::Val*
     }
 }
 
+// --------------------------------------------------------------------------
+// Rows of at most 1024 positions: one wave per line, lane l holding the P
+// consecutive positions [P l, P l + P).  The candidates are filtered exactly as
+// above (bound U and chunk-minimiser test over chunks of 16 positions), then
+// the envelope of the survivors is found in rounds: every surviving candidate
+// checks, against its current neighbours in the line, the dominance test of
+// PR-EDT Figure 5, and all dominated ones leave together.  A point above the
+// segment between two points of the set stays above the lower hull of what
+// remains, so when a round removes nothing the survivors form a locally and
+// hence globally convex chain: the envelope.  Every lane takes the same steps
+// for its own few candidates, so the work follows the candidates, not the
+// slowest chunk.  Each member then marks where it starts to own (against its
+// predecessor), a prefix maximum gives each position its owner, and lane l
+// writes its P outputs.
+// --------------------------------------------------------------------------
+
+template <class Geo, int P>
+__global__ __launch_bounds__(64) void k_rows_wave(const typename Geo::Val* __restrict__ in, int L,
+                                                  Geo geo, int32_t* __restrict__ sqdist,
+                                                  float* __restrict__ dist,
+                                                  int32_t* __restrict__ indices, int vec_io) {
+    using Val = typename Geo::Val;
+    static_assert(P >= 1 && P <= 16 && (P & (P - 1)) == 0, "1 to 16 positions per lane");
+    constexpr int NP = 64 * P;
+    constexpr int KC = 16;          // chunk of the candidate bound and filter
+    constexpr int GL = KC / P;      // lanes per chunk
+    constexpr unsigned kNoneV = sizeof(Val) == 2 ? kNone16 : kNone32;
+    __shared__ double Ys[NP];       // Y = F + s^2 q^2 of position q (+inf: no candidate)
+    __shared__ Val vs[NP];          // the values, for the owners' outputs
+    __shared__ unsigned marks[NP];  // owner + 1 where an owned interval starts
+    __shared__ unsigned lanes_alive[64];
+
+    const int lane = threadIdx.x;
+    const int64_t line = blockIdx.x;
+    const int base = lane * P;
+    const double s2 = geo.s2l;
+    const typename Geo::Line gl = geo.line(line);
+
+    // 1. values and heights
+    const Val* src = in + line * (int64_t)L;
+    Val v[P];
+    if (P >= 4 && vec_io) {   // L % 4 == 0, 4-value pieces aligned
+#pragma unroll
+        for (int t = 0; t < P; t += 4) {
+            const int p = base + t;
+            if (p < L) {
+                if constexpr (sizeof(Val) == 4) {
+                    const uint4 w = *reinterpret_cast<const uint4*>(src + p);
+                    v[t] = w.x; v[t + 1] = w.y; v[t + 2] = w.z; v[t + 3] = w.w;
+                } else {
+                    const uint2 w = *reinterpret_cast<const uint2*>(src + p);
+                    v[t] = (Val)w.x; v[t + 1] = (Val)(w.x >> 16); v[t + 2] = (Val)w.y; v[t + 3] = (Val)(w.y >> 16);
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) v[t + j] = (Val)kNoneV;
+            }
+        }
+    } else {
+#pragma unroll
+        for (int t = 0; t < P; ++t) v[t] = base + t < L ? src[base + t] : (Val)kNoneV;
+    }
+    double F[P];
+    unsigned vmask = 0;
+    double fmin = __builtin_huge_val();
+    int amin = -1;
+#pragma unroll
+    for (int t = 0; t < P; ++t) {
+        const int p = base + t;
+        const bool ok = p < L && Geo::valid(v[t]);
+        F[t] = ok ? geo.f(gl, v[t]) : __builtin_huge_val();
+        if (ok) vmask |= 1u << t;
+        Ys[p] = ok ? F[t] + s2 * (double)p * (double)p : __builtin_huge_val();
+        vs[p] = v[t];
+        marks[p] = 0u;
+        if (F[t] < fmin) { fmin = F[t]; amin = p; }
+    }
+
+    // 2. chunk minimum and first minimiser (GL lanes per chunk), the bound U
+#pragma unroll
+    for (int o = 1; o < GL; o <<= 1) {
+        const double f2 = __shfl_xor(fmin, o);
+        const int a2 = __shfl_xor(amin, o);
+        if (f2 < fmin || (f2 == fmin && a2 >= 0 && (amin < 0 || a2 < amin))) { fmin = f2; amin = a2; }
+    }
+    double fpv = __shfl(fmin, (lane - GL) & 63), fnx = __shfl(fmin, (lane + GL) & 63);
+    int apv = __shfl(amin, (lane - GL) & 63), anx = __shfl(amin, (lane + GL) & 63);
+    if (lane < GL) { fpv = __builtin_huge_val(); apv = -1; }
+    if (lane + GL >= 64) { fnx = __builtin_huge_val(); anx = -1; }
+    double U = (lane / GL) * KC < L ? chunk_bound(fmin, fpv, fnx, s2, KC) : 0.0;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) U = fmax(U, __shfl_xor(U, o));
+    __syncthreads();
+
+    // 3. candidates: valid, F <= U, not dominated by the nearest chunk minimisers
+    const double Ycur = amin >= 0 ? Ys[amin] : 0.0;
+    const double Yprev = apv >= 0 ? Ys[apv] : 0.0;
+    const double Ynext = anx >= 0 ? Ys[anx] : 0.0;
+    unsigned alive = 0;
+#pragma unroll
+    for (int t = 0; t < P; ++t) {
+        const int p = base + t;
+        const double Yp = F[t] + s2 * (double)p * (double)p;
+        const int lo = amin >= 0 && amin < p ? amin : apv;
+        const double Ylo = amin >= 0 && amin < p ? Ycur : Yprev;
+        const int hi = amin > p ? amin : anx;
+        const double Yhi = amin > p ? Ycur : Ynext;
+        const bool gone = lo >= 0 && hi >= 0 && dominated(lo, Ylo, p, Yp, hi, Yhi);
+        if (((vmask >> t) & 1u) && F[t] <= U && !gone) alive |= 1u << t;
+    }
+
+    // neighbours of the candidate at offset t among the alive set of the round
+    // (nz: lanes with an alive candidate; lanes_alive: their sets)
+    auto pred_of = [&](int t, uint64_t nz) -> int {
+        const unsigned below = alive & ((1u << t) - 1u);
+        if (below) return base + 31 - __builtin_clz(below);
+        const uint64_t lm = nz & ((uint64_t(1) << lane) - 1);
+        if (!lm) return -1;
+        const int j = 63 - __builtin_clzll(lm);
+        return j * P + 31 - __builtin_clz(lanes_alive[j]);
+    };
+    auto succ_of = [&](int t, uint64_t nz) -> int {
+        const unsigned above = alive & ~((2u << t) - 1u);
+        if (above) return base + __builtin_ctz(above);
+        const uint64_t rm = lane == 63 ? 0 : nz & ~((uint64_t(2) << lane) - 1);
+        if (!rm) return -1;
+        const int j = __builtin_ctzll(rm);
+        return j * P + __builtin_ctz(lanes_alive[j]);
+    };
+
+    // 4. envelope of the lane's own candidates (insertion sweep, stack as a
+    //    bit mask), then rounds over the lane boundaries: only a lane's first
+    //    and last members have neighbours outside it, and a member whose
+    //    neighbours change by a removal becomes a first or last one, so each
+    //    round tests those two per lane, removes the dominated ones together,
+    //    and stops when a round removes nothing.
+    {
+        unsigned m = 0, cand = alive;
+        int top = -1, sec = -1;
+        double Ytop = 0.0, Ysec = 0.0;
+        while (cand) {
+            const int t = __builtin_ctz(cand);
+            cand &= cand - 1u;
+            const int p = base + t;
+            const double Y = Ys[p];
+            while (sec >= 0 && dominated(sec, Ysec, top, Ytop, p, Y)) {
+                m &= ~(1u << (top - base));
+                top = sec;
+                Ytop = Ysec;
+                const unsigned below = m & ((1u << (top - base)) - 1u);
+                if (below) {
+                    sec = base + 31 - __builtin_clz(below);
+                    Ysec = Ys[sec];
+                } else {
+                    sec = -1;
+                }
+            }
+            m |= 1u << t;
+            sec = top;
+            Ysec = Ytop;
+            top = p;
+            Ytop = Y;
+        }
+        alive = m;
+    }
+    for (;;) {
+        lanes_alive[lane] = alive;
+        const uint64_t nz = __ballot(alive != 0u);
+        __syncthreads();
+        unsigned dead = 0;
+        if (alive) {
+            const int t0 = __builtin_ctz(alive), t1 = 31 - __builtin_clz(alive);
+            {
+                const int p = base + t0, pp = pred_of(t0, nz), pn = succ_of(t0, nz);
+                if (pp >= 0 && pn >= 0 && dominated(pp, Ys[pp], p, Ys[p], pn, Ys[pn])) dead |= 1u << t0;
+            }
+            if (t1 != t0) {
+                const int p = base + t1, pp = pred_of(t1, nz), pn = succ_of(t1, nz);
+                if (pp >= 0 && pn >= 0 && dominated(pp, Ys[pp], p, Ys[p], pn, Ys[pn])) dead |= 1u << t1;
+            }
+        }
+        alive &= ~dead;
+        const bool more = __ballot(dead != 0u) != 0;
+        __syncthreads();
+        if (!more) break;
+    }
+    lanes_alive[lane] = alive;
+    __syncthreads();
+
+    // 5. every member marks the first position it owns (strictly nearer than
+    //    its predecessor there; ties stay with the smaller coordinate)
+    {
+        const uint64_t nz = __ballot(alive != 0u);   // lanes_alive already holds alive
+        unsigned rest = alive;
+        while (rest) {
+            const int t = __builtin_ctz(rest);
+            rest &= rest - 1u;
+            const int p = base + t;
+            const int pp = pred_of(t, nz);
+            const int st = pp < 0 ? 0 : first_index_beating(Ys[p] - Ys[pp], 2.0 * s2 * (double)(p - pp), L);
+            if (st < L) atomicMax(&marks[st], (unsigned)(p + 1));
+        }
+    }
+    __syncthreads();
+
+    // 6. owner of each position: prefix maximum of the marks along the line
+    unsigned own[P];
+    unsigned run = 0;
+#pragma unroll
+    for (int t = 0; t < P; ++t) {
+        const unsigned mk = marks[base + t];
+        run = mk > run ? mk : run;
+        own[t] = run;
+    }
+    unsigned incl = run;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const unsigned x = __shfl_up(incl, o);
+        if (lane >= o) incl = x > incl ? x : incl;
+    }
+    unsigned excl = __shfl_up(incl, 1);
+    if (lane == 0) excl = 0;
+
+    // 7. outputs (owner + 1 == 0: the line has no background, the virtual element)
+    const double fvirt = geo.virt_f(gl);
+    const int32_t ivirt = geo.virt_index();
+    const int64_t lbase = line * (int64_t)L;
+    int32_t osq[P];
+    float od[P];
+    int32_t oix[P];
+#pragma unroll
+    for (int t = 0; t < P; ++t) {
+        const int q = base + t;
+        const int ow = (int)(own[t] > excl ? own[t] : excl) - 1;
+        const Val vo = vs[ow < 0 ? 0 : ow];
+        const double qq = (double)q;
+        const double dq = (double)(q - ow);
+        const double Fq = ow < 0 ? fvirt + s2 * qq * qq : geo.f(gl, vo) + s2 * dq * dq;
+        osq[t] = sqdist ? (int32_t)Fq : 0;
+        od[t] = __builtin_amdgcn_sqrtf((float)Fq);
+        oix[t] = ow < 0 ? ivirt : geo.index(gl, vo, ow);
+    }
+    if (P >= 4 && vec_io) {
+#pragma unroll
+        for (int t = 0; t < P; t += 4) {
+            const int q = base + t;
+            if (q < L) {
+                if (sqdist) *reinterpret_cast<int4*>(sqdist + lbase + q) = make_int4(osq[t], osq[t + 1], osq[t + 2], osq[t + 3]);
+                if (dist) *reinterpret_cast<float4*>(dist + lbase + q) = make_float4(od[t], od[t + 1], od[t + 2], od[t + 3]);
+                if (indices) *reinterpret_cast<int4*>(indices + lbase + q) = make_int4(oix[t], oix[t + 1], oix[t + 2], oix[t + 3]);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int t = 0; t < P; ++t) {
+            const int q = base + t;
+            if (q < L) {
+                if (sqdist) sqdist[lbase + q] = osq[t];
+                if (dist) dist[lbase + q] = od[t];
+                if (indices) indices[lbase + q] = oix[t];
+            }
+        }
+    }
+}
+
+template <class Geo, int P>
+static hipError_t launch_rows_wave_t(const typename Geo::Val* in, int L, int64_t nlines, const Geo& geo,
+                                     int32_t* sqdist, float* dist, int32_t* indices, hipStream_t s,
+                                     KernelTimer* tm, const char* kname) {
+    constexpr int VB = (int)sizeof(typename Geo::Val);
+    const bool vec = L % 4 == 0 && (((uintptr_t)in & (4 * VB - 1)) == 0) &&
+                     ((((uintptr_t)sqdist | (uintptr_t)dist | (uintptr_t)indices) & 15) == 0);
+    EDT_LAUNCH(tm, kname, s,
+               hipLaunchKernelGGL((k_rows_wave<Geo, P>), dim3((unsigned)nlines), dim3(64), 0, s, in, L,
+                                  geo, sqdist, dist, indices, vec ? 1 : 0));
+    return hipSuccess;
+}
+
+// Few lines of at most 1024 positions take the one-wave kernel: it launches
+// one wave per line where the chunk kernel would leave most CUs idle (for
+// many lines the two run at about the same speed, the chunk kernel slightly
+// ahead on 512-position lines).  Returns false when the chunk kernel is used.
+template <class Geo>
+static bool launch_rows_wave(const typename Geo::Val* in, int L, int64_t nlines, const Geo& geo,
+                             int32_t* sqdist, float* dist, int32_t* indices, hipStream_t s,
+                             KernelTimer* tm, const char* kname, hipError_t* err) {
+    if (L > 1024 || nlines > 65536) return false;
+    if (L <= 64) *err = launch_rows_wave_t<Geo, 1>(in, L, nlines, geo, sqdist, dist, indices, s, tm, kname);
+    else if (L <= 128) *err = launch_rows_wave_t<Geo, 2>(in, L, nlines, geo, sqdist, dist, indices, s, tm, kname);
+    else if (L <= 256) *err = launch_rows_wave_t<Geo, 4>(in, L, nlines, geo, sqdist, dist, indices, s, tm, kname);
+    else if (L <= 512) *err = launch_rows_wave_t<Geo, 8>(in, L, nlines, geo, sqdist, dist, indices, s, tm, kname);
+    else *err = launch_rows_wave_t<Geo, 16>(in, L, nlines, geo, sqdist, dist, indices, s, tm, kname);
+    return true;
+}
+
 struct RowPlan {
     int K, Gp, LPW, VW;
     size_t lds;
@@ -892,14 +1192,18 @@ hipError_t launch_rows_2d(const uint16_t* c0, int H, int W, double s2_0, double 
                           int32_t* sqdist, float* dist, int32_t* indices, hipStream_t s,
                           KernelTimer* tm) {
     Geo2D geo{s2_0, s2_1, W};
+    hipError_t e = hipSuccess;
+    if (launch_rows_wave<Geo2D>(c0, W, H, geo, sqdist, dist, indices, s, tm, "envelope_rows_2d", &e)) return e;
     return launch_rows_any<Geo2D, 32>(c0, W, H, geo, sqdist, dist, indices, s, tm, "envelope_rows_2d");
 }
 
 hipError_t launch_rows_3d(const uint32_t* c01, int B, int D, int H, int W, double s2_0,
                           double s2_1, double s2_2, int32_t* sqdist, float* dist,
                           int32_t* indices, hipStream_t s, KernelTimer* tm) {
-    Geo3D geo{s2_0, s2_1, s2_2, D, H, W};
+    Geo3D geo{s2_0, s2_1, s2_2, D, H, W, (int64_t)D * H < (1 << 24)};
     const int64_t nlines = (int64_t)B * D * H;
+    hipError_t e = hipSuccess;
+    if (launch_rows_wave<Geo3D>(c01, W, nlines, geo, sqdist, dist, indices, s, tm, "envelope_rows_3d", &e)) return e;
     return launch_rows_any<Geo3D, 16>(c01, W, nlines, geo, sqdist, dist, indices, s, tm, "envelope_rows_3d");
 }
 

@@ -182,6 +182,23 @@ def test_edge_cases_3d(torch_dev):
     check(torch_dev, mask)
 
 
+def test_many_short_lines(torch_dev):
+    """More than 65536 rows of at most 1024 positions in a volume batch: the
+    chunk-per-lane row kernel (fewer lines take the one-wave-per-line kernel,
+    which the small shapes above exercise), with partial last chunks.  (2-D
+    images have at most 65535 rows; their rows over 1024 positions use the
+    chunk kernel, see the 4100- and 1031-wide shapes.)"""
+    rng = np.random.default_rng([42, 3004])
+    for shape in ((1, 300, 230, 70), (2, 260, 130, 20)):
+        for p in (0.002, 0.3):
+            mask = (rng.random(shape) >= p).astype(np.uint8)
+            for b in range(shape[0]):
+                mask[b].reshape(-1)[b] = 0
+            _say(f"3d {shape} p={p}")
+            check(torch_dev, mask)
+            check(torch_dev, mask, (2.5, 1.0, 1.0))
+
+
 def test_background_runs(torch_dev):
     """Whole chunks of background next to foreground: such chunks own
     themselves, and the members they offer to the neighbouring chunks must be
