@@ -76,7 +76,8 @@ def algorithmic_bytes(kernel: str, shape, n_out: int) -> int:
     """Bytes a kernel must move through HBM by the per-element byte model:
     every input it needs read once and every output written once, at the
     narrowest exact width (mask 1 B, axis-0 coordinate 2 B, packed coordinate
-    pair 4 B, each requested output 4 B; segment summaries 2 B each)."""
+    pair 4 B, each requested output 4 B; segment summaries 2 B each, and the
+    64-bit background-row mask of each 64-row segment, 1 bit per element)."""
     n = int(np.prod(shape))
     if len(shape) == 2:
         n0, M, B = shape[0], shape[1], 1
@@ -84,12 +85,13 @@ def algorithmic_bytes(kernel: str, shape, n_out: int) -> int:
         B, n0, M = shape[0], shape[1], shape[2] * shape[3]
     nseg = (n0 + 63) // 64
     summ = B * nseg * M * 2 * 2          # first + last, uint16 each
+    rows = B * nseg * M * 8              # background-row masks
     if kernel == "axis0_summary":
-        return n + summ
+        return n + summ + rows
     if kernel == "axis0_scan":
         return 2 * summ
     if kernel == "axis0_resolve":
-        return n + summ + 2 * n
+        return rows + summ + 2 * n
     if kernel == "envelope_rows_2d":
         return 2 * n + 4 * n * n_out
     if kernel == "envelope_cols_3d":

@@ -25,7 +25,7 @@ constexpr size_t kAlign = 256;
 size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-    size_t c0 = 0, c01 = 0, first = 0, last = 0, total = 0;
+    size_t c0 = 0, c01 = 0, first = 0, last = 0, bits = 0, total = 0;
 };
 
 bool shape2d_ok(int32_t H, int32_t W) {
@@ -50,7 +50,8 @@ Layout layout2d(int32_t H, int32_t W) {
     L.c0 = 0;
     L.first = round_up(n * 2);
     L.last = L.first + round_up(nseg * W * 2);
-    L.total = L.last + round_up(nseg * W * 2);
+    L.bits = L.last + round_up(nseg * W * 2);
+    L.total = L.bits + round_up(nseg * W * 8);
     return L;
 }
 
@@ -63,7 +64,8 @@ Layout layout3d(int32_t B, int32_t D, int32_t H, int32_t W) {
     L.c01 = round_up(n * 2);
     L.first = L.c01 + round_up(n * 4);
     L.last = L.first + round_up(summ);
-    L.total = L.last + round_up(summ);
+    L.bits = L.last + round_up(summ);
+    L.total = L.bits + round_up(summ * 4);
     return L;
 }
 
@@ -125,7 +127,8 @@ edt_status run2d(const uint8_t* mask, int32_t H, int32_t W, const float* samplin
     uint16_t* c0 = reinterpret_cast<uint16_t*>(base + L.c0);
     uint16_t* first = reinterpret_cast<uint16_t*>(base + L.first);
     uint16_t* last = reinterpret_cast<uint16_t*>(base + L.last);
-    if (edt::launch_axis0(mask, 1, H, W, first, last, c0, stream, tm) != hipSuccess) return EDT_ERR_HIP;
+    uint64_t* bits = reinterpret_cast<uint64_t*>(base + L.bits);
+    if (edt::launch_axis0(mask, 1, H, W, first, last, bits, c0, stream, tm) != hipSuccess) return EDT_ERR_HIP;
     if (edt::launch_rows_2d(c0, H, W, s2[0], s2[1], sqdist, dist, indices, stream, tm) != hipSuccess)
         return EDT_ERR_HIP;
     return EDT_OK;
@@ -152,7 +155,8 @@ edt_status run3d(const uint8_t* mask, int32_t B, int32_t D, int32_t H, int32_t W
     uint32_t* c01 = reinterpret_cast<uint32_t*>(base + L.c01);
     uint16_t* first = reinterpret_cast<uint16_t*>(base + L.first);
     uint16_t* last = reinterpret_cast<uint16_t*>(base + L.last);
-    if (edt::launch_axis0(mask, B, D, (int64_t)H * W, first, last, c0, stream, tm) != hipSuccess)
+    uint64_t* bits = reinterpret_cast<uint64_t*>(base + L.bits);
+    if (edt::launch_axis0(mask, B, D, (int64_t)H * W, first, last, bits, c0, stream, tm) != hipSuccess)
         return EDT_ERR_HIP;
     if (edt::launch_cols_3d(c0, B, D, H, W, s2[0], s2[1], c01, stream, tm) != hipSuccess)
         return EDT_ERR_HIP;

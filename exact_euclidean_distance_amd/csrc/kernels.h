@@ -26,9 +26,10 @@ struct KernelTimer {
 
 // Axis-0 pass: for every line along axis 0 (B images of n0 x M elements), the
 // axis-0 coordinate of the nearest background element on that line (kNone16 if
-// the line has none).  first/last: workspace of B * nseg * M uint16 each.
+// the line has none).  first/last: workspace of B * nseg * M uint16 each;
+// bits: B * nseg * M uint64 (nseg = ceil(n0 / kSegRows)).
 hipError_t launch_axis0(const uint8_t* mask, int B, int n0, int64_t M,
-                        uint16_t* first, uint16_t* last, uint16_t* c0,
+                        uint16_t* first, uint16_t* last, uint64_t* bits, uint16_t* c0,
                         hipStream_t s, KernelTimer* tm);
 
 // Envelope pass along the last axis of a 2-D image (lines = rows of length W).

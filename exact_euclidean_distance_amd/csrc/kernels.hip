@@ -73,10 +73,12 @@ hipError_t KernelTimer::end(hipStream_t s) {
 // --------------------------------------------------------------------------
 // Pass 0: nearest background along axis 0, in three kernels over segments of
 // kSegRows rows (so that long, few lines still fill the machine):
-//   summary  first/last background row of every (segment, column);
+//   summary  per (segment, column), the 64-bit mask of background rows and the
+//            first/last of them;
 //   scan     per column, nearest background strictly above / below each segment;
-//   resolve  per (segment, column), the nearest background of every row from a
-//            64-bit background bitmask of the segment plus the two carries.
+//   resolve  per (segment, column), the nearest background of every row from
+//            the segment's mask plus the two carries (the mask bytes are read
+//            once, by the summary).
 // Columns are the contiguous innermost index m (one lane per VEC columns), so
 // every load and store is coalesced.
 // --------------------------------------------------------------------------
@@ -142,7 +144,8 @@ template <int VEC>
 __global__ __launch_bounds__(256) void k_axis0_summary(const uint8_t* __restrict__ mask, int n0,
                                                         int64_t M, int nseg,
                                                         uint16_t* __restrict__ first,
-                                                        uint16_t* __restrict__ last) {
+                                                        uint16_t* __restrict__ last,
+                                                        uint64_t* __restrict__ bits) {
     const int64_t col = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * VEC;
     const int s = blockIdx.y;
     const int b = blockIdx.z;
@@ -150,23 +153,27 @@ __global__ __launch_bounds__(256) void k_axis0_summary(const uint8_t* __restrict
     const int i0 = s * kSegRows;
     const int i1 = min(n0, i0 + kSegRows);
     const uint8_t* src = mask + (int64_t)b * n0 * M + col;
-    uint16_t f[VEC], l[VEC];
+    uint64_t bm[VEC];   // bit r: row i0 + r is background
 #pragma unroll
-    for (int v = 0; v < VEC; ++v) { f[v] = kNone16; l[v] = kNone16; }
+    for (int v = 0; v < VEC; ++v) bm[v] = 0;
 #pragma unroll 4
     for (int i = i0; i < i1; ++i) {
         uint8_t x[VEC];
         load_bytes<VEC>(src + (int64_t)i * M, x);
 #pragma unroll
-        for (int v = 0; v < VEC; ++v) {
-            const bool bg = (x[v] == 0);
-            f[v] = (bg && f[v] == kNone16) ? (uint16_t)i : f[v];
-            l[v] = bg ? (uint16_t)i : l[v];
-        }
+        for (int v = 0; v < VEC; ++v) bm[v] |= (uint64_t)(x[v] == 0) << (i - i0);
+    }
+    uint16_t f[VEC], l[VEC];
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) {
+        f[v] = bm[v] ? (uint16_t)(i0 + __builtin_ctzll(bm[v])) : kNone16;
+        l[v] = bm[v] ? (uint16_t)(i0 + 63 - __builtin_clzll(bm[v])) : kNone16;
     }
     const int64_t o = ((int64_t)b * nseg + s) * M + col;
     store_u16<VEC>(first + o, f);
     store_u16<VEC>(last + o, l);
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) bits[o + v] = bm[v];
 }
 
 // After this kernel last[b][s][m] holds the nearest background row above
@@ -227,7 +234,7 @@ __device__ __forceinline__ int switch_row(int p, int n) {
 }
 
 template <int VEC>
-__global__ __launch_bounds__(256) void k_axis0_resolve(const uint8_t* __restrict__ mask, int n0,
+__global__ __launch_bounds__(256) void k_axis0_resolve(const uint64_t* __restrict__ bits, int n0,
                                                         int64_t M, int nseg,
                                                         const uint16_t* __restrict__ up_carry,
                                                         const uint16_t* __restrict__ dn_carry,
@@ -238,18 +245,10 @@ __global__ __launch_bounds__(256) void k_axis0_resolve(const uint8_t* __restrict
     if (col >= M) return;
     const int i0 = s * kSegRows;
     const int i1 = min(n0, i0 + kSegRows);
-    const uint8_t* src = mask + (int64_t)b * n0 * M + col;
-    uint64_t bm[VEC];
-#pragma unroll
-    for (int v = 0; v < VEC; ++v) bm[v] = 0;
-#pragma unroll 4
-    for (int i = i0; i < i1; ++i) {
-        uint8_t x[VEC];
-        load_bytes<VEC>(src + (int64_t)i * M, x);
-#pragma unroll
-        for (int v = 0; v < VEC; ++v) bm[v] |= (uint64_t)(x[v] == 0) << (i - i0);
-    }
     const int64_t so = ((int64_t)b * nseg + s) * M + col;
+    uint64_t bm[VEC];   // the segment's background rows, from the summary
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) bm[v] = bits[so + v];
     uint16_t upc[VEC], dnc[VEC];
     load_u16<VEC>(up_carry + so, upc);
     load_u16<VEC>(dn_carry + so, dnc);
@@ -295,7 +294,7 @@ __global__ __launch_bounds__(256) void k_axis0_resolve(const uint8_t* __restrict
 }
 
 hipError_t launch_axis0(const uint8_t* mask, int B, int n0, int64_t M, uint16_t* first,
-                        uint16_t* last, uint16_t* c0, hipStream_t s, KernelTimer* tm) {
+                        uint16_t* last, uint64_t* bits, uint16_t* c0, hipStream_t s, KernelTimer* tm) {
     const int nseg = (n0 + kSegRows - 1) / kSegRows;
     int vec = 1;
     if (M % 16 == 0 && ((uintptr_t)mask & 15) == 0) vec = 16;
@@ -307,20 +306,20 @@ hipError_t launch_axis0(const uint8_t* mask, int B, int n0, int64_t M, uint16_t*
     };
     const int svec = vec;
     if (svec == 16) {
-        EDT_LAUNCH(tm, "axis0_summary", s, hipLaunchKernelGGL(k_axis0_summary<16>, grid_for(16), block, 0, s, mask, n0, M, nseg, first, last));
+        EDT_LAUNCH(tm, "axis0_summary", s, hipLaunchKernelGGL(k_axis0_summary<16>, grid_for(16), block, 0, s, mask, n0, M, nseg, first, last, bits));
     } else if (svec == 4) {
-        EDT_LAUNCH(tm, "axis0_summary", s, hipLaunchKernelGGL(k_axis0_summary<4>, grid_for(4), block, 0, s, mask, n0, M, nseg, first, last));
+        EDT_LAUNCH(tm, "axis0_summary", s, hipLaunchKernelGGL(k_axis0_summary<4>, grid_for(4), block, 0, s, mask, n0, M, nseg, first, last, bits));
     } else {
-        EDT_LAUNCH(tm, "axis0_summary", s, hipLaunchKernelGGL(k_axis0_summary<1>, grid_for(1), block, 0, s, mask, n0, M, nseg, first, last));
+        EDT_LAUNCH(tm, "axis0_summary", s, hipLaunchKernelGGL(k_axis0_summary<1>, grid_for(1), block, 0, s, mask, n0, M, nseg, first, last, bits));
     }
     dim3 sgrid((unsigned)((M + 63) / 64), (unsigned)B);
     dim3 sblock(64, kScanQ);
     EDT_LAUNCH(tm, "axis0_scan", s, hipLaunchKernelGGL(k_axis0_scan, sgrid, sblock, 0, s, first, last, nseg, M));
     // the resolve keeps per-column state in registers: 4 columns per lane
     if (vec >= 4) {
-        EDT_LAUNCH(tm, "axis0_resolve", s, hipLaunchKernelGGL(k_axis0_resolve<4>, grid_for(4), block, 0, s, mask, n0, M, nseg, last, first, c0));
+        EDT_LAUNCH(tm, "axis0_resolve", s, hipLaunchKernelGGL(k_axis0_resolve<4>, grid_for(4), block, 0, s, bits, n0, M, nseg, last, first, c0));
     } else {
-        EDT_LAUNCH(tm, "axis0_resolve", s, hipLaunchKernelGGL(k_axis0_resolve<1>, grid_for(1), block, 0, s, mask, n0, M, nseg, last, first, c0));
+        EDT_LAUNCH(tm, "axis0_resolve", s, hipLaunchKernelGGL(k_axis0_resolve<1>, grid_for(1), block, 0, s, bits, n0, M, nseg, last, first, c0));
     }
     return hipSuccess;
 }
