@@ -231,6 +231,9 @@ EDT_HD inline int first_index_beating(double A, double B, int cap) {
     return c;
 }
 
+template <bool Narrow> struct SeqBits { using T = uint64_t; };
+template <> struct SeqBits<true> { using T = uint32_t; };
+
 // Up to eight 16-bit values held in four 32-bit registers; no array, so
 // nothing is placed in scratch memory whatever the index.
 struct Packed8 {
@@ -273,6 +276,8 @@ template <int K, int CAP, class View, class Mask, class Mark>
 EDT_HD inline bool chunk_owner_marks(View& v, int c, int G, int L, Mask M, Mark mark) {
     static_assert(2 * CAP + K <= 64, "sequence index space must fit 64 bits");
     static_assert(CAP <= 8, "reach lists hold at most eight members");
+    // bit set over the sequence index space below (32 bits when it fits)
+    using Seq = typename SeqBits<2 * CAP + K <= 32>::T;
     const int b = c * K;
     const int n = L - b < K ? L - b : K;
     const int e = b + n - 1;
@@ -355,17 +360,17 @@ EDT_HD inline bool chunk_owner_marks(View& v, int c, int G, int L, Mask M, Mark 
     // member below it are kept with their positions and heights, and the chunk's
     // own members, already convex, are appended without tests once two of them
     // lead the stack)
-    uint64_t alive = 0;
+    Seq alive = 0;
     int top = -1, sec = -1, ptop = 0, psec = 0;
     double Ytop = 0.0, Ysec = 0.0;
     auto insert = [&](int i, int p) {
         const double Y = v.Y(p);
         while (sec >= 0 && dominated(psec, Ysec, ptop, Ytop, p, Y)) {
-            alive &= ~(uint64_t(1) << top);
+            alive &= ~(Seq(1) << top);
             top = sec;
             ptop = psec;
             Ytop = Ysec;
-            const uint64_t below = alive & ((uint64_t(1) << top) - 1);
+            const Seq below = alive & ((Seq(1) << top) - 1);
             if (below) {
                 sec = high_bit(below);
                 psec = pos_of(sec);
@@ -374,7 +379,7 @@ EDT_HD inline bool chunk_owner_marks(View& v, int c, int G, int L, Mask M, Mark 
                 sec = -1;
             }
         }
-        alive |= uint64_t(1) << i;
+        alive |= Seq(1) << i;
         sec = top;
         psec = ptop;
         Ysec = Ytop;
@@ -386,7 +391,7 @@ EDT_HD inline bool chunk_owner_marks(View& v, int c, int G, int L, Mask M, Mark 
     Mask rest = M;
     while (rest) {
         if (sec >= CAP) {   // top and sec are both members of the chunk
-            alive |= (uint64_t)rest << CAP;
+            alive |= (Seq)rest << CAP;
             const int t_last = high_bit(rest);
             const Mask below = rest & ~(Mask(1) << t_last);
             if (below) {
@@ -417,7 +422,7 @@ EDT_HD inline bool chunk_owner_marks(View& v, int c, int G, int L, Mask M, Mark 
     double Yi = v.Y(pi);
     int st = b;
     for (;;) {
-        const uint64_t after = alive & ~((uint64_t(2) << i) - 1);
+        const Seq after = i + 1 < (int)(8 * sizeof(Seq)) ? alive & ~((Seq(2) << i) - 1) : Seq(0);
         int en = e + 1;
         int j = -1, pj = 0;
         double Yj = 0.0;

@@ -1218,15 +1218,16 @@ struct ColPlan {
     size_t lds;
 };
 
-// H <= 512: chunks of 32 and 8 lines per block; H <= 1024: chunks of 64 and
-// 32 lines per block (LDS holds TW lines of values and marks; narrower tiles
+// H <= 512: chunks of 32 and 64 / Gp lines per block (at least 8); H <= 1024:
+// chunks of 64 and 32 lines per block (LDS holds TW lines of values and marks; narrower tiles
 // mean smaller blocks, more of them resident per CU).
 static ColPlan plan_cols(int H) {
     ColPlan p{};
     p.K = H <= 512 ? 32 : 64;
-    p.TW = H <= 512 ? 8 : 32;
     p.Gp = 1;
     while (p.Gp * p.K < H) p.Gp <<= 1;
+    // the narrowest tile that still fills one wave (8 lines at the least)
+    p.TW = p.K == 64 ? 32 : (64 / p.Gp > 8 ? 64 / p.Gp : 8);
     p.lds = p.K == 32 ? Slots<uint16_t, 32>::bytes(p.Gp * p.TW, p.Gp) : Slots<uint16_t, 64>::bytes(p.Gp * p.TW, p.Gp);
     return p;
 }
@@ -1324,8 +1325,13 @@ static hipError_t launch_cols_t(const uint16_t* c0, int B, int D, int H, int W, 
 hipError_t launch_cols_3d(const uint16_t* c0, int B, int D, int H, int W, double s2_0,
                           double s2_1, uint32_t* c01, hipStream_t s, KernelTimer* tm) {
     const ColPlan p = plan_cols(H);
-    if (p.K == 32) return launch_cols_t<32, 8>(c0, B, D, H, W, s2_0, s2_1, c01, p, s, tm);
-    return launch_cols_t<64, 32>(c0, B, D, H, W, s2_0, s2_1, c01, p, s, tm);
+    if (p.K == 64) return launch_cols_t<64, 32>(c0, B, D, H, W, s2_0, s2_1, c01, p, s, tm);
+    switch (p.TW) {
+        case 8: return launch_cols_t<32, 8>(c0, B, D, H, W, s2_0, s2_1, c01, p, s, tm);
+        case 16: return launch_cols_t<32, 16>(c0, B, D, H, W, s2_0, s2_1, c01, p, s, tm);
+        case 32: return launch_cols_t<32, 32>(c0, B, D, H, W, s2_0, s2_1, c01, p, s, tm);
+        default: return launch_cols_t<32, 64>(c0, B, D, H, W, s2_0, s2_1, c01, p, s, tm);
+    }
 }
 
 }  // namespace edt
