@@ -50,77 +50,44 @@ EDT_HD inline bool dominated(int a, double Ya, int b, double Yb, int c, double Y
 // lower envelope of its chunk with the insertion sweep of PR-EDT Algorithm 1
 // (insert by increasing coordinate, drop the members the new one dominates);
 // the stack is a K-bit mask of surviving positions, so it needs no storage
-// beyond one register.  Neighbouring chunk envelopes are then merged in a
-// binary tree: at each junction one lane removes, from the inner ends of the
-// two convex chains, members dominated by their current neighbours until both
-// junction triples are convex -- the outward re-checks of PR-EDT Algorithm 2.
-// Every merged chain stays locally convex, hence is the envelope of its union.
+// beyond one register.  The line's envelope then follows either per chunk
+// (chunk_owner_marks, below) or for whole lines in rounds (boundary_dead):
+// only a chunk's first and last members have neighbours in other chunks, and
+// a member whose neighbours change by a removal becomes a first or last one,
+// so each round tests those two members of every chunk against the nearest
+// members around them, all dominated ones leave together, and the rounds stop
+// when one removes nothing.  A point above the segment between two points of
+// the set stays above the lower hull of what remains, so the survivors are the
+// envelope of the line -- PR-EDT Algorithm 2's outward re-checks, done at every
+// junction at once.
 // --------------------------------------------------------------------------
 
-// View of one line: chunk masks, parabola heights Y and the search for
-// non-empty chunks (last_nonempty / first_nonempty over a half-open chunk
-// range, -1 if none; mark_empty when a chunk loses its last member).
-// Implemented by the kernels' LDS layouts and by the host model.
-template <class View, class Mask, int K>
-struct Chain {
-    View& v;
-    EDT_HD Chain(View& vv) : v(vv) {}
-
-    EDT_HD int last_in(int c0, int c1) {  // largest member in chunks [c0, c1)
-        const int c = v.last_nonempty(c0, c1);
-        return c < 0 ? -1 : c * K + high_bit(v.mask(c));
+// One round for chunk c of a line of G chunks with member mask m: the bits of
+// its first and last members that the dominance test removes, against the
+// line as it stands at the start of the round.  View: mask(c), Y(pos),
+// last_nonempty / first_nonempty over a half-open chunk range (-1 if none).
+template <int K, class View, class Mask>
+EDT_HD inline Mask boundary_dead(View& v, int c, int G, Mask m) {
+    if (!m) return 0;
+    const int base = c * K;
+    const int tf = low_bit(m), tl = high_bit(m);
+    const int cp = v.last_nonempty(0, c), cn = v.first_nonempty(c + 1, G);
+    const int pl = cp < 0 ? -1 : cp * K + high_bit(v.mask(cp));   // last member before the chunk
+    const int nf = cn < 0 ? -1 : cn * K + low_bit(v.mask(cn));    // first member after it
+    Mask dead = 0;
+    {
+        const int p = base + tf;
+        const Mask above = m & bits_above<Mask>(tf);
+        const int pn = above ? base + low_bit(above) : nf;
+        if (pl >= 0 && pn >= 0 && dominated(pl, v.Y(pl), p, v.Y(p), pn, v.Y(pn))) dead |= Mask(1) << tf;
     }
-    EDT_HD int first_in(int c0, int c1) {  // smallest member in chunks [c0, c1)
-        const int c = v.first_nonempty(c0, c1);
-        return c < 0 ? -1 : c * K + low_bit(v.mask(c));
+    if (tl != tf) {
+        const int p = base + tl;
+        const int pp = base + high_bit(m & bits_below<Mask>(tl));
+        if (nf >= 0 && dominated(pp, v.Y(pp), p, v.Y(p), nf, v.Y(nf))) dead |= Mask(1) << tl;
     }
-    EDT_HD int prev_member(int pos, int c_lo) {  // largest member < pos, chunks >= c_lo
-        const int c = pos / K;
-        const Mask m = v.mask(c) & bits_below<Mask>(pos % K);
-        if (m) return c * K + high_bit(m);
-        return last_in(c_lo, c);
-    }
-    EDT_HD int next_member(int pos, int c_hi) {  // smallest member > pos, chunks < c_hi
-        const int c = pos / K;
-        const Mask m = v.mask(c) & bits_above<Mask>(pos % K);
-        if (m) return c * K + low_bit(m);
-        return first_in(c + 1, c_hi);
-    }
-    EDT_HD void remove(int pos) {
-        const int c = pos / K;
-        const Mask m = v.mask(c) & ~(Mask(1) << (pos % K));
-        v.set_mask(c, m);
-        if (!m) v.mark_empty(c);
-    }
-
-    // Merge the envelopes of chunks [cl, cm) and [cm, cr).
-    EDT_HD void junction(int cl, int cm, int cr) {
-        int a = last_in(cl, cm);
-        if (a < 0) return;
-        int b = first_in(cm, cr);
-        if (b < 0) return;
-        double Ya = v.Y(a), Yb = v.Y(b);
-        int a2 = prev_member(a, cl);
-        double Ya2 = a2 >= 0 ? v.Y(a2) : 0.0;
-        int b2 = next_member(b, cr);
-        double Yb2 = b2 >= 0 ? v.Y(b2) : 0.0;
-        for (;;) {
-            if (a2 >= 0 && dominated(a2, Ya2, a, Ya, b, Yb)) {
-                remove(a);
-                a = a2; Ya = Ya2;
-                a2 = prev_member(a, cl);
-                if (a2 >= 0) Ya2 = v.Y(a2);
-            } else if (b2 >= 0 && dominated(a, Ya, b, Yb, b2, Yb2)) {
-                remove(b);
-                b = b2; Yb = Yb2;
-                b2 = next_member(b, cr);
-                if (b2 >= 0) Yb2 = v.Y(b2);
-            } else {
-                break;
-            }
-        }
-    }
-};
+    return dead;
+}
 
 // Non-empty chunk search over an occupancy bit set (bit c of word c / 64 set
 // when chunk c has a member), for views that keep one.
@@ -271,7 +238,8 @@ struct Packed8 {
 // nearest position is no better than the best value so far.  Returns false
 // without marking if more than CAP members reach in from one side.
 // View: Y(pos), f(pos), s2l, mask(c), last_nonempty / first_nonempty (as for
-// Chain), fmin_lb(c) (a lower bound of F over chunk c).  Needs 2 CAP + K <= 64.
+// boundary_dead), fmin_lb(c) (a lower bound of F over chunk c).  Needs
+// 2 CAP + K <= 64.
 template <int K, int CAP, class View, class Mask, class Mark>
 EDT_HD inline bool chunk_owner_marks(View& v, int c, int G, int L, Mask M, Mark mark) {
     static_assert(2 * CAP + K <= 64, "sequence index space must fit 64 bits");

@@ -343,8 +343,9 @@ hipError_t launch_axis0(const uint8_t* mask, int B, int n0, int64_t M, uint16_t*
 //   3. each lane resolves its chunk alone from its own envelope and the few
 //      members of other chunks that reach into it (chunk_owner_marks), writing
 //      owner + 1 where each owned interval starts; if a chunk has more reaching
-//      members than fit, the block instead merges whole lines (merge tree,
-//      every member marking the start of its interval, a chunk-level scan);
+//      members than fit (or the layout skips this step), the block instead
+//      takes the envelope of whole lines in rounds (boundary_dead), every
+//      member marking the start of its interval, then a chunk-level scan;
 //   4. each lane scans its chunk: the owner of position q is the latest mark at
 //      or before q, so the outputs follow without any per-position search.
 // --------------------------------------------------------------------------
@@ -381,7 +382,8 @@ struct SlotArrays {
     unsigned* bound;  // per line: the candidate bound U (float32 bits); shares
                       // the storage of last/first, used before they are written
     uint64_t* occ;    // per line: bit c set while chunk c has a member
-    unsigned* flag;   // per block: some chunk needs the whole-line merge
+    unsigned* flag;   // per block: [0] some chunk needs whole lines; [1], [2]: a round of
+                      // the whole-line envelope removed a member (alternating)
     __device__ SlotArrays(unsigned char* smem, int nslots, int Gp) {
         size_t off = 0;
         val = reinterpret_cast<Val*>(smem);
@@ -458,8 +460,9 @@ __device__ void line_scans(T* a, uint16_t* b, int myslot, int g, int gs, int Gp)
 // Phases 1-4 for the lane's chunk g of its line (local line index lslot).
 // Fills the owner marks of the lane's chunk: the owner of a position is the
 // largest mark at or before it within the chunk.  Every thread of the block
-// must call it (it contains barriers).
-template <int K, class Val, class View, class IsValid, class FOfVal>
+// must call it (it contains barriers).  PerChunk: try phase 3's per-chunk
+// resolution first (otherwise whole lines in rounds straight away).
+template <int K, bool PerChunk, class Val, class View, class IsValid, class FOfVal>
 __device__ void resolve_line(View& view, SlotArrays<Val, K>& sa, const Val* mychunk,
                             uint16_t* mymarks, int g, int Gp, int L, bool active, int myslot,
                             int lslot, IsValid valid, FOfVal fval) {
@@ -509,7 +512,7 @@ __device__ void resolve_line(View& view, SlotArrays<Val, K>& sa, const Val* mych
     sa.mask[myslot] = (Mask)(amin < 0 ? 0 : base + amin + 1);
     if (g == 0) sa.bound[lslot] = 0u;
     if ((g & 63) == 0) view.occ[g >> 6] = 0ull;
-    if (myslot == 0) *sa.flag = 0u;
+    if (myslot == 0) { sa.flag[0] = 0u; sa.flag[1] = 0u; }
     __syncthreads();
     int aprev = -1, anext = -1;
     if (n > 0) {
@@ -568,32 +571,41 @@ __device__ void resolve_line(View& view, SlotArrays<Val, K>& sa, const Val* mych
     // 3. owners of the chunk from its own envelope and the members of other
     //    chunks that reach into it (chunk_owner_marks); only if some chunk of
     //    the block has more reaching members than the lists hold does the
-    //    block merge whole lines instead
-    bool ok = false;
-    if constexpr (2 * kReach + K <= 64) {
+    //    block take whole lines instead
+    if constexpr (PerChunk && 2 * kReach + K <= 64) {
 #pragma unroll
         for (int t = 0; t < K; t += 2) *reinterpret_cast<uint32_t*>(mymarks + t) = 0u;
-        ok = true;
+        bool ok = true;
         if (selfowned) {
             for (int t = 0; t < n; ++t) mymarks[t] = (uint16_t)(base + t + 1);
         } else if (n > 0) {
             ok = chunk_owner_marks<K, kReach>(view, g, G, L, m,
                                               [&](int t, int o) { mymarks[t] = (uint16_t)(o + 1); });
         }
-    }
-    if (!ok) atomicOr(sa.flag, 1u);
-    __syncthreads();
-    if (*sa.flag == 0u) return;
-
-    // 4. fallback: merge tree of the chunk envelopes over whole lines
-    for (int h = 1; h < Gp; h <<= 1) {
+        if (!ok) atomicOr(sa.flag, 1u);
         __syncthreads();
-        if (active && (g & (2 * h - 1)) == h) {
-            Chain<View, Mask, K> ch(view);
-            ch.junction(g - h, g, min(g + h, Gp));
-        }
+        if (*sa.flag == 0u) return;
     }
-    __syncthreads();
+
+    // 4. whole lines: the envelope from the chunk envelopes in rounds
+    //    (boundary_dead: every chunk's first and last members tested against
+    //    the nearest members around them, dominated ones removed together,
+    //    until a round removes nothing), then marks from every member.
+    //    flag[1] was cleared with flag[0]; each round clears the other one.
+    for (int r = 0;; ++r) {
+        m = sa.mask[myslot];
+        const Mask dead = active ? boundary_dead<K>(view, g, G, m) : Mask(0);
+        __syncthreads();
+        if (myslot == 0) sa.flag[1 + ((r + 1) & 1)] = 0u;   // the last round's flag, read by all
+        if (dead) {
+            m &= ~dead;
+            sa.mask[myslot] = m;
+            if (!m) view.mark_empty(g);
+            atomicOr(&sa.flag[1 + (r & 1)], 1u);
+        }
+        __syncthreads();
+        if (sa.flag[1 + (r & 1)] == 0u) break;
+    }
 
     // last member up to each chunk, first member from each chunk on; clear marks
     m = sa.mask[myslot];
@@ -657,6 +669,10 @@ __device__ void resolve_line(View& view, SlotArrays<Val, K>& sa, const Val* mych
 
 struct Geo2D {          // rows of an H x W image; value = axis-0 coordinate
     using Val = uint16_t;
+    // Rows of an image follow the nearest background of one column each, so
+    // their F varies freely along the row and many chunks see more reaching
+    // members than the per-chunk lists hold: whole lines in rounds are faster.
+    static constexpr bool kPerChunk = false;
     double s2a, s2l;    // squared spacing of axis 0 and along the row
     int W;
     struct Line { int row; };
@@ -678,6 +694,7 @@ struct Geo2D {          // rows of an H x W image; value = axis-0 coordinate
 };
 
 struct Geo3D {          // rows along W of B x D x H x W volumes; value = packed (axis0, axis1)
+    static constexpr bool kPerChunk = true;
     using Val = uint32_t;
     double s2a, s2b, s2l;
     int D, H, W;
@@ -772,7 +789,7 @@ __global__ __launch_bounds__(1024) void k_envelope_rows(const typename Geo::Val*
     LineView<Val, K, decltype(fof), 1> view{sa.val, sa.mask, sa.occ + (size_t)r * ((Gp + 63) / 64),
                                             sa.own, slot0, geo.s2l, fof};
     uint16_t* mymarks = sa.mark + (size_t)tid * CM;
-    resolve_line<K>(view, sa, sa.val + (size_t)tid * CS, mymarks, g, Gp, L, active, tid, r,
+    resolve_line<K, Geo::kPerChunk>(view, sa, sa.val + (size_t)tid * CS, mymarks, g, Gp, L, active, tid, r,
                     [](Val v) { return Geo::valid(v); }, fof);
 
     // 5. outputs.  mk is owner + 1 of position q (0: the line has no
@@ -1289,7 +1306,7 @@ __global__ __launch_bounds__(1024) void k_envelope_cols(const uint16_t* __restri
     };
     LineView<uint16_t, K, decltype(fof), TW> view{sa.val, sa.mask, sa.occ + x, sa.own, x, s2l, fof};
     uint16_t* mymarks = sa.mark + (size_t)tid * CM;
-    resolve_line<K>(view, sa, mine, mymarks, g, Gp, H, active, tid, x,
+    resolve_line<K, true>(view, sa, mine, mymarks, g, Gp, H, active, tid, x,
                     [](uint16_t v) { return v != kNone16; }, fof);
     int o = 0;
 

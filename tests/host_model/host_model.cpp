@@ -2,7 +2,7 @@
 // exact_euclidean_distance_amd/csrc/envelope.h.
 //
 // Runs, for one line at a time, the same functions the envelope kernels run
-// (chunk_bound, build_chunk, chunk_owner_marks, Chain::junction,
+// (chunk_bound, build_chunk, chunk_owner_marks, boundary_dead,
 // first_index_beating) in the same
 // phase order as the kernels, with plain arrays in place of LDS, so the CPU
 // test-suite can check the algorithm against the definition.  Not part of the
@@ -42,7 +42,7 @@ struct LineView {
 
 // G chunk slots of K positions (G * K >= L; slots past the line stay empty).
 // CAP: members reaching into a chunk from one side before the line falls back
-// to the merge tree (0: always the merge tree).
+// to whole-line rounds (0: always whole-line rounds).
 template <int K, int CAP>
 int run_line(const double* fb, int L, double s2l, int G, int32_t* owner) {
     using Mask = typename edt::MaskOf<K>::T;
@@ -104,31 +104,41 @@ int run_line(const double* fb, int L, double s2l, int G, int32_t* owner) {
     }
     if (!ok) {
         std::fill(mark.begin(), mark.end(), 0);
-        // phase 2': merge tree, one level at a time
-        for (int h = 1; h < G; h <<= 1) {
+        // phase 2': whole-line rounds; every chunk is tested against the line
+        // as it stands at the start of the round, the removals land together
+        for (;;) {
+            std::vector<Mask> dead(G, 0);
+            bool any = false;
             for (int g = 0; g < G; ++g) {
-                if ((g & (2 * h - 1)) == h) {
-                    edt::Chain<LineView<K>, Mask, K> ch(view);
-                    ch.junction(g - h, g, g + h < G ? g + h : G);
-                }
+                dead[g] = edt::boundary_dead<K>(view, g, G, masks[g]);
+                any = any || dead[g] != 0;
+            }
+            if (!any) break;
+            for (int g = 0; g < G; ++g) {
+                if (!dead[g]) continue;
+                masks[g] &= ~dead[g];
+                if (!masks[g]) view.mark_empty(g);
             }
         }
         // phase 3': every member v owns [st, en): st where it beats its
         // predecessor, en where its successor takes over; a non-empty interval
         // marks v + 1 at st (one writer per mark)
-        edt::Chain<LineView<K>, Mask, K> ch(view);
-        int u = -1;
-        double Yu = 0.0;
-        for (int v = ch.first_in(0, G); v >= 0;) {
+        std::vector<int> members;
+        for (int g = 0; g < G; ++g)
+            for (Mask mm = masks[g]; mm; mm &= mm - 1) members.push_back(g * K + edt::low_bit(mm));
+        for (size_t i = 0; i < members.size(); ++i) {
+            const int v = members[i];
             const double Yv = view.Y(v);
-            const int st = u < 0 ? 0 : edt::first_index_beating(Yv - Yu, 2.0 * s2l * (double)(v - u), L);
-            const int w = ch.next_member(v, G);
-            int en = L;
-            if (w >= 0) en = edt::first_index_beating(view.Y(w) - Yv, 2.0 * s2l * (double)(w - v), L);
+            int st = 0, en = L;
+            if (i > 0) {
+                const int u = members[i - 1];
+                st = edt::first_index_beating(Yv - view.Y(u), 2.0 * s2l * (double)(v - u), L);
+            }
+            if (i + 1 < members.size()) {
+                const int w = members[i + 1];
+                en = edt::first_index_beating(view.Y(w) - Yv, 2.0 * s2l * (double)(w - v), L);
+            }
             if (st < en) mark[st] = v + 1;
-            u = v;
-            Yu = Yv;
-            v = w;
         }
     }
     // phase 4: the owner of q is the latest mark at or before q

@@ -2,8 +2,8 @@
 
 tests/host_model/host_model.cpp compiles the device helpers of
 exact_euclidean_distance_amd/csrc/envelope.h as host C++ and drives them in the
-kernels' phase order (chunk envelopes -> merge tree -> first owned chunk ->
-walk).  Here that model is checked against the definition of a 1-D pass
+kernels' phase order (candidate filter -> chunk envelopes -> per-chunk owners,
+or whole-line rounds -> interval marks -> scan).  Here that model is checked against the definition of a 1-D pass
 (brute force over all candidates) and, composed into full transforms, against
 the oracle.  No GPU is needed.
 """
