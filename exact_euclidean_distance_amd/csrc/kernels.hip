@@ -368,6 +368,7 @@ struct Slots {
 
 constexpr uint16_t kNoFirst = 0xFFFFu;   // "no member" in the first-member scan
 constexpr int kReach = 8;                // reaching members kept per chunk side
+constexpr int kSparseCand = 12;          // above: a wave tests every position of its chunks
 
 // LDS carve-up shared by both layouts.
 template <class Val, int K>
@@ -441,19 +442,48 @@ struct LineView {
     __device__ void set_mask(int c, Mask m) { masks[slot(c)] = m; }
 };
 
-// Inclusive scans over the Gp chunks of every line (slot step gs), in LDS:
+// Inclusive scans over the Gp chunks of every line (slot step GS), in LDS:
 // prefix maximum of a[], and (when b is non-null) suffix minimum of b[].
-// Every thread of the block calls it; it ends with a barrier.
-template <class T>
-__device__ void line_scans(T* a, uint16_t* b, int myslot, int g, int gs, int Gp) {
-    for (int d = 1; d < Gp; d <<= 1) {
-        __syncthreads();
-        const T x = (g >= d) ? a[myslot - d * gs] : T(0);
-        const uint16_t y = (b && g + d < Gp) ? b[myslot + d * gs] : kNoFirst;
-        __syncthreads();
-        if (x > a[myslot]) a[myslot] = x;
-        if (b && y < b[myslot]) b[myslot] = y;
+// Chunk g of a line sits GS lanes after chunk g - 1, so the S = min(Gp, 64/GS)
+// chunks of a line that share a wave scan with lane shuffles; lines longer
+// than one wave then add the totals of their earlier (later) waves.  Every
+// thread of the block calls it; it starts and ends with a barrier.
+template <int GS, class T>
+__device__ void line_scans(T* a, uint16_t* b, int myslot, int g, int Gp) {
+    constexpr int kLanes = 64 / GS > 0 ? 64 / GS : 1;   // chunks of a line per wave
+    const int S = Gp < kLanes ? Gp : kLanes;
+    const int pos = g & (S - 1);
+    __syncthreads();
+    int x = (int)a[myslot];
+    int y = b ? (int)b[myslot] : 0;
+    for (int d = 1; d < S; d <<= 1) {
+        const int xu = __shfl_up(x, d * GS);
+        if (pos >= d && xu > x) x = xu;
+        if (b) {
+            const int yd = __shfl_down(y, d * GS);
+            if (pos + d < S && yd < y) y = yd;
+        }
     }
+    if (S < Gp) {
+        a[myslot] = (T)x;
+        if (b) b[myslot] = (uint16_t)y;
+        __syncthreads();
+        // totals of the other waves of the line: the last (first) chunk of each
+        const int w0 = g - pos;   // first chunk of this wave
+        for (int c = w0 - 1; c >= 0; c -= S) {
+            const int v = (int)a[myslot - (g - c) * GS];
+            if (v > x) x = v;
+        }
+        if (b) {
+            for (int c = w0 + S; c < Gp; c += S) {
+                const int v = (int)b[myslot + (c - g) * GS];
+                if (v < y) y = v;
+            }
+        }
+        __syncthreads();
+    }
+    a[myslot] = (T)x;
+    if (b) b[myslot] = (uint16_t)y;
     __syncthreads();
 }
 
@@ -551,8 +581,23 @@ __device__ void resolve_line(View& view, SlotArrays<Val, K>& sa, const Val* mych
             if (here && f <= U && !gone) cand |= Mask(1) << t;
         };
         if constexpr (kKeepF) {
+            // Most positions of a line far from the background fail F <= U, so
+            // the dominance test runs only on those that pass -- one at a time
+            // unless some lane of the wave has many of them.
+            Mask pass = 0;
 #pragma unroll
-            for (int t = 0; t < K; ++t) consider(t, Fr[t], (vmask >> t) & 1);
+            for (int t = 0; t < K; ++t)
+                if (Fr[t] <= U) pass |= Mask(1) << t;
+            pass &= vmask;
+            if (__any(__builtin_popcount(pass) > kSparseCand)) {
+#pragma unroll
+                for (int t = 0; t < K; ++t) consider(t, Fr[t], (pass >> t) & 1);
+            } else {
+                for (Mask rest = pass; rest; rest &= rest - 1) {
+                    const int t = low_bit(rest);
+                    consider(t, fval(mychunk[t]), true);
+                }
+            }
         } else {
 #pragma unroll 8
             for (int t = 0; t < n; ++t) {
@@ -614,7 +659,7 @@ __device__ void resolve_line(View& view, SlotArrays<Val, K>& sa, const Val* mych
     sa.own[myslot] = 0;
 #pragma unroll
     for (int t = 0; t < K; t += 2) *reinterpret_cast<uint32_t*>(mymarks + t) = 0u;
-    line_scans(sa.last, sa.first, myslot, g, gs, Gp);
+    line_scans<gs>(sa.last, sa.first, myslot, g, Gp);
 
     // owned intervals of the members: v owns [st, en), st against its
     // predecessor u, en where its successor w takes over
@@ -652,7 +697,7 @@ __device__ void resolve_line(View& view, SlotArrays<Val, K>& sa, const Val* mych
             st = en;
         }
     }
-    line_scans(sa.own, (uint16_t*)nullptr, myslot, g, gs, Gp);
+    line_scans<gs>(sa.own, (uint16_t*)nullptr, myslot, g, Gp);
     // the owner entering the chunk becomes its first mark (marks only grow)
     const int enter = g > 0 ? sa.own[myslot - gs] : 0;
     if (n > 0 && enter > (int)mymarks[0]) mymarks[0] = (uint16_t)enter;
