@@ -140,6 +140,11 @@ __device__ __forceinline__ void load_u16(const uint16_t* p, uint16_t (&v)[VEC]) 
     }
 }
 
+// Bit 7 of each byte of the result is set where that byte of w is zero.
+__device__ __forceinline__ uint32_t zero_bytes(uint32_t w) {
+    return ~(((w & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) | w) & 0x80808080u;
+}
+
 template <int VEC>
 __global__ __launch_bounds__(256) void k_axis0_summary(const uint8_t* __restrict__ mask, int n0,
                                                         int64_t M, int nseg,
@@ -156,12 +161,30 @@ __global__ __launch_bounds__(256) void k_axis0_summary(const uint8_t* __restrict
     uint64_t bm[VEC];   // bit r: row i0 + r is background
 #pragma unroll
     for (int v = 0; v < VEC; ++v) bm[v] = 0;
-#pragma unroll 4
-    for (int i = i0; i < i1; ++i) {
-        uint8_t x[VEC];
-        load_bytes<VEC>(src + (int64_t)i * M, x);
+    if (VEC == 4 && i1 - i0 == kSegRows) {
+        // A full segment, one 32-bit word (4 columns) per row: byte v of t
+        // collects the zero flags of column v over 8 rows, which then fill
+        // bits 8k .. 8k + 7 of that column's mask.
+        const uint8_t* rp = src + (int64_t)i0 * M;
 #pragma unroll
-        for (int v = 0; v < VEC; ++v) bm[v] |= (uint64_t)(x[v] == 0) << (i - i0);
+        for (int k = 0; k < kSegRows / 8; ++k) {
+            uint32_t w[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) w[j] = *reinterpret_cast<const uint32_t*>(rp + (int64_t)(8 * k + j) * M);
+            uint32_t t = 0;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) t |= (zero_bytes(w[j]) >> 7) << j;
+#pragma unroll
+            for (int v = 0; v < VEC; ++v) bm[v] |= (uint64_t)((t >> (8 * v)) & 0xFFu) << (8 * k);
+        }
+    } else {
+#pragma unroll 4
+        for (int i = i0; i < i1; ++i) {
+            uint8_t x[VEC];
+            load_bytes<VEC>(src + (int64_t)i * M, x);
+#pragma unroll
+            for (int v = 0; v < VEC; ++v) bm[v] |= (uint64_t)(x[v] == 0) << (i - i0);
+        }
     }
     uint16_t f[VEC], l[VEC];
 #pragma unroll
@@ -304,10 +327,9 @@ hipError_t launch_axis0(const uint8_t* mask, int B, int n0, int64_t M, uint16_t*
         const int64_t lanes = M / v + (M % v ? 1 : 0);
         return dim3((unsigned)((lanes + 255) / 256), (unsigned)nseg, (unsigned)B);
     };
-    const int svec = vec;
-    if (svec == 16) {
-        EDT_LAUNCH(tm, "axis0_summary", s, hipLaunchKernelGGL(k_axis0_summary<16>, grid_for(16), block, 0, s, mask, n0, M, nseg, first, last, bits));
-    } else if (svec == 4) {
+    // the summary reads one 32-bit word per lane and row: more lanes in flight
+    // than 16-byte reads give for the same bytes
+    if (vec >= 4) {
         EDT_LAUNCH(tm, "axis0_summary", s, hipLaunchKernelGGL(k_axis0_summary<4>, grid_for(4), block, 0, s, mask, n0, M, nseg, first, last, bits));
     } else {
         EDT_LAUNCH(tm, "axis0_summary", s, hipLaunchKernelGGL(k_axis0_summary<1>, grid_for(1), block, 0, s, mask, n0, M, nseg, first, last, bits));
