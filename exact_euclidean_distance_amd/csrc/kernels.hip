@@ -170,7 +170,8 @@ __global__ __launch_bounds__(256) void k_axis0_summary(const uint8_t* __restrict
         for (int k = 0; k < kSegRows / 8; ++k) {
             uint32_t w[8];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) w[j] = *reinterpret_cast<const uint32_t*>(rp + (int64_t)(8 * k + j) * M);
+            for (int j = 0; j < 8; ++j)   // read once: keep it out of the caches
+                w[j] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(rp + (int64_t)(8 * k + j) * M));
             uint32_t t = 0;
 #pragma unroll
             for (int j = 0; j < 8; ++j) t |= (zero_bytes(w[j]) >> 7) << j;
