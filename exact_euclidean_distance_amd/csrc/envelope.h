@@ -148,6 +148,37 @@ EDT_HD inline Mask build_chunk(int base, Mask cand, ValAt val_at, HeightOf heigh
     return m;
 }
 
+// The same sweep with the heights of the chunk's K positions at hand (Yr[t] is
+// Y of position base + t; unrolled over t, so that Yr can live in registers);
+// y_at(p) gives the height of an earlier position that a removal uncovers.
+template <int K, class Mask, class YAt>
+EDT_HD inline Mask build_chunk_unrolled(int base, Mask cand, const double (&Yr)[K], YAt y_at) {
+    Mask m = 0;
+    int top = -1, sec = -1;
+    double Ytop = 0.0, Ysec = 0.0;
+#pragma unroll
+    for (int t = 0; t < K; ++t) {
+        if (!((cand >> t) & Mask(1))) continue;
+        const int p = base + t;
+        const double Y = Yr[t];
+        while (sec >= 0 && dominated(sec, Ysec, top, Ytop, p, Y)) {
+            m &= ~(Mask(1) << (top - base));
+            top = sec; Ytop = Ysec;
+            const Mask below = m & bits_below<Mask>(top - base);
+            if (below) {
+                sec = base + high_bit(below);
+                Ysec = y_at(sec);
+            } else {
+                sec = -1;
+            }
+        }
+        m |= Mask(1) << t;
+        sec = top; Ysec = Ytop;
+        top = p; Ytop = Y;
+    }
+    return m;
+}
+
 // Candidate bound.  If U bounds the final squared distance of every position
 // of a line, a candidate with F_j > U owns no position (its parabola stays
 // above U everywhere) and can be left out without changing any result.  A

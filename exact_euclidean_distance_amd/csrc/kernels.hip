@@ -593,20 +593,21 @@ __device__ void resolve_line(View& view, SlotArrays<Val, K>& sa, const Val* mych
     } else {
         Mask cand = 0;
         // (U may be +inf when a chunk and both its neighbours hold no candidate)
-        auto consider = [&](int t, double f, bool here) {
+        auto consider = [&](int t, double Yp, bool here) {
             const int p = base + t;
-            const double Yp = f + s2l * (double)p * (double)p;
             const int lo = acur >= 0 && acur < p ? acur : aprev;
             const double Ylo = acur >= 0 && acur < p ? Ycur : Yprev;
             const int hi = acur > p ? acur : anext;
             const double Yhi = acur > p ? Ycur : Ynext;
             const bool gone = lo >= 0 && hi >= 0 && dominated(lo, Ylo, p, Yp, hi, Yhi);
-            if (here && f <= U && !gone) cand |= Mask(1) << t;
+            if (here && !gone) cand |= Mask(1) << t;
         };
+        auto height = [&](Val v, int p) { return fval(v) + s2l * (double)p * (double)p; };
         if constexpr (kKeepF) {
             // Most positions of a line far from the background fail F <= U, so
             // the dominance test runs only on those that pass -- one at a time
-            // unless some lane of the wave has many of them.
+            // unless some lane of the wave has many of them; then every
+            // position's height comes from the registers of phase 1.
             Mask pass = 0;
 #pragma unroll
             for (int t = 0; t < K; ++t)
@@ -614,22 +615,30 @@ __device__ void resolve_line(View& view, SlotArrays<Val, K>& sa, const Val* mych
             pass &= vmask;
             if (__any(__builtin_popcount(pass) > kSparseCand)) {
 #pragma unroll
-                for (int t = 0; t < K; ++t) consider(t, Fr[t], (pass >> t) & 1);
+                for (int t = 0; t < K; ++t) {
+                    Fr[t] += s2l * (double)(base + t) * (double)(base + t);   // now Y
+                    consider(t, Fr[t], (pass >> t) & 1);
+                }
+                if constexpr (K <= 16)   // (for longer chunks the registers run out)
+                    m = build_chunk_unrolled<K>(base, cand, Fr, [&](int p) { return view.Y(p); });
+                else
+                    m = build_chunk<Mask>(base, cand, [&](int t) { return mychunk[t]; }, height);
             } else {
                 for (Mask rest = pass; rest; rest &= rest - 1) {
                     const int t = low_bit(rest);
-                    consider(t, fval(mychunk[t]), true);
+                    consider(t, height(mychunk[t], base + t), true);
                 }
+                m = build_chunk<Mask>(base, cand, [&](int t) { return mychunk[t]; }, height);
             }
         } else {
 #pragma unroll 8
             for (int t = 0; t < n; ++t) {
                 const Val v = mychunk[t];
-                consider(t, fval(v), valid(v));
+                const double f = fval(v);
+                consider(t, height(v, base + t), valid(v) && f <= U);
             }
+            m = build_chunk<Mask>(base, cand, [&](int t) { return mychunk[t]; }, height);
         }
-        m = build_chunk<Mask>(base, cand, [&](int t) { return mychunk[t]; },
-                              [&](Val v, int p) { return fval(v) + s2l * (double)p * (double)p; });
     }
     sa.mask[myslot] = m;
     if (m) atomicOr(&view.occ[g >> 6], uint64_t(1) << (g & 63));

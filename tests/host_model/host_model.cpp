@@ -89,6 +89,11 @@ int run_line(const double* fb, int L, double s2l, int G, int32_t* owner) {
         masks[g] = edt::build_chunk<Mask>(
             base, cand, [&](int t) { return fb[base + t]; },
             [&](double v, int p) { return v + s2l * (double)p * (double)p; });
+        // the unrolled sweep over heights held per position must agree
+        double Yr[K];
+        for (int t = 0; t < K; ++t) Yr[t] = t < n ? view.Y(base + t) : 0.0;
+        if (edt::build_chunk_unrolled<K>(base, cand, Yr, [&](int p) { return view.Y(p); }) != masks[g])
+            return -2;
         if (masks[g]) occ[g >> 6] |= uint64_t(1) << (g & 63);
     }
     std::vector<int> mark(L, 0);
