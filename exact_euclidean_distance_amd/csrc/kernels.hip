@@ -430,7 +430,8 @@ struct SlotArrays {
 };
 
 // One line as seen by the envelope helpers: chunk c of the line lives in slot
-// slot0 + c * gs; occ points at the line's occupancy words.
+// slot0 + c * gs; occ points at the line's occupancy words.  (LDS offsets are
+// products of small slot indices and strides: 24-bit multiplies suffice.)
 template <class Val, int K, class FOf, int GS>
 struct LineView {
     using Mask = typename MaskOf<K>::T;
@@ -457,7 +458,7 @@ struct LineView {
     __device__ void mark_empty(int c) { atomicAnd(&occ[c >> 6], ~(uint64_t(1) << (c & 63))); }
     __device__ int slot(int c) const { return slot0 + c * gs; }
     __device__ Val val(int pos) const {
-        return vals[slot((unsigned)pos / K) * CS + ((unsigned)pos % K)];
+        return vals[__umul24((unsigned)slot((unsigned)pos / K), CS) + ((unsigned)pos % K)];
     }
     __device__ double f(int pos) const { return fof(val(pos)); }
     __device__ double Y(int pos) const { return f(pos) + s2l * (double)pos * (double)pos; }
@@ -719,7 +720,7 @@ __device__ void resolve_line(View& view, SlotArrays<Val, K>& sa, const Val* mych
             }
             if (st < en) {   // st < L follows from en <= L
                 const int cs = (unsigned)st / K;
-                sa.mark[(size_t)view.slot(cs) * CM + ((unsigned)st % K)] = (uint16_t)(v + 1);
+                sa.mark[__umul24((unsigned)view.slot(cs), CM) + ((unsigned)st % K)] = (uint16_t)(v + 1);
                 atomicMax(&sa.own[view.slot(cs)], v + 1);
             }
             if (!mm) break;
@@ -827,7 +828,7 @@ __device__ inline void load_row_line(const Val* __restrict__ src, int L, int g, 
             const int k = g + (i0 + i) * Gp;
             if (k < PL) {
                 const int p = k * VW;
-                Val* d = dst + ((unsigned)p / K) * CS + ((unsigned)p % K);
+                Val* d = dst + __umul24((unsigned)p / K, CS) + ((unsigned)p % K);
                 if constexpr (VW * sizeof(Val) == 16) {
                     uint32_t* d32 = reinterpret_cast<uint32_t*>(d);   // 4-byte aligned (CS even for uint16)
                     d32[0] = buf[i].x; d32[1] = buf[i].y; d32[2] = buf[i].z; d32[3] = buf[i].w;
@@ -858,15 +859,15 @@ __global__ __launch_bounds__(1024) void k_envelope_rows(const typename Geo::Val*
     const int64_t line = (int64_t)blockIdx.x * LPW + r;
     const bool active = line < nlines;
 
-    if (active) load_row_line<Val, K, VW>(in + line * (int64_t)L, L, g, Gp, sa.val + (size_t)slot0 * CS);
+    if (active) load_row_line<Val, K, VW>(in + line * (int64_t)L, L, g, Gp, sa.val + __umul24(slot0, CS));
     __syncthreads();
 
     const typename Geo::Line gl = geo.line(active ? line : 0);
     auto fof = [&](Val v) { return geo.f(gl, v); };
     LineView<Val, K, decltype(fof), 1> view{sa.val, sa.mask, sa.occ + (size_t)r * ((Gp + 63) / 64),
                                             sa.own, slot0, geo.s2l, fof};
-    uint16_t* mymarks = sa.mark + (size_t)tid * CM;
-    resolve_line<K, Geo::kPerChunk>(view, sa, sa.val + (size_t)tid * CS, mymarks, g, Gp, L, active, tid, r,
+    uint16_t* mymarks = sa.mark + __umul24(tid, CM);
+    resolve_line<K, Geo::kPerChunk>(view, sa, sa.val + __umul24(tid, CS), mymarks, g, Gp, L, active, tid, r,
                     [](Val v) { return Geo::valid(v); }, fof);
 
     // 5. outputs.  mk is owner + 1 of position q (0: the line has no
@@ -877,10 +878,10 @@ __global__ __launch_bounds__(1024) void k_envelope_rows(const typename Geo::Val*
     const int32_t ivirt = geo.virt_index();
     auto one = [&](int q, int mk, int32_t& osq, float& od, int32_t& oix) {
         const int ow = mk - 1;
-        const Val vo = view.val(ow < 0 ? 0 : ow);
-        const double qq = (double)q;
-        const double dq = (double)(q - ow);
-        const double F = ow < 0 ? fvirt + s2l * qq * qq : fof(vo) + s2l * dq * dq;
+        const int oq = ow < 0 ? 0 : ow;   // the virtual element acts as one at position 0
+        const Val vo = view.val(oq);
+        const double dq = (double)(q - oq);
+        const double F = (ow < 0 ? fvirt : fof(vo)) + s2l * dq * dq;
         osq = sqdist ? (int32_t)F : 0;
         od = __builtin_amdgcn_sqrtf((float)F);
         oix = ow < 0 ? ivirt : geo.index(gl, vo, ow);
@@ -905,20 +906,20 @@ __global__ __launch_bounds__(1024) void k_envelope_rows(const typename Geo::Val*
     }
     __syncthreads();
     if (!active) return;   // no barrier follows
-    const uint16_t* marks = sa.mark + (size_t)slot0 * CM;
+    const uint16_t* marks = sa.mark + __umul24(slot0, CM);
     if (vec_out) {   // L % 4 == 0 and 16-byte aligned outputs
 #pragma unroll 2
         for (int i = 0; i < K / 4; ++i) {
             const int p = 4 * (i * Gp + g);
             if (p >= L) break;
-            const uint16_t* om = marks + (unsigned)p / K * CM + (unsigned)p % K;
+            const uint16_t* om = marks + __umul24((unsigned)p / K, CM) + (unsigned)p % K;
 #pragma unroll
             for (int j = 0; j < 4; ++j) one(p + j, om[j], osq[j], od[j], oix[j]);
             store4(lbase + p);
         }
     } else {
         for (int p = g; p < L; p += Gp) {
-            one(p, marks[(unsigned)p / K * CM + (unsigned)p % K], osq[0], od[0], oix[0]);
+            one(p, marks[__umul24((unsigned)p / K, CM) + (unsigned)p % K], osq[0], od[0], oix[0]);
             if (sqdist) sqdist[lbase + p] = osq[0];
             if (dist) dist[lbase + p] = od[0];
             if (indices) indices[lbase + p] = oix[0];
@@ -1363,7 +1364,7 @@ __global__ __launch_bounds__(1024) void k_envelope_cols(const uint16_t* __restri
 
     // own chunk: rows base .. base + n - 1 of column w0 + x (all loads issued
     // before any is used; rows past the end read row n - 1 and are discarded)
-    uint16_t* mine = sa.val + (size_t)tid * CS;
+    uint16_t* mine = sa.val + __umul24(tid, CS);
     if (n > 0) {
         const uint16_t* src = c0 + plane * (int64_t)H * W + (int64_t)base * W + w0 + x;
         uint16_t buf[K];
@@ -1382,7 +1383,7 @@ __global__ __launch_bounds__(1024) void k_envelope_cols(const uint16_t* __restri
         return s2a * t * t;
     };
     LineView<uint16_t, K, decltype(fof), TW> view{sa.val, sa.mask, sa.occ + x, sa.own, x, s2l, fof};
-    uint16_t* mymarks = sa.mark + (size_t)tid * CM;
+    uint16_t* mymarks = sa.mark + __umul24(tid, CM);
     resolve_line<K, true>(view, sa, mine, mymarks, g, Gp, H, active, tid, x,
                     [](uint16_t v) { return v != kNone16; }, fof);
     int o = 0;
