@@ -535,18 +535,16 @@ __device__ void resolve_line(View& view, SlotArrays<Val, K>& sa, const Val* mych
     //    when the chunk is short enough (+inf: no candidate there).
     constexpr bool kKeepF = K <= 32;
     double Fr[kKeepF ? K : 1];
-    Mask vmask = 0;   // valid positions of the chunk
     double fmin = __builtin_huge_val();
     int amin = -1;
     bool allzero = true;   // every position is background itself (F = 0)
     if constexpr (kKeepF) {
 #pragma unroll
         for (int t = 0; t < K; ++t) {
-            const Val v = mychunk[t];   // entries past n are stale but in bounds
-            const bool here = t < n && valid(v);
+            const Val v = mychunk[t];   // positions past the line hold "no background"
+            const bool here = valid(v);
             Fr[t] = here ? fval(v) : __builtin_huge_val();
-            if (here) vmask |= Mask(1) << t;
-            if (t < n && Fr[t] != 0.0) allzero = false;
+            if (Fr[t] != 0.0) allzero = false;
             if (Fr[t] < fmin) { fmin = Fr[t]; amin = t; }
         }
     } else {
@@ -600,8 +598,10 @@ __device__ void resolve_line(View& view, SlotArrays<Val, K>& sa, const Val* mych
             const double Ylo = acur >= 0 && acur < p ? Ycur : Yprev;
             const int hi = acur > p ? acur : anext;
             const double Yhi = acur > p ? Ycur : Ynext;
-            const bool gone = lo >= 0 && hi >= 0 && dominated(lo, Ylo, p, Yp, hi, Yhi);
-            if (here && !gone) cand |= Mask(1) << t;
+            // (no short-circuit: the test is cheap, and a branch here keeps one
+            // lane mask per position alive until the loop ends)
+            const bool gone = (lo >= 0) & (hi >= 0) & dominated(lo, Ylo, p, Yp, hi, Yhi);
+            cand |= (Mask)(here & !gone) << t;
         };
         auto height = [&](Val v, int p) { return fval(v) + s2l * (double)p * (double)p; };
         if constexpr (kKeepF) {
@@ -609,11 +609,13 @@ __device__ void resolve_line(View& view, SlotArrays<Val, K>& sa, const Val* mych
             // the dominance test runs only on those that pass -- one at a time
             // unless some lane of the wave has many of them; then every
             // position's height comes from the registers of phase 1.
+            // (F is +inf exactly where a position has no background; U itself
+            // may be +inf, so the test runs against the largest finite value)
+            const double Ufin = U < __DBL_MAX__ ? U : __DBL_MAX__;
             Mask pass = 0;
 #pragma unroll
             for (int t = 0; t < K; ++t)
-                if (Fr[t] <= U) pass |= Mask(1) << t;
-            pass &= vmask;
+                if (Fr[t] <= Ufin) pass |= Mask(1) << t;
             if (__any(__builtin_popcount(pass) > kSparseCand)) {
 #pragma unroll
                 for (int t = 0; t < K; ++t) {
@@ -747,6 +749,7 @@ __device__ void resolve_line(View& view, SlotArrays<Val, K>& sa, const Val* mych
 
 struct Geo2D {          // rows of an H x W image; value = axis-0 coordinate
     using Val = uint16_t;
+    static constexpr Val kNoneVal = kNone16;
     // Rows of an image follow the nearest background of one column each, so
     // their F varies freely along the row and many chunks see more reaching
     // members than the per-chunk lists hold: whole lines in rounds are faster.
@@ -774,6 +777,7 @@ struct Geo2D {          // rows of an H x W image; value = axis-0 coordinate
 struct Geo3D {          // rows along W of B x D x H x W volumes; value = packed (axis0, axis1)
     static constexpr bool kPerChunk = true;
     using Val = uint32_t;
+    static constexpr Val kNoneVal = kNone32;
     double s2a, s2b, s2l;
     int D, H, W;
     bool dh24;          // D * H < 2^24: the flat index needs only 24-bit products
@@ -860,6 +864,12 @@ __global__ __launch_bounds__(1024) void k_envelope_rows(const typename Geo::Val*
     const bool active = line < nlines;
 
     if (active) load_row_line<Val, K, VW>(in + line * (int64_t)L, L, g, Gp, sa.val + __umul24(slot0, CS));
+    {   // positions past the end of the line (all of an inactive one) hold
+        // "no background", so that validity alone marks the chunk's positions
+        const int nv = active ? L - g * K : 0;
+        Val* mc = sa.val + __umul24(tid, CS);
+        for (int t = nv < 0 ? 0 : nv; t < K; ++t) mc[t] = Geo::kNoneVal;
+    }
     __syncthreads();
 
     const typename Geo::Line gl = geo.line(active ? line : 0);
@@ -1376,6 +1386,9 @@ __global__ __launch_bounds__(1024) void k_envelope_cols(const uint16_t* __restri
             const uint32_t hi = t + 1 < n ? buf[t + 1] : kNone16;
             *reinterpret_cast<uint32_t*>(mine + t) = lo | (hi << 16);
         }
+    } else {   // no rows: every position holds "no background"
+#pragma unroll
+        for (int t = 0; t < K; t += 2) *reinterpret_cast<uint32_t*>(mine + t) = kNone16 | (kNone16 << 16);
     }
 
     auto fof = [&](uint16_t v) {
