@@ -182,6 +182,41 @@ def test_edge_cases_3d(torch_dev):
     check(torch_dev, mask)
 
 
+def test_long_equal_value_envelopes(torch_dev):
+    """Lines whose envelope holds every candidate (all F equal) far from the
+    background: a full background column or plane makes every axis-1 or
+    axis-2 line an envelope of equal parabolas; also mixed with sparse noise,
+    and the longest lines along axes 0 and 1 in one volume."""
+    rng = np.random.default_rng([42, 3005])
+    # full background column x = 0 in every plane: F = x^2 along every axis-1 line
+    mask = np.ones((1, 6, 300, 200), np.uint8)
+    mask[:, :, :, 0] = 0
+    _say("3d column x=0 (1,6,300,200)")
+    check(torch_dev, mask)
+    # full background plane y = 0: F = y^2 along every axis-0 line
+    mask = np.ones((2, 400, 90, 64), np.uint8)
+    mask[:, :, 0, :] = 0
+    _say("3d plane y=0 (2,400,90,64)")
+    check(torch_dev, mask)
+    check(torch_dev, mask, (2.5, 1.0, 1.0))
+    # the same with sparse noise: some lanes of a wave overflow, others not
+    mask = (rng.random((1, 300, 70, 130)) >= 0.0005).astype(np.uint8)
+    mask[:, :, 0, :] = 0
+    mask[:, :, :, 0] = 0
+    _say("3d mixed (1,300,70,130)")
+    check(torch_dev, mask)
+    check(torch_dev, mask, (2.5, 1.0, 1.0))
+    # long lines along axis 0 (2048) and the longest along axis 1 (1024)
+    mask = (rng.random((1, 2048, 3, 64)) >= 0.001).astype(np.uint8)
+    mask[0, 0, 0, 0] = 0
+    _say("3d D=2048")
+    check(torch_dev, mask)
+    mask = (rng.random((1, 2, 1024, 64)) >= 0.001).astype(np.uint8)
+    mask[0, 1, 7, 3] = 0
+    _say("3d H=1024")
+    check(torch_dev, mask)
+
+
 def test_many_short_lines(torch_dev):
     """More than 65536 rows of at most 1024 positions in a volume batch: the
     chunk-per-lane row kernel (fewer lines take the one-wave-per-line kernel,
