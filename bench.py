@@ -61,6 +61,8 @@ WORKLOADS = {
           "isotropic; output float32 dist",
     "c5": "3D 512^3 uint8, background Bernoulli(1e-3) + 64-voxel background slab, "
           "sampling (2.5,1,1); outputs float32 dist + int32 index",
+    "b2d": "batched 2D: 32 images of 1024x1024 uint8, background i.i.d. Bernoulli(0.01) "
+           "per image, isotropic; outputs sqdist + dist + index (flat per image)",
 }
 OUTPUTS = {
     "c1": ("sqdist", "dist", "indices"),
@@ -69,6 +71,7 @@ OUTPUTS = {
     "c3": ("sqdist", "dist"),
     "c4": ("dist",),
     "c5": ("dist", "indices"),
+    "b2d": ("sqdist", "dist", "indices"),
 }
 
 
@@ -81,6 +84,8 @@ def algorithmic_bytes(kernel: str, shape, n_out: int) -> int:
     n = int(np.prod(shape))
     if len(shape) == 2:
         n0, M, B = shape[0], shape[1], 1
+    elif len(shape) == 3:             # a batch of 2-D images
+        B, n0, M = shape
     else:
         B, n0, M = shape[0], shape[1], shape[2] * shape[3]
     nseg = (n0 + 63) // 64
@@ -236,7 +241,7 @@ def cpu_baseline(name, mask, sampling, budget_s=15.0):
                 if dt >= budget_s / 4 or take == vols:
                     break
                 take = min(vols, int(take * max(2.0, budget_s / max(dt, 1e-3) * 0.8)))
-            desc = f"oracle on {take} of {vols} volumes of {mask.shape[1:]}"
+            desc = f"oracle on {take} of {vols} images of {mask.shape[1:]}"
         else:
             take = max(1, min(D, 8))
             while True:
@@ -281,7 +286,7 @@ def main(argv=None):
         return probe_copy()
 
     import torch
-    from exact_euclidean_distance_amd import alloc_workspace, edt2d, edt3d, workspace_size_2d, \
+    from exact_euclidean_distance_amd import alloc_workspace, edt2d, edt3d, workspace_size_2d_batched, \
         workspace_size_3d
     from workloads import make_config
 
@@ -299,8 +304,8 @@ def main(argv=None):
     sq = torch.empty(shape, dtype=torch.int32, device=dev) if "sqdist" in want else None
     ds = torch.empty(shape, dtype=torch.float32, device=dev) if "dist" in want else None
     ix = torch.empty(shape, dtype=torch.int32, device=dev) if "indices" in want else None
-    if len(shape) == 2:
-        ws = alloc_workspace(workspace_size_2d(*shape), dev)
+    if len(shape) in (2, 3):
+        ws = alloc_workspace(workspace_size_2d_batched(*((1,) + shape)[-3:]), dev)
         fn = edt2d
     else:
         ws = alloc_workspace(workspace_size_3d(*shape), dev)
@@ -356,7 +361,7 @@ def main(argv=None):
         compare(mask_np, sampling, ref,
                 None if sq is None else sq.cpu().numpy(),
                 None if ds is None else ds.cpu().numpy(),
-                None if ix is None else ix.cpu().numpy(), batch=(len(shape) == 4))
+                None if ix is None else ix.cpu().numpy(), batch=(len(shape) > 2))
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -4,18 +4,22 @@ The computation lives in ``libedt_mi355x.so`` (hand-written HIP kernels behind
 the C ABI of ``include/edt.h``); this package only marshals arguments.
 
     from exact_euclidean_distance_amd import edt2d, edt3d
-    r = edt2d(mask_u8_cuda, return_sqdist=True, return_indices=True)
+    r = edt2d(mask_u8_cuda, return_sqdist=True, return_indices=True)   # (H, W) or (B, H, W)
 """
 
 from ._lib import EDTError, LIB_PATH  # noqa: F401
 from .api import (  # noqa: F401
     EDTResult,
     alloc_workspace,
+    edt1d,
     edt2d,
     edt3d,
+    unravel_indices,
     workspace_size_2d,
+    workspace_size_2d_batched,
     workspace_size_3d,
 )
 
-__all__ = ["edt2d", "edt3d", "EDTResult", "EDTError", "workspace_size_2d",
-           "workspace_size_3d", "alloc_workspace"]
+__all__ = ["edt1d", "edt2d", "edt3d", "unravel_indices", "EDTResult", "EDTError",
+           "workspace_size_2d", "workspace_size_2d_batched", "workspace_size_3d",
+           "alloc_workspace"]

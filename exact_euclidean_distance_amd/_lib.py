@@ -23,6 +23,8 @@ STATUS = {
 EXPORTS = (
     "edt2d_workspace_size", "edt2d_u8", "edt3d_workspace_size", "edt3d_u8_batched",
     "edt2d_u8_timed", "edt3d_u8_batched_timed", "edt_status_string", "edt_version",
+    "edt2d_batched_workspace_size", "edt2d_u8_batched", "edt2d_u8_batched_timed",
+    "edt1d_workspace_size", "edt1d_u8_batched", "edt_unravel_indices",
 )
 
 _lib = None
@@ -62,6 +64,20 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.edt3d_u8_batched_timed.argtypes = [vp, i32, i32, i32, i32, fp, vp, vp, vp, vp, sz, vp,
                                            fp, ctypes.POINTER(ctypes.c_char_p), i32,
                                            ctypes.POINTER(i32)]
+    ip = ctypes.POINTER(i32)
+    lib.edt2d_batched_workspace_size.restype = sz
+    lib.edt2d_batched_workspace_size.argtypes = [i32, i32, i32]
+    lib.edt2d_u8_batched.restype = ctypes.c_int
+    lib.edt2d_u8_batched.argtypes = [vp, i32, i32, i32, fp, vp, vp, vp, vp, sz, vp]
+    lib.edt2d_u8_batched_timed.restype = ctypes.c_int
+    lib.edt2d_u8_batched_timed.argtypes = [vp, i32, i32, i32, fp, vp, vp, vp, vp, sz, vp,
+                                           fp, ctypes.POINTER(ctypes.c_char_p), i32, ip]
+    lib.edt1d_workspace_size.restype = sz
+    lib.edt1d_workspace_size.argtypes = [i32, i32]
+    lib.edt1d_u8_batched.restype = ctypes.c_int
+    lib.edt1d_u8_batched.argtypes = [vp, i32, i32, fp, vp, vp, vp, vp, sz, vp]
+    lib.edt_unravel_indices.restype = ctypes.c_int
+    lib.edt_unravel_indices.argtypes = [vp, i32, i32, ip, vp, vp]
     lib.edt_status_string.restype = ctypes.c_char_p
     lib.edt_status_string.argtypes = [ctypes.c_int]
     lib.edt_version.restype = ctypes.c_char_p

@@ -79,37 +79,107 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def workspace_size_2d_batched(B: int, H: int, W: int) -> int:
+    return int(_lib.load().edt2d_batched_workspace_size(B, H, W))
+
+
+def _timed_call(fn, name, args):
+    ms = (ctypes.c_float * 8)()
+    names = (ctypes.c_char_p * 8)()
+    cnt = ctypes.c_int32(0)
+    st = fn(*args, ms, names, 8, ctypes.byref(cnt))
+    if st != 0:
+        raise EDTError(st, name)
+    return [(names[i].decode(), ms[i]) for i in range(cnt.value)]
+
+
 def edt2d(mask: torch.Tensor, sampling=None, *, return_distances: bool = True,
           return_sqdist: bool = False, return_indices: bool = False,
           dist=None, sqdist=None, indices=None, workspace=None, stream=None,
           timed: bool = False):
-    """Exact EDT of one (H, W) uint8 mask.  Returns :class:`EDTResult` (and the
-    per-kernel times in ms when ``timed``)."""
-    _check_mask(mask, (2,))
-    H, W = mask.shape
+    """Exact EDT of one (H, W) uint8 mask, or of a batch (B, H, W) of
+    independent images (indices flat within each image).  Returns
+    :class:`EDTResult` (and the per-kernel times in ms when ``timed``)."""
+    _check_mask(mask, (2, 3))
+    m3 = mask if mask.dim() == 3 else mask.unsqueeze(0)
+    B, H, W = m3.shape
+    shape = tuple(mask.shape)
     dev = mask.device
-    sq = _out(sqdist, (H, W), torch.int32, dev, return_sqdist)
-    ds = _out(dist, (H, W), torch.float32, dev, return_distances)
-    ix = _out(indices, (H, W), torch.int32, dev, return_indices)
+    sq = _out(sqdist, shape, torch.int32, dev, return_sqdist)
+    ds = _out(dist, shape, torch.float32, dev, return_distances)
+    ix = _out(indices, shape, torch.int32, dev, return_indices)
     lib = _lib.load()
-    need = int(lib.edt2d_workspace_size(H, W))
+    need = int(lib.edt2d_batched_workspace_size(B, H, W))
     if workspace is None:
         workspace = alloc_workspace(need, dev)
     samp = _sampling(sampling, 2)
-    args = [_ptr(mask), H, W, samp, _ptr(sq), _ptr(ds), _ptr(ix), _ptr(workspace),
-            workspace.numel() * workspace.element_size(), _stream(stream)]
+    wsb = workspace.numel() * workspace.element_size()
+    if mask.dim() == 2:
+        args = [_ptr(mask), H, W, samp, _ptr(sq), _ptr(ds), _ptr(ix), _ptr(workspace), wsb,
+                _stream(stream)]
+        fn, tfn, name = lib.edt2d_u8, lib.edt2d_u8_timed, "edt2d_u8"
+    else:
+        args = [_ptr(mask), B, H, W, samp, _ptr(sq), _ptr(ds), _ptr(ix), _ptr(workspace), wsb,
+                _stream(stream)]
+        fn, tfn, name = lib.edt2d_u8_batched, lib.edt2d_u8_batched_timed, "edt2d_u8_batched"
     if not timed:
-        st = lib.edt2d_u8(*args)
+        st = fn(*args)
         if st != 0:
-            raise EDTError(st, "edt2d_u8")
+            raise EDTError(st, name)
         return EDTResult(sq, ds, ix)
-    ms = (ctypes.c_float * 8)()
-    names = (ctypes.c_char_p * 8)()
-    cnt = ctypes.c_int32(0)
-    st = lib.edt2d_u8_timed(*args, ms, names, 8, ctypes.byref(cnt))
+    return EDTResult(sq, ds, ix), _timed_call(tfn, name + "_timed", args)
+
+
+def edt1d(mask: torch.Tensor, sampling=None, *, return_distances: bool = True,
+          return_sqdist: bool = False, return_indices: bool = False,
+          dist=None, sqdist=None, indices=None, workspace=None, stream=None):
+    """Exact distance transform of one (N,) uint8 line or a batch (B, N) of
+    independent lines; indices are positions within each line (-1: the
+    virtual element of a line without background)."""
+    _check_mask(mask, (1, 2))
+    m2 = mask if mask.dim() == 2 else mask.unsqueeze(0)
+    B, N = m2.shape
+    shape = tuple(mask.shape)
+    dev = mask.device
+    sq = _out(sqdist, shape, torch.int32, dev, return_sqdist)
+    ds = _out(dist, shape, torch.float32, dev, return_distances)
+    ix = _out(indices, shape, torch.int32, dev, return_indices)
+    lib = _lib.load()
+    need = int(lib.edt1d_workspace_size(B, N))
+    if workspace is None:
+        workspace = alloc_workspace(need, dev)
+    samp = _sampling(sampling, 1)
+    st = lib.edt1d_u8_batched(_ptr(m2), B, N, samp, _ptr(sq), _ptr(ds), _ptr(ix), _ptr(workspace),
+                              workspace.numel() * workspace.element_size(), _stream(stream))
     if st != 0:
-        raise EDTError(st, "edt2d_u8_timed")
-    return EDTResult(sq, ds, ix), [(names[i].decode(), ms[i]) for i in range(cnt.value)]
+        raise EDTError(st, "edt1d_u8_batched")
+    return EDTResult(sq, ds, ix)
+
+
+def unravel_indices(indices: torch.Tensor, image_shape: Sequence[int], *, out=None, stream=None):
+    """Per-axis coordinates of flat indices returned by the transforms:
+    (*batch, *image_shape) int32 -> (*batch, ndim, *image_shape), the layout of
+    SciPy's feature transform (virtual index -> (-1, 0, ...))."""
+    if not isinstance(indices, torch.Tensor) or indices.dtype != torch.int32:
+        raise TypeError("indices must be an int32 torch.Tensor")
+    if not indices.is_cuda or not indices.is_contiguous():
+        raise ValueError("indices must be a contiguous device tensor")
+    img = tuple(int(s) for s in image_shape)
+    nd = len(img)
+    if tuple(indices.shape[indices.dim() - nd:]) != img:
+        raise ValueError(f"indices must end with the image shape {img}")
+    batch = tuple(indices.shape[:indices.dim() - nd])
+    images = 1
+    for b in batch:
+        images *= int(b)
+    shape = batch + (nd,) + img
+    coords = _out(out, shape, torch.int32, indices.device, True)
+    shp = (ctypes.c_int32 * nd)(*img)
+    st = _lib.load().edt_unravel_indices(_ptr(indices), images, nd, shp, _ptr(coords),
+                                         _stream(stream))
+    if st != 0:
+        raise EDTError(st, "edt_unravel_indices")
+    return coords
 
 
 def edt3d(mask: torch.Tensor, sampling=None, *, return_distances: bool = True,
@@ -138,10 +208,5 @@ def edt3d(mask: torch.Tensor, sampling=None, *, return_distances: bool = True,
         if st != 0:
             raise EDTError(st, "edt3d_u8_batched")
         return EDTResult(sq, ds, ix)
-    ms = (ctypes.c_float * 8)()
-    names = (ctypes.c_char_p * 8)()
-    cnt = ctypes.c_int32(0)
-    st = lib.edt3d_u8_batched_timed(*args, ms, names, 8, ctypes.byref(cnt))
-    if st != 0:
-        raise EDTError(st, "edt3d_u8_batched_timed")
-    return EDTResult(sq, ds, ix), [(names[i].decode(), ms[i]) for i in range(cnt.value)]
+    return EDTResult(sq, ds, ix), _timed_call(lib.edt3d_u8_batched_timed, "edt3d_u8_batched_timed",
+                                              args)

@@ -4,7 +4,8 @@
 // argument handling in one validation layer); every check runs before the
 // first HIP call, so a rejected call touches no buffer.  The planner carves
 // the caller's workspace and enqueues the passes on the caller's stream:
-//   2-D:  axis-0 scan (3 kernels) -> row envelope + epilogue
+//   2-D:  axis-0 scan (3 kernels) -> row envelope + epilogue (B images at once;
+//         a 1-D line of n elements is an n x 1 image)
 //   3-D:  axis-0 scan (3 kernels) -> axis-1 envelope -> axis-2 envelope + epilogue
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -28,8 +29,8 @@ struct Layout {
     size_t c0 = 0, c01 = 0, first = 0, last = 0, bits = 0, total = 0;
 };
 
-bool shape2d_ok(int32_t H, int32_t W) {
-    if (H < 1 || W < 1 || H > kMaxExtent || W > kMaxExtent) return false;
+bool shape2d_ok(int32_t B, int32_t H, int32_t W) {
+    if (B < 1 || H < 1 || W < 1 || B > kMaxExtent || H > kMaxExtent || W > kMaxExtent) return false;
     if (W > kMaxW2D) return false;
     if ((int64_t)H * W > INT32_MAX) return false;
     return edt::rows_lds_bytes(W, 2) != 0;
@@ -43,10 +44,10 @@ bool shape3d_ok(int32_t B, int32_t D, int32_t H, int32_t W) {
     return edt::rows_lds_bytes(W, 4) != 0;
 }
 
-Layout layout2d(int32_t H, int32_t W) {
+Layout layout2d(int32_t B, int32_t H, int32_t W) {
     Layout L;
-    const size_t n = (size_t)H * W;
-    const size_t nseg = (size_t)(H + edt::kSegRows - 1) / edt::kSegRows;
+    const size_t n = (size_t)B * H * W;
+    const size_t nseg = (size_t)B * ((H + edt::kSegRows - 1) / edt::kSegRows);
     L.c0 = 0;
     L.first = round_up(n * 2);
     L.last = L.first + round_up(nseg * W * 2);
@@ -108,19 +109,19 @@ edt_status check_buffers(const uint8_t* mask, size_t n, int32_t* sqdist, float* 
     return EDT_OK;
 }
 
-edt_status run2d(const uint8_t* mask, int32_t H, int32_t W, const float* sampling,
+edt_status run2d(const uint8_t* mask, int32_t B, int32_t H, int32_t W, const float* sampling,
                  int32_t* sqdist, float* dist, int32_t* indices, void* ws, size_t ws_bytes,
                  hipStream_t stream, edt::KernelTimer* tm) {
-    if (H < 1 || W < 1) return EDT_ERR_INVALID_ARGUMENT;
-    if (!shape2d_ok(H, W)) return EDT_ERR_UNSUPPORTED_SHAPE;
+    if (B < 1 || H < 1 || W < 1) return EDT_ERR_INVALID_ARGUMENT;
+    if (!shape2d_ok(B, H, W)) return EDT_ERR_UNSUPPORTED_SHAPE;
     double s2[2];
     bool unit;
     edt_status st = read_sampling(sampling, 2, s2, &unit);
     if (st != EDT_OK) return st;
     if (sqdist && !unit) return EDT_ERR_INVALID_ARGUMENT;
     if (sqdist && (double)H * H + (double)W * W > (double)INT32_MAX) return EDT_ERR_UNSUPPORTED_SHAPE;
-    const Layout L = layout2d(H, W);
-    st = check_buffers(mask, (size_t)H * W, sqdist, dist, indices, ws, ws_bytes, L.total);
+    const Layout L = layout2d(B, H, W);
+    st = check_buffers(mask, (size_t)B * H * W, sqdist, dist, indices, ws, ws_bytes, L.total);
     if (st != EDT_OK) return st;
 
     char* base = static_cast<char*>(ws);
@@ -128,8 +129,8 @@ edt_status run2d(const uint8_t* mask, int32_t H, int32_t W, const float* samplin
     uint16_t* first = reinterpret_cast<uint16_t*>(base + L.first);
     uint16_t* last = reinterpret_cast<uint16_t*>(base + L.last);
     uint64_t* bits = reinterpret_cast<uint64_t*>(base + L.bits);
-    if (edt::launch_axis0(mask, 1, H, W, first, last, bits, c0, stream, tm) != hipSuccess) return EDT_ERR_HIP;
-    if (edt::launch_rows_2d(c0, H, W, s2[0], s2[1], sqdist, dist, indices, stream, tm) != hipSuccess)
+    if (edt::launch_axis0(mask, B, H, W, first, last, bits, c0, stream, tm) != hipSuccess) return EDT_ERR_HIP;
+    if (edt::launch_rows_2d(c0, B, H, W, s2[0], s2[1], sqdist, dist, indices, stream, tm) != hipSuccess)
         return EDT_ERR_HIP;
     return EDT_OK;
 }
@@ -192,8 +193,16 @@ edt_status finish_timed(edt_status st, edt::KernelTimer& tm, hipStream_t stream,
 extern "C" {
 
 size_t edt2d_workspace_size(int32_t H, int32_t W) {
-    if (!shape2d_ok(H, W)) return 0;
-    return layout2d(H, W).total;
+    return edt2d_batched_workspace_size(1, H, W);
+}
+
+size_t edt2d_batched_workspace_size(int32_t B, int32_t H, int32_t W) {
+    if (!shape2d_ok(B, H, W)) return 0;
+    return layout2d(B, H, W).total;
+}
+
+size_t edt1d_workspace_size(int32_t B, int32_t N) {
+    return edt2d_batched_workspace_size(B, N, 1);
 }
 
 size_t edt3d_workspace_size(int32_t B, int32_t D, int32_t H, int32_t W) {
@@ -204,8 +213,45 @@ size_t edt3d_workspace_size(int32_t B, int32_t D, int32_t H, int32_t W) {
 edt_status edt2d_u8(const uint8_t* mask, int32_t H, int32_t W, const float* sampling,
                     int32_t* sqdist, float* dist, int32_t* indices, void* workspace,
                     size_t workspace_bytes, hipStream_t stream) {
-    return run2d(mask, H, W, sampling, sqdist, dist, indices, workspace, workspace_bytes, stream,
+    return run2d(mask, 1, H, W, sampling, sqdist, dist, indices, workspace, workspace_bytes, stream,
                  nullptr);
+}
+
+edt_status edt2d_u8_batched(const uint8_t* mask, int32_t B, int32_t H, int32_t W,
+                            const float* sampling, int32_t* sqdist, float* dist, int32_t* indices,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    return run2d(mask, B, H, W, sampling, sqdist, dist, indices, workspace, workspace_bytes, stream,
+                 nullptr);
+}
+
+edt_status edt1d_u8_batched(const uint8_t* mask, int32_t B, int32_t N, const float* sampling,
+                            int32_t* sqdist, float* dist, int32_t* indices, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
+    // a line of N elements is an N x 1 image: the axis-0 pass alone decides,
+    // and the virtual element (-1, 0) gives (p + 1)^2 and index -1
+    const float s2d[2] = {sampling ? sampling[0] : 1.0f, 1.0f};
+    return run2d(mask, B, N, 1, s2d, sqdist, dist, indices, workspace, workspace_bytes, stream,
+                 nullptr);
+}
+
+edt_status edt_unravel_indices(const int32_t* indices, int32_t images, int32_t ndim,
+                               const int32_t* shape, int32_t* coords, hipStream_t stream) {
+    if (!indices || !coords || !shape || images < 1 || ndim < 1 || ndim > 3)
+        return EDT_ERR_INVALID_ARGUMENT;
+    if (((uintptr_t)indices & 3) || ((uintptr_t)coords & 3)) return EDT_ERR_INVALID_ARGUMENT;
+    int64_t per = 1;
+    for (int k = 0; k < ndim; ++k) {
+        if (shape[k] < 1 || shape[k] > kMaxExtent) return EDT_ERR_INVALID_ARGUMENT;
+        per *= shape[k];
+    }
+    if (per > INT32_MAX) return EDT_ERR_UNSUPPORTED_SHAPE;
+    const size_t nin = (size_t)images * (size_t)per * 4;
+    if (overlap(indices, nin, coords, nin * (size_t)ndim)) return EDT_ERR_INVALID_ARGUMENT;
+    const int n1 = ndim >= 2 ? shape[1] : 1;
+    const int n2 = ndim >= 3 ? shape[2] : 1;
+    if (edt::launch_unravel(indices, images, per, ndim, n1, n2, coords, stream) != hipSuccess)
+        return EDT_ERR_HIP;
+    return EDT_OK;
 }
 
 edt_status edt3d_u8_batched(const uint8_t* mask, int32_t B, int32_t D, int32_t H, int32_t W,
@@ -222,8 +268,21 @@ edt_status edt2d_u8_timed(const uint8_t* mask, int32_t H, int32_t W, const float
     if (!kernel_ms || capacity < 1) return EDT_ERR_INVALID_ARGUMENT;
     edt::KernelTimer tm;
     tm.capacity = capacity;
-    edt_status st = run2d(mask, H, W, sampling, sqdist, dist, indices, workspace, workspace_bytes,
+    edt_status st = run2d(mask, 1, H, W, sampling, sqdist, dist, indices, workspace, workspace_bytes,
                           stream, &tm);
+    return finish_timed(st, tm, stream, kernel_ms, kernel_names, count);
+}
+
+edt_status edt2d_u8_batched_timed(const uint8_t* mask, int32_t B, int32_t H, int32_t W,
+                                  const float* sampling, int32_t* sqdist, float* dist,
+                                  int32_t* indices, void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream, float* kernel_ms, const char** kernel_names,
+                                  int32_t capacity, int32_t* count) {
+    if (!kernel_ms || capacity < 1) return EDT_ERR_INVALID_ARGUMENT;
+    edt::KernelTimer tm;
+    tm.capacity = capacity;
+    edt_status st = run2d(mask, B, H, W, sampling, sqdist, dist, indices, workspace,
+                          workspace_bytes, stream, &tm);
     return finish_timed(st, tm, stream, kernel_ms, kernel_names, count);
 }
 

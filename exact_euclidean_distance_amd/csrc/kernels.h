@@ -32,8 +32,8 @@ hipError_t launch_axis0(const uint8_t* mask, int B, int n0, int64_t M,
                         uint16_t* first, uint16_t* last, uint64_t* bits, uint16_t* c0,
                         hipStream_t s, KernelTimer* tm);
 
-// Envelope pass along the last axis of a 2-D image (lines = rows of length W).
-hipError_t launch_rows_2d(const uint16_t* c0, int H, int W, double s2_0, double s2_1,
+// Envelope pass along the last axis of B 2-D images (lines = rows of length W).
+hipError_t launch_rows_2d(const uint16_t* c0, int B, int H, int W, double s2_0, double s2_1,
                           int32_t* sqdist, float* dist, int32_t* indices,
                           hipStream_t s, KernelTimer* tm);
 
@@ -48,6 +48,12 @@ hipError_t launch_rows_3d(const uint32_t* c01, int B, int D, int H, int W,
                           double s2_0, double s2_1, double s2_2,
                           int32_t* sqdist, float* dist, int32_t* indices,
                           hipStream_t s, KernelTimer* tm);
+
+// Flat per-image indices of `images` images of per_image elements -> per-axis
+// coordinates, image-major: coords[b][k][i] (ndim 1..3; n1, n2: the extents of
+// axes 1 and 2 of an image, unused beyond ndim).
+hipError_t launch_unravel(const int32_t* flat, int64_t images, int64_t per_image, int ndim, int n1,
+                          int n2, int32_t* coords, hipStream_t s);
 
 // Dynamic LDS each envelope launch needs (0 if the line is too long).
 size_t rows_lds_bytes(int L, int value_bytes);

@@ -747,7 +747,7 @@ __device__ void resolve_line(View& view, SlotArrays<Val, K>& sa, const Val* mych
 // over one cache line per lane).
 // --------------------------------------------------------------------------
 
-struct Geo2D {          // rows of an H x W image; value = axis-0 coordinate
+struct Geo2D {          // rows of B images of H x W; value = axis-0 coordinate
     using Val = uint16_t;
     static constexpr Val kNoneVal = kNone16;
     // Rows of an image follow the nearest background of one column each, so
@@ -756,8 +756,11 @@ struct Geo2D {          // rows of an H x W image; value = axis-0 coordinate
     static constexpr bool kPerChunk = false;
     double s2a, s2l;    // squared spacing of axis 0 and along the row
     int W;
+    int H;              // rows per image: line ln is row ln % H of image ln / H
     struct Line { int row; };
-    __device__ Line line(int64_t ln) const { return Line{(int)ln}; }
+    __device__ Line line(int64_t ln) const {
+        return Line{ln < 0x100000000ll ? (int)((unsigned)ln % (unsigned)H) : (int)(ln % H)};
+    }
     __device__ static bool valid(uint16_t v) { return v != kNone16; }
     __device__ double f(const Line& l, uint16_t v) const {
         const double t = (double)(l.row - (int)v);
@@ -1292,13 +1295,59 @@ static hipError_t launch_rows_any(const typename Geo::Val* in, int L, int64_t nl
     return launch_rows_t<Geo, K, 1>(in, L, nlines, p, geo, sqdist, dist, indices, s, tm, kname);
 }
 
-hipError_t launch_rows_2d(const uint16_t* c0, int H, int W, double s2_0, double s2_1,
+hipError_t launch_rows_2d(const uint16_t* c0, int B, int H, int W, double s2_0, double s2_1,
                           int32_t* sqdist, float* dist, int32_t* indices, hipStream_t s,
                           KernelTimer* tm) {
-    Geo2D geo{s2_0, s2_1, W};
+    Geo2D geo{s2_0, s2_1, W, H};
+    const int64_t nlines = (int64_t)B * H;
     hipError_t e = hipSuccess;
-    if (launch_rows_wave<Geo2D>(c0, W, H, geo, sqdist, dist, indices, s, tm, "envelope_rows_2d", &e)) return e;
-    return launch_rows_any<Geo2D, 32>(c0, W, H, geo, sqdist, dist, indices, s, tm, "envelope_rows_2d");
+    if (launch_rows_wave<Geo2D>(c0, W, nlines, geo, sqdist, dist, indices, s, tm, "envelope_rows_2d", &e))
+        return e;
+    return launch_rows_any<Geo2D, 32>(c0, W, nlines, geo, sqdist, dist, indices, s, tm, "envelope_rows_2d");
+}
+
+// --------------------------------------------------------------------------
+// Flat indices -> per-axis coordinates (the layout SciPy's feature transform
+// returns: per image an array of ndim planes, plane k holding the axis-k
+// coordinate of every element's nearest background element).  Division
+// rounds toward minus infinity, so the virtual element's negative flat index
+// -(n1 * ... * n_{d-1}) becomes (-1, 0, ..., 0).
+// --------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_unravel(const int32_t* __restrict__ flat, int64_t total,
+                                                 int64_t per_image, int ndim, int n1, int n2,
+                                                 int32_t* __restrict__ coords) {
+    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (e >= total) return;
+    const int64_t b = e / per_image;
+    const int64_t i = e - b * per_image;
+    int f = flat[e];
+    int c[3] = {0, 0, 0};
+    auto divmod = [](int x, int d, int& q, int& r) {   // floor division, 0 <= r < d
+        q = x / d;
+        r = x - q * d;
+        if (r < 0) { r += d; --q; }
+    };
+    if (ndim == 1) {
+        c[0] = f;
+    } else if (ndim == 2) {
+        divmod(f, n1, c[0], c[1]);
+    } else {
+        int t;
+        divmod(f, n2, t, c[2]);
+        divmod(t, n1, c[0], c[1]);
+    }
+    int32_t* dst = coords + b * (int64_t)ndim * per_image + i;
+    for (int k = 0; k < ndim; ++k) dst[(int64_t)k * per_image] = c[k];
+}
+
+hipError_t launch_unravel(const int32_t* flat, int64_t images, int64_t per_image, int ndim, int n1,
+                          int n2, int32_t* coords, hipStream_t s) {
+    const int64_t total = images * per_image;
+    if (total == 0) return hipSuccess;
+    const unsigned blocks = (unsigned)((total + 255) / 256);
+    hipLaunchKernelGGL(k_unravel, dim3(blocks), dim3(256), 0, s, flat, total, per_image, ndim, n1, n2,
+                       coords);
+    return hipGetLastError();
 }
 
 hipError_t launch_rows_3d(const uint32_t* c01, int B, int D, int H, int W, double s2_0,

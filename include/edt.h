@@ -86,6 +86,45 @@ edt_status edt2d_u8(const uint8_t* mask, int32_t H, int32_t W,
                     int32_t* sqdist, float* dist, int32_t* indices,
                     void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Bytes of workspace edt2d_u8_batched needs for B images of H x W (0 if the
+   shape is outside the limits; B <= 65535). */
+size_t edt2d_batched_workspace_size(int32_t B, int32_t H, int32_t W);
+
+/* 2-D transform of B independent H x W images stored back to back
+   ([B][H][W]): the per-image result of edt2d_u8 for each, in one set of
+   launches (the batched tensors of TorchMorph's transforms).  indices are flat
+   within each image (r*W + c); an image without background gets the virtual
+   element on its own, whatever the other images hold. */
+edt_status edt2d_u8_batched(const uint8_t* mask, int32_t B, int32_t H, int32_t W,
+                            const float* sampling,
+                            int32_t* sqdist, float* dist, int32_t* indices,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace edt1d_u8_batched needs for B lines of N elements. */
+size_t edt1d_workspace_size(int32_t B, int32_t N);
+
+/* 1-D transform of B independent lines of N elements ([B][N]): for each
+   element the distance along the line to the nearest background element of
+   its own line.  sampling is {s} or NULL.  indices are the position within the
+   line; a line without background gets the virtual element at -1, so
+   sqdist = s^2 (p + 1)^2 and index -1.  (Computed as B images of N x 1.) */
+edt_status edt1d_u8_batched(const uint8_t* mask, int32_t B, int32_t N,
+                            const float* sampling,
+                            int32_t* sqdist, float* dist, int32_t* indices,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Per-axis coordinates of flat indices, the layout SciPy's feature transform
+   returns (TorchMorph's `return_indices` follows SciPy's interface).
+   indices: device int32 [images][n] as returned by the transforms above for
+   images of shape shape[0..ndim) (ndim 1..3, n = product of the extents).
+   coords:  device int32 [images][ndim][n]: plane k of image b holds the axis-k
+   coordinate.  A virtual index -(shape[1] * ... ) becomes (-1, 0, ..., 0).
+   Both buffers are caller-owned, 4-byte aligned and must not overlap; shape
+   is a HOST pointer.  Asynchronous on `stream`; argument errors return before
+   any HIP call. */
+edt_status edt_unravel_indices(const int32_t* indices, int32_t images, int32_t ndim,
+                               const int32_t* shape, int32_t* coords, hipStream_t stream);
+
 /* Bytes of workspace edt3d_u8_batched needs for B volumes of D x H x W. */
 size_t edt3d_workspace_size(int32_t B, int32_t D, int32_t H, int32_t W);
 
@@ -97,7 +136,7 @@ edt_status edt3d_u8_batched(const uint8_t* mask, int32_t B, int32_t D, int32_t H
                             int32_t* sqdist, float* dist, int32_t* indices,
                             void* workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* Same as edt2d_u8 / edt3d_u8_batched, for measurement: records a HIP event
+/* Same as edt2d_u8 / edt2d_u8_batched / edt3d_u8_batched, for measurement: records a HIP event
    pair around every kernel it enqueues, waits for the stream, and returns each
    kernel's duration in milliseconds (launch order) in kernel_ms[0..*count) and
    its name in kernel_names[] (static strings; may be NULL).  Fails with
@@ -109,6 +148,14 @@ edt_status edt2d_u8_timed(const uint8_t* mask, int32_t H, int32_t W,
                           void* workspace, size_t workspace_bytes, hipStream_t stream,
                           float* kernel_ms, const char** kernel_names,
                           int32_t capacity, int32_t* count);
+
+edt_status edt2d_u8_batched_timed(const uint8_t* mask, int32_t B, int32_t H, int32_t W,
+                                  const float* sampling,
+                                  int32_t* sqdist, float* dist, int32_t* indices,
+                                  void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream, float* kernel_ms,
+                                  const char** kernel_names, int32_t capacity,
+                                  int32_t* count);
 
 edt_status edt3d_u8_batched_timed(const uint8_t* mask, int32_t B, int32_t D, int32_t H,
                                   int32_t W, const float* sampling,

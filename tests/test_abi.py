@@ -119,3 +119,55 @@ def test_python_binding_refuses_cpu_tensors():
         edt2d(torch.zeros((4, 4), dtype=torch.uint8))
     with pytest.raises(TypeError):
         edt2d(torch.zeros((4, 4), dtype=torch.float32))
+
+
+def call2db(lib, mask=MASK, B=3, H=64, W=64, sampling=None, sq=SQ, dist=DIST, idx=IDX, ws=WS,
+            ws_bytes=BIG):
+    samp = None if sampling is None else (ctypes.c_float * 2)(*sampling)
+    return lib.edt2d_u8_batched(mask, B, H, W, samp, sq, dist, idx, ws, ws_bytes, None)
+
+
+def call1d(lib, mask=MASK, B=3, N=64, sampling=None, sq=SQ, dist=DIST, idx=IDX, ws=WS,
+           ws_bytes=BIG):
+    samp = None if sampling is None else (ctypes.c_float * 1)(*sampling)
+    return lib.edt1d_u8_batched(mask, B, N, samp, sq, dist, idx, ws, ws_bytes, None)
+
+
+def test_batched_2d_and_1d_argument_errors(lib):
+    assert lib.edt2d_batched_workspace_size(1, 64, 64) == lib.edt2d_workspace_size(64, 64)
+    assert lib.edt2d_batched_workspace_size(4, 64, 64) >= 4 * 64 * 64 * 2
+    assert lib.edt2d_batched_workspace_size(0, 64, 64) == 0
+    assert lib.edt2d_batched_workspace_size(70000, 8, 8) == 0
+    assert lib.edt1d_workspace_size(5, 100) == lib.edt2d_batched_workspace_size(5, 100, 1)
+    assert call2db(lib, mask=None) == INVALID
+    assert call2db(lib, B=0) == INVALID
+    assert call2db(lib, B=70000) == SHAPE
+    assert call2db(lib, W=40000) == SHAPE
+    assert call2db(lib, sampling=(2.0, 1.0)) == INVALID
+    assert call2db(lib, ws_bytes=lib.edt2d_batched_workspace_size(3, 64, 64) - 1) == SMALL
+    # the outputs of a batch span B images: an output starting inside the
+    # third image's part of another output aliases it
+    assert call2db(lib, dist=SQ + 2 * 64 * 64 * 4) == INVALID
+    assert call2db(lib, sq=None, dist=None, idx=None) == INVALID
+    assert call1d(lib, mask=None) == INVALID
+    assert call1d(lib, N=0) == INVALID
+    assert call1d(lib, N=70000) == SHAPE
+    assert call1d(lib, sampling=(2.0,)) == INVALID           # sqdist needs unit spacing
+    assert call1d(lib, sampling=(0.0,), sq=None) == INVALID
+    assert call1d(lib, ws_bytes=lib.edt1d_workspace_size(3, 64) - 1) == SMALL
+
+
+def test_unravel_argument_errors(lib):
+    shp = (ctypes.c_int32 * 3)(4, 5, 6)
+    assert lib.edt_unravel_indices(None, 1, 3, shp, DIST, None) == INVALID
+    assert lib.edt_unravel_indices(IDX, 1, 3, shp, None, None) == INVALID
+    assert lib.edt_unravel_indices(IDX, 1, 3, None, DIST, None) == INVALID
+    assert lib.edt_unravel_indices(IDX, 0, 3, shp, DIST, None) == INVALID
+    assert lib.edt_unravel_indices(IDX, 1, 4, shp, DIST, None) == INVALID
+    assert lib.edt_unravel_indices(IDX, 1, 0, shp, DIST, None) == INVALID
+    assert lib.edt_unravel_indices(IDX + 2, 1, 3, shp, DIST, None) == INVALID
+    assert lib.edt_unravel_indices(IDX, 1, 3, shp, IDX + 16, None) == INVALID   # overlap
+    bad = (ctypes.c_int32 * 3)(4, 0, 6)
+    assert lib.edt_unravel_indices(IDX, 1, 3, bad, DIST, None) == INVALID
+    big = (ctypes.c_int32 * 3)(65535, 65535, 2)
+    assert lib.edt_unravel_indices(IDX, 1, 3, big, DIST, None) == SHAPE

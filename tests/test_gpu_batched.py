@@ -1,0 +1,204 @@
+"""GPU parity of the batched 2-D and 1-D entry points and of the per-axis
+index layout, through the C ABI, against the CPU oracle run image by image.
+
+Same bar as the single-image tests: int32 squared distances bit-exact (unit
+spacing), float32 distances within 1e-6 / 1e-5 relative, every index attains
+the oracle's minimum exactly.  Outputs are poisoned before each call.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from gpu_check import compare
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch_dev():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    from exact_euclidean_distance_amd import _lib
+    _lib.load()
+    return torch, torch.device("cuda:0")
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def _poisoned(torch, dev, shape, want):
+    sq = torch.full(shape, -7, dtype=torch.int32, device=dev) if "sqdist" in want else None
+    ds = torch.full(shape, float("nan"), dtype=torch.float32, device=dev) if "dist" in want else None
+    ix = torch.full(shape, -7, dtype=torch.int32, device=dev) if "indices" in want else None
+    return sq, ds, ix
+
+
+def _np(t):
+    return None if t is None else t.cpu().numpy()
+
+
+def run_batched_2d(torch_dev, masks, sampling=None):
+    torch, dev = torch_dev
+    from exact_euclidean_distance_amd import edt2d
+    iso = sampling is None or all(float(s) == 1.0 for s in sampling)
+    want = ("sqdist", "dist", "indices") if iso else ("dist", "indices")
+    sq, ds, ix = _poisoned(torch, dev, masks.shape, want)
+    edt2d(torch.from_numpy(masks).to(dev), sampling, sqdist=sq, dist=ds, indices=ix)
+    torch.cuda.synchronize()
+    ref = np.stack([oracle.edt(m, sampling, features=False)[0] for m in masks])
+    compare(masks, sampling, ref, _np(sq), _np(ds), _np(ix), batch=True)
+    return ref, _np(ix)
+
+
+def test_batched_2d_matches_per_image(torch_dev):
+    rng = np.random.default_rng([42, 5001])
+    # few short lines (one wave per line), many lines (chunk kernel), long rows
+    for shape in ((5, 40, 70), (3, 1, 517), (70, 1000, 3), (2, 37, 1031), (4, 300, 260)):
+        for p in (0.003, 0.2):
+            masks = (rng.random(shape) >= p).astype(np.uint8)
+            for b in range(shape[0]):
+                masks[b].reshape(-1)[rng.integers(masks[b].size)] = 0
+            _say(f"batched 2d {shape} p={p}")
+            run_batched_2d(torch_dev, masks)
+            run_batched_2d(torch_dev, masks, (2.5, 1.0))
+            run_batched_2d(torch_dev, masks, (0.5, 1.25))
+
+
+def test_batched_2d_image_without_background(torch_dev):
+    """Each image of a batch takes the virtual element on its own."""
+    rng = np.random.default_rng([42, 5002])
+    masks = (rng.random((4, 33, 90)) >= 0.01).astype(np.uint8)
+    masks[0] = 1
+    masks[2] = 1
+    masks[1, 0, 0] = 0
+    masks[3, 32, 89] = 0
+    _say("batched 2d with empty images")
+    ref, ix = run_batched_2d(torch_dev, masks)
+    H, W = masks.shape[1:]
+    r, c = np.meshgrid(np.arange(H), np.arange(W), indexing="ij")
+    for b in (0, 2):
+        assert (ref[b] == (r + 1) ** 2 + c ** 2).all()
+        assert (ix[b] == -W).all()
+
+
+def test_batched_2d_equals_single_calls(torch_dev):
+    """The batched entry point gives bit-identical outputs to one call per image."""
+    torch, dev = torch_dev
+    from exact_euclidean_distance_amd import edt2d
+    rng = np.random.default_rng([42, 5003])
+    masks = (rng.random((3, 129, 4100)) >= 0.001).astype(np.uint8)
+    masks[:, 5, 7] = 0
+    m = torch.from_numpy(masks).to(dev)
+    rb = edt2d(m, return_sqdist=True, return_indices=True)
+    for b in range(3):
+        r1 = edt2d(m[b].contiguous(), return_sqdist=True, return_indices=True)
+        torch.cuda.synchronize()
+        assert torch.equal(rb.sqdist[b], r1.sqdist)
+        assert torch.equal(rb.dist[b], r1.dist)
+        assert torch.equal(rb.indices[b], r1.indices)
+
+
+def test_1d_lines(torch_dev):
+    torch, dev = torch_dev
+    from exact_euclidean_distance_amd import edt1d
+    rng = np.random.default_rng([42, 5004])
+    # 46000: the longest line whose squared distances (up to N^2) fit in int32
+    for B, N in ((1, 1), (1, 7), (5, 1000), (300, 257), (2, 46000)):
+        for p in (0.001, 0.05, 0.6):
+            masks = (rng.random((B, N)) >= p).astype(np.uint8)
+            masks[0] = 1                       # a line without background
+            for s in (None, (2.5,)):
+                iso = s is None
+                want = ("sqdist", "dist", "indices") if iso else ("dist", "indices")
+                sq, ds, ix = _poisoned(torch, dev, (B, N), want)
+                edt1d(torch.from_numpy(masks).to(dev), s, sqdist=sq, dist=ds, indices=ix)
+                torch.cuda.synchronize()
+                ref = np.stack([oracle.edt(m, s, features=False)[0] for m in masks])
+                _say(f"1d B={B} N={N} p={p} s={s}")
+                compare(masks, s, ref, _np(sq), _np(ds), _np(ix), batch=True)
+                pos = np.arange(N)
+                s0 = 1.0 if s is None else s[0]
+                assert (ref[0] == (s0 * (pos + 1.0)) ** 2).all()
+                assert (_np(ix)[0] == -1).all()
+    # longer lines: distances only (their squared distances would overflow int32)
+    from exact_euclidean_distance_amd import EDTError
+    masks = (rng.random((2, 65535)) >= 0.001).astype(np.uint8)
+    masks[0] = 1
+    with pytest.raises(EDTError):
+        edt1d(torch.from_numpy(masks).to(dev), return_sqdist=True)
+    sq, ds, ix = _poisoned(torch, dev, masks.shape, ("dist", "indices"))
+    edt1d(torch.from_numpy(masks).to(dev), dist=ds, indices=ix)
+    torch.cuda.synchronize()
+    ref = np.stack([oracle.edt(m, None, features=False)[0] for m in masks])
+    compare(masks, None, ref, None, _np(ds), _np(ix), batch=True)
+    # a single (N,) line
+    mask = np.ones(50, np.uint8)
+    mask[[3, 40]] = 0
+    r = edt1d(torch.from_numpy(mask).to(dev), return_sqdist=True, return_indices=True)
+    torch.cuda.synchronize()
+    ref, _ = oracle.edt(mask, None, features=False)
+    compare(mask, None, ref, _np(r.sqdist), _np(r.dist), _np(r.indices))
+
+
+def _unravel_ref(flat, shape):
+    """Floor-division unravel of flat indices (NumPy), per image."""
+    f = flat.astype(np.int64)
+    out = []
+    for n in reversed(shape[1:]):
+        out.append(np.mod(f, n))
+        f = np.floor_divide(f, n)
+    out.append(f)
+    return np.stack(out[::-1]).astype(np.int32)
+
+
+def test_unravel_indices(torch_dev):
+    torch, dev = torch_dev
+    from exact_euclidean_distance_amd import edt2d, edt3d, unravel_indices
+    rng = np.random.default_rng([42, 5005])
+    # 3-D batch with a volume without background: its coordinates are (-1, 0, 0)
+    vols = (rng.random((3, 9, 17, 30)) >= 0.02).astype(np.uint8)
+    vols[1] = 1
+    vols[0, 0, 0, 0] = 0
+    vols[2, 8, 16, 29] = 0
+    r = edt3d(torch.from_numpy(vols).to(dev), return_indices=True)
+    co = unravel_indices(r.indices, vols.shape[1:])
+    torch.cuda.synchronize()
+    assert tuple(co.shape) == (3, 3, 9, 17, 30)
+    flat = r.indices.cpu().numpy()
+    got = co.cpu().numpy()
+    for b in range(3):
+        assert (got[b] == _unravel_ref(flat[b], vols.shape[1:])).all()
+    assert (got[1, 0] == -1).all() and (got[1, 1:] == 0).all()
+    _, feat = oracle.edt(vols[1], None, features=True)
+    assert (np.moveaxis(got[1], 0, -1) == feat).all()
+    # single background element: the coordinates are that element everywhere
+    vol = np.ones((1, 6, 7, 8), np.uint8)
+    vol[0, 2, 3, 4] = 0
+    r = edt3d(torch.from_numpy(vol).to(dev), return_indices=True)
+    co = unravel_indices(r.indices, vol.shape[1:]).cpu().numpy()
+    assert (co[0, 0] == 2).all() and (co[0, 1] == 3).all() and (co[0, 2] == 4).all()
+    # 2-D batch and one image; 1-D
+    imgs = (rng.random((2, 31, 45)) >= 0.05).astype(np.uint8)
+    imgs[0] = 1
+    imgs[1, 3, 3] = 0
+    r = edt2d(torch.from_numpy(imgs).to(dev), return_indices=True)
+    co = unravel_indices(r.indices, imgs.shape[1:]).cpu().numpy()
+    flat = r.indices.cpu().numpy()
+    for b in range(2):
+        assert (co[b] == _unravel_ref(flat[b], imgs.shape[1:])).all()
+    assert (co[0, 0] == -1).all() and (co[0, 1] == 0).all()
+    co1 = unravel_indices(r.indices[1].contiguous(), imgs.shape[1:]).cpu().numpy()
+    assert (co1 == co[1]).all()
+    flat1 = torch.tensor([-1, 0, 3, 2], dtype=torch.int32, device=dev)   # one line of 4
+    assert (unravel_indices(flat1, (4,)).cpu().numpy() == [[-1, 0, 3, 2]]).all()
+
+
+def test_full_size_batched_workload(torch_dev):
+    """The batched 2-D workload the benchmark times, at full size, with the
+    outputs it times."""
+    from workloads import make_config
+    masks, sampling, _ = make_config("b2d")
+    _say(f"b2d {masks.shape}: GPU + oracle")
+    run_batched_2d(torch_dev, masks, sampling)

@@ -39,9 +39,11 @@ CONFIGS = {
     "c3": dict(shape=(16384, 16384), sampling=None, outputs=("sqdist", "dist")),
     "c4": dict(shape=(16, 128, 128, 128), sampling=None, outputs=("dist",)),
     "c5": dict(shape=(1, 512, 512, 512), sampling=(2.5, 1.0, 1.0), outputs=("dist", "indices")),
+    # batched 2-D (not one of the five headline workloads): 32 images shaped like c1
+    "b2d": dict(shape=(32, 1024, 1024), sampling=None, outputs=("sqdist", "dist", "indices")),
 }
 
-_CFG_ID = {"c1": 1, "c2a": 2, "c2b": 2, "c3": 3, "c4": 4, "c5": 5, "stress_row": 6}
+_CFG_ID = {"c1": 1, "c2a": 2, "c2b": 2, "c3": 3, "c4": 4, "c5": 5, "stress_row": 6, "b2d": 7}
 _SUB_ID = {"c2a": 0, "c2b": 1}
 
 
@@ -180,6 +182,10 @@ def make_config(name: str, scale: int = 1):
         n = 512 // scale
         m, z0 = slab_volume(rng_for(name), n, 1e-3, max(1, 64 // scale))
         return m[None], (2.5, 1.0, 1.0), {"z0": z0}
+    if name == "b2d":
+        n = 1024 // scale
+        rng = rng_for(name)
+        return np.stack([bernoulli_2d(rng, n, n, 0.01) for _ in range(32)]), None, {}
     if name == "stress_row":
         n = 4096 // scale
         m, r0 = full_row_2d(rng_for(name), n, n)
