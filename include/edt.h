@@ -47,7 +47,8 @@
  * return without touching any buffer.  EDT_ERR_HIP means a kernel launch was
  * rejected (hipGetLastError after the launch); outputs are then unspecified.
  *
- * Limits.  Every extent in [1, 65535]; elements per image/volume <= 2^31-1;
+ * Limits.  Every extent and every batch size B in [1, 65535]; elements per
+ * image/volume <= 2^31-1;
  * when sqdist is requested the largest possible squared distance
  * (sum of extent^2) must fit in int32.  The lower envelope of a line is kept in
  * LDS, which bounds the line lengths of the envelope passes:
