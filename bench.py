@@ -64,6 +64,11 @@ WORKLOADS = {
     "b2d": "batched 2D: 32 images of 1024x1024 uint8, background i.i.d. Bernoulli(0.01) "
            "per image, isotropic; outputs sqdist + dist + index (flat per image)",
 }
+for _n in (1024, 2048, 4096, 8192):
+    for _pct in (1, 99):
+        WORKLOADS[f"p1_{_n}_{_pct}"] = (
+            f"2D {_n}x{_n} uint8, background i.i.d. Bernoulli({_pct / 100:g}) (PR-EDT's "
+            f"workload, its Table 1), isotropic; output float32 dist")
 OUTPUTS = {
     "c1": ("sqdist", "dist", "indices"),
     "c2a": ("sqdist", "dist", "indices"),
@@ -73,6 +78,7 @@ OUTPUTS = {
     "c5": ("dist", "indices"),
     "b2d": ("sqdist", "dist", "indices"),
 }
+OUTPUTS.update({k: ("dist",) for k in WORKLOADS if k.startswith("p1_")})
 
 
 def algorithmic_bytes(kernel: str, shape, n_out: int) -> int:

@@ -1,5 +1,6 @@
-"""GPU parity of the batched 2-D and 1-D entry points and of the per-axis
-index layout, through the C ABI, against the CPU oracle run image by image.
+"""GPU parity of the batched 2-D and 1-D entry points, of the per-axis index
+layout and of PR-EDT's own workloads, through the C ABI, against the CPU
+oracle run image by image.
 
 Same bar as the single-image tests: int32 squared distances bit-exact (unit
 spacing), float32 distances within 1e-6 / 1e-5 relative, every index attains
@@ -202,3 +203,19 @@ def test_full_size_batched_workload(torch_dev):
     masks, sampling, _ = make_config("b2d")
     _say(f"b2d {masks.shape}: GPU + oracle")
     run_batched_2d(torch_dev, masks, sampling)
+
+
+@pytest.mark.parametrize("name", ["p1_1024_1", "p1_1024_99", "p1_8192_1", "p1_8192_99"])
+def test_pr_edt_workloads(torch_dev, name):
+    """PR-EDT's own workloads (random squares, seed 42, 1 % / 99 % background),
+    as benchmarked, with exact squared distances and indices checked too."""
+    torch, dev = torch_dev
+    from exact_euclidean_distance_amd import edt2d
+    from workloads import make_config
+    mask, _, _ = make_config(name)
+    _say(f"{name}: GPU + oracle")
+    sq, ds, ix = _poisoned(torch, dev, mask.shape, ("sqdist", "dist", "indices"))
+    edt2d(torch.from_numpy(mask).to(dev), sqdist=sq, dist=ds, indices=ix)
+    torch.cuda.synchronize()
+    ref, _ = oracle.edt(mask, None, features=False)
+    compare(mask, None, ref, _np(sq), _np(ds), _np(ix))
