@@ -268,6 +268,57 @@ def cpu_baseline(name, mask, sampling, budget_s=15.0):
             "cpu": platform.processor() or platform.machine()}
 
 
+FP64_PEAK_TFLOPS = 78.6   # MI355X vector fp64
+
+
+def bench_brute(args):
+    """Time the device brute force (every element against every background
+    element of its image) on a workload; ALU-bound: 3 fp64 flops per axis and
+    (element, background element) pair, against the fp64 vector peak."""
+    import torch
+    from exact_euclidean_distance_amd import edt_brute
+    from workloads import make_config
+    name = args.config
+    mask_np, sampling, _ = make_config(name)
+    batched = mask_np.ndim >= 3          # batches of images (and the volume workloads)
+    imgs = mask_np if batched else mask_np[None]
+    ndim = imgs.ndim - 1
+    pairs = int(sum(int(m.size) * int((m == 0).sum()) for m in imgs))
+    dev = torch.device("cuda:0")
+    mask = torch.from_numpy(mask_np).to(dev)
+    want = OUTPUTS[name]
+    kw = dict(batched=batched, return_sqdist="sqdist" in want, return_indices="indices" in want,
+              return_distances="dist" in want)
+    for _ in range(args.warmup):
+        edt_brute(mask, sampling, **kw)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    stream = torch.cuda.current_stream()
+    e0.record(stream)
+    for _ in range(args.steps):
+        edt_brute(mask, sampling, **kw)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / max(1, args.steps)
+    tflops = pairs * 3 * ndim / (ms * 1e-3) / 1e12
+    line = {
+        "metric": METRIC + " (device brute-force check, not the transform's path)",
+        "value": round(mask_np.size / (ms * 1e-3) / 1e9, 4), "unit": "Gpixel/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f64",
+        "data": "synthetic",
+        "config": {"workload": f"{name}: {WORKLOADS[name]}", "shape": list(mask_np.shape),
+                   "path": "brute force", "pairs": pairs},
+        "roofline": {"bound": "alu", "achieved": round(tflops, 3), "peak": FP64_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / FP64_PEAK_TFLOPS, 4), "traffic": None},
+        "Gpairs_per_s": round(pairs / (ms * 1e-3) / 1e9, 2),
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -276,6 +327,8 @@ def main(argv=None):
     ap.add_argument("--config", default=DEFAULT_CONFIG, choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--check", action="store_true", help="also compare with the oracle")
+    ap.add_argument("--brute", action="store_true",
+                    help="time the device brute-force transform (the exactness check) instead")
     ap.add_argument("--probe-copy", action="store_true")
     ap.add_argument("--summarize-traffic", nargs=4, metavar="DIR")
     args = ap.parse_args(argv)
@@ -295,6 +348,9 @@ def main(argv=None):
     from exact_euclidean_distance_amd import alloc_workspace, edt2d, edt3d, workspace_size_2d_batched, \
         workspace_size_3d
     from workloads import make_config
+
+    if args.brute:
+        return bench_brute(args)
 
     if not torch.cuda.is_available():
         print("bench.py: no HIP device", file=sys.stderr)

@@ -167,6 +167,18 @@ edt_status run3d(const uint8_t* mask, int32_t B, int32_t D, int32_t H, int32_t W
     return EDT_OK;
 }
 
+bool brute_shape_ok(int32_t B, int32_t ndim, const int32_t* shape, int64_t* per) {
+    if (!shape || ndim < 1 || ndim > 3 || B < 1 || B > kMaxExtent) return false;
+    int64_t p = 1;
+    for (int k = 0; k < ndim; ++k) {
+        if (shape[k] < 1 || shape[k] > kMaxExtent) return false;
+        p *= shape[k];
+    }
+    if (p > INT32_MAX) return false;
+    *per = p;
+    return true;
+}
+
 edt_status finish_timed(edt_status st, edt::KernelTimer& tm, hipStream_t stream, float* kernel_ms,
                         const char** kernel_names, int32_t* count) {
     if (st == EDT_OK && hipStreamSynchronize(stream) != hipSuccess) st = EDT_ERR_HIP;
@@ -297,6 +309,44 @@ edt_status edt3d_u8_batched_timed(const uint8_t* mask, int32_t B, int32_t D, int
     edt_status st = run3d(mask, B, D, H, W, sampling, sqdist, dist, indices, workspace,
                           workspace_bytes, stream, &tm);
     return finish_timed(st, tm, stream, kernel_ms, kernel_names, count);
+}
+
+size_t edt_brute_workspace_size(int32_t B, int32_t ndim, const int32_t* shape) {
+    int64_t per = 0;
+    if (!brute_shape_ok(B, ndim, shape, &per)) return 0;
+    return round_up((size_t)B * (size_t)per * 4) + round_up((size_t)B * 4);
+}
+
+edt_status edt_brute_u8(const uint8_t* mask, int32_t B, int32_t ndim, const int32_t* shape,
+                        const float* sampling, int32_t* sqdist, float* dist, int32_t* indices,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (!shape || ndim < 1 || ndim > 3 || B < 1) return EDT_ERR_INVALID_ARGUMENT;
+    for (int k = 0; k < ndim; ++k)
+        if (shape[k] < 1) return EDT_ERR_INVALID_ARGUMENT;
+    int64_t per = 0;
+    if (!brute_shape_ok(B, ndim, shape, &per)) return EDT_ERR_UNSUPPORTED_SHAPE;
+    double s2[3];
+    bool unit;
+    edt_status st = read_sampling(sampling, ndim, s2, &unit);
+    if (st != EDT_OK) return st;
+    if (sqdist) {
+        if (!unit) return EDT_ERR_INVALID_ARGUMENT;
+        double mx = 0.0;
+        for (int k = 0; k < ndim; ++k) mx += (double)shape[k] * shape[k];
+        if (mx > (double)INT32_MAX) return EDT_ERR_UNSUPPORTED_SHAPE;
+    }
+    const size_t list_bytes = round_up((size_t)B * (size_t)per * 4);
+    const size_t need = list_bytes + round_up((size_t)B * 4);
+    st = check_buffers(mask, (size_t)B * per, sqdist, dist, indices, workspace, workspace_bytes, need);
+    if (st != EDT_OK) return st;
+    char* base = static_cast<char*>(workspace);
+    int n[3];
+    for (int k = 0; k < ndim; ++k) n[k] = shape[k];
+    if (edt::launch_brute(mask, B, ndim, n, s2, reinterpret_cast<int32_t*>(base),
+                          reinterpret_cast<int32_t*>(base + list_bytes), sqdist, dist, indices,
+                          stream) != hipSuccess)
+        return EDT_ERR_HIP;
+    return EDT_OK;
 }
 
 const char* edt_status_string(edt_status status) {

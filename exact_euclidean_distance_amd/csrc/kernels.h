@@ -55,6 +55,12 @@ hipError_t launch_rows_3d(const uint32_t* c01, int B, int D, int H, int W,
 hipError_t launch_unravel(const int32_t* flat, int64_t images, int64_t per_image, int ndim, int n1,
                           int n2, int32_t* coords, hipStream_t s);
 
+// The transform by its definition (brute force), B images of ndim (1..3)
+// extents n[]: list / counts are workspace (B * elements and B int32).
+hipError_t launch_brute(const uint8_t* mask, int B, int ndim, const int* n, const double* s2,
+                        int32_t* list, int32_t* counts, int32_t* sqdist, float* dist,
+                        int32_t* indices, hipStream_t s);
+
 // Dynamic LDS each envelope launch needs (0 if the line is too long).
 size_t rows_lds_bytes(int L, int value_bytes);
 size_t cols_lds_bytes(int H);

@@ -126,6 +126,24 @@ edt_status edt1d_u8_batched(const uint8_t* mask, int32_t B, int32_t N,
 edt_status edt_unravel_indices(const int32_t* indices, int32_t images, int32_t ndim,
                                const int32_t* shape, int32_t* coords, hipStream_t stream);
 
+/* Bytes of workspace edt_brute_u8 needs (0 if the shape is outside its
+   limits).  shape is a HOST pointer to ndim extents. */
+size_t edt_brute_workspace_size(int32_t B, int32_t ndim, const int32_t* shape);
+
+/* The same transform by its definition, for checking on the device: every
+   element against every background element of its image (TorchMorph keeps a
+   brute-force transform beside its EDT as an exactness oracle).  B images of
+   ndim = 1..3 axes, extents shape[0..ndim) (HOST pointer), mask [B][...];
+   sampling {s_0, ..} or NULL; outputs, indices and the virtual element as for
+   the transforms above.  Among equally near background elements the smallest
+   flat index is returned.  Cost O(elements x background elements): meant for
+   small images.  Limits: B and every extent in [1, 65535], elements per image
+   <= 2^31-1; sqdist as above. */
+edt_status edt_brute_u8(const uint8_t* mask, int32_t B, int32_t ndim, const int32_t* shape,
+                        const float* sampling,
+                        int32_t* sqdist, float* dist, int32_t* indices,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Bytes of workspace edt3d_u8_batched needs for B volumes of D x H x W. */
 size_t edt3d_workspace_size(int32_t B, int32_t D, int32_t H, int32_t W);
 

@@ -171,3 +171,30 @@ def test_unravel_argument_errors(lib):
     assert lib.edt_unravel_indices(IDX, 1, 3, bad, DIST, None) == INVALID
     big = (ctypes.c_int32 * 3)(65535, 65535, 2)
     assert lib.edt_unravel_indices(IDX, 1, 3, big, DIST, None) == SHAPE
+
+
+def test_brute_argument_errors(lib):
+    shp = (ctypes.c_int32 * 3)(8, 9, 10)
+    need = lib.edt_brute_workspace_size(2, 3, shp)
+    assert need >= 2 * 8 * 9 * 10 * 4
+    assert lib.edt_brute_workspace_size(2, 4, shp) == 0
+    assert lib.edt_brute_workspace_size(0, 3, shp) == 0
+
+    def call(mask=MASK, B=2, ndim=3, shape=shp, sampling=None, sq=SQ, dist=DIST, idx=IDX, ws=WS,
+             ws_bytes=BIG):
+        samp = None if sampling is None else (ctypes.c_float * ndim)(*sampling)
+        return lib.edt_brute_u8(mask, B, ndim, shape, samp, sq, dist, idx, ws, ws_bytes, None)
+
+    assert call(mask=None) == INVALID
+    assert call(B=0) == INVALID
+    assert call(ndim=0) == INVALID
+    assert call(ndim=4) == INVALID
+    assert call(shape=None) == INVALID
+    assert call(shape=(ctypes.c_int32 * 3)(8, 0, 10)) == INVALID
+    assert call(shape=(ctypes.c_int32 * 3)(8, 70000, 10)) == SHAPE
+    assert call(B=70000) == SHAPE
+    assert call(sampling=(2.0, 1.0, 1.0)) == INVALID          # sqdist needs unit spacing
+    assert call(sampling=(2.0, -1.0, 1.0), sq=None) == INVALID
+    assert call(ws_bytes=need - 1) == SMALL
+    assert call(sq=None, dist=None, idx=None) == INVALID
+    assert call(idx=SQ + 4) == INVALID

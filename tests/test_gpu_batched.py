@@ -219,3 +219,56 @@ def test_pr_edt_workloads(torch_dev, name):
     torch.cuda.synchronize()
     ref, _ = oracle.edt(mask, None, features=False)
     compare(mask, None, ref, _np(sq), _np(ds), _np(ix))
+
+
+def test_brute_force_transform(torch_dev):
+    """The device brute force against the oracle's brute force (the definition;
+    both return the smallest index among equally near background elements,
+    so indices match exactly) and against the separable GPU path."""
+    torch, dev = torch_dev
+    from exact_euclidean_distance_amd import edt1d, edt2d, edt3d, edt_brute
+    rng = np.random.default_rng([42, 5006])
+    cases = [((40,), None), ((300,), (2.5,)), ((23, 57), None), ((64, 64), (2.5, 1.0)),
+             ((9, 13, 17), None), ((16, 16, 16), (2.5, 1.0, 1.0)), ((5, 31, 2), (0.5, 1.25, 2.0))]
+    for shape, samp in cases:
+        for p in (0.002, 0.05, 0.5):
+            mask = (rng.random(shape) >= p).astype(np.uint8)
+            mask.reshape(-1)[rng.integers(mask.size)] = 0
+            iso = samp is None
+            _say(f"brute {shape} p={p} s={samp}")
+            r = edt_brute(torch.from_numpy(mask).to(dev), samp, return_sqdist=iso, return_indices=True)
+            torch.cuda.synchronize()
+            ref, feat = oracle.edt_brute(mask, samp, features=True)
+            compare(mask, samp, ref, _np(r.sqdist), _np(r.dist), _np(r.indices))
+            assert (_np(r.indices) == oracle.flat_index(feat, mask.shape)).all()
+    # batched, with an image without background (virtual element)
+    masks = (rng.random((3, 20, 30)) >= 0.02).astype(np.uint8)
+    masks[1] = 1
+    masks[0, 0, 0] = 0
+    masks[2, 19, 29] = 0
+    r = edt_brute(torch.from_numpy(masks).to(dev), batched=True, return_sqdist=True,
+                  return_indices=True)
+    torch.cuda.synchronize()
+    ref = np.stack([oracle.edt_brute(m, None, features=False)[0] for m in masks])
+    compare(masks, None, ref, _np(r.sqdist), _np(r.dist), _np(r.indices), batch=True)
+    assert (_np(r.indices)[1] == -30).all()
+    # the device check of the fast path on sizes beyond the quick CPU brute force
+    m2 = (rng.random((2, 700, 900)) >= 0.003).astype(np.uint8)
+    m2[:, 1, 1] = 0
+    t2 = torch.from_numpy(m2).to(dev)
+    a = edt_brute(t2, batched=True, return_sqdist=True)
+    b = edt2d(t2, return_sqdist=True)
+    m3 = (rng.random((2, 40, 50, 60)) >= 0.01).astype(np.uint8)
+    m3[:, 0, 0, 0] = 0
+    t3 = torch.from_numpy(m3).to(dev)
+    c = edt_brute(t3, (2.5, 1.0, 1.0), batched=True)
+    d = edt3d(t3, (2.5, 1.0, 1.0))
+    m1 = (rng.random((4, 5000)) >= 0.01).astype(np.uint8)
+    m1[:, 0] = 0
+    t1 = torch.from_numpy(m1).to(dev)
+    e = edt_brute(t1, batched=True, return_sqdist=True)
+    f = edt1d(t1, return_sqdist=True)
+    torch.cuda.synchronize()
+    assert torch.equal(a.sqdist, b.sqdist) and torch.equal(a.dist, b.dist)
+    assert torch.equal(c.dist, d.dist)
+    assert torch.equal(e.sqdist, f.sqdist)
