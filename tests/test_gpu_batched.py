@@ -272,3 +272,56 @@ def test_brute_force_transform(torch_dev):
     assert torch.equal(a.sqdist, b.sqdist) and torch.equal(a.dist, b.dist)
     assert torch.equal(c.dist, d.dist)
     assert torch.equal(e.sqdist, f.sqdist)
+
+
+def test_randomized_sweep(torch_dev):
+    """Seeded random cases across every entry point: shapes (ragged, tiny,
+    lines of one), densities, dyadic spacings (exact in float64), images
+    without background inside batches and full background lines.  Each case
+    is checked against the oracle and, bit for bit, against the device brute
+    force (both exact)."""
+    torch, dev = torch_dev
+    from exact_euclidean_distance_amd import edt1d, edt2d, edt3d, edt_brute
+    rng = np.random.default_rng([42, 5007])
+    spacings = (0.5, 1.0, 1.25, 2.5)
+    for case in range(200):
+        kind = case % 4
+        if kind == 0:
+            shape = (int(rng.integers(1, 4)), int(rng.integers(1, 700)))
+        elif kind == 1:
+            shape = (int(rng.integers(1, 260)), int(rng.integers(1, 260)))
+        elif kind == 2:
+            shape = (int(rng.integers(1, 5)), int(rng.integers(1, 120)), int(rng.integers(1, 120)))
+        else:
+            shape = (int(rng.integers(1, 4)), int(rng.integers(1, 30)), int(rng.integers(1, 30)),
+                     int(rng.integers(1, 40)))
+        p = float(rng.choice([0.0005, 0.01, 0.1, 0.5, 0.95]))
+        mask = (rng.random(shape) >= p).astype(np.uint8)
+        batched = kind in (0, 2, 3)
+        imgs = mask if batched else mask[None]
+        for b in range(imgs.shape[0]):
+            r = rng.random()
+            if r < 0.15:
+                imgs[b] = 1                                  # no background
+            elif r < 0.3:
+                ax = int(rng.integers(imgs[b].ndim))         # a full background line / plane
+                sl = [slice(None)] * imgs[b].ndim
+                sl[ax] = int(rng.integers(imgs[b].shape[ax]))
+                imgs[b][tuple(sl)] = 0
+        nd = imgs.ndim - 1
+        samp = None if rng.random() < 0.5 else tuple(float(rng.choice(spacings)) for _ in range(nd))
+        iso = samp is None or all(s == 1.0 for s in samp)
+        want = ("sqdist", "dist", "indices") if iso else ("dist", "indices")
+        t = torch.from_numpy(mask).to(dev)
+        sq, ds, ix = _poisoned(torch, dev, mask.shape, want)
+        fn = {0: edt1d, 1: edt2d, 2: edt2d, 3: edt3d}[kind]
+        _say(f"sweep {case}: {fn.__name__} {shape} p={p} s={samp}")
+        fn(t, samp, sqdist=sq, dist=ds, indices=ix)
+        br = edt_brute(t, samp, batched=batched, return_sqdist=iso)
+        torch.cuda.synchronize()
+        ref = np.stack([oracle.edt(m, samp, features=False)[0] for m in imgs])
+        compare(imgs, samp, ref, None if sq is None else _np(sq).reshape(imgs.shape), _np(ds).reshape(imgs.shape),
+                _np(ix).reshape(imgs.shape), batch=True)
+        assert torch.equal(br.dist, ds)
+        if iso:
+            assert torch.equal(br.sqdist, sq)
