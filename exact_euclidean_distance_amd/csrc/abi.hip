@@ -36,11 +36,12 @@ bool shape2d_ok(int32_t B, int32_t H, int32_t W) {
     return edt::rows_lds_bytes(W, 2) != 0;
 }
 
+// Volumes over 2^31 - 1 elements are accepted here (offsets are 64-bit
+// throughout); only their int32 flat indices cannot be returned (run3d).
 bool shape3d_ok(int32_t B, int32_t D, int32_t H, int32_t W) {
     if (B < 1 || D < 1 || H < 1 || W < 1) return false;
     if (B > kMaxExtent || D > kMaxExtent || H > kMaxExtent || W > kMaxExtent) return false;
     if (H > kMaxH3D || W > kMaxW3D) return false;
-    if ((int64_t)D * H * W > INT32_MAX) return false;
     return edt::rows_lds_bytes(W, 4) != 0;
 }
 
@@ -147,6 +148,7 @@ edt_status run3d(const uint8_t* mask, int32_t B, int32_t D, int32_t H, int32_t W
     if (sqdist && !unit) return EDT_ERR_INVALID_ARGUMENT;
     if (sqdist && (double)D * D + (double)H * H + (double)W * W > (double)INT32_MAX)
         return EDT_ERR_UNSUPPORTED_SHAPE;
+    if (indices && (int64_t)D * H * W > INT32_MAX) return EDT_ERR_UNSUPPORTED_SHAPE;
     const Layout L = layout3d(B, D, H, W);
     st = check_buffers(mask, (size_t)B * D * H * W, sqdist, dist, indices, ws, ws_bytes, L.total);
     if (st != EDT_OK) return st;

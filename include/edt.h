@@ -48,7 +48,9 @@
  * rejected (hipGetLastError after the launch); outputs are then unspecified.
  *
  * Limits.  Every extent and every batch size B in [1, 65535]; elements per
- * image/volume <= 2^31-1;
+ * image <= 2^31-1, and per volume too when indices are requested (a volume of
+ * more elements, which HBM holds easily, is transformed when only sqdist
+ * and/or dist are asked for);
  * when sqdist is requested the largest possible squared distance
  * (sum of extent^2) must fit in int32.  The lower envelope of a line is kept in
  * LDS, which bounds the line lengths of the envelope passes:

@@ -51,7 +51,8 @@ def test_workspace_sizes(lib):
     assert lib.edt2d_workspace_size(70000, 5) == 0
     assert lib.edt3d_workspace_size(1, 8, 2000, 8) == 0
     assert lib.edt3d_workspace_size(1, 8, 8, 20000) == 0
-    assert lib.edt3d_workspace_size(1, 65535, 1024, 64) == 0    # > 2^31-1 elements
+    # > 2^31-1 elements: a workspace for distances (indices are refused by the call)
+    assert lib.edt3d_workspace_size(1, 2100, 1024, 1000) >= 2100 * 1024 * 1000 * 6
 
 
 def call2d(lib, mask=MASK, H=64, W=64, sampling=None, sq=SQ, dist=DIST, idx=IDX, ws=WS,
@@ -103,6 +104,8 @@ def test_3d_argument_errors(lib):
     assert call3d(lib, ws_bytes=lib.edt3d_workspace_size(2, 8, 8, 8) - 1) == SMALL
     assert call3d(lib, idx=IDX + 1) == INVALID
     assert call3d(lib, dist=WS) == INVALID
+    # a volume over 2^31-1 elements cannot return int32 indices
+    assert call3d(lib, B=1, D=2100, H=1024, W=1000, sq=None, dist=None) == SHAPE
 
 
 def test_timed_entry_rejects_without_buffer(lib):

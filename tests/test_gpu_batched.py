@@ -325,3 +325,82 @@ def test_randomized_sweep(torch_dev):
         assert torch.equal(br.dist, ds)
         if iso:
             assert torch.equal(br.sqdist, sq)
+
+
+def _brute_points(pos, pts, s2):
+    """Exact squared distance of each position (rows of pos) to the nearest of
+    the background points pts (float64, chunked)."""
+    out = np.full(len(pos), np.inf)
+    for i in range(0, len(pos), 1 << 16):
+        d = ((pos[i:i + (1 << 16), None, :] - pts[None, :, :]).astype(np.float64) ** 2 * s2).sum(-1)
+        out[i:i + (1 << 16)] = d.min(1)
+    return out
+
+
+@pytest.mark.timeout(600)
+def test_volume_over_2_31_elements(torch_dev):
+    """A volume of 2100 x 1024 x 1000 (2.15e9 voxels, more than int32 can
+    index; about 24 GB of HBM with its workspace): distances with 64-bit
+    offsets everywhere.  Checked exactly on the whole last plane (offsets past
+    2^31) and on a million random voxels against brute force over the
+    background points; indices are refused.  Then three volumes with indices
+    whose batch together passes 2^31 elements."""
+    torch, dev = torch_dev
+    from exact_euclidean_distance_amd import EDTError, edt3d
+    rng = np.random.default_rng([42, 5008])
+    D, H, W = 2100, 1024, 1000
+    n = D * H * W
+    assert n > 2 ** 31
+    flat = np.ones(n, np.uint8)
+    bg = rng.choice(n, 400, replace=False)
+    flat[bg] = 0
+    pts = np.stack(np.unravel_index(bg, (D, H, W)), 1)
+    _say("volume 2100x1024x1000: transfer")
+    m = torch.from_numpy(flat).to(dev).view(1, D, H, W)
+    del flat
+    with pytest.raises(EDTError):
+        edt3d(m, return_indices=True)
+    for samp in (None, (2.5, 1.0, 1.0)):
+        _say(f"volume 2100x1024x1000: transform, spacing {samp}")
+        r = edt3d(m, samp, return_sqdist=samp is None)
+        torch.cuda.synchronize()
+        s2 = np.array([1.0, 1.0, 1.0] if samp is None else [s * s for s in samp])
+        yy, xx = np.indices((H, W))
+        last = np.stack([np.full(H * W, D - 1), yy.ravel(), xx.ravel()], 1)
+        pick = np.sort(rng.choice(n, 1_000_000, replace=False))
+        rand = np.stack(np.unravel_index(pick, (D, H, W)), 1)
+        pos = np.concatenate([last, rand])
+        lin = torch.from_numpy(np.ravel_multi_index(pos.T, (D, H, W))).to(dev)
+        ref = _brute_points(pos, pts, s2)
+        got = r.dist.view(-1)[lin].cpu().numpy().astype(np.float64)
+        tol = 1e-6 if samp is None else 1e-5
+        assert np.all(np.abs(got - np.sqrt(ref)) <= tol * np.sqrt(ref)), "dist mismatch"
+        if samp is None:
+            assert (r.sqdist.view(-1)[lin].cpu().numpy() == ref).all(), "sqdist mismatch"
+        del r
+    del m
+    torch.cuda.empty_cache()
+    # a batch over 2^31 elements in total, indices within each volume
+    B, D, H, W = 3, 700, 1024, 1024
+    flat = np.ones(B * D * H * W, np.uint8)
+    per = D * H * W
+    pts3 = []
+    for b in range(B):
+        bgb = rng.choice(per, 300, replace=False)
+        flat[b * per + bgb] = 0
+        pts3.append(np.stack(np.unravel_index(bgb, (D, H, W)), 1))
+    _say("batch 3x700x1024x1024: transform with indices")
+    m = torch.from_numpy(flat).to(dev).view(B, D, H, W)
+    del flat
+    r = edt3d(m, return_sqdist=True, return_indices=True)
+    torch.cuda.synchronize()
+    b = B - 1
+    yy, xx = np.indices((H, W))
+    pos = np.stack([np.full(H * W, D - 1), yy.ravel(), xx.ravel()], 1)
+    ref = _brute_points(pos, pts3[b], np.ones(3))
+    got_sq = r.sqdist[b, D - 1].cpu().numpy().ravel()
+    got_ix = r.indices[b, D - 1].cpu().numpy().ravel().astype(np.int64)
+    assert (got_sq == ref).all()
+    fz, fy, fx = np.unravel_index(got_ix, (D, H, W))
+    d2 = (fz - pos[:, 0]) ** 2 + (fy - pos[:, 1]) ** 2 + (fx - pos[:, 2]) ** 2
+    assert (d2 == ref).all(), "index does not attain the minimum"
