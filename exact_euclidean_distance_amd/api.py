@@ -22,7 +22,7 @@ from ._lib import EDTError
 class EDTResult:
     sqdist: Optional[torch.Tensor]   # int32, exact squared distances
     dist: Optional[torch.Tensor]     # float32 distances
-    indices: Optional[torch.Tensor]  # int32 flat index of the nearest background (per image)
+    indices: Optional[torch.Tensor]  # flat index of the nearest background (per image), int32 or int64
 
 
 def workspace_size_2d(H: int, W: int) -> int:
@@ -216,9 +216,12 @@ def edt_brute(mask: torch.Tensor, sampling=None, *, batched: bool = False,
 def edt3d(mask: torch.Tensor, sampling=None, *, return_distances: bool = True,
           return_sqdist: bool = False, return_indices: bool = False,
           dist=None, sqdist=None, indices=None, workspace=None, stream=None,
-          timed: bool = False):
+          timed: bool = False, index_dtype=torch.int32):
     """Exact EDT of a batch of volumes, mask (B, D, H, W) or (D, H, W) uint8.
-    Indices are flat within each volume."""
+    Indices are flat within each volume; ``index_dtype=torch.int64`` returns
+    them as int64 (volumes over 2^31 - 1 elements)."""
+    if index_dtype not in (torch.int32, torch.int64):
+        raise ValueError("index_dtype must be torch.int32 or torch.int64")
     _check_mask(mask, (3, 4))
     m4 = mask if mask.dim() == 4 else mask.unsqueeze(0)
     B, D, H, W = m4.shape
@@ -226,7 +229,7 @@ def edt3d(mask: torch.Tensor, sampling=None, *, return_distances: bool = True,
     dev = mask.device
     sq = _out(sqdist, shape, torch.int32, dev, return_sqdist)
     ds = _out(dist, shape, torch.float32, dev, return_distances)
-    ix = _out(indices, shape, torch.int32, dev, return_indices)
+    ix = _out(indices, shape, index_dtype, dev, return_indices)
     lib = _lib.load()
     need = int(lib.edt3d_workspace_size(B, D, H, W))
     if workspace is None:
@@ -234,6 +237,13 @@ def edt3d(mask: torch.Tensor, sampling=None, *, return_distances: bool = True,
     samp = _sampling(sampling, 3)
     args = [_ptr(m4), B, D, H, W, samp, _ptr(sq), _ptr(ds), _ptr(ix), _ptr(workspace),
             workspace.numel() * workspace.element_size(), _stream(stream)]
+    if index_dtype == torch.int64:
+        if timed:
+            raise ValueError("timed calls return int32 indices")
+        st = lib.edt3d_u8_batched_idx64(*args)
+        if st != 0:
+            raise EDTError(st, "edt3d_u8_batched_idx64")
+        return EDTResult(sq, ds, ix)
     if not timed:
         st = lib.edt3d_u8_batched(*args)
         if st != 0:

@@ -94,16 +94,18 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
 }
 
 // Common checks on outputs and workspace; n = total element count.
+// indices: int32 (idx_bytes 4) or int64 (idx_bytes 8) per element
 edt_status check_buffers(const uint8_t* mask, size_t n, int32_t* sqdist, float* dist,
-                         int32_t* indices, void* ws, size_t ws_bytes, size_t ws_need) {
+                         void* indices, void* ws, size_t ws_bytes, size_t ws_need,
+                         size_t idx_bytes = 4) {
     if (!mask) return EDT_ERR_INVALID_ARGUMENT;
     if (!sqdist && !dist && !indices) return EDT_ERR_INVALID_ARGUMENT;
-    if (((uintptr_t)sqdist & 3) || ((uintptr_t)dist & 3) || ((uintptr_t)indices & 3))
+    if (((uintptr_t)sqdist & 3) || ((uintptr_t)dist & 3) || ((uintptr_t)indices & (idx_bytes - 1)))
         return EDT_ERR_INVALID_ARGUMENT;
     if (!ws || ((uintptr_t)ws & (kAlign - 1))) return EDT_ERR_INVALID_ARGUMENT;
     if (ws_bytes < ws_need) return EDT_ERR_WORKSPACE_TOO_SMALL;
     const void* bufs[5] = {mask, sqdist, dist, indices, ws};
-    const size_t sizes[5] = {n, sqdist ? n * 4 : 0, dist ? n * 4 : 0, indices ? n * 4 : 0, ws_need};
+    const size_t sizes[5] = {n, sqdist ? n * 4 : 0, dist ? n * 4 : 0, indices ? n * idx_bytes : 0, ws_need};
     for (int i = 0; i < 5; ++i)
         for (int j = i + 1; j < 5; ++j)
             if (overlap(bufs[i], sizes[i], bufs[j], sizes[j])) return EDT_ERR_INVALID_ARGUMENT;
@@ -138,7 +140,8 @@ edt_status run2d(const uint8_t* mask, int32_t B, int32_t H, int32_t W, const flo
 
 edt_status run3d(const uint8_t* mask, int32_t B, int32_t D, int32_t H, int32_t W,
                  const float* sampling, int32_t* sqdist, float* dist, int32_t* indices,
-                 void* ws, size_t ws_bytes, hipStream_t stream, edt::KernelTimer* tm) {
+                 void* ws, size_t ws_bytes, hipStream_t stream, edt::KernelTimer* tm,
+                 int64_t* indices64 = nullptr) {
     if (B < 1 || D < 1 || H < 1 || W < 1) return EDT_ERR_INVALID_ARGUMENT;
     if (!shape3d_ok(B, D, H, W)) return EDT_ERR_UNSUPPORTED_SHAPE;
     double s2[3];
@@ -150,7 +153,10 @@ edt_status run3d(const uint8_t* mask, int32_t B, int32_t D, int32_t H, int32_t W
         return EDT_ERR_UNSUPPORTED_SHAPE;
     if (indices && (int64_t)D * H * W > INT32_MAX) return EDT_ERR_UNSUPPORTED_SHAPE;
     const Layout L = layout3d(B, D, H, W);
-    st = check_buffers(mask, (size_t)B * D * H * W, sqdist, dist, indices, ws, ws_bytes, L.total);
+    st = indices64 ? check_buffers(mask, (size_t)B * D * H * W, sqdist, dist, indices64, ws, ws_bytes,
+                                   L.total, 8)
+                   : check_buffers(mask, (size_t)B * D * H * W, sqdist, dist, indices, ws, ws_bytes,
+                                   L.total);
     if (st != EDT_OK) return st;
 
     char* base = static_cast<char*>(ws);
@@ -163,7 +169,8 @@ edt_status run3d(const uint8_t* mask, int32_t B, int32_t D, int32_t H, int32_t W
         return EDT_ERR_HIP;
     if (edt::launch_cols_3d(c0, B, D, H, W, s2[0], s2[1], c01, stream, tm) != hipSuccess)
         return EDT_ERR_HIP;
-    if (edt::launch_rows_3d(c01, B, D, H, W, s2[0], s2[1], s2[2], sqdist, dist, indices, stream, tm) !=
+    if (edt::launch_rows_3d(c01, B, D, H, W, s2[0], s2[1], s2[2], sqdist, dist, indices, indices64,
+                            stream, tm) !=
         hipSuccess)
         return EDT_ERR_HIP;
     return EDT_OK;
@@ -273,6 +280,14 @@ edt_status edt3d_u8_batched(const uint8_t* mask, int32_t B, int32_t D, int32_t H
                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
     return run3d(mask, B, D, H, W, sampling, sqdist, dist, indices, workspace, workspace_bytes,
                  stream, nullptr);
+}
+
+edt_status edt3d_u8_batched_idx64(const uint8_t* mask, int32_t B, int32_t D, int32_t H,
+                                  int32_t W, const float* sampling, int32_t* sqdist, float* dist,
+                                  int64_t* indices, void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream) {
+    return run3d(mask, B, D, H, W, sampling, sqdist, dist, nullptr, workspace, workspace_bytes,
+                 stream, nullptr, indices);
 }
 
 edt_status edt2d_u8_timed(const uint8_t* mask, int32_t H, int32_t W, const float* sampling,

@@ -43,10 +43,11 @@ hipError_t launch_cols_3d(const uint16_t* c0, int B, int D, int H, int W,
                           double s2_0, double s2_1, uint32_t* c01,
                           hipStream_t s, KernelTimer* tm);
 
-// Envelope pass along axis 2 of B volumes (lines of length W) with the epilogue.
+// Envelope pass along axis 2 of B volumes (lines of length W) with the epilogue;
+// flat indices as int32 (indices) or int64 (indices64), at most one of them.
 hipError_t launch_rows_3d(const uint32_t* c01, int B, int D, int H, int W,
                           double s2_0, double s2_1, double s2_2,
-                          int32_t* sqdist, float* dist, int32_t* indices,
+                          int32_t* sqdist, float* dist, int32_t* indices, int64_t* indices64,
                           hipStream_t s, KernelTimer* tm);
 
 // Flat per-image indices of `images` images of per_image elements -> per-axis

@@ -805,6 +805,10 @@ struct Geo3D {          // rows along W of B x D x H x W volumes; value = packed
         return s2a * t0 * t0 + s2b * (double)l.h * (double)l.h;
     }
     __device__ int32_t virt_index() const { return -(H * W); }
+    // the same flat index for volumes over 2^31 - 1 elements
+    __device__ int64_t index64(const Line&, uint32_t v, int pos) const {
+        return ((int64_t)(v >> 16) * H + (v & 0xFFFFu)) * (int64_t)W + pos;
+    }
 };
 
 template <int BYTES> struct RawVec;
@@ -847,12 +851,12 @@ __device__ inline void load_row_line(const Val* __restrict__ src, int L, int g, 
     }
 }
 
-template <class Geo, int K, int VW>
+template <class Geo, int K, int VW, class Ix = int32_t>
 __global__ __launch_bounds__(1024) void k_envelope_rows(const typename Geo::Val* __restrict__ in,
                                                         int L, int64_t nlines, int Gp, int LPW,
                                                         Geo geo, int32_t* __restrict__ sqdist,
                                                         float* __restrict__ dist,
-                                                        int32_t* __restrict__ indices, int vec_out) {
+                                                        Ix* __restrict__ indices, int vec_out) {
     using Val = typename Geo::Val;
     constexpr int CS = Slots<Val, K>::CS;
     constexpr int CM = Slots<Val, K>::CM;
@@ -889,7 +893,7 @@ __global__ __launch_bounds__(1024) void k_envelope_rows(const typename Geo::Val*
     const double s2l = geo.s2l;
     const double fvirt = geo.virt_f(gl);
     const int32_t ivirt = geo.virt_index();
-    auto one = [&](int q, int mk, int32_t& osq, float& od, int32_t& oix) {
+    auto one = [&](int q, int mk, int32_t& osq, float& od, Ix& oix) {
         const int ow = mk - 1;
         const int oq = ow < 0 ? 0 : ow;   // the virtual element acts as one at position 0
         const Val vo = view.val(oq);
@@ -897,16 +901,24 @@ __global__ __launch_bounds__(1024) void k_envelope_rows(const typename Geo::Val*
         const double F = (ow < 0 ? fvirt : fof(vo)) + s2l * dq * dq;
         osq = sqdist ? (int32_t)F : 0;
         od = __builtin_amdgcn_sqrtf((float)F);
-        oix = ow < 0 ? ivirt : geo.index(gl, vo, ow);
+        if constexpr (sizeof(Ix) == 8) oix = ow < 0 ? (Ix)ivirt : (Ix)geo.index64(gl, vo, ow);
+        else oix = ow < 0 ? ivirt : geo.index(gl, vo, ow);
     };
     const int64_t lbase = line * (int64_t)L;
     int32_t osq[4];
     float od[4];
-    int32_t oix[4];
+    Ix oix[4];
     auto store4 = [&](int64_t ob) {
         if (sqdist) *reinterpret_cast<int4*>(sqdist + ob) = make_int4(osq[0], osq[1], osq[2], osq[3]);
         if (dist) *reinterpret_cast<float4*>(dist + ob) = make_float4(od[0], od[1], od[2], od[3]);
-        if (indices) *reinterpret_cast<int4*>(indices + ob) = make_int4(oix[0], oix[1], oix[2], oix[3]);
+        if (indices) {
+            if constexpr (sizeof(Ix) == 8) {
+                *reinterpret_cast<longlong2*>(indices + ob) = make_longlong2(oix[0], oix[1]);
+                *reinterpret_cast<longlong2*>(indices + ob + 2) = make_longlong2(oix[2], oix[3]);
+            } else {
+                *reinterpret_cast<int4*>(indices + ob) = make_int4(oix[0], oix[1], oix[2], oix[3]);
+            }
+        }
     };
     // The marks of the own chunk become owners (running maximum, in place);
     // then lane g writes the 4-position pieces g, g + Gp, ... of the line, so
@@ -1265,28 +1277,28 @@ size_t rows_lds_bytes(int L, int value_bytes) {
     return p.lds;
 }
 
-template <class Geo, int K, int VW>
+template <class Geo, int K, int VW, class Ix>
 static hipError_t launch_rows_t(const typename Geo::Val* in, int L, int64_t nlines, const RowPlan& p,
-                                const Geo& geo, int32_t* sqdist, float* dist, int32_t* indices,
+                                const Geo& geo, int32_t* sqdist, float* dist, Ix* indices,
                                 hipStream_t s, KernelTimer* tm, const char* kname) {
     static bool attr_done = false;
     if (!attr_done) {
-        allow_large_lds((const void*)k_envelope_rows<Geo, K, VW>);
+        allow_large_lds((const void*)k_envelope_rows<Geo, K, VW, Ix>);
         attr_done = true;
     }
     const int64_t nblocks = (nlines + p.LPW - 1) / p.LPW;
     const bool aligned16 = (((uintptr_t)sqdist | (uintptr_t)dist | (uintptr_t)indices) & 15) == 0;
     const int vec_out = (L % 4 == 0 && aligned16) ? 1 : 0;
     EDT_LAUNCH(tm, kname, s,
-               hipLaunchKernelGGL((k_envelope_rows<Geo, K, VW>), dim3((unsigned)nblocks),
+               hipLaunchKernelGGL((k_envelope_rows<Geo, K, VW, Ix>), dim3((unsigned)nblocks),
                                   dim3(p.Gp * p.LPW), p.lds, s, in, L, nlines, p.Gp, p.LPW, geo,
                                   sqdist, dist, indices, vec_out));
     return hipSuccess;
 }
 
-template <class Geo, int K>
+template <class Geo, int K, class Ix>
 static hipError_t launch_rows_any(const typename Geo::Val* in, int L, int64_t nlines, const Geo& geo,
-                                  int32_t* sqdist, float* dist, int32_t* indices, hipStream_t s,
+                                  int32_t* sqdist, float* dist, Ix* indices, hipStream_t s,
                                   KernelTimer* tm, const char* kname) {
     constexpr int VB = (int)sizeof(typename Geo::Val);
     constexpr int V16 = 16 / VB;
@@ -1352,9 +1364,12 @@ hipError_t launch_unravel(const int32_t* flat, int64_t images, int64_t per_image
 
 hipError_t launch_rows_3d(const uint32_t* c01, int B, int D, int H, int W, double s2_0,
                           double s2_1, double s2_2, int32_t* sqdist, float* dist,
-                          int32_t* indices, hipStream_t s, KernelTimer* tm) {
+                          int32_t* indices, int64_t* indices64, hipStream_t s, KernelTimer* tm) {
     Geo3D geo{s2_0, s2_1, s2_2, D, H, W, (int64_t)D * H < (1 << 24)};
     const int64_t nlines = (int64_t)B * D * H;
+    if (indices64)   // int64 indices: the chunk kernel for any number of lines
+        return launch_rows_any<Geo3D, 16>(c01, W, nlines, geo, sqdist, dist, indices64, s, tm,
+                                          "envelope_rows_3d");
     hipError_t e = hipSuccess;
     if (launch_rows_wave<Geo3D>(c01, W, nlines, geo, sqdist, dist, indices, s, tm, "envelope_rows_3d", &e)) return e;
     return launch_rows_any<Geo3D, 16>(c01, W, nlines, geo, sqdist, dist, indices, s, tm, "envelope_rows_3d");

@@ -157,6 +157,15 @@ edt_status edt3d_u8_batched(const uint8_t* mask, int32_t B, int32_t D, int32_t H
                             int32_t* sqdist, float* dist, int32_t* indices,
                             void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* edt3d_u8_batched with int64 flat indices (int64_t [B*D*H*W], 8-byte
+   aligned; NULL for none), for volumes of more than 2^31 - 1 elements, which
+   the int32 form refuses indices for; same workspace, limits and errors
+   otherwise. */
+edt_status edt3d_u8_batched_idx64(const uint8_t* mask, int32_t B, int32_t D, int32_t H,
+                                  int32_t W, const float* sampling,
+                                  int32_t* sqdist, float* dist, int64_t* indices,
+                                  void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Same as edt2d_u8 / edt2d_u8_batched / edt3d_u8_batched, for measurement: records a HIP event
    pair around every kernel it enqueues, waits for the stream, and returns each
    kernel's duration in milliseconds (launch order) in kernel_ms[0..*count) and

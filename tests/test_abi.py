@@ -201,3 +201,17 @@ def test_brute_argument_errors(lib):
     assert call(ws_bytes=need - 1) == SMALL
     assert call(sq=None, dist=None, idx=None) == INVALID
     assert call(idx=SQ + 4) == INVALID
+
+
+def test_idx64_argument_errors(lib):
+    def call(idx=IDX, **kw):
+        a = dict(mask=MASK, B=2, D=8, H=8, W=8, samp=None, sq=SQ, dist=DIST, ws=WS, ws_bytes=BIG)
+        a.update(kw)
+        return lib.edt3d_u8_batched_idx64(a["mask"], a["B"], a["D"], a["H"], a["W"], a["samp"],
+                                          a["sq"], a["dist"], idx, a["ws"], a["ws_bytes"], None)
+    assert call(mask=None) == INVALID
+    assert call(idx=IDX + 4) == INVALID                  # int64 indices need 8-byte alignment
+    assert call(idx=SQ + 8) == INVALID                   # overlaps sqdist
+    assert call(sq=IDX + 4096) == INVALID                # sqdist inside the int64 indices (2*8*8*8*8 B)
+    assert call(ws_bytes=lib.edt3d_workspace_size(2, 8, 8, 8) - 1) == SMALL
+    assert call(H=2000) == SHAPE

@@ -353,6 +353,8 @@ def test_volume_over_2_31_elements(torch_dev):
     assert n > 2 ** 31
     flat = np.ones(n, np.uint8)
     bg = rng.choice(n, 400, replace=False)
+    # and five in the last plane, whose flat indices pass 2^31
+    bg = np.unique(np.concatenate([bg, (D - 1) * H * W + rng.choice(H * W, 5, replace=False)]))
     flat[bg] = 0
     pts = np.stack(np.unravel_index(bg, (D, H, W)), 1)
     _say("volume 2100x1024x1000: transfer")
@@ -378,7 +380,16 @@ def test_volume_over_2_31_elements(torch_dev):
         if samp is None:
             assert (r.sqdist.view(-1)[lin].cpu().numpy() == ref).all(), "sqdist mismatch"
         del r
-    del m
+    _say("volume 2100x1024x1000: int64 indices")
+    r = edt3d(m, return_distances=False, return_indices=True, index_dtype=torch.int64)
+    torch.cuda.synchronize()
+    got = r.indices.view(-1)[lin].cpu().numpy()
+    fz, fy, fx = np.unravel_index(got, (D, H, W))
+    d2 = (fz - pos[:, 0]) ** 2 + (fy - pos[:, 1]) ** 2 + (fx - pos[:, 2]) ** 2
+    ref = _brute_points(pos, pts, np.ones(3))
+    assert (d2 == ref).all(), "int64 index does not attain the minimum"
+    assert (got.reshape(-1)[:H * W] >= 2 ** 31).any()   # the last plane's owners lie past 2^31
+    del r, m
     torch.cuda.empty_cache()
     # a batch over 2^31 elements in total, indices within each volume
     B, D, H, W = 3, 700, 1024, 1024
@@ -404,3 +415,30 @@ def test_volume_over_2_31_elements(torch_dev):
     fz, fy, fx = np.unravel_index(got_ix, (D, H, W))
     d2 = (fz - pos[:, 0]) ** 2 + (fy - pos[:, 1]) ** 2 + (fx - pos[:, 2]) ** 2
     assert (d2 == ref).all(), "index does not attain the minimum"
+
+
+def test_int64_indices_small(torch_dev):
+    """int64 indices (chunk row kernel for any shape) attain the minimum and
+    come with the same distances as the int32 call."""
+    torch, dev = torch_dev
+    from exact_euclidean_distance_amd import edt3d
+    rng = np.random.default_rng([42, 5009])
+    for shape, samp in (((2, 9, 17, 30), None), ((1, 40, 33, 70), (2.5, 1.0, 1.0)),
+                        ((3, 5, 7, 513), None), ((2, 20, 30, 40), (0.5, 1.25, 1.0))):
+        vols = (rng.random(shape) >= 0.02).astype(np.uint8)
+        vols[0] = 1                                   # a volume without background
+        vols[-1].reshape(-1)[0] = 0
+        t = torch.from_numpy(vols).to(dev)
+        iso = samp is None
+        r64 = edt3d(t, samp, return_sqdist=iso, return_indices=True, index_dtype=torch.int64)
+        r32 = edt3d(t, samp, return_sqdist=iso, return_indices=True)
+        torch.cuda.synchronize()
+        assert r64.indices.dtype == torch.int64
+        assert torch.equal(r64.dist, r32.dist)
+        if iso:
+            assert torch.equal(r64.sqdist, r32.sqdist)
+        ix = r64.indices.cpu().numpy()
+        assert (np.abs(ix) < 2 ** 31).all()
+        ref = np.stack([oracle.edt(v, samp, features=False)[0] for v in vols])
+        _say(f"int64 indices {shape} s={samp}")
+        compare(vols, samp, ref, None, None, ix.astype(np.int32), batch=True)
