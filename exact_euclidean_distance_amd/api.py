@@ -97,11 +97,11 @@ def edt2d(mask: torch.Tensor, sampling=None, *, return_distances: bool = True,
           return_sqdist: bool = False, return_indices: bool = False,
           dist=None, sqdist=None, indices=None, workspace=None, stream=None,
           timed: bool = False):
-    """Exact EDT of one (H, W) uint8 mask, or of a batch (B, H, W) of
-    independent images (indices flat within each image).  Returns
-    :class:`EDTResult` (and the per-kernel times in ms when ``timed``)."""
-    _check_mask(mask, (2, 3))
-    m3 = mask if mask.dim() == 3 else mask.unsqueeze(0)
+    """Exact EDT of one (H, W) uint8 mask, or of a batch (B, H, W) or
+    (B, C, H, W) of independent images (indices flat within each image).
+    Returns :class:`EDTResult` (and the per-kernel times in ms when ``timed``)."""
+    _check_mask(mask, (2, 3, 4))
+    m3 = mask if mask.dim() == 3 else (mask.unsqueeze(0) if mask.dim() == 2 else mask.flatten(0, 1))
     B, H, W = m3.shape
     shape = tuple(mask.shape)
     dev = mask.device
@@ -119,6 +119,8 @@ def edt2d(mask: torch.Tensor, sampling=None, *, return_distances: bool = True,
                 _stream(stream)]
         fn, tfn, name = lib.edt2d_u8, lib.edt2d_u8_timed, "edt2d_u8"
     else:
+        if B > 65535:
+            raise ValueError("at most 65535 images per call")
         args = [_ptr(mask), B, H, W, samp, _ptr(sq), _ptr(ds), _ptr(ix), _ptr(workspace), wsb,
                 _stream(stream)]
         fn, tfn, name = lib.edt2d_u8_batched, lib.edt2d_u8_batched_timed, "edt2d_u8_batched"
@@ -217,13 +219,14 @@ def edt3d(mask: torch.Tensor, sampling=None, *, return_distances: bool = True,
           return_sqdist: bool = False, return_indices: bool = False,
           dist=None, sqdist=None, indices=None, workspace=None, stream=None,
           timed: bool = False, index_dtype=torch.int32):
-    """Exact EDT of a batch of volumes, mask (B, D, H, W) or (D, H, W) uint8.
-    Indices are flat within each volume; ``index_dtype=torch.int64`` returns
-    them as int64 (volumes over 2^31 - 1 elements)."""
+    """Exact EDT of a batch of volumes, mask (B, D, H, W), (B, C, D, H, W) or
+    (D, H, W) uint8.  Indices are flat within each volume;
+    ``index_dtype=torch.int64`` returns them as int64 (volumes over 2^31 - 1
+    elements)."""
     if index_dtype not in (torch.int32, torch.int64):
         raise ValueError("index_dtype must be torch.int32 or torch.int64")
-    _check_mask(mask, (3, 4))
-    m4 = mask if mask.dim() == 4 else mask.unsqueeze(0)
+    _check_mask(mask, (3, 4, 5))
+    m4 = mask if mask.dim() == 4 else (mask.unsqueeze(0) if mask.dim() == 3 else mask.flatten(0, 1))
     B, D, H, W = m4.shape
     shape = tuple(mask.shape)
     dev = mask.device

@@ -442,3 +442,30 @@ def test_int64_indices_small(torch_dev):
         ref = np.stack([oracle.edt(v, samp, features=False)[0] for v in vols])
         _say(f"int64 indices {shape} s={samp}")
         compare(vols, samp, ref, None, None, ix.astype(np.int32), batch=True)
+
+
+def test_channel_axes(torch_dev):
+    """(B, C, H, W) and (B, C, D, H, W) inputs: every (batch, channel) image
+    or volume is transformed on its own."""
+    torch, dev = torch_dev
+    from exact_euclidean_distance_amd import edt2d, edt3d
+    rng = np.random.default_rng([42, 5010])
+    m = (rng.random((2, 3, 40, 70)) >= 0.02).astype(np.uint8)
+    m[1, 2] = 1
+    m[0, 0, 0, 0] = 0
+    r = edt2d(torch.from_numpy(m).to(dev), return_sqdist=True, return_indices=True)
+    torch.cuda.synchronize()
+    assert tuple(r.sqdist.shape) == m.shape
+    flat = m.reshape(-1, 40, 70)
+    ref = np.stack([oracle.edt(x, None, features=False)[0] for x in flat])
+    compare(flat, None, ref, _np(r.sqdist).reshape(flat.shape), _np(r.dist).reshape(flat.shape),
+            _np(r.indices).reshape(flat.shape), batch=True)
+    v = (rng.random((2, 2, 9, 20, 30)) >= 0.02).astype(np.uint8)
+    v[0, 1] = 1
+    v[1, 1, 0, 0, 0] = 0
+    r = edt3d(torch.from_numpy(v).to(dev), (2.5, 1.0, 1.0), return_indices=True)
+    torch.cuda.synchronize()
+    flat = v.reshape(-1, 9, 20, 30)
+    ref = np.stack([oracle.edt(x, (2.5, 1.0, 1.0), features=False)[0] for x in flat])
+    compare(flat, (2.5, 1.0, 1.0), ref, None, _np(r.dist).reshape(flat.shape),
+            _np(r.indices).reshape(flat.shape), batch=True)
