@@ -64,6 +64,8 @@ WORKLOADS = {
     "b2d": "batched 2D: 32 images of 1024x1024 uint8, background i.i.d. Bernoulli(0.01) "
            "per image, isotropic; outputs sqdist + dist + index (flat per image)",
 }
+WORKLOADS["v2048"] = ("3D 64x2048x2048 uint8 (a stack of 2048^2 slices), background i.i.d. "
+                      "Bernoulli(1e-3), isotropic; output float32 dist")
 for _n in (1024, 2048, 4096, 8192):
     for _pct in (1, 99):
         WORKLOADS[f"p1_{_n}_{_pct}"] = (
@@ -79,6 +81,7 @@ OUTPUTS = {
     "b2d": ("sqdist", "dist", "indices"),
 }
 OUTPUTS.update({k: ("dist",) for k in WORKLOADS if k.startswith("p1_")})
+OUTPUTS["v2048"] = ("dist",)
 
 
 def algorithmic_bytes(kernel: str, shape, n_out: int) -> int:

@@ -19,7 +19,7 @@ namespace {
 
 constexpr int32_t kMaxExtent = 65535;
 constexpr int32_t kMaxW2D = 32768;
-constexpr int32_t kMaxH3D = 1024;
+constexpr int32_t kMaxH3D = 32768;
 constexpr int32_t kMaxW3D = 16384;
 constexpr size_t kAlign = 256;
 
@@ -42,6 +42,7 @@ bool shape3d_ok(int32_t B, int32_t D, int32_t H, int32_t W) {
     if (B < 1 || D < 1 || H < 1 || W < 1) return false;
     if (B > kMaxExtent || D > kMaxExtent || H > kMaxExtent || W > kMaxExtent) return false;
     if (H > kMaxH3D || W > kMaxW3D) return false;
+    if (H > 1 && edt::cols_lds_bytes(H) == 0) return false;
     return edt::rows_lds_bytes(W, 4) != 0;
 }
 

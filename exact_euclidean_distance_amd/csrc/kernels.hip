@@ -75,7 +75,8 @@ hipError_t KernelTimer::end(hipStream_t s) {
 // kSegRows rows (so that long, few lines still fill the machine):
 //   summary  per (segment, column), the 64-bit mask of background rows and the
 //            first/last of them;
-//   scan     per column, nearest background strictly above / below each segment;
+//   scan     per column, nearest background strictly above / below each segment
+//            (not needed, and not launched, when a line is a single segment);
 //   resolve  per (segment, column), the nearest background of every row from
 //            the segment's mask plus the two carries (the mask bytes are read
 //            once, by the summary).
@@ -274,8 +275,13 @@ __global__ __launch_bounds__(256) void k_axis0_resolve(const uint64_t* __restric
 #pragma unroll
     for (int v = 0; v < VEC; ++v) bm[v] = bits[so + v];
     uint16_t upc[VEC], dnc[VEC];
-    load_u16<VEC>(up_carry + so, upc);
-    load_u16<VEC>(dn_carry + so, dnc);
+    if (nseg > 1) {
+        load_u16<VEC>(up_carry + so, upc);
+        load_u16<VEC>(dn_carry + so, dnc);
+    } else {   // one segment: nothing above or below it (no scan ran)
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) upc[v] = dnc[v] = kNone16;
+    }
 
     // Per column: the background rows just above (prev) and at or below (next)
     // the current row, and the row where the answer switches from one to the
@@ -335,9 +341,11 @@ hipError_t launch_axis0(const uint8_t* mask, int B, int n0, int64_t M, uint16_t*
     } else {
         EDT_LAUNCH(tm, "axis0_summary", s, hipLaunchKernelGGL(k_axis0_summary<1>, grid_for(1), block, 0, s, mask, n0, M, nseg, first, last, bits));
     }
-    dim3 sgrid((unsigned)((M + 63) / 64), (unsigned)B);
-    dim3 sblock(64, kScanQ);
-    EDT_LAUNCH(tm, "axis0_scan", s, hipLaunchKernelGGL(k_axis0_scan, sgrid, sblock, 0, s, first, last, nseg, M));
+    if (nseg > 1) {   // carries between segments (a single segment has none)
+        dim3 sgrid((unsigned)((M + 63) / 64), (unsigned)B);
+        dim3 sblock(64, kScanQ);
+        EDT_LAUNCH(tm, "axis0_scan", s, hipLaunchKernelGGL(k_axis0_scan, sgrid, sblock, 0, s, first, last, nseg, M));
+    }
     // the resolve keeps per-column state in registers: 4 columns per lane
     if (vec >= 4) {
         EDT_LAUNCH(tm, "axis0_resolve", s, hipLaunchKernelGGL(k_axis0_resolve<4>, grid_for(4), block, 0, s, bits, n0, M, nseg, last, first, c0));
@@ -1387,23 +1395,25 @@ struct ColPlan {
     size_t lds;
 };
 
-// H <= 512: chunks of 32 and 64 / Gp lines per block (at least 8); H <= 1024:
-// chunks of 64 and 32 lines per block (LDS holds TW lines of values and marks; narrower tiles
-// mean smaller blocks, more of them resident per CU).
+// H <= 512: chunks of 32 and 64 / Gp lines per block (at least 8); longer
+// lines: chunks of 64 and 512 / Gp lines per block (32 lines up to H = 1024,
+// one line at H = 32768), so that a block's 512 slots of values and marks
+// stay within the LDS (narrower tiles mean smaller blocks, more of them
+// resident per CU).
 static ColPlan plan_cols(int H) {
     ColPlan p{};
     p.K = H <= 512 ? 32 : 64;
     p.Gp = 1;
     while (p.Gp * p.K < H) p.Gp <<= 1;
     // the narrowest tile that still fills one wave (8 lines at the least)
-    p.TW = p.K == 64 ? 32 : (64 / p.Gp > 8 ? 64 / p.Gp : 8);
+    p.TW = p.K == 64 ? (512 / p.Gp > 0 ? 512 / p.Gp : 0) : (64 / p.Gp > 8 ? 64 / p.Gp : 8);
     p.lds = p.K == 32 ? Slots<uint16_t, 32>::bytes(p.Gp * p.TW, p.Gp) : Slots<uint16_t, 64>::bytes(p.Gp * p.TW, p.Gp);
     return p;
 }
 
 size_t cols_lds_bytes(int H) {
     const ColPlan p = plan_cols(H);
-    return (p.Gp * p.TW > 1024 || p.lds > 160 * 1024) ? 0 : p.lds;
+    return (p.TW < 1 || p.Gp * p.TW > 1024 || p.lds > 160 * 1024) ? 0 : p.lds;
 }
 
 template <int K, int TW>
@@ -1497,7 +1507,17 @@ static hipError_t launch_cols_t(const uint16_t* c0, int B, int D, int H, int W, 
 hipError_t launch_cols_3d(const uint16_t* c0, int B, int D, int H, int W, double s2_0,
                           double s2_1, uint32_t* c01, hipStream_t s, KernelTimer* tm) {
     const ColPlan p = plan_cols(H);
-    if (p.K == 64) return launch_cols_t<64, 32>(c0, B, D, H, W, s2_0, s2_1, c01, p, s, tm);
+    if (p.K == 64) {
+        switch (p.TW) {
+            case 32: return launch_cols_t<64, 32>(c0, B, D, H, W, s2_0, s2_1, c01, p, s, tm);
+            case 16: return launch_cols_t<64, 16>(c0, B, D, H, W, s2_0, s2_1, c01, p, s, tm);
+            case 8: return launch_cols_t<64, 8>(c0, B, D, H, W, s2_0, s2_1, c01, p, s, tm);
+            case 4: return launch_cols_t<64, 4>(c0, B, D, H, W, s2_0, s2_1, c01, p, s, tm);
+            case 2: return launch_cols_t<64, 2>(c0, B, D, H, W, s2_0, s2_1, c01, p, s, tm);
+            case 1: return launch_cols_t<64, 1>(c0, B, D, H, W, s2_0, s2_1, c01, p, s, tm);
+            default: return hipErrorInvalidValue;
+        }
+    }
     switch (p.TW) {
         case 8: return launch_cols_t<32, 8>(c0, B, D, H, W, s2_0, s2_1, c01, p, s, tm);
         case 16: return launch_cols_t<32, 16>(c0, B, D, H, W, s2_0, s2_1, c01, p, s, tm);

@@ -54,7 +54,7 @@
  * when sqdist is requested the largest possible squared distance
  * (sum of extent^2) must fit in int32.  The lower envelope of a line is kept in
  * LDS, which bounds the line lengths of the envelope passes:
- *   2-D: W <= 32768;  3-D: H <= 1024 and W <= 16384.
+ *   2-D: W <= 32768;  3-D: H <= 32768 and W <= 16384.
  * Shapes beyond the limits return EDT_ERR_UNSUPPORTED_SHAPE.
  */
 #ifndef EDT_MI355X_H

@@ -24,6 +24,20 @@ def lib():
     return _lib.load()
 
 
+def _has_gpu():
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:  # pragma: no cover
+        return False
+
+
+# The argument tests pass fake device addresses: a call that validation let
+# through by mistake would launch kernels on them, so they run only where no
+# HIP device exists (the GPU tests cover the same entry points with buffers).
+fake_pointers = pytest.mark.skipif(_has_gpu(), reason="fake device pointers; CPU-only checks")
+
+
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
@@ -49,7 +63,7 @@ def test_workspace_sizes(lib):
     assert lib.edt2d_workspace_size(0, 5) == 0
     assert lib.edt2d_workspace_size(5, 40000) == 0
     assert lib.edt2d_workspace_size(70000, 5) == 0
-    assert lib.edt3d_workspace_size(1, 8, 2000, 8) == 0
+    assert lib.edt3d_workspace_size(1, 8, 40000, 8) == 0   # H over the column-pass limit
     assert lib.edt3d_workspace_size(1, 8, 8, 20000) == 0
     # > 2^31-1 elements: a workspace for distances (indices are refused by the call)
     assert lib.edt3d_workspace_size(1, 2100, 1024, 1000) >= 2100 * 1024 * 1000 * 6
@@ -67,6 +81,7 @@ def call3d(lib, mask=MASK, B=2, D=8, H=8, W=8, sampling=None, sq=SQ, dist=DIST, 
     return lib.edt3d_u8_batched(mask, B, D, H, W, samp, sq, dist, idx, ws, ws_bytes, None)
 
 
+@fake_pointers
 def test_2d_argument_errors(lib):
     assert call2d(lib, mask=None) == INVALID
     assert call2d(lib, H=0) == INVALID
@@ -90,11 +105,12 @@ def test_2d_argument_errors(lib):
     assert call2d(lib, H=50000, W=50000, sampling=None, dist=None, idx=None) == SHAPE
 
 
+@fake_pointers
 def test_3d_argument_errors(lib):
     assert call3d(lib, mask=None) == INVALID
     assert call3d(lib, B=0) == INVALID
     assert call3d(lib, D=0) == INVALID
-    assert call3d(lib, H=2000) == SHAPE
+    assert call3d(lib, H=40000) == SHAPE
     assert call3d(lib, W=20000) == SHAPE
     assert call3d(lib, D=70000) == SHAPE
     assert call3d(lib, sq=None, dist=None, idx=None) == INVALID
@@ -108,6 +124,7 @@ def test_3d_argument_errors(lib):
     assert call3d(lib, B=1, D=2100, H=1024, W=1000, sq=None, dist=None) == SHAPE
 
 
+@fake_pointers
 def test_timed_entry_rejects_without_buffer(lib):
     cnt = ctypes.c_int32(0)
     st = lib.edt2d_u8_timed(MASK, 8, 8, None, SQ, DIST, IDX, WS, BIG, None,
@@ -136,6 +153,7 @@ def call1d(lib, mask=MASK, B=3, N=64, sampling=None, sq=SQ, dist=DIST, idx=IDX, 
     return lib.edt1d_u8_batched(mask, B, N, samp, sq, dist, idx, ws, ws_bytes, None)
 
 
+@fake_pointers
 def test_batched_2d_and_1d_argument_errors(lib):
     assert lib.edt2d_batched_workspace_size(1, 64, 64) == lib.edt2d_workspace_size(64, 64)
     assert lib.edt2d_batched_workspace_size(4, 64, 64) >= 4 * 64 * 64 * 2
@@ -160,6 +178,7 @@ def test_batched_2d_and_1d_argument_errors(lib):
     assert call1d(lib, ws_bytes=lib.edt1d_workspace_size(3, 64) - 1) == SMALL
 
 
+@fake_pointers
 def test_unravel_argument_errors(lib):
     shp = (ctypes.c_int32 * 3)(4, 5, 6)
     assert lib.edt_unravel_indices(None, 1, 3, shp, DIST, None) == INVALID
@@ -176,6 +195,7 @@ def test_unravel_argument_errors(lib):
     assert lib.edt_unravel_indices(IDX, 1, 3, big, DIST, None) == SHAPE
 
 
+@fake_pointers
 def test_brute_argument_errors(lib):
     shp = (ctypes.c_int32 * 3)(8, 9, 10)
     need = lib.edt_brute_workspace_size(2, 3, shp)
@@ -203,6 +223,7 @@ def test_brute_argument_errors(lib):
     assert call(idx=SQ + 4) == INVALID
 
 
+@fake_pointers
 def test_idx64_argument_errors(lib):
     def call(idx=IDX, **kw):
         a = dict(mask=MASK, B=2, D=8, H=8, W=8, samp=None, sq=SQ, dist=DIST, ws=WS, ws_bytes=BIG)
@@ -214,4 +235,4 @@ def test_idx64_argument_errors(lib):
     assert call(idx=SQ + 8) == INVALID                   # overlaps sqdist
     assert call(sq=IDX + 4096) == INVALID                # sqdist inside the int64 indices (2*8*8*8*8 B)
     assert call(ws_bytes=lib.edt3d_workspace_size(2, 8, 8, 8) - 1) == SMALL
-    assert call(H=2000) == SHAPE
+    assert call(H=40000) == SHAPE

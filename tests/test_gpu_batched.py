@@ -469,3 +469,33 @@ def test_channel_axes(torch_dev):
     ref = np.stack([oracle.edt(x, (2.5, 1.0, 1.0), features=False)[0] for x in flat])
     compare(flat, (2.5, 1.0, 1.0), ref, None, _np(r.dist).reshape(flat.shape),
             _np(r.indices).reshape(flat.shape), batch=True)
+
+
+def test_long_middle_axis(torch_dev):
+    """Volumes whose middle axis is longer than 1024 (stacks of 2048^2 and
+    larger slices): column tiles of 512 / Gp lines, down to one line per block
+    at H = 32768; ragged lengths, spacing, and a full background plane."""
+    torch, dev = torch_dev
+    from exact_euclidean_distance_amd import edt3d
+    rng = np.random.default_rng([42, 5011])
+    for shape, p in (((1, 3, 2048, 40), 0.002), ((2, 2, 4100, 17), 0.001), ((1, 2, 16384, 6), 0.0005),
+                     ((1, 1, 32768, 3), 0.0003)):
+        vols = (rng.random(shape) >= p).astype(np.uint8)
+        vols[:, 0, 0, 0] = 0
+        for samp in (None, (2.5, 1.0, 1.0)):
+            iso = samp is None
+            want = ("sqdist", "dist", "indices") if iso else ("dist", "indices")
+            sq, ds, ix = _poisoned(torch, dev, vols.shape, want)
+            edt3d(torch.from_numpy(vols).to(dev), samp, sqdist=sq, dist=ds, indices=ix)
+            torch.cuda.synchronize()
+            ref = np.stack([oracle.edt(v, samp, features=False)[0] for v in vols])
+            _say(f"long middle axis {shape} s={samp}")
+            compare(vols, samp, ref, _np(sq), _np(ds), _np(ix), batch=True)
+    vols = np.ones((1, 4, 3000, 20), np.uint8)
+    vols[0, :, :, 7] = 0                          # full background plane across the last axis
+    vols[0, 1, 1500, :] = 0
+    ref = np.stack([oracle.edt(v, None, features=False)[0] for v in vols])
+    sq, ds, ix = _poisoned(torch, dev, vols.shape, ("sqdist", "dist", "indices"))
+    edt3d(torch.from_numpy(vols).to(dev), sqdist=sq, dist=ds, indices=ix)
+    torch.cuda.synchronize()
+    compare(vols, None, ref, _np(sq), _np(ds), _np(ix), batch=True)

@@ -41,6 +41,8 @@ CONFIGS = {
     "c5": dict(shape=(1, 512, 512, 512), sampling=(2.5, 1.0, 1.0), outputs=("dist", "indices")),
     # batched 2-D (not one of the five headline workloads): 32 images shaped like c1
     "b2d": dict(shape=(32, 1024, 1024), sampling=None, outputs=("sqdist", "dist", "indices")),
+    # a stack of 2048^2 slices (middle axis longer than 1024)
+    "v2048": dict(shape=(1, 64, 2048, 2048), sampling=None, outputs=("dist",)),
 }
 # PR-EDT's own workloads (its §4.1 and Table 1): random square images, seed 42,
 # background ratio 1 % or 99 %; distances timed
@@ -48,7 +50,8 @@ for _n in (1024, 2048, 4096, 8192):
     for _pct in (1, 99):
         CONFIGS[f"p1_{_n}_{_pct}"] = dict(shape=(_n, _n), sampling=None, outputs=("dist",))
 
-_CFG_ID = {"c1": 1, "c2a": 2, "c2b": 2, "c3": 3, "c4": 4, "c5": 5, "stress_row": 6, "b2d": 7}
+_CFG_ID = {"c1": 1, "c2a": 2, "c2b": 2, "c3": 3, "c4": 4, "c5": 5, "stress_row": 6, "b2d": 7,
+           "v2048": 8}
 _CFG_ID.update({f"p1_{n}_{pct}": 100 + 10 * i + pct % 10
                 for i, n in enumerate((1024, 2048, 4096, 8192)) for pct in (1, 99)})
 _SUB_ID = {"c2a": 0, "c2b": 1}
@@ -193,6 +196,9 @@ def make_config(name: str, scale: int = 1):
         n = 1024 // scale
         rng = rng_for(name)
         return np.stack([bernoulli_2d(rng, n, n, 0.01) for _ in range(32)]), None, {}
+    if name == "v2048":
+        n = 2048 // scale
+        return bernoulli_3d(rng_for(name), max(1, 64 // scale), n, n, 1e-3)[None], None, {}
     if name.startswith("p1_"):
         _, n, pct = name.split("_")
         n = int(n) // scale
