@@ -203,8 +203,9 @@ __global__ __launch_bounds__(256) void k_axis0_summary(const uint8_t* __restrict
 
 // After this kernel last[b][s][m] holds the nearest background row above
 // segment s (kNone16 if none) and first[b][s][m] the nearest one below it.
-constexpr int kScanQ = 16;   // segment groups per column (threads along y)
-
+// Q segment groups per column (threads along y): 16 for long columns; few
+// segments are walked by fewer threads (one, for at most 8 segments).
+template <int kScanQ>
 __global__ __launch_bounds__(64 * kScanQ) void k_axis0_scan(uint16_t* __restrict__ first,
                                                             uint16_t* __restrict__ last,
                                                             int nseg, int64_t M) {
@@ -343,8 +344,13 @@ hipError_t launch_axis0(const uint8_t* mask, int B, int n0, int64_t M, uint16_t*
     }
     if (nseg > 1) {   // carries between segments (a single segment has none)
         dim3 sgrid((unsigned)((M + 63) / 64), (unsigned)B);
-        dim3 sblock(64, kScanQ);
-        EDT_LAUNCH(tm, "axis0_scan", s, hipLaunchKernelGGL(k_axis0_scan, sgrid, sblock, 0, s, first, last, nseg, M));
+        if (nseg <= 8) {
+            EDT_LAUNCH(tm, "axis0_scan", s, hipLaunchKernelGGL(k_axis0_scan<1>, sgrid, dim3(64, 1), 0, s, first, last, nseg, M));
+        } else if (nseg <= 32) {
+            EDT_LAUNCH(tm, "axis0_scan", s, hipLaunchKernelGGL(k_axis0_scan<4>, sgrid, dim3(64, 4), 0, s, first, last, nseg, M));
+        } else {
+            EDT_LAUNCH(tm, "axis0_scan", s, hipLaunchKernelGGL(k_axis0_scan<16>, sgrid, dim3(64, 16), 0, s, first, last, nseg, M));
+        }
     }
     // the resolve keeps per-column state in registers: 4 columns per lane
     if (vec >= 4) {
