@@ -8,6 +8,10 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 * :func:`edt_brute` -- the definition, every element against every background
   element, in the same C file (``oracle_edt_brute``).
 * :func:`brute_numpy` -- an independent NumPy transcription of the definition.
+* :func:`taxicab_brute` / :func:`taxicab_to` -- the city-block (L1) distance
+  transform by its definition, and the L1 distance to a given flat index (for
+  the chamfer transforms TorchMorph ships beside its EDT; the pages name them
+  without defining them -- read as the L1 metric, as SciPy's ``taxicab``).
 
 Pinning (see ``tests/test_oracle.py``): hand-derived fixtures under
 ``tests/golden/``, closed forms (one background element, full background
@@ -160,3 +164,47 @@ def sqdist_to(feature_flat, shape, sampling=None):
             d += s2[k] * t * t
         out[r0:r1] = d
     return out
+
+
+def taxicab_brute(mask):
+    """City-block (L1) distance transform by its definition: for every element
+    the minimum over all background elements of sum_k |p_k - b_k| (int64);
+    without background, the virtual element at (-1, 0, ...).  Also returns the
+    flat index of the first (smallest-index) minimiser."""
+    mask = np.asarray(mask)
+    shape = mask.shape
+    coords = np.indices(shape).reshape(mask.ndim, -1).T.astype(np.int64)
+    bgi = np.flatnonzero(mask.reshape(-1) == 0)
+    if len(bgi) == 0:
+        bg = np.zeros((1, mask.ndim), np.int64)
+        bg[0, 0] = -1
+        bgi = np.array([-(int(np.prod(shape[1:])) if mask.ndim > 1 else 1)])
+    else:
+        bg = coords[bgi]
+    out = np.empty(len(coords), np.int64)
+    who = np.empty(len(coords), np.int64)
+    step = max(1, (1 << 22) // len(bg))
+    for i in range(0, len(coords), step):
+        d = np.abs(coords[i:i + step, None, :] - bg[None, :, :]).sum(-1)
+        k = d.argmin(1)
+        out[i:i + step] = d[np.arange(len(k)), k]
+        who[i:i + step] = bgi[k]
+    return out.reshape(shape), who.reshape(shape)
+
+
+def taxicab_to(feature_flat, shape):
+    """L1 distance from every element to the element at the given flat index
+    (same image); negative indices are decoded as the virtual background."""
+    shape = tuple(shape)
+    ndim = len(shape)
+    idx = np.asarray(feature_flat, np.int64).reshape(shape)
+    inner = int(np.prod(shape[1:])) if ndim > 1 else 1
+    a0 = np.floor_divide(idx, inner)
+    rest = idx - a0 * inner
+    comps = [a0]
+    for k in range(1, ndim):
+        st = int(np.prod(shape[k + 1:])) if k + 1 < ndim else 1
+        comps.append(rest // st)
+        rest = rest % st
+    grid = np.indices(shape)
+    return sum(np.abs(grid[k] - comps[k]) for k in range(ndim))

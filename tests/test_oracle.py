@@ -110,3 +110,40 @@ def test_planted_mistake_is_caught(name, tmp_path):
         except AssertionError:
             failed.append(pin.__name__)
     assert failed, f"no pin caught the planted mistake {name}"
+
+
+def test_taxicab_oracle_pins():
+    """The L1 oracle against closed forms: one background element, two, all
+    background, none (virtual element), the 1-D nearest-background case, and
+    the index it returns attains its minimum."""
+    rng = np.random.default_rng([42, 7001])
+    for shape in ((1,), (9,), (7, 11), (5, 6, 7)):
+        m = np.ones(shape, np.uint8)
+        b = tuple(int(rng.integers(n)) for n in shape)
+        m[b] = 0
+        d, who = oracle.taxicab_brute(m)
+        grid = np.indices(shape)
+        assert (d == sum(np.abs(grid[k] - b[k]) for k in range(len(shape)))).all()
+        assert (who == np.ravel_multi_index(b, shape)).all()
+    m = np.ones((6, 9), np.uint8)
+    m[1, 2] = 0
+    m[4, 7] = 0
+    d, _ = oracle.taxicab_brute(m)
+    g = np.indices(m.shape)
+    assert (d == np.minimum(abs(g[0] - 1) + abs(g[1] - 2), abs(g[0] - 4) + abs(g[1] - 7))).all()
+    assert (oracle.taxicab_brute(np.zeros((4, 5), np.uint8))[0] == 0).all()
+    d, who = oracle.taxicab_brute(np.ones((3, 4), np.uint8))
+    assert (d == (g[0][:3, :4] + 1) + g[1][:3, :4]).all() and (who == -4).all()
+    line = (rng.random(200) >= 0.05).astype(np.uint8)
+    line[17] = 0
+    d, _ = oracle.taxicab_brute(line)
+    bgp = np.flatnonzero(line == 0)
+    k = np.searchsorted(bgp, np.arange(200))
+    lo = bgp[np.clip(k - 1, 0, len(bgp) - 1)]
+    hi = bgp[np.clip(k, 0, len(bgp) - 1)]
+    assert (d == np.minimum(np.abs(np.arange(200) - lo), np.abs(hi - np.arange(200)))).all()
+    m = (rng.random((13, 17, 5)) >= 0.1).astype(np.uint8)
+    m[0, 0, 0] = 0
+    d, who = oracle.taxicab_brute(m)
+    assert (oracle.taxicab_to(who, m.shape) == d).all()
+    assert (m.reshape(-1)[who.reshape(-1)] == 0).all()
