@@ -322,6 +322,53 @@ def bench_brute(args):
     return 0
 
 
+def bench_taxicab(args):
+    """Time the city-block transform (int32 distances, plus indices when the
+    workload times them) on a 2-D, batched 2-D or 3-D workload.  Bytes of the
+    path: mask 1 B, axis-0 coordinate 2 + 2 B, (3-D: the middle pass reads the
+    coordinate twice and writes and reads its packed owners, 2 + 2 + 4 + 4 + 4 B),
+    4 B per output."""
+    import torch
+    from exact_euclidean_distance_amd import taxicab
+    from workloads import make_config
+    name = args.config
+    mask_np, _, _ = make_config(name)
+    dev = torch.device("cuda:0")
+    mask = torch.from_numpy(mask_np).to(dev)
+    want_idx = "indices" in OUTPUTS[name]
+    r = taxicab(mask, return_indices=want_idx)
+    for _ in range(args.warmup):
+        taxicab(mask, return_indices=want_idx, dist=r.dist, indices=r.indices)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    stream = torch.cuda.current_stream()
+    e0.record(stream)
+    for _ in range(args.steps):
+        taxicab(mask, return_indices=want_idx, dist=r.dist, indices=r.indices)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / max(1, args.steps)
+    n = mask_np.size
+    per = 1 + 4 + (16 if mask_np.ndim == 4 else 0) + 4 * (2 if want_idx else 1)
+    gbs = n * per / (ms * 1e-3) / 1e9
+    line = {
+        "metric": "city-block (taxicab) transform Gpixel/s at 1 GPU (adjacent operator, not the EDT)",
+        "value": round(n / (ms * 1e-3) / 1e9, 3), "unit": "Gpixel/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int32",
+        "data": "synthetic",
+        "config": {"workload": f"{name}: {WORKLOADS[name]}", "shape": list(mask_np.shape),
+                   "outputs": ["dist"] + (["indices"] if want_idx else [])},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "note": "whole path, bytes per element as in the docstring"},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -332,6 +379,8 @@ def main(argv=None):
     ap.add_argument("--check", action="store_true", help="also compare with the oracle")
     ap.add_argument("--brute", action="store_true",
                     help="time the device brute-force transform (the exactness check) instead")
+    ap.add_argument("--taxicab", action="store_true",
+                    help="time the city-block (L1) transform on the workload instead")
     ap.add_argument("--probe-copy", action="store_true")
     ap.add_argument("--summarize-traffic", nargs=4, metavar="DIR")
     args = ap.parse_args(argv)
@@ -354,6 +403,8 @@ def main(argv=None):
 
     if args.brute:
         return bench_brute(args)
+    if args.taxicab:
+        return bench_taxicab(args)
 
     if not torch.cuda.is_available():
         print("bench.py: no HIP device", file=sys.stderr)

@@ -215,6 +215,37 @@ def edt_brute(mask: torch.Tensor, sampling=None, *, batched: bool = False,
     return EDTResult(sq, ds, ix)
 
 
+def taxicab(mask: torch.Tensor, *, return_indices: bool = False, dist=None, indices=None,
+            workspace=None, stream=None):
+    """City-block (L1) distance transform: int32 distances (and flat indices)
+    of one (H, W) image, a batch (B, H, W), or a batch of volumes
+    (B, D, H, W)."""
+    _check_mask(mask, (2, 3, 4))
+    shape = tuple(mask.shape)
+    dev = mask.device
+    ds = _out(dist, shape, torch.int32, dev, True)
+    ix = _out(indices, shape, torch.int32, dev, return_indices)
+    lib = _lib.load()
+    if mask.dim() == 4:
+        B, D, H, W = shape
+        need = int(lib.edt3d_workspace_size(B, D, H, W))
+    else:
+        B, H, W = (1,) + shape if mask.dim() == 2 else shape
+        need = int(lib.edt2d_batched_workspace_size(B, H, W))
+    if workspace is None:
+        workspace = alloc_workspace(need, dev)
+    wsb = workspace.numel() * workspace.element_size()
+    if mask.dim() == 4:
+        st = lib.edt3d_taxicab_u8_batched(_ptr(mask), B, D, H, W, _ptr(ds), _ptr(ix), _ptr(workspace),
+                                          wsb, _stream(stream))
+    else:
+        st = lib.edt2d_taxicab_u8_batched(_ptr(mask), B, H, W, _ptr(ds), _ptr(ix), _ptr(workspace), wsb,
+                                          _stream(stream))
+    if st != 0:
+        raise EDTError(st, "taxicab")
+    return EDTResult(None, ds, ix)
+
+
 def edt3d(mask: torch.Tensor, sampling=None, *, return_distances: bool = True,
           return_sqdist: bool = False, return_indices: bool = False,
           dist=None, sqdist=None, indices=None, workspace=None, stream=None,

@@ -367,6 +367,50 @@ edt_status edt_brute_u8(const uint8_t* mask, int32_t B, int32_t ndim, const int3
     return EDT_OK;
 }
 
+edt_status edt2d_taxicab_u8_batched(const uint8_t* mask, int32_t B, int32_t H, int32_t W,
+                                    int32_t* dist, int32_t* indices, void* workspace,
+                                    size_t workspace_bytes, hipStream_t stream) {
+    if (B < 1 || H < 1 || W < 1) return EDT_ERR_INVALID_ARGUMENT;
+    if (!shape2d_ok(B, H, W)) return EDT_ERR_UNSUPPORTED_SHAPE;
+    const Layout L = layout2d(B, H, W);
+    edt_status st = check_buffers(mask, (size_t)B * H * W, dist, nullptr, indices, workspace,
+                                  workspace_bytes, L.total);
+    if (st != EDT_OK) return st;
+    char* base = static_cast<char*>(workspace);
+    uint16_t* c0 = reinterpret_cast<uint16_t*>(base + L.c0);
+    if (edt::launch_axis0(mask, B, H, W, reinterpret_cast<uint16_t*>(base + L.first),
+                          reinterpret_cast<uint16_t*>(base + L.last),
+                          reinterpret_cast<uint64_t*>(base + L.bits), c0, stream, nullptr) != hipSuccess)
+        return EDT_ERR_HIP;
+    if (edt::launch_l1_rows_2d(c0, B, H, W, dist, indices, stream, nullptr) != hipSuccess)
+        return EDT_ERR_HIP;
+    return EDT_OK;
+}
+
+edt_status edt3d_taxicab_u8_batched(const uint8_t* mask, int32_t B, int32_t D, int32_t H,
+                                    int32_t W, int32_t* dist, int32_t* indices, void* workspace,
+                                    size_t workspace_bytes, hipStream_t stream) {
+    if (B < 1 || D < 1 || H < 1 || W < 1) return EDT_ERR_INVALID_ARGUMENT;
+    if (!shape3d_ok(B, D, H, W)) return EDT_ERR_UNSUPPORTED_SHAPE;
+    if (indices && (int64_t)D * H * W > INT32_MAX) return EDT_ERR_UNSUPPORTED_SHAPE;
+    const Layout L = layout3d(B, D, H, W);
+    edt_status st = check_buffers(mask, (size_t)B * D * H * W, dist, nullptr, indices, workspace,
+                                  workspace_bytes, L.total);
+    if (st != EDT_OK) return st;
+    char* base = static_cast<char*>(workspace);
+    uint16_t* c0 = reinterpret_cast<uint16_t*>(base + L.c0);
+    uint32_t* c01 = reinterpret_cast<uint32_t*>(base + L.c01);
+    if (edt::launch_axis0(mask, B, D, (int64_t)H * W, reinterpret_cast<uint16_t*>(base + L.first),
+                          reinterpret_cast<uint16_t*>(base + L.last),
+                          reinterpret_cast<uint64_t*>(base + L.bits), c0, stream, nullptr) != hipSuccess)
+        return EDT_ERR_HIP;
+    if (edt::launch_l1_cols_3d(c0, B, D, H, W, c01, stream, nullptr) != hipSuccess)
+        return EDT_ERR_HIP;
+    if (edt::launch_l1_rows_3d(c01, B, D, H, W, dist, indices, stream, nullptr) != hipSuccess)
+        return EDT_ERR_HIP;
+    return EDT_OK;
+}
+
 const char* edt_status_string(edt_status status) {
     switch (status) {
         case EDT_OK: return "EDT_OK";

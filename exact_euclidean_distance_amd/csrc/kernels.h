@@ -24,6 +24,16 @@ struct KernelTimer {
     hipError_t end(hipStream_t s);
 };
 
+// Launch bracket: optional timing events, then the launch error check.
+#define EDT_LAUNCH(tm, kname, stream, ...)                                   \
+    do {                                                                     \
+        if (tm) { hipError_t e_ = (tm)->begin(kname, stream); if (e_ != hipSuccess) return e_; } \
+        __VA_ARGS__;                                                         \
+        hipError_t e2_ = hipGetLastError();                                  \
+        if (e2_ != hipSuccess) return e2_;                                   \
+        if (tm) { hipError_t e_ = (tm)->end(stream); if (e_ != hipSuccess) return e_; } \
+    } while (0)
+
 // Axis-0 pass: for every line along axis 0 (B images of n0 x M elements), the
 // axis-0 coordinate of the nearest background element on that line (kNone16 if
 // the line has none).  first/last: workspace of B * nseg * M uint16 each;
@@ -61,6 +71,16 @@ hipError_t launch_unravel(const int32_t* flat, int64_t images, int64_t per_image
 hipError_t launch_brute(const uint8_t* mask, int B, int ndim, const int* n, const double* s2,
                         int32_t* list, int32_t* counts, int32_t* sqdist, float* dist,
                         int32_t* indices, hipStream_t s);
+
+// City-block (taxicab) transform (chamfer.hip): last-axis pass with int32
+// distances / indices for B images or volumes, and the middle-axis pass of
+// volumes (packed owners, as launch_cols_3d).
+hipError_t launch_l1_rows_2d(const uint16_t* c0, int B, int H, int W, int32_t* dist,
+                             int32_t* indices, hipStream_t s, KernelTimer* tm);
+hipError_t launch_l1_cols_3d(const uint16_t* c0, int B, int D, int H, int W, uint32_t* c01,
+                             hipStream_t s, KernelTimer* tm);
+hipError_t launch_l1_rows_3d(const uint32_t* c01, int B, int D, int H, int W, int32_t* dist,
+                             int32_t* indices, hipStream_t s, KernelTimer* tm);
 
 // Dynamic LDS each envelope launch needs (0 if the line is too long).
 size_t rows_lds_bytes(int L, int value_bytes);

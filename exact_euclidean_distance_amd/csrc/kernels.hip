@@ -60,15 +60,6 @@ hipError_t KernelTimer::end(hipStream_t s) {
     return e;
 }
 
-// Launch bracket: optional timing events, then the launch error check.
-#define EDT_LAUNCH(tm, kname, stream, ...)                                   \
-    do {                                                                     \
-        if (tm) { hipError_t e_ = (tm)->begin(kname, stream); if (e_ != hipSuccess) return e_; } \
-        __VA_ARGS__;                                                         \
-        hipError_t e2_ = hipGetLastError();                                  \
-        if (e2_ != hipSuccess) return e2_;                                   \
-        if (tm) { hipError_t e_ = (tm)->end(stream); if (e_ != hipSuccess) return e_; } \
-    } while (0)
 
 // --------------------------------------------------------------------------
 // Pass 0: nearest background along axis 0, in three kernels over segments of

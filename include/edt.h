@@ -146,6 +146,24 @@ edt_status edt_brute_u8(const uint8_t* mask, int32_t B, int32_t ndim, const int3
                         int32_t* sqdist, float* dist, int32_t* indices,
                         void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* City-block (taxicab, L1) distance transform, one of the chamfer
+   transforms TorchMorph ships beside its EDT (read as the L1 metric, like
+   SciPy's "taxicab"): for every element, min over background elements of
+   sum_k |p_k - b_k|, as int32 (unit spacing), and optionally the flat index of
+   such an element (ties: any).  B images H x W ([B][H][W]) or B volumes
+   D x H x W; an image/volume without background uses the virtual element at
+   (-1, 0, ...) (distance (p0 + 1) + sum_{k>0} p_k, index as above).  dist
+   and/or indices (int32, device, 4-byte aligned); workspace of
+   edt2d_batched_workspace_size / edt3d_workspace_size bytes; the same shape
+   limits as the EDT entry points (volumes with indices: <= 2^31-1 elements);
+   errors as above. */
+edt_status edt2d_taxicab_u8_batched(const uint8_t* mask, int32_t B, int32_t H, int32_t W,
+                                    int32_t* dist, int32_t* indices,
+                                    void* workspace, size_t workspace_bytes, hipStream_t stream);
+edt_status edt3d_taxicab_u8_batched(const uint8_t* mask, int32_t B, int32_t D, int32_t H,
+                                    int32_t W, int32_t* dist, int32_t* indices,
+                                    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Bytes of workspace edt3d_u8_batched needs for B volumes of D x H x W. */
 size_t edt3d_workspace_size(int32_t B, int32_t D, int32_t H, int32_t W);
 

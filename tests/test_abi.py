@@ -236,3 +236,25 @@ def test_idx64_argument_errors(lib):
     assert call(sq=IDX + 4096) == INVALID                # sqdist inside the int64 indices (2*8*8*8*8 B)
     assert call(ws_bytes=lib.edt3d_workspace_size(2, 8, 8, 8) - 1) == SMALL
     assert call(H=40000) == SHAPE
+
+
+@fake_pointers
+def test_taxicab_argument_errors(lib):
+    def c2(mask=MASK, B=2, H=8, W=8, dist=DIST, idx=IDX, ws=WS, ws_bytes=BIG):
+        return lib.edt2d_taxicab_u8_batched(mask, B, H, W, dist, idx, ws, ws_bytes, None)
+
+    def c3(mask=MASK, B=2, D=8, H=8, W=8, dist=DIST, idx=IDX, ws=WS, ws_bytes=BIG):
+        return lib.edt3d_taxicab_u8_batched(mask, B, D, H, W, dist, idx, ws, ws_bytes, None)
+
+    assert c2(mask=None) == INVALID
+    assert c2(B=0) == INVALID
+    assert c2(W=40000) == SHAPE
+    assert c2(dist=None, idx=None) == INVALID
+    assert c2(dist=DIST + 2) == INVALID
+    assert c2(idx=DIST) == INVALID
+    assert c2(ws_bytes=lib.edt2d_batched_workspace_size(2, 8, 8) - 1) == SMALL
+    assert c3(mask=None) == INVALID
+    assert c3(D=0) == INVALID
+    assert c3(W=20000) == SHAPE
+    assert c3(B=1, D=2100, H=1024, W=1000) == SHAPE      # int32 indices of > 2^31 elements
+    assert c3(ws_bytes=lib.edt3d_workspace_size(2, 8, 8, 8) - 1) == SMALL

@@ -499,3 +499,38 @@ def test_long_middle_axis(torch_dev):
     edt3d(torch.from_numpy(vols).to(dev), sqdist=sq, dist=ds, indices=ix)
     torch.cuda.synchronize()
     compare(vols, None, ref, _np(sq), _np(ds), _np(ix), batch=True)
+
+
+def test_taxicab(torch_dev):
+    """City-block transform against the L1 oracle (its definition): exact int32
+    distances, indices attaining them; 2-D, batched 2-D (rows up to 20000 across
+    several waves), batched 3-D, images without background, full background
+    lines."""
+    torch, dev = torch_dev
+    from exact_euclidean_distance_amd import taxicab
+    rng = np.random.default_rng([42, 5012])
+    cases = [(1, 1), (1, 70), (37, 1), (64, 64), (33, 517), (5, 20000), (3, 40, 70),
+             (2, 13, 17, 30), (3, 9, 40, 64), (1, 5, 1100, 33)]
+    for shape in cases:
+        # (dense backgrounds only on small cases: the oracle is a brute force)
+        for p in ((0.003, 0.1, 0.6) if np.prod(shape) <= 20000 else (0.002,)):
+            m = (rng.random(shape) >= p).astype(np.uint8)
+            if len(shape) > 2:
+                m[0] = 1                                 # one image/volume without background
+            m.reshape(-1)[-1] = 0
+            if len(shape) == 2 and shape[0] > 2:
+                m[shape[0] // 2, :] = 0                  # a full background row
+            r = taxicab(torch.from_numpy(m).to(dev), return_indices=True)
+            torch.cuda.synchronize()
+            d = r.dist.cpu().numpy()
+            ix = r.indices.cpu().numpy()
+            batch = [m] if len(shape) == 2 else list(m)
+            dd = [d] if len(shape) == 2 else list(d)
+            ii = [ix] if len(shape) == 2 else list(ix)
+            _say(f"taxicab {shape} p={p}")
+            for mm, d1, i1 in zip(batch, dd, ii):
+                ref, _ = oracle.taxicab_brute(mm)
+                assert (d1 == ref).all(), "taxicab distance mismatch"
+                assert (oracle.taxicab_to(i1, mm.shape) == ref).all(), "index does not attain it"
+                if (mm == 0).any():
+                    assert (mm.reshape(-1)[i1.reshape(-1)] == 0).all()
