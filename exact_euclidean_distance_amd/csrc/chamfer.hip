@@ -11,14 +11,17 @@
 // taken over packed 64-bit keys ((value + offset) << 32 | j), so that one
 // integer minimum gives both the value and its (smallest) position.
 //
-//   k_l1_rows   last axis + outputs: lane g of a line holds K = 32 consecutive
-//               positions; in-chunk prefix minima stay in registers, the
-//               chunks of a line are joined by segmented wave shuffles (and
-//               LDS across the waves of a long line), then a backward sweep
-//               adds the suffix minima and writes int32 distances and indices.
+//   k_l1_rows   last axis + outputs: a wave takes tiles of 256 positions of a
+//               line, four consecutive positions per lane (coalesced loads
+//               and stores); prefix minima in a forward sweep and suffix
+//               minima in a backward one, each in-lane, then by a wave scan,
+//               then across tiles (and across the waves of a long line
+//               through LDS); the keys carry the owner's source value, so
+//               the index needs no second read.
 //   k_l1_cols   middle axis of a volume: one lane per line (neighbouring lanes,
 //               neighbouring columns), a forward sweep storing the prefix
-//               owners and a backward sweep finishing them.
+//               owners and a backward sweep finishing them, both reading
+//               batches of rows so that many loads are in flight.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -28,7 +31,6 @@ namespace edt {
 
 namespace {
 
-constexpr int kL1K = 32;                       // positions per lane (last axis)
 constexpr int64_t kL1Off = int64_t(1) << 20;   // keeps g - j + offset positive
 constexpr uint64_t kL1Inf = ~uint64_t(0);
 
@@ -79,104 +81,186 @@ struct L1Rows3D {
     __device__ int32_t virt_index() const { return -(H * W); }
 };
 
-// Gp lanes per line (power of two, Gp * kL1K >= L), LPW lines per block of
-// max(Gp, 64) threads.  For Gp > 64 the line spans Gp / 64 waves.
-template <class Geo>
+// Keys of the row pass: value << 47 | position << 32 | source value.  The
+// value is below 2^17 (g <= 65534 + 32767, rows of at most 32768, offset
+// 2^15 on the forward side) and the position below 2^15, so one unsigned
+// minimum gives the smallest value, then the smallest position, and carries
+// the owner's source value along for its index.
+constexpr int kRowOff = 1 << 15;   // g(j) - j + kRowOff >= 1
+
+__device__ inline uint64_t row_key(int val, int j, uint32_t v) {
+    return ((uint64_t)(uint32_t)val << 47) | ((uint64_t)(uint32_t)j << 32) | v;
+}
+__device__ inline int row_val(uint64_t k) { return (int)(k >> 47); }
+__device__ inline int row_pos(uint64_t k) { return (int)((k >> 32) & 0x7FFFu); }
+
+__device__ inline uint64_t wave_prefix_min(uint64_t x, int lane) {   // lanes <= lane
+    for (int d = 1; d < 64; d <<= 1) {
+        const uint64_t u = __shfl_up(x, d, 64);
+        if (lane >= d) x = umin64(x, u);
+    }
+    return x;
+}
+__device__ inline uint64_t wave_suffix_min(uint64_t x, int lane) {   // lanes >= lane
+    for (int d = 1; d < 64; d <<= 1) {
+        const uint64_t u = __shfl_down(x, d, 64);
+        if (lane + d < 64) x = umin64(x, u);
+    }
+    return x;
+}
+__device__ inline uint64_t wave_min(uint64_t x) {
+    for (int d = 1; d < 64; d <<= 1) x = umin64(x, __shfl_xor(x, d, 64));
+    return x;
+}
+
+// Last axis + outputs.  A wave owns a segment of T tiles of 256 positions of a
+// line; in tile t lane l holds the four positions 256 t + 4 l + (0..3), so that
+// loads and stores are coalesced 8- or 16-byte pieces.  A forward sweep over
+// the tiles takes prefix minima of the forward keys (in-lane, then a wave scan,
+// then the running minimum of the tiles before); a backward sweep takes the
+// suffix minima the same way and writes each position's nearer side.  NW == 1:
+// four lines per block, one per wave; NW > 1: one line per block, its NW waves
+// joined through the per-wave minima in LDS.
+template <class Geo, int T>
 __global__ __launch_bounds__(1024) void k_l1_rows(const typename Geo::Val* __restrict__ in, int L,
-                                                  int64_t nlines, int lgGp, Geo geo,
+                                                  int64_t nlines, int NW, int vec, Geo geo,
                                                   int32_t* __restrict__ dist,
                                                   int32_t* __restrict__ indices) {
     using Val = typename Geo::Val;
-    __shared__ uint64_t wf[16], wb[16];   // per-wave totals of a long line
-    const int Gp = 1 << lgGp;
-    const int tid = threadIdx.x;
-    const int g = tid & (Gp - 1);
-    const int64_t line = (int64_t)blockIdx.x * (blockDim.x >> lgGp) + (tid >> lgGp);
-    const bool active = line < nlines;
-    const unsigned c = geo.ctx(active ? line : 0);
-    const Val* src = in + (active ? line : 0) * (int64_t)L;
-    const int p0 = g * kL1K;
+    constexpr Val kNone = (Val)~Val(0);
+    __shared__ uint64_t wtf[16], wtb[16];   // per-wave minima of a line of several waves
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int64_t line = NW == 1 ? (int64_t)blockIdx.x * (blockDim.x >> 6) + w : (int64_t)blockIdx.x;
+    if (line >= nlines) return;   // only when NW == 1: no barrier follows there
+    const int seg0 = NW == 1 ? 0 : w * (T * 256);
+    const unsigned c = geo.ctx(line);
+    const Val* src = in + line * (int64_t)L;
 
-    // in-chunk prefix minima of the forward keys (kept as the winner's offset
-    // in the chunk, 8 bits each, 0xFF: none yet), and the chunk's backward minimum
-    uint32_t pk[kL1K / 4];
-    uint64_t run = kL1Inf, bmin = kL1Inf;
-    uint32_t woff = 0xFFu;
+    Val v[T][4];
 #pragma unroll
-    for (int t = 0; t < kL1K; ++t) {
-        const int p = p0 + t;
-        if (active && p < L) {
-            const Val v = src[p];
-            if (Geo::valid(v)) {
-                const int gv = geo.g(c, v);
-                const uint64_t kf = l1_key((int64_t)gv - p, p);
-                if (kf < run) { run = kf; woff = (uint32_t)t; }
-                bmin = umin64(bmin, l1_key((int64_t)gv + p, p));
+    for (int t = 0; t < T; ++t) {
+        const int p = seg0 + 256 * t + 4 * lane;
+        if (vec && p < L) {   // L % 4 == 0: the whole piece is in the line
+            if constexpr (sizeof(Val) == 4) {
+                const uint4 x = *reinterpret_cast<const uint4*>(src + p);
+                v[t][0] = x.x; v[t][1] = x.y; v[t][2] = x.z; v[t][3] = x.w;
+            } else {
+                const uint2 x = *reinterpret_cast<const uint2*>(src + p);
+                v[t][0] = (Val)x.x; v[t][1] = (Val)(x.x >> 16); v[t][2] = (Val)x.y; v[t][3] = (Val)(x.y >> 16);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[t][i] = p + i < L ? src[p + i] : kNone;
+        }
+    }
+    auto kf = [&](int t, int i) -> uint64_t {   // forward key of a position (none: all ones)
+        const Val x = v[t][i];
+        const int p = seg0 + 256 * t + 4 * lane + i;
+        return Geo::valid(x) ? row_key(geo.g(c, x) - p + kRowOff, p, (uint32_t)x) : kL1Inf;
+    };
+    auto kb = [&](int t, int i) -> uint64_t {   // backward key
+        const Val x = v[t][i];
+        const int p = seg0 + 256 * t + 4 * lane + i;
+        return Geo::valid(x) ? row_key(geo.g(c, x) + p, p, (uint32_t)x) : kL1Inf;
+    };
+
+    uint64_t cf = kL1Inf, cb = kL1Inf;   // minima over the positions before / after the segment
+    if (NW > 1) {
+        uint64_t tf = kL1Inf, tb = kL1Inf;
+#pragma unroll
+        for (int t = 0; t < T; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                tf = umin64(tf, kf(t, i));
+                tb = umin64(tb, kb(t, i));
+            }
+        tf = wave_min(tf);
+        tb = wave_min(tb);
+        if (lane == 0) {
+            wtf[w] = tf;
+            wtb[w] = tb;
+        }
+        __syncthreads();
+        for (int k = 0; k < w; ++k) cf = umin64(cf, wtf[k]);
+        for (int k = w + 1; k < NW; ++k) cb = umin64(cb, wtb[k]);
+    }
+
+    // forward sweep: fx[t] = minimum over the positions before this lane's piece
+    uint64_t fx[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+        uint64_t a = kL1Inf;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a = umin64(a, kf(t, i));
+        const uint64_t inc = wave_prefix_min(a, lane);
+        uint64_t ex = __shfl_up(inc, 1, 64);
+        if (lane == 0) ex = kL1Inf;
+        fx[t] = umin64(ex, cf);
+        cf = umin64(cf, __shfl(inc, 63, 64));
+    }
+
+    // backward sweep and outputs
+    const bool vout = vec != 0;
+    int32_t* drow = dist ? dist + line * (int64_t)L : nullptr;
+    int32_t* irow = indices ? indices + line * (int64_t)L : nullptr;
+#pragma unroll
+    for (int t = T - 1; t >= 0; --t) {
+        uint64_t b = kL1Inf;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) b = umin64(b, kb(t, i));
+        const uint64_t sinc = wave_suffix_min(b, lane);
+        uint64_t rb = __shfl_down(sinc, 1, 64);
+        if (lane == 63) rb = kL1Inf;
+        rb = umin64(rb, cb);
+        cb = umin64(cb, __shfl(sinc, 0, 64));
+
+        const int p = seg0 + 256 * t + 4 * lane;
+        if (p >= L) continue;
+        uint64_t f[4];
+        uint64_t run = fx[t];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            run = umin64(run, kf(t, i));
+            f[i] = run;
+        }
+        int out[4];
+        int32_t ix[4];
+#pragma unroll
+        for (int i = 3; i >= 0; --i) {
+            rb = umin64(rb, kb(t, i));
+            const int q = p + i;
+            if (f[i] == kL1Inf && rb == kL1Inf) {   // no background in the image
+                out[i] = geo.virt(c, q);
+                ix[i] = geo.virt_index();
+            } else {
+                const int vf = f[i] == kL1Inf ? INT32_MAX : row_val(f[i]) - kRowOff + q;
+                const int vb = rb == kL1Inf ? INT32_MAX : row_val(rb) - q;
+                const uint64_t k = vf <= vb ? f[i] : rb;
+                out[i] = vf <= vb ? vf : vb;
+                ix[i] = geo.index(c, (Val)(uint32_t)k, row_pos(k));
             }
         }
-        if ((t & 3) == 0) pk[t >> 2] = 0;
-        pk[t >> 2] |= woff << (8 * (t & 3));
-    }
-    // exclusive minima over the chunks before (forward) and after (backward)
-    const int S = Gp < 64 ? Gp : 64;   // chunks of the line in this wave
-    const int pos = g & (S - 1);
-    uint64_t fx = run, bx = bmin;
-    for (int d = 1; d < S; d <<= 1) {
-        const uint64_t u = __shfl_up(fx, d, S);
-        const uint64_t w = __shfl_down(bx, d, S);
-        if (pos >= d) fx = umin64(fx, u);
-        if (pos + d < S) bx = umin64(bx, w);
-    }
-    uint64_t fe = __shfl_up(fx, 1, S), be = __shfl_down(bx, 1, S);
-    if (pos == 0) fe = kL1Inf;
-    if (pos == S - 1) be = kL1Inf;
-    if (Gp > 64) {   // the waves of one long line (one line per block)
-        const int wv = tid >> 6, nw = Gp >> 6;
-        if ((tid & 63) == 63) wf[wv] = fx;
-        if ((tid & 63) == 0) wb[wv] = bx;
-        __syncthreads();
-        for (int k = 0; k < wv; ++k) fe = umin64(fe, wf[k]);
-        for (int k = wv + 1; k < nw; ++k) be = umin64(be, wb[k]);
-    }
-    if (!active || p0 >= L) return;
-
-    // backward sweep: suffix minima, combined with the forward ones
-    int32_t* dst = dist ? dist + line * (int64_t)L : nullptr;
-    int32_t* ixd = indices ? indices + line * (int64_t)L : nullptr;
-    uint64_t rb = be;
+        if (vout) {
+            if (drow) *reinterpret_cast<int4*>(drow + p) = make_int4(out[0], out[1], out[2], out[3]);
+            if (irow) *reinterpret_cast<int4*>(irow + p) = make_int4(ix[0], ix[1], ix[2], ix[3]);
+        } else {
 #pragma unroll
-    for (int t = kL1K - 1; t >= 0; --t) {
-        const int p = p0 + t;
-        if (p < L) {
-            const Val v = src[p];
-            if (Geo::valid(v)) rb = umin64(rb, l1_key((int64_t)geo.g(c, v) + p, p));
-            const uint32_t o = (pk[t >> 2] >> (8 * (t & 3))) & 0xFFu;
-            uint64_t kf = fe;
-            if (o != 0xFFu) {
-                const int jf = p0 + (int)o;
-                kf = umin64(kf, l1_key((int64_t)geo.g(c, src[jf]) - jf, jf));
+            for (int i = 0; i < 4; ++i) {
+                if (p + i < L) {
+                    if (drow) drow[p + i] = out[i];
+                    if (irow) irow[p + i] = ix[i];
+                }
             }
-            int out;
-            int32_t ix;
-            if (kf == kL1Inf && rb == kL1Inf) {   // no background in the image
-                out = geo.virt(c, p);
-                ix = geo.virt_index();
-            } else {
-                const int64_t vf = kf == kL1Inf ? INT64_MAX : l1_val(kf) + p;
-                const int64_t vb = rb == kL1Inf ? INT64_MAX : l1_val(rb) - p;
-                const bool f = vf <= vb;
-                const int j = f ? l1_arg(kf) : l1_arg(rb);
-                out = (int)(f ? vf : vb);
-                ix = geo.index(c, src[j], j);
-            }
-            if (dst) dst[p] = out;
-            if (ixd) ixd[p] = ix;
         }
     }
 }
 
 // Middle axis of B volumes: lines along axis 1 at fixed (volume, d, w); input
 // the axis-0 nearest coordinate, output packed (axis0 << 16 | axis1) owners.
+// Rows are read kColBatch at a time, so that a lane keeps that many loads in
+// flight instead of one.
+constexpr int kColBatch = 16;
+
 __global__ __launch_bounds__(256) void k_l1_cols(const uint16_t* __restrict__ c0,
                                                  uint32_t* __restrict__ out, int D, int H, int W,
                                                  int64_t nlines) {
@@ -190,35 +274,56 @@ __global__ __launch_bounds__(256) void k_l1_cols(const uint16_t* __restrict__ c0
     // forward: owner of the smallest g(j) - j over j <= y
     uint64_t run = kL1Inf;
     uint32_t rz = 0;
-    for (int y = 0; y < H; ++y) {
-        const uint16_t v = src[(int64_t)y * W];
-        if (v != kNone16) {
-            const int gv = d > (int)v ? d - (int)v : (int)v - d;
-            const uint64_t k = l1_key((int64_t)gv - y, y);
-            if (k < run) { run = k; rz = v; }
+    for (int y0 = 0; y0 < H; y0 += kColBatch) {
+        uint16_t vb[kColBatch];
+#pragma unroll
+        for (int i = 0; i < kColBatch; ++i) vb[i] = y0 + i < H ? src[(int64_t)(y0 + i) * W] : kNone16;
+#pragma unroll
+        for (int i = 0; i < kColBatch; ++i) {
+            const int y = y0 + i;
+            if (y >= H) break;
+            const uint16_t v = vb[i];
+            if (v != kNone16) {
+                const int gv = d > (int)v ? d - (int)v : (int)v - d;
+                const uint64_t k = l1_key((int64_t)gv - y, y);
+                if (k < run) { run = k; rz = v; }
+            }
+            dst[(int64_t)y * W] = run == kL1Inf ? kNone32 : ((rz << 16) | (uint32_t)l1_arg(run));
         }
-        dst[(int64_t)y * W] = run == kL1Inf ? kNone32 : ((rz << 16) | (uint32_t)l1_arg(run));
     }
     // backward: owner of the smallest g(j) + j over j >= y; keep the nearer
     run = kL1Inf;
     rz = 0;
-    for (int y = H - 1; y >= 0; --y) {
-        const uint16_t v = src[(int64_t)y * W];
-        if (v != kNone16) {
-            const int gv = d > (int)v ? d - (int)v : (int)v - d;
-            const uint64_t k = l1_key((int64_t)gv + y, y);
-            if (k < run) { run = k; rz = v; }
+    for (int y0 = ((H - 1) / kColBatch) * kColBatch; y0 >= 0; y0 -= kColBatch) {
+        uint16_t vb[kColBatch];
+        uint32_t fb[kColBatch];
+#pragma unroll
+        for (int i = 0; i < kColBatch; ++i) {
+            const bool in = y0 + i < H;
+            vb[i] = in ? src[(int64_t)(y0 + i) * W] : kNone16;
+            fb[i] = in ? dst[(int64_t)(y0 + i) * W] : kNone32;
         }
-        if (run == kL1Inf) continue;   // the forward owner (or none) stands
-        const uint32_t f = dst[(int64_t)y * W];
-        const int64_t vb = l1_val(run) - y;
-        bool take_b = true;
-        if (f != kNone32) {
-            const int z = (int)(f >> 16), yf = (int)(f & 0xFFFFu);
-            const int64_t vf = (d > z ? d - z : z - d) + (y - yf);
-            take_b = vb < vf;
+#pragma unroll
+        for (int i = kColBatch - 1; i >= 0; --i) {
+            const int y = y0 + i;
+            if (y >= H) continue;
+            const uint16_t v = vb[i];
+            if (v != kNone16) {
+                const int gv = d > (int)v ? d - (int)v : (int)v - d;
+                const uint64_t k = l1_key((int64_t)gv + y, y);
+                if (k < run) { run = k; rz = v; }
+            }
+            if (run == kL1Inf) continue;   // the forward owner (or none) stands
+            const uint32_t f = fb[i];
+            const int64_t vbk = l1_val(run) - y;
+            bool take_b = true;
+            if (f != kNone32) {
+                const int z = (int)(f >> 16), yf = (int)(f & 0xFFFFu);
+                const int64_t vf = (d > z ? d - z : z - d) + (y - yf);
+                take_b = vbk < vf;
+            }
+            if (take_b) dst[(int64_t)y * W] = (rz << 16) | (uint32_t)l1_arg(run);
         }
-        if (take_b) dst[(int64_t)y * W] = (rz << 16) | (uint32_t)l1_arg(run);
     }
 }
 
@@ -227,16 +332,27 @@ namespace {
 template <class Geo>
 hipError_t launch_l1_rows_t(const typename Geo::Val* in, int L, int64_t nlines, const Geo& geo,
                             int32_t* dist, int32_t* indices, hipStream_t s, KernelTimer* tm) {
-    int lg = 0;
-    while ((kL1K << lg) < L) ++lg;
-    if (lg > 10) return hipErrorInvalidValue;   // more than 1024 lanes
-    const int Gp = 1 << lg;
-    const int threads = Gp < 64 ? 64 : Gp;
-    const int64_t per_block = threads >> lg;
-    const int64_t blocks = (nlines + per_block - 1) / per_block;
-    EDT_LAUNCH(tm, "taxicab_rows", s,
-               hipLaunchKernelGGL(k_l1_rows<Geo>, dim3((unsigned)blocks), dim3(threads), 0, s, in, L,
-                                  nlines, lg, geo, dist, indices));
+    using Val = typename Geo::Val;
+    const int T = L <= 256 ? 1 : L <= 512 ? 2 : L <= 16384 ? 4 : 8;
+    const int NW = (L + 256 * T - 1) / (256 * T);
+    if (L > 32768 || NW > 16) return hipErrorInvalidValue;
+    const int threads = NW == 1 ? 256 : 64 * NW;
+    const int64_t blocks = NW == 1 ? (nlines + 3) / 4 : nlines;
+    if (blocks > INT32_MAX) return hipErrorInvalidValue;
+    const bool al_in = ((uintptr_t)in % (4 * sizeof(Val))) == 0;
+    const bool al_out = ((uintptr_t)dist % 16) == 0 && ((uintptr_t)indices % 16) == 0;
+    const int vec = (L % 4 == 0 && al_in && al_out) ? 1 : 0;
+#define EDT_L1_ROWS(TT)                                                                          \
+    EDT_LAUNCH(tm, "taxicab_rows", s,                                                            \
+               hipLaunchKernelGGL((k_l1_rows<Geo, TT>), dim3((unsigned)blocks), dim3(threads), 0, s, \
+                                  in, L, nlines, NW, vec, geo, dist, indices))
+    switch (T) {
+        case 1: EDT_L1_ROWS(1); break;
+        case 2: EDT_L1_ROWS(2); break;
+        case 4: EDT_L1_ROWS(4); break;
+        default: EDT_L1_ROWS(8); break;
+    }
+#undef EDT_L1_ROWS
     return hipSuccess;
 }
 
