@@ -192,6 +192,23 @@ def taxicab_brute(mask):
     return out.reshape(shape), who.reshape(shape)
 
 
+def taxicab_at(mask, points):
+    """City-block (L1) distance by its definition at the elements with the given
+    flat indices, one by one: the minimum over all background elements of
+    sum_k |p_k - b_k| (int64); without background, the virtual element at
+    (-1, 0, ...).  For sampled checks of images too large for taxicab_brute."""
+    mask = np.asarray(mask)
+    pts = np.stack(np.unravel_index(np.asarray(points, np.int64), mask.shape), 1).astype(np.int64)
+    bg = np.argwhere(mask == 0).astype(np.int64)
+    if len(bg) == 0:
+        bg = np.zeros((1, mask.ndim), np.int64)
+        bg[0, 0] = -1
+    out = np.empty(len(pts), np.int64)
+    for i, p in enumerate(pts):
+        out[i] = np.abs(bg - p[None, :]).sum(1).min()
+    return out
+
+
 def taxicab_to(feature_flat, shape):
     """L1 distance from every element to the element at the given flat index
     (same image); negative indices are decoded as the virtual background."""

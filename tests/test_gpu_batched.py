@@ -509,8 +509,10 @@ def test_taxicab(torch_dev):
     torch, dev = torch_dev
     from exact_euclidean_distance_amd import taxicab
     rng = np.random.default_rng([42, 5012])
-    cases = [(1, 1), (1, 70), (37, 1), (64, 64), (33, 517), (5, 20000), (3, 40, 70),
-             (2, 13, 17, 30), (3, 9, 40, 64), (1, 5, 1100, 33)]
+    # rows of 1, 2, 4 and 8 tiles of 256, of one wave and of several
+    cases = [(1, 1), (1, 70), (37, 1), (64, 64), (4, 300), (33, 517), (3, 1100), (5, 20000),
+             (3, 40, 70), (2, 13, 17, 30), (3, 9, 40, 64), (2, 3, 5, 400), (1, 5, 1100, 33),
+             (1, 2, 3, 2000)]
     for shape in cases:
         # (dense backgrounds only on small cases: the oracle is a brute force)
         for p in ((0.003, 0.1, 0.6) if np.prod(shape) <= 20000 else (0.002,)):
@@ -534,3 +536,44 @@ def test_taxicab(torch_dev):
                 assert (oracle.taxicab_to(i1, mm.shape) == ref).all(), "index does not attain it"
                 if (mm == 0).any():
                     assert (mm.reshape(-1)[i1.reshape(-1)] == 0).all()
+
+
+@pytest.mark.parametrize("name", ["b2d", "c5", "c3"])
+def test_taxicab_full_size(torch_dev, name):
+    """City-block transform at the full sizes that bench.py --taxicab times, in
+    the same launch shapes: over the whole output, every index names a
+    background element of its image at exactly the returned L1 distance
+    (checked on the device), and sampled elements plus the corners equal
+    the definition's minimum (oracle, one by one)."""
+    torch, dev = torch_dev
+    from workloads import make_config
+    from exact_euclidean_distance_amd import taxicab
+    mask, _, _ = make_config(name)
+    _say(f"taxicab full size {name} {mask.shape}")
+    m = torch.from_numpy(mask).to(dev)
+    r = taxicab(m, return_indices=True)
+    torch.cuda.synchronize()
+    img = mask.shape[1:] if mask.ndim >= 3 else mask.shape   # one image / volume
+    nb = mask.shape[0] if mask.ndim >= 3 else 1
+    per = int(np.prod(img))
+    d = r.dist.reshape(nb, per).long()
+    ix = r.indices.reshape(nb, per).long()
+    assert (ix >= 0).all(), "every benchmark image has background"
+    assert (torch.gather(m.reshape(nb, per), 1, ix) == 0).all()
+    flat = torch.arange(per, device=dev)
+    l1 = torch.zeros_like(d)
+    div = per
+    for n in img:                      # decode axis by axis, first axis first
+        div //= n
+        a = (flat // div) % n
+        b = (ix // div) % n
+        l1 += (a[None, :] - b).abs()
+    assert (l1 == d).all(), "an index does not attain the returned distance"
+    rng = np.random.default_rng([42, 5013])
+    dh = d.cpu().numpy()
+    # (fewer samples where the background is large: each is a pass over all of it)
+    ns = 384 if (mask == 0).sum() < 10**6 else 24
+    for k in range(nb if nb <= 2 else 2):
+        pts = np.concatenate([rng.integers(0, per, ns // min(nb, 2)), [0, per - 1]])
+        ref = oracle.taxicab_at(mask[k] if mask.ndim >= 3 else mask, pts)
+        assert (dh[k][pts] == ref).all(), f"sampled distance mismatch in image {k}"

@@ -147,3 +147,23 @@ def test_taxicab_oracle_pins():
     d, who = oracle.taxicab_brute(m)
     assert (oracle.taxicab_to(who, m.shape) == d).all()
     assert (m.reshape(-1)[who.reshape(-1)] == 0).all()
+
+
+def test_taxicab_at_pins():
+    """The one-by-one L1 oracle: the closed form for one background element and
+    for none (virtual element at (-1, 0, ...)), and the pinned brute-force
+    transform at every element of random 2-D and 3-D masks."""
+    rng = np.random.default_rng([42, 7002])
+    m = np.ones((8, 9, 10), np.uint8)
+    m[3, 7, 2] = 0
+    pts = rng.integers(0, m.size, 50)
+    z, y, x = np.unravel_index(pts, m.shape)
+    assert (oracle.taxicab_at(m, pts) == abs(z - 3) + abs(y - 7) + abs(x - 2)).all()
+    e = np.ones((6, 7), np.uint8)
+    r, c = np.unravel_index(np.arange(e.size), e.shape)
+    assert (oracle.taxicab_at(e, np.arange(e.size)) == (r + 1) + c).all()
+    for shape, p in (((23, 31), 0.05), ((7, 9, 11), 0.02)):
+        m = (rng.random(shape) >= p).astype(np.uint8)
+        m.reshape(-1)[5] = 0
+        d, _ = oracle.taxicab_brute(m)
+        assert (oracle.taxicab_at(m, np.arange(m.size)) == d.reshape(-1)).all()
