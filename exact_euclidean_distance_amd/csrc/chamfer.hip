@@ -259,7 +259,7 @@ __global__ __launch_bounds__(1024) void k_l1_rows(const typename Geo::Val* __res
 // the axis-0 nearest coordinate, output packed (axis0 << 16 | axis1) owners.
 // Rows are read kColBatch at a time, so that a lane keeps that many loads in
 // flight instead of one.
-constexpr int kColBatch = 16;
+constexpr int kColBatch = 8;
 
 __global__ __launch_bounds__(256) void k_l1_cols(const uint16_t* __restrict__ c0,
                                                  uint32_t* __restrict__ out, int D, int H, int W,
