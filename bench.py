@@ -381,6 +381,8 @@ def main(argv=None):
                     help="time the device brute-force transform (the exactness check) instead")
     ap.add_argument("--taxicab", action="store_true",
                     help="time the city-block (L1) transform on the workload instead")
+    ap.add_argument("--graph", action="store_true",
+                    help="time replays of a HIP graph holding one transform (launch gaps removed)")
     ap.add_argument("--probe-copy", action="store_true")
     ap.add_argument("--summarize-traffic", nargs=4, metavar="DIR")
     args = ap.parse_args(argv)
@@ -428,14 +430,23 @@ def main(argv=None):
         fn = edt3d
     stream = torch.cuda.current_stream()
 
-    def step(timed=False):
+    def step(timed=False, s=stream):
         return fn(mask, sampling, sqdist=sq, dist=ds, indices=ix, return_distances=ds is not None,
-                  workspace=ws, stream=stream, timed=timed)
+                  workspace=ws, stream=s, timed=timed)
 
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+
+    graph = None
+    if args.graph:   # one transform captured once; each timed step is one replay
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step(s=torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
 
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
     e0 = torch.cuda.Event(enable_timing=True)
@@ -443,7 +454,10 @@ def main(argv=None):
     torch.cuda.synchronize()
     e0.record(stream)
     for _ in range(args.steps):
-        step()
+        if graph is not None:
+            graph.replay()
+        else:
+            step()
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / max(1, args.steps)
@@ -500,7 +514,8 @@ def main(argv=None):
         "dtype": "f64",
         "data": "synthetic",
         "config": {"workload": f"{name}: {WORKLOADS[name]}", "shape": list(shape),
-                   "sampling": list(sampling) if sampling else None, "outputs": list(want)},
+                   "sampling": list(sampling) if sampling else None, "outputs": list(want),
+                   "launch": "graph" if graph is not None else "stream"},
         "roofline": {"bound": "hbm", "kernel": dom["name"], "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic},
