@@ -192,6 +192,67 @@ def taxicab_brute(mask):
     return out.reshape(shape), who.reshape(shape)
 
 
+def chessboard_brute(mask):
+    """Chessboard (L-infinity) distance transform by its definition: for every
+    element the minimum over all background elements of max_k |p_k - b_k|
+    (int64); without background, the virtual element at (-1, 0, ...).  Also
+    returns the flat index of the first (smallest-index) minimiser."""
+    mask = np.asarray(mask)
+    shape = mask.shape
+    coords = np.indices(shape).reshape(mask.ndim, -1).T.astype(np.int64)
+    bgi = np.flatnonzero(mask.reshape(-1) == 0)
+    if len(bgi) == 0:
+        bg = np.zeros((1, mask.ndim), np.int64)
+        bg[0, 0] = -1
+        bgi = np.array([-(int(np.prod(shape[1:])) if mask.ndim > 1 else 1)])
+    else:
+        bg = coords[bgi]
+    out = np.empty(len(coords), np.int64)
+    who = np.empty(len(coords), np.int64)
+    step = max(1, (1 << 22) // len(bg))
+    for i in range(0, len(coords), step):
+        d = np.abs(coords[i:i + step, None, :] - bg[None, :, :]).max(-1)
+        k = d.argmin(1)
+        out[i:i + step] = d[np.arange(len(k)), k]
+        who[i:i + step] = bgi[k]
+    return out.reshape(shape), who.reshape(shape)
+
+
+def chessboard_at(mask, points):
+    """Chessboard (L-infinity) distance by its definition at the elements with
+    the given flat indices, one by one (int64; virtual element without
+    background).  For sampled checks of large images."""
+    mask = np.asarray(mask)
+    pts = np.stack(np.unravel_index(np.asarray(points, np.int64), mask.shape), 1).astype(np.int64)
+    bg = np.argwhere(mask == 0).astype(np.int64)
+    if len(bg) == 0:
+        bg = np.zeros((1, mask.ndim), np.int64)
+        bg[0, 0] = -1
+    out = np.empty(len(pts), np.int64)
+    for i, p in enumerate(pts):
+        out[i] = np.abs(bg - p[None, :]).max(1).min()
+    return out
+
+
+def chessboard_to(feature_flat, shape):
+    """L-infinity distance from every element to the element at the given flat
+    index (same image); negative indices are decoded as the virtual background
+    (floor division: -(n1 * ... ) becomes (-1, 0, ...))."""
+    shape = tuple(shape)
+    ndim = len(shape)
+    idx = np.asarray(feature_flat, np.int64).reshape(shape)
+    inner = int(np.prod(shape[1:])) if ndim > 1 else 1
+    a0 = np.floor_divide(idx, inner)
+    rest = idx - a0 * inner
+    comps = [a0]
+    for k in range(1, ndim):
+        st = int(np.prod(shape[k + 1:])) if k + 1 < ndim else 1
+        comps.append(rest // st)
+        rest = rest % st
+    grid = np.indices(shape)
+    return np.max([np.abs(grid[k] - comps[k]) for k in range(ndim)], axis=0)
+
+
 def taxicab_at(mask, points):
     """City-block (L1) distance by its definition at the elements with the given
     flat indices, one by one: the minimum over all background elements of

@@ -167,3 +167,51 @@ def test_taxicab_at_pins():
         m.reshape(-1)[5] = 0
         d, _ = oracle.taxicab_brute(m)
         assert (oracle.taxicab_at(m, np.arange(m.size)) == d.reshape(-1)).all()
+
+
+def test_chessboard_oracle_pins():
+    """The L-infinity oracle against what the mathematics fixes: one background
+    element (closed form), none (virtual element), 1-D (equal to the L1
+    transform there), the 2-D identity max(|a|, |b|) = (|a + b| + |a - b|) / 2
+    (half the L1 transform of the same points on the 45-degree rotated grid),
+    the bounds L-inf <= L1 <= n L-inf and L-inf^2 <= EDT^2 <= n L-inf^2, the
+    returned index attaining the minimum, and the one-by-one form."""
+    rng = np.random.default_rng([42, 7003])
+    for shape in ((1,), (9,), (7, 11), (5, 6, 7)):
+        m = np.ones(shape, np.uint8)
+        b = tuple(int(rng.integers(n)) for n in shape)
+        m[b] = 0
+        d, who = oracle.chessboard_brute(m)
+        grid = np.indices(shape)
+        assert (d == np.max([np.abs(grid[k] - b[k]) for k in range(len(shape))], axis=0)).all()
+        assert (who == np.ravel_multi_index(b, shape)).all()
+    g = np.indices((3, 4))
+    d, who = oracle.chessboard_brute(np.ones((3, 4), np.uint8))
+    assert (d == np.maximum(g[0] + 1, g[1])).all() and (who == -4).all()
+    line = (rng.random(300) >= 0.05).astype(np.uint8)
+    line[40] = 0
+    assert (oracle.chessboard_brute(line)[0] == oracle.taxicab_brute(line)[0]).all()
+    # 2-D: (x, y) -> (x + y, x - y + W - 1) on an (H + W - 1)^2 grid
+    H, W = 13, 17
+    m = (rng.random((H, W)) >= 0.08).astype(np.uint8)
+    m[3, 5] = 0
+    R = np.ones((H + W - 1, H + W - 1), np.uint8)
+    xs, ys = np.nonzero(m == 0)
+    R[xs + ys, xs - ys + W - 1] = 0
+    l1r, _ = oracle.taxicab_brute(R)
+    gx, gy = np.indices((H, W))
+    d, who = oracle.chessboard_brute(m)
+    assert (2 * d == l1r[gx + gy, gx - gy + W - 1]).all()
+    assert (oracle.chessboard_to(who, m.shape) == d).all()
+    assert (m.reshape(-1)[who.reshape(-1)] == 0).all()
+    for shape, p in (((19, 23), 0.03), ((6, 9, 11), 0.02)):
+        m = (rng.random(shape) >= p).astype(np.uint8)
+        m.reshape(-1)[7] = 0
+        d, who = oracle.chessboard_brute(m)
+        l1, _ = oracle.taxicab_brute(m)
+        e2, _ = oracle.edt(m, None, features=False)
+        n = len(shape)
+        assert (d <= l1).all() and (l1 <= n * d).all()
+        assert (d * d <= e2).all() and (e2 <= n * d * d).all()
+        assert (oracle.chessboard_to(who, shape) == d).all()
+        assert (oracle.chessboard_at(m, np.arange(m.size)) == d.reshape(-1)).all()
