@@ -322,38 +322,44 @@ def bench_brute(args):
     return 0
 
 
-def bench_taxicab(args):
-    """Time the city-block transform (int32 distances, plus indices when the
-    workload times them) on a 2-D, batched 2-D or 3-D workload.  Bytes of the
-    path: mask 1 B, axis-0 coordinate 2 + 2 B, (3-D: the middle pass reads the
-    coordinate twice and writes and reads its packed owners, 2 + 2 + 4 + 4 + 4 B),
-    4 B per output."""
+def bench_chamfer(args, metric):
+    """Time a chamfer transform, city-block ("taxicab") or chessboard (int32
+    distances, plus indices when the workload times them), on a 2-D, batched
+    2-D or 3-D workload.  Bytes of the path per element: mask 1 B, axis-0
+    coordinate written and read 2 + 2 B, 4 B per output; 3-D adds the middle
+    pass: taxicab reads the coordinate twice and writes, reads back and
+    rewrites its packed owners, which the row pass reads (2 + 2 + 4 + 4 + 4 B,
+    as counted here), chessboard writes the owners once and the row pass reads
+    them (4 + 4 B)."""
     import torch
-    from exact_euclidean_distance_amd import taxicab
+    import exact_euclidean_distance_amd as pkg
     from workloads import make_config
+    fn = getattr(pkg, metric)
     name = args.config
     mask_np, _, _ = make_config(name)
     dev = torch.device("cuda:0")
     mask = torch.from_numpy(mask_np).to(dev)
     want_idx = "indices" in OUTPUTS[name]
-    r = taxicab(mask, return_indices=want_idx)
+    r = fn(mask, return_indices=want_idx)
     for _ in range(args.warmup):
-        taxicab(mask, return_indices=want_idx, dist=r.dist, indices=r.indices)
+        fn(mask, return_indices=want_idx, dist=r.dist, indices=r.indices)
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     stream = torch.cuda.current_stream()
     e0.record(stream)
     for _ in range(args.steps):
-        taxicab(mask, return_indices=want_idx, dist=r.dist, indices=r.indices)
+        fn(mask, return_indices=want_idx, dist=r.dist, indices=r.indices)
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / max(1, args.steps)
     n = mask_np.size
-    per = 1 + 4 + (16 if mask_np.ndim == 4 else 0) + 4 * (2 if want_idx else 1)
+    mid = (16 if metric == "taxicab" else 8) if mask_np.ndim == 4 else 0
+    per = 1 + 4 + mid + 4 * (2 if want_idx else 1)
     gbs = n * per / (ms * 1e-3) / 1e9
+    title = {"taxicab": "city-block (taxicab)", "chessboard": "chessboard (L-infinity)"}[metric]
     line = {
-        "metric": "city-block (taxicab) transform Gpixel/s at 1 GPU (adjacent operator, not the EDT)",
+        "metric": f"{title} transform Gpixel/s at 1 GPU (adjacent operator, not the EDT)",
         "value": round(n / (ms * 1e-3) / 1e9, 3), "unit": "Gpixel/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int32",
@@ -381,6 +387,8 @@ def main(argv=None):
                     help="time the device brute-force transform (the exactness check) instead")
     ap.add_argument("--taxicab", action="store_true",
                     help="time the city-block (L1) transform on the workload instead")
+    ap.add_argument("--chessboard", action="store_true",
+                    help="time the chessboard (L-infinity) transform on the workload instead")
     ap.add_argument("--graph", action="store_true",
                     help="time replays of a HIP graph holding one transform (launch gaps removed)")
     ap.add_argument("--probe-copy", action="store_true")
@@ -406,7 +414,9 @@ def main(argv=None):
     if args.brute:
         return bench_brute(args)
     if args.taxicab:
-        return bench_taxicab(args)
+        return bench_chamfer(args, "taxicab")
+    if args.chessboard:
+        return bench_chamfer(args, "chessboard")
 
     if not torch.cuda.is_available():
         print("bench.py: no HIP device", file=sys.stderr)

@@ -15,6 +15,7 @@ from .api import (  # noqa: F401
     edt2d,
     edt3d,
     edt_brute,
+    chessboard,
     taxicab,
     unravel_indices,
     workspace_size_2d,
@@ -22,6 +23,6 @@ from .api import (  # noqa: F401
     workspace_size_3d,
 )
 
-__all__ = ["edt1d", "edt2d", "edt3d", "edt_brute", "taxicab", "unravel_indices", "EDTResult", "EDTError",
+__all__ = ["chessboard", "edt1d", "edt2d", "edt3d", "edt_brute", "taxicab", "unravel_indices", "EDTResult", "EDTError",
            "workspace_size_2d", "workspace_size_2d_batched", "workspace_size_3d",
            "alloc_workspace"]

@@ -27,6 +27,7 @@ EXPORTS = (
     "edt1d_workspace_size", "edt1d_u8_batched", "edt_unravel_indices",
     "edt_brute_workspace_size", "edt_brute_u8", "edt3d_u8_batched_idx64",
     "edt2d_taxicab_u8_batched", "edt3d_taxicab_u8_batched",
+    "edt2d_chessboard_u8_batched", "edt3d_chessboard_u8_batched",
 )
 
 _lib = None
@@ -90,6 +91,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.edt2d_taxicab_u8_batched.argtypes = [vp, i32, i32, i32, vp, vp, vp, sz, vp]
     lib.edt3d_taxicab_u8_batched.restype = ctypes.c_int
     lib.edt3d_taxicab_u8_batched.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, sz, vp]
+    lib.edt2d_chessboard_u8_batched.restype = ctypes.c_int
+    lib.edt2d_chessboard_u8_batched.argtypes = [vp, i32, i32, i32, vp, vp, vp, sz, vp]
+    lib.edt3d_chessboard_u8_batched.restype = ctypes.c_int
+    lib.edt3d_chessboard_u8_batched.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, sz, vp]
     lib.edt_status_string.restype = ctypes.c_char_p
     lib.edt_status_string.argtypes = [ctypes.c_int]
     lib.edt_version.restype = ctypes.c_char_p

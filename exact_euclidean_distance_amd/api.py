@@ -215,11 +215,7 @@ def edt_brute(mask: torch.Tensor, sampling=None, *, batched: bool = False,
     return EDTResult(sq, ds, ix)
 
 
-def taxicab(mask: torch.Tensor, *, return_indices: bool = False, dist=None, indices=None,
-            workspace=None, stream=None):
-    """City-block (L1) distance transform: int32 distances (and flat indices)
-    of one (H, W) image, a batch (B, H, W), or a batch of volumes
-    (B, D, H, W)."""
+def _chamfer(metric: str, mask: torch.Tensor, return_indices: bool, dist, indices, workspace, stream):
     _check_mask(mask, (2, 3, 4))
     shape = tuple(mask.shape)
     dev = mask.device
@@ -236,14 +232,30 @@ def taxicab(mask: torch.Tensor, *, return_indices: bool = False, dist=None, indi
         workspace = alloc_workspace(need, dev)
     wsb = workspace.numel() * workspace.element_size()
     if mask.dim() == 4:
-        st = lib.edt3d_taxicab_u8_batched(_ptr(mask), B, D, H, W, _ptr(ds), _ptr(ix), _ptr(workspace),
-                                          wsb, _stream(stream))
+        fn = getattr(lib, f"edt3d_{metric}_u8_batched")
+        st = fn(_ptr(mask), B, D, H, W, _ptr(ds), _ptr(ix), _ptr(workspace), wsb, _stream(stream))
     else:
-        st = lib.edt2d_taxicab_u8_batched(_ptr(mask), B, H, W, _ptr(ds), _ptr(ix), _ptr(workspace), wsb,
-                                          _stream(stream))
+        fn = getattr(lib, f"edt2d_{metric}_u8_batched")
+        st = fn(_ptr(mask), B, H, W, _ptr(ds), _ptr(ix), _ptr(workspace), wsb, _stream(stream))
     if st != 0:
-        raise EDTError(st, "taxicab")
+        raise EDTError(st, metric)
     return EDTResult(None, ds, ix)
+
+
+def taxicab(mask: torch.Tensor, *, return_indices: bool = False, dist=None, indices=None,
+            workspace=None, stream=None):
+    """City-block (L1) distance transform: int32 distances (and flat indices)
+    of one (H, W) image, a batch (B, H, W), or a batch of volumes
+    (B, D, H, W)."""
+    return _chamfer("taxicab", mask, return_indices, dist, indices, workspace, stream)
+
+
+def chessboard(mask: torch.Tensor, *, return_indices: bool = False, dist=None, indices=None,
+               workspace=None, stream=None):
+    """Chessboard (L-infinity) distance transform: int32 distances (and flat
+    indices) of one (H, W) image, a batch (B, H, W), or a batch of volumes
+    (B, D, H, W)."""
+    return _chamfer("chessboard", mask, return_indices, dist, indices, workspace, stream)
 
 
 def edt3d(mask: torch.Tensor, sampling=None, *, return_distances: bool = True,

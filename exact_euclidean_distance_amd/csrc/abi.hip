@@ -367,9 +367,13 @@ edt_status edt_brute_u8(const uint8_t* mask, int32_t B, int32_t ndim, const int3
     return EDT_OK;
 }
 
-edt_status edt2d_taxicab_u8_batched(const uint8_t* mask, int32_t B, int32_t H, int32_t W,
-                                    int32_t* dist, int32_t* indices, void* workspace,
-                                    size_t workspace_bytes, hipStream_t stream) {
+namespace {
+
+enum class Chamfer { kTaxicab, kChessboard };
+
+edt_status chamfer2d(Chamfer metric, const uint8_t* mask, int32_t B, int32_t H, int32_t W,
+                     int32_t* dist, int32_t* indices, void* workspace, size_t workspace_bytes,
+                     hipStream_t stream) {
     if (B < 1 || H < 1 || W < 1) return EDT_ERR_INVALID_ARGUMENT;
     if (!shape2d_ok(B, H, W)) return EDT_ERR_UNSUPPORTED_SHAPE;
     const Layout L = layout2d(B, H, W);
@@ -382,14 +386,15 @@ edt_status edt2d_taxicab_u8_batched(const uint8_t* mask, int32_t B, int32_t H, i
                           reinterpret_cast<uint16_t*>(base + L.last),
                           reinterpret_cast<uint64_t*>(base + L.bits), c0, stream, nullptr) != hipSuccess)
         return EDT_ERR_HIP;
-    if (edt::launch_l1_rows_2d(c0, B, H, W, dist, indices, stream, nullptr) != hipSuccess)
-        return EDT_ERR_HIP;
-    return EDT_OK;
+    const hipError_t e = metric == Chamfer::kTaxicab
+                             ? edt::launch_l1_rows_2d(c0, B, H, W, dist, indices, stream, nullptr)
+                             : edt::launch_linf_rows_2d(c0, B, H, W, dist, indices, stream, nullptr);
+    return e == hipSuccess ? EDT_OK : EDT_ERR_HIP;
 }
 
-edt_status edt3d_taxicab_u8_batched(const uint8_t* mask, int32_t B, int32_t D, int32_t H,
-                                    int32_t W, int32_t* dist, int32_t* indices, void* workspace,
-                                    size_t workspace_bytes, hipStream_t stream) {
+edt_status chamfer3d(Chamfer metric, const uint8_t* mask, int32_t B, int32_t D, int32_t H, int32_t W,
+                     int32_t* dist, int32_t* indices, void* workspace, size_t workspace_bytes,
+                     hipStream_t stream) {
     if (B < 1 || D < 1 || H < 1 || W < 1) return EDT_ERR_INVALID_ARGUMENT;
     if (!shape3d_ok(B, D, H, W)) return EDT_ERR_UNSUPPORTED_SHAPE;
     if (indices && (int64_t)D * H * W > INT32_MAX) return EDT_ERR_UNSUPPORTED_SHAPE;
@@ -404,11 +409,44 @@ edt_status edt3d_taxicab_u8_batched(const uint8_t* mask, int32_t B, int32_t D, i
                           reinterpret_cast<uint16_t*>(base + L.last),
                           reinterpret_cast<uint64_t*>(base + L.bits), c0, stream, nullptr) != hipSuccess)
         return EDT_ERR_HIP;
-    if (edt::launch_l1_cols_3d(c0, B, D, H, W, c01, stream, nullptr) != hipSuccess)
+    const bool l1 = metric == Chamfer::kTaxicab;
+    if ((l1 ? edt::launch_l1_cols_3d(c0, B, D, H, W, c01, stream, nullptr)
+            : edt::launch_linf_cols_3d(c0, B, D, H, W, c01, stream, nullptr)) != hipSuccess)
         return EDT_ERR_HIP;
-    if (edt::launch_l1_rows_3d(c01, B, D, H, W, dist, indices, stream, nullptr) != hipSuccess)
+    if ((l1 ? edt::launch_l1_rows_3d(c01, B, D, H, W, dist, indices, stream, nullptr)
+            : edt::launch_linf_rows_3d(c01, B, D, H, W, dist, indices, stream, nullptr)) != hipSuccess)
         return EDT_ERR_HIP;
     return EDT_OK;
+}
+
+}  // namespace
+
+edt_status edt2d_taxicab_u8_batched(const uint8_t* mask, int32_t B, int32_t H, int32_t W,
+                                    int32_t* dist, int32_t* indices, void* workspace,
+                                    size_t workspace_bytes, hipStream_t stream) {
+    return chamfer2d(Chamfer::kTaxicab, mask, B, H, W, dist, indices, workspace, workspace_bytes,
+                     stream);
+}
+
+edt_status edt3d_taxicab_u8_batched(const uint8_t* mask, int32_t B, int32_t D, int32_t H,
+                                    int32_t W, int32_t* dist, int32_t* indices, void* workspace,
+                                    size_t workspace_bytes, hipStream_t stream) {
+    return chamfer3d(Chamfer::kTaxicab, mask, B, D, H, W, dist, indices, workspace, workspace_bytes,
+                     stream);
+}
+
+edt_status edt2d_chessboard_u8_batched(const uint8_t* mask, int32_t B, int32_t H, int32_t W,
+                                       int32_t* dist, int32_t* indices, void* workspace,
+                                       size_t workspace_bytes, hipStream_t stream) {
+    return chamfer2d(Chamfer::kChessboard, mask, B, H, W, dist, indices, workspace, workspace_bytes,
+                     stream);
+}
+
+edt_status edt3d_chessboard_u8_batched(const uint8_t* mask, int32_t B, int32_t D, int32_t H,
+                                       int32_t W, int32_t* dist, int32_t* indices, void* workspace,
+                                       size_t workspace_bytes, hipStream_t stream) {
+    return chamfer3d(Chamfer::kChessboard, mask, B, D, H, W, dist, indices, workspace,
+                     workspace_bytes, stream);
 }
 
 const char* edt_status_string(edt_status status) {

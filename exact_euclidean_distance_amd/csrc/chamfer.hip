@@ -22,6 +22,22 @@
 //               neighbouring columns), a forward sweep storing the prefix
 //               owners and a backward sweep finishing them, both reading
 //               batches of rows so that many loads are in flight.
+//
+// The chessboard (L-infinity) distance separates as well: after the axis-0
+// pass every further axis applies h(q) = min_j max(g(j), |q - j|).  That
+// min-max has no prefix-minimum form, so each position searches outward from
+// itself over its line staged in LDS (r = 0, 1, 2, ...): a source r away adds
+// at least r, so the search ends once r reaches the best value found.  The
+// work per position is its own distance along the axis; neighbours differ by
+// at most one, so the lanes of a wave stay together.  Lines without any
+// source are flagged while they are staged and never searched.
+//
+//   k_linf_cols  middle axis of a volume: a block stages TW neighbouring
+//                columns of one plane (all rows) and writes packed
+//                (axis0 << 16 | axis1) owners.
+//   k_linf_rows  last axis + outputs: a block stages whole lines (several
+//                short ones or one long one) and writes int32 distances and
+//                flat indices.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -327,6 +343,167 @@ __global__ __launch_bounds__(256) void k_l1_cols(const uint16_t* __restrict__ c0
     }
 }
 
+// ---------------------------------------------------------------------------
+// Chessboard (L-infinity) transform
+// ---------------------------------------------------------------------------
+
+// Rows of B images (2-D): value = nearest background row of the column.
+struct LinfRows2D {
+    using Val = uint16_t;
+    int H, W;
+    __device__ static bool valid(Val v) { return v != kNone16; }
+    __device__ unsigned ctx(int64_t ln) const { return (unsigned)(ln % H); }
+    __device__ int g(unsigned c, Val v) const {
+        const int row = (int)c;
+        return row > (int)v ? row - (int)v : (int)v - row;
+    }
+    __device__ int32_t index(unsigned, Val v, int j) const { return (int32_t)v * W + j; }
+    __device__ int virt(unsigned c, int q) const { return max((int)c + 1, q); }
+    __device__ int32_t virt_index() const { return -W; }
+};
+
+// Rows of B volumes (3-D): value = packed (axis0 << 16 | axis1) owner.
+struct LinfRows3D {
+    using Val = uint32_t;
+    int D, H, W;
+    __device__ static bool valid(Val v) { return v != kNone32; }
+    __device__ unsigned ctx(int64_t ln) const {
+        const int64_t dh = ln % ((int64_t)D * H);
+        return (unsigned)(((dh / H) << 16) | (dh % H));
+    }
+    __device__ int g(unsigned c, Val v) const {
+        const int d = (int)(c >> 16), h = (int)(c & 0xFFFFu);
+        const int z = (int)(v >> 16), y = (int)(v & 0xFFFFu);
+        return max(d > z ? d - z : z - d, h > y ? h - y : y - h);
+    }
+    __device__ int32_t index(unsigned, Val v, int j) const {
+        return (int32_t)(((int64_t)(v >> 16) * H + (v & 0xFFFFu)) * W + j);
+    }
+    __device__ int virt(unsigned c, int q) const {
+        return max(max((int)(c >> 16) + 1, (int)(c & 0xFFFFu)), q);
+    }
+    __device__ int32_t virt_index() const { return -(H * W); }
+};
+
+constexpr int kLinfStage = 2048;   // lines up to this length share a block
+
+__host__ __device__ inline size_t linf_flags_offset(size_t bytes) { return (bytes + 15) & ~size_t(15); }
+
+// Smallest max(g(j), |q - j|) over the sources of a staged line of L values,
+// stride apart (at least one is a source), searching outward from q; ties go
+// to the nearer, then the lower j.  gof(v): g of a source value, -1 for none.
+template <class Val, class GFn>
+__device__ inline int linf_search(const Val* lv, int stride, int q, int L, const GFn& gof, int& bj) {
+    int best = INT32_MAX;
+    bj = -1;
+    for (int r = 0; r < best; ++r) {
+        const int j0 = q - r, j1 = q + r;
+        if (j0 < 0 && j1 >= L) break;
+        if (j0 >= 0) {
+            const int gv = gof(lv[j0 * stride]);
+            if (gv >= 0) {
+                const int v = max(gv, r);
+                if (v < best) { best = v; bj = j0; }
+            }
+        }
+        if (r > 0 && j1 < L) {
+            const int gv = gof(lv[j1 * stride]);
+            if (gv >= 0) {
+                const int v = max(gv, r);
+                if (v < best) { best = v; bj = j1; }
+            }
+        }
+    }
+    return best;
+}
+
+// LPB lines of L values per block (L <= kLinfStage: LPB = kLinfStage / L,
+// else 1); threads take consecutive positions of the block's lines.
+template <class Geo>
+__global__ __launch_bounds__(256) void k_linf_rows(const typename Geo::Val* __restrict__ in, int L,
+                                                   int64_t nlines, int LPB, Geo geo,
+                                                   int32_t* __restrict__ dist,
+                                                   int32_t* __restrict__ indices) {
+    using Val = typename Geo::Val;
+    extern __shared__ __align__(16) unsigned char smem[];
+    Val* sv = reinterpret_cast<Val*>(smem);                                       // [LPB][L]
+    int* any = reinterpret_cast<int*>(smem + linf_flags_offset((size_t)LPB * L * sizeof(Val)));
+    const int tid = threadIdx.x, nt = blockDim.x;
+    const int64_t line0 = (int64_t)blockIdx.x * LPB;
+    const int nl = (int)min<int64_t>(LPB, nlines - line0);
+    const int total = nl * L;
+    for (int l = tid; l < LPB; l += nt) any[l] = 0;
+    __syncthreads();
+    const Val* src = in + line0 * (int64_t)L;
+    for (int e = tid; e < total; e += nt) {
+        const Val v = src[e];
+        sv[e] = v;
+        if (Geo::valid(v)) any[e / L] = 1;   // every writer stores the same 1
+    }
+    __syncthreads();
+    for (int e = tid; e < total; e += nt) {
+        const int l = e / L, q = e - l * L;
+        const int64_t ln = line0 + l;
+        const unsigned c = geo.ctx(ln);
+        int best;
+        int32_t ix;
+        if (!any[l]) {   // no source on the line: only in an image without background
+            best = geo.virt(c, q);
+            ix = geo.virt_index();
+        } else {
+            const Val* lv = sv + l * L;
+            int bj;
+            auto gof = [&](Val v) { return Geo::valid(v) ? geo.g(c, v) : -1; };
+            best = linf_search(lv, 1, q, L, gof, bj);
+            ix = geo.index(c, lv[bj], bj);
+        }
+        if (dist) dist[ln * (int64_t)L + q] = best;
+        if (indices) indices[ln * (int64_t)L + q] = ix;
+    }
+}
+
+// Middle axis of B volumes: a block stages TW neighbouring columns (w0 ..
+// w0 + TW - 1) of one plane (volume, d), all H rows, as sv[y][x]; thread x of
+// row group yg answers rows yg, yg + 256 / TW, ... of column x.  Output: the
+// packed (axis0 << 16 | axis1) owner, kNone32 for a column without a source.
+__global__ __launch_bounds__(256) void k_linf_cols(const uint16_t* __restrict__ c0,
+                                                   uint32_t* __restrict__ out, int D, int H, int W,
+                                                   int TW) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    uint16_t* sv = reinterpret_cast<uint16_t*>(smem);                              // [H][TW]
+    int* any = reinterpret_cast<int*>(smem + linf_flags_offset((size_t)H * TW * 2));   // [TW]
+    const int tid = threadIdx.x;
+    const int tiles = (W + TW - 1) / TW;
+    const int64_t plane = blockIdx.x / tiles;          // volume * D + d
+    const int w0 = (int)(blockIdx.x % tiles) * TW;
+    const int d = (int)(plane % D);
+    const int tw = min(TW, W - w0);                    // columns of this tile
+    const uint16_t* src = c0 + plane * (int64_t)H * W + w0;
+    uint32_t* dst = out + plane * (int64_t)H * W + w0;
+    for (int x = tid; x < TW; x += 256) any[x] = 0;
+    __syncthreads();
+    for (int e = tid; e < H * TW; e += 256) {
+        const int y = e / TW, x = e - y * TW;
+        const uint16_t v = x < tw ? src[(int64_t)y * W + x] : kNone16;
+        sv[e] = v;
+        if (v != kNone16) any[x] = 1;   // every writer stores the same 1
+    }
+    __syncthreads();
+    const int x = tid % TW, yg = tid / TW, ys = 256 / TW;
+    if (x >= tw || yg >= ys) return;   // no barrier follows
+    const bool has = any[x] != 0;
+    auto gof = [&](uint16_t v) { return v != kNone16 ? (d > (int)v ? d - (int)v : (int)v - d) : -1; };
+    for (int y = yg; y < H; y += ys) {
+        uint32_t o = kNone32;
+        if (has) {
+            int bj;
+            linf_search(sv + x, TW, y, H, gof, bj);
+            o = ((uint32_t)sv[bj * TW + x] << 16) | (uint32_t)bj;
+        }
+        dst[(int64_t)y * W + x] = o;
+    }
+}
+
 namespace {
 
 template <class Geo>
@@ -375,6 +552,63 @@ hipError_t launch_l1_cols_3d(const uint16_t* c0, int B, int D, int H, int W, uin
 hipError_t launch_l1_rows_3d(const uint32_t* c01, int B, int D, int H, int W, int32_t* dist,
                              int32_t* indices, hipStream_t s, KernelTimer* tm) {
     return launch_l1_rows_t(c01, W, (int64_t)B * D * H, L1Rows3D{D, H, W}, dist, indices, s, tm);
+}
+
+namespace {
+
+void linf_allow_lds(const void* fn) {
+    if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) != hipSuccess)
+        (void)hipGetLastError();
+}
+
+template <class Geo>
+hipError_t launch_linf_rows_t(const typename Geo::Val* in, int L, int64_t nlines, const Geo& geo,
+                              int32_t* dist, int32_t* indices, hipStream_t s, KernelTimer* tm) {
+    using Val = typename Geo::Val;
+    static bool attr = false;
+    if (!attr) {
+        linf_allow_lds((const void*)k_linf_rows<Geo>);
+        attr = true;
+    }
+    const int LPB = L <= kLinfStage ? kLinfStage / L : 1;
+    const size_t lds = linf_flags_offset((size_t)LPB * L * sizeof(Val)) + (size_t)LPB * 4;
+    const int64_t blocks = (nlines + LPB - 1) / LPB;
+    if (blocks > INT32_MAX || lds > 160 * 1024) return hipErrorInvalidValue;
+    EDT_LAUNCH(tm, "chessboard_rows", s,
+               hipLaunchKernelGGL(k_linf_rows<Geo>, dim3((unsigned)blocks), dim3(256), lds, s, in, L,
+                                  nlines, LPB, geo, dist, indices));
+    return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_linf_rows_2d(const uint16_t* c0, int B, int H, int W, int32_t* dist,
+                               int32_t* indices, hipStream_t s, KernelTimer* tm) {
+    return launch_linf_rows_t(c0, W, (int64_t)B * H, LinfRows2D{H, W}, dist, indices, s, tm);
+}
+
+hipError_t launch_linf_cols_3d(const uint16_t* c0, int B, int D, int H, int W, uint32_t* c01,
+                               hipStream_t s, KernelTimer* tm) {
+    static bool attr = false;
+    if (!attr) {
+        linf_allow_lds((const void*)k_linf_cols);
+        attr = true;
+    }
+    int TW = 64;   // columns per block: their H rows of 2-byte values within 64 KB
+    while (TW > 1 && (size_t)H * TW * 2 > 64 * 1024) TW >>= 1;
+    if ((size_t)H * TW * 2 > 64 * 1024) return hipErrorInvalidValue;
+    const size_t lds = linf_flags_offset((size_t)H * TW * 2) + (size_t)TW * 4;
+    const int64_t blocks = (int64_t)B * D * ((W + TW - 1) / TW);
+    if (blocks > INT32_MAX) return hipErrorInvalidValue;
+    EDT_LAUNCH(tm, "chessboard_cols", s,
+               hipLaunchKernelGGL(k_linf_cols, dim3((unsigned)blocks), dim3(256), lds, s, c0, c01, D, H,
+                                  W, TW));
+    return hipSuccess;
+}
+
+hipError_t launch_linf_rows_3d(const uint32_t* c01, int B, int D, int H, int W, int32_t* dist,
+                               int32_t* indices, hipStream_t s, KernelTimer* tm) {
+    return launch_linf_rows_t(c01, W, (int64_t)B * D * H, LinfRows3D{D, H, W}, dist, indices, s, tm);
 }
 
 }  // namespace edt

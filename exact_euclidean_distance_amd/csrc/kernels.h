@@ -81,6 +81,13 @@ hipError_t launch_l1_cols_3d(const uint16_t* c0, int B, int D, int H, int W, uin
                              hipStream_t s, KernelTimer* tm);
 hipError_t launch_l1_rows_3d(const uint32_t* c01, int B, int D, int H, int W, int32_t* dist,
                              int32_t* indices, hipStream_t s, KernelTimer* tm);
+// chessboard (L-infinity) transform: last axis with outputs, and the middle axis of volumes
+hipError_t launch_linf_rows_2d(const uint16_t* c0, int B, int H, int W, int32_t* dist,
+                               int32_t* indices, hipStream_t s, KernelTimer* tm);
+hipError_t launch_linf_cols_3d(const uint16_t* c0, int B, int D, int H, int W, uint32_t* c01,
+                               hipStream_t s, KernelTimer* tm);
+hipError_t launch_linf_rows_3d(const uint32_t* c01, int B, int D, int H, int W, int32_t* dist,
+                               int32_t* indices, hipStream_t s, KernelTimer* tm);
 
 // Dynamic LDS each envelope launch needs (0 if the line is too long).
 size_t rows_lds_bytes(int L, int value_bytes);

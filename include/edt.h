@@ -164,6 +164,21 @@ edt_status edt3d_taxicab_u8_batched(const uint8_t* mask, int32_t B, int32_t D, i
                                     int32_t W, int32_t* dist, int32_t* indices,
                                     void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Chessboard (L-infinity) distance transform, the other chamfer transform
+   TorchMorph ships beside its EDT (read as the L-infinity metric, like SciPy's
+   "chessboard"): for every element, min over background elements of
+   max_k |p_k - b_k|, as int32, and optionally the flat index of such an
+   element (ties: any).  Layouts, the virtual element (distance
+   max(p0 + 1, p1, ...)), buffers, workspace, limits and errors exactly as for
+   the taxicab entry points above.  The work per element grows with its own
+   distance (each element searches outward along each axis). */
+edt_status edt2d_chessboard_u8_batched(const uint8_t* mask, int32_t B, int32_t H, int32_t W,
+                                       int32_t* dist, int32_t* indices,
+                                       void* workspace, size_t workspace_bytes, hipStream_t stream);
+edt_status edt3d_chessboard_u8_batched(const uint8_t* mask, int32_t B, int32_t D, int32_t H,
+                                       int32_t W, int32_t* dist, int32_t* indices,
+                                       void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Bytes of workspace edt3d_u8_batched needs for B volumes of D x H x W. */
 size_t edt3d_workspace_size(int32_t B, int32_t D, int32_t H, int32_t W);
 

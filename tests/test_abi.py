@@ -239,12 +239,16 @@ def test_idx64_argument_errors(lib):
 
 
 @fake_pointers
-def test_taxicab_argument_errors(lib):
+@pytest.mark.parametrize("metric", ["taxicab", "chessboard"])
+def test_chamfer_argument_errors(lib, metric):
+    f2 = getattr(lib, f"edt2d_{metric}_u8_batched")
+    f3 = getattr(lib, f"edt3d_{metric}_u8_batched")
+
     def c2(mask=MASK, B=2, H=8, W=8, dist=DIST, idx=IDX, ws=WS, ws_bytes=BIG):
-        return lib.edt2d_taxicab_u8_batched(mask, B, H, W, dist, idx, ws, ws_bytes, None)
+        return f2(mask, B, H, W, dist, idx, ws, ws_bytes, None)
 
     def c3(mask=MASK, B=2, D=8, H=8, W=8, dist=DIST, idx=IDX, ws=WS, ws_bytes=BIG):
-        return lib.edt3d_taxicab_u8_batched(mask, B, D, H, W, dist, idx, ws, ws_bytes, None)
+        return f3(mask, B, D, H, W, dist, idx, ws, ws_bytes, None)
 
     assert c2(mask=None) == INVALID
     assert c2(B=0) == INVALID

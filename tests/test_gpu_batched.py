@@ -577,3 +577,76 @@ def test_taxicab_full_size(torch_dev, name):
         pts = np.concatenate([rng.integers(0, per, ns // min(nb, 2)), [0, per - 1]])
         ref = oracle.taxicab_at(mask[k] if mask.ndim >= 3 else mask, pts)
         assert (dh[k][pts] == ref).all(), f"sampled distance mismatch in image {k}"
+
+
+def test_chessboard(torch_dev):
+    """Chessboard (L-infinity) transform against its oracle (the definition):
+    exact int32 distances, indices attaining them; the same shapes as the
+    taxicab test (rows of every staging form, batched 2-D, 3-D, images without
+    background, full background rows)."""
+    torch, dev = torch_dev
+    from exact_euclidean_distance_amd import chessboard
+    rng = np.random.default_rng([42, 5014])
+    cases = [(1, 1), (1, 70), (37, 1), (64, 64), (4, 300), (33, 517), (3, 1100), (5, 20000),
+             (3, 40, 70), (2, 13, 17, 30), (3, 9, 40, 64), (2, 3, 5, 400), (1, 5, 1100, 33),
+             (1, 2, 3, 2000), (1, 3, 700, 9)]
+    for shape in cases:
+        for p in ((0.003, 0.1, 0.6) if np.prod(shape) <= 20000 else (0.002,)):
+            m = (rng.random(shape) >= p).astype(np.uint8)
+            if len(shape) > 2:
+                m[0] = 1                                 # one image/volume without background
+            m.reshape(-1)[-1] = 0
+            if len(shape) == 2 and shape[0] > 2:
+                m[shape[0] // 2, :] = 0                  # a full background row
+            _say(f"chessboard {shape} p={p}")
+            r = chessboard(torch.from_numpy(m).to(dev), return_indices=True)
+            torch.cuda.synchronize()
+            d = r.dist.cpu().numpy()
+            ix = r.indices.cpu().numpy()
+            batch = [m] if len(shape) == 2 else list(m)
+            dd = [d] if len(shape) == 2 else list(d)
+            ii = [ix] if len(shape) == 2 else list(ix)
+            for mm, d1, i1 in zip(batch, dd, ii):
+                ref, _ = oracle.chessboard_brute(mm)
+                assert (d1 == ref).all(), "chessboard distance mismatch"
+                assert (oracle.chessboard_to(i1, mm.shape) == ref).all(), "index does not attain it"
+                if (mm == 0).any():
+                    assert (mm.reshape(-1)[i1.reshape(-1)] == 0).all()
+
+
+@pytest.mark.parametrize("name", ["b2d", "c5", "c3"])
+def test_chessboard_full_size(torch_dev, name):
+    """Chessboard transform at the full sizes that bench.py --chessboard times:
+    over the whole output, every index names a background element of its
+    image at exactly the returned L-infinity distance (on the device), and
+    sampled elements plus the corners equal the definition's minimum (oracle,
+    one by one)."""
+    torch, dev = torch_dev
+    from workloads import make_config
+    from exact_euclidean_distance_amd import chessboard
+    mask, _, _ = make_config(name)
+    _say(f"chessboard full size {name} {mask.shape}")
+    m = torch.from_numpy(mask).to(dev)
+    r = chessboard(m, return_indices=True)
+    torch.cuda.synchronize()
+    img = mask.shape[1:] if mask.ndim >= 3 else mask.shape
+    nb = mask.shape[0] if mask.ndim >= 3 else 1
+    per = int(np.prod(img))
+    d = r.dist.reshape(nb, per).long()
+    ix = r.indices.reshape(nb, per).long()
+    assert (ix >= 0).all(), "every benchmark image has background"
+    assert (torch.gather(m.reshape(nb, per), 1, ix) == 0).all()
+    flat = torch.arange(per, device=dev)
+    linf = torch.zeros_like(d)
+    div = per
+    for n in img:
+        div //= n
+        linf = torch.maximum(linf, ((flat // div) % n)[None, :].sub((ix // div) % n).abs())
+    assert (linf == d).all(), "an index does not attain the returned distance"
+    rng = np.random.default_rng([42, 5015])
+    dh = d.cpu().numpy()
+    ns = 384 if (mask == 0).sum() < 10**6 else 24
+    for k in range(nb if nb <= 2 else 2):
+        pts = np.concatenate([rng.integers(0, per, ns // min(nb, 2)), [0, per - 1]])
+        ref = oracle.chessboard_at(mask[k] if mask.ndim >= 3 else mask, pts)
+        assert (dh[k][pts] == ref).all(), f"sampled distance mismatch in image {k}"
