@@ -394,24 +394,25 @@ __host__ __device__ inline size_t linf_flags_offset(size_t bytes) { return (byte
 // to the nearer, then the lower j.  gof(v): g of a source value, -1 for none.
 template <class Val, class GFn>
 __device__ inline int linf_search(const Val* lv, int stride, int q, int L, const GFn& gof, int& bj) {
+    constexpr int R = 4;   // radii per step: their 2R reads are issued together
     int best = INT32_MAX;
     bj = -1;
-    for (int r = 0; r < best; ++r) {
-        const int j0 = q - r, j1 = q + r;
-        if (j0 < 0 && j1 >= L) break;
-        if (j0 >= 0) {
-            const int gv = gof(lv[j0 * stride]);
-            if (gv >= 0) {
-                const int v = max(gv, r);
-                if (v < best) { best = v; bj = j0; }
-            }
+    for (int r0 = 0; r0 < best; r0 += R) {
+        if (q - r0 < 0 && q + r0 >= L) break;
+        int gl[R], gr[R];
+#pragma unroll
+        for (int k = 0; k < R; ++k) {
+            const int j0 = q - r0 - k, j1 = q + r0 + k;
+            gl[k] = j0 >= 0 ? gof(lv[j0 * stride]) : -1;
+            gr[k] = j1 < L ? gof(lv[j1 * stride]) : -1;
         }
-        if (r > 0 && j1 < L) {
-            const int gv = gof(lv[j1 * stride]);
-            if (gv >= 0) {
-                const int v = max(gv, r);
-                if (v < best) { best = v; bj = j1; }
-            }
+        // in the order of a one-radius-at-a-time search (radii past the end
+        // add max(g, r) >= best and change nothing)
+#pragma unroll
+        for (int k = 0; k < R; ++k) {
+            const int r = r0 + k;
+            if (gl[k] >= 0 && max(gl[k], r) < best) { best = max(gl[k], r); bj = q - r; }
+            if (r > 0 && gr[k] >= 0 && max(gr[k], r) < best) { best = max(gr[k], r); bj = q + r; }
         }
     }
     return best;
@@ -421,7 +422,7 @@ __device__ inline int linf_search(const Val* lv, int stride, int q, int L, const
 // else 1); threads take consecutive positions of the block's lines.
 template <class Geo>
 __global__ __launch_bounds__(256) void k_linf_rows(const typename Geo::Val* __restrict__ in, int L,
-                                                   int64_t nlines, int LPB, Geo geo,
+                                                   int64_t nlines, int LPB, int vec, Geo geo,
                                                    int32_t* __restrict__ dist,
                                                    int32_t* __restrict__ indices) {
     using Val = typename Geo::Val;
@@ -435,10 +436,26 @@ __global__ __launch_bounds__(256) void k_linf_rows(const typename Geo::Val* __re
     for (int l = tid; l < LPB; l += nt) any[l] = 0;
     __syncthreads();
     const Val* src = in + line0 * (int64_t)L;
-    for (int e = tid; e < total; e += nt) {
-        const Val v = src[e];
-        sv[e] = v;
-        if (Geo::valid(v)) any[e / L] = 1;   // every writer stores the same 1
+    if (vec) {   // 16-byte pieces, each within one line (L * sizeof(Val) % 16 == 0)
+        constexpr int VN = 16 / (int)sizeof(Val);
+        const int npc = total / VN;
+#pragma unroll 4
+        for (int i = tid; i < npc; i += nt) {
+            const uint4 w = reinterpret_cast<const uint4*>(src)[i];
+            reinterpret_cast<uint4*>(sv)[i] = w;
+            const Val* pv = reinterpret_cast<const Val*>(&w);
+            bool ok = false;
+#pragma unroll
+            for (int k = 0; k < VN; ++k) ok |= Geo::valid(pv[k]);
+            if (ok) any[(i * VN) / L] = 1;   // every writer stores the same 1
+        }
+    } else {
+#pragma unroll 4
+        for (int e = tid; e < total; e += nt) {
+            const Val v = src[e];
+            sv[e] = v;
+            if (Geo::valid(v)) any[e / L] = 1;
+        }
     }
     __syncthreads();
     for (int e = tid; e < total; e += nt) {
@@ -468,7 +485,7 @@ __global__ __launch_bounds__(256) void k_linf_rows(const typename Geo::Val* __re
 // packed (axis0 << 16 | axis1) owner, kNone32 for a column without a source.
 __global__ __launch_bounds__(256) void k_linf_cols(const uint16_t* __restrict__ c0,
                                                    uint32_t* __restrict__ out, int D, int H, int W,
-                                                   int TW) {
+                                                   int TW, int vec) {
     extern __shared__ __align__(16) unsigned char smem[];
     uint16_t* sv = reinterpret_cast<uint16_t*>(smem);                              // [H][TW]
     int* any = reinterpret_cast<int*>(smem + linf_flags_offset((size_t)H * TW * 2));   // [TW]
@@ -482,11 +499,26 @@ __global__ __launch_bounds__(256) void k_linf_cols(const uint16_t* __restrict__ 
     uint32_t* dst = out + plane * (int64_t)H * W + w0;
     for (int x = tid; x < TW; x += 256) any[x] = 0;
     __syncthreads();
-    for (int e = tid; e < H * TW; e += 256) {
-        const int y = e / TW, x = e - y * TW;
-        const uint16_t v = x < tw ? src[(int64_t)y * W + x] : kNone16;
-        sv[e] = v;
-        if (v != kNone16) any[x] = 1;   // every writer stores the same 1
+    if (vec && tw == TW) {   // rows of the tile in 16-byte pieces of 8 columns
+        const int pr = TW / 8;   // pieces per row
+#pragma unroll 4
+        for (int i = tid; i < H * pr; i += 256) {
+            const int y = i / pr, k = i - y * pr;
+            const uint4 w = *reinterpret_cast<const uint4*>(src + (int64_t)y * W + 8 * k);
+            reinterpret_cast<uint4*>(sv + y * TW)[k] = w;
+            const uint16_t* pv = reinterpret_cast<const uint16_t*>(&w);
+#pragma unroll
+            for (int c = 0; c < 8; ++c)
+                if (pv[c] != kNone16) any[8 * k + c] = 1;   // every writer stores the same 1
+        }
+    } else {
+#pragma unroll 4
+        for (int e = tid; e < H * TW; e += 256) {
+            const int y = e / TW, x = e - y * TW;
+            const uint16_t v = x < tw ? src[(int64_t)y * W + x] : kNone16;
+            sv[e] = v;
+            if (v != kNone16) any[x] = 1;
+        }
     }
     __syncthreads();
     const int x = tid % TW, yg = tid / TW, ys = 256 / TW;
@@ -574,9 +606,10 @@ hipError_t launch_linf_rows_t(const typename Geo::Val* in, int L, int64_t nlines
     const size_t lds = linf_flags_offset((size_t)LPB * L * sizeof(Val)) + (size_t)LPB * 4;
     const int64_t blocks = (nlines + LPB - 1) / LPB;
     if (blocks > INT32_MAX || lds > 160 * 1024) return hipErrorInvalidValue;
+    const int vec = ((size_t)L * sizeof(Val) % 16 == 0 && ((uintptr_t)in & 15) == 0) ? 1 : 0;
     EDT_LAUNCH(tm, "chessboard_rows", s,
                hipLaunchKernelGGL(k_linf_rows<Geo>, dim3((unsigned)blocks), dim3(256), lds, s, in, L,
-                                  nlines, LPB, geo, dist, indices));
+                                  nlines, LPB, vec, geo, dist, indices));
     return hipSuccess;
 }
 
@@ -594,15 +627,18 @@ hipError_t launch_linf_cols_3d(const uint16_t* c0, int B, int D, int H, int W, u
         linf_allow_lds((const void*)k_linf_cols);
         attr = true;
     }
-    int TW = 64;   // columns per block: their H rows of 2-byte values within 64 KB
-    while (TW > 1 && (size_t)H * TW * 2 > 64 * 1024) TW >>= 1;
+    int TW = 32;   // columns per block: their H rows of 2-byte values within 32 KB (64 KB
+                   // for one column of the longest lines), several blocks per CU
+    while (TW > 1 && (size_t)H * TW * 2 > 32 * 1024) TW >>= 1;
     if ((size_t)H * TW * 2 > 64 * 1024) return hipErrorInvalidValue;
     const size_t lds = linf_flags_offset((size_t)H * TW * 2) + (size_t)TW * 4;
     const int64_t blocks = (int64_t)B * D * ((W + TW - 1) / TW);
     if (blocks > INT32_MAX) return hipErrorInvalidValue;
+    // 16-byte pieces: rows 16-byte aligned and tiles of whole pieces
+    const int vec = (W % 8 == 0 && TW % 8 == 0 && ((uintptr_t)c0 & 15) == 0) ? 1 : 0;
     EDT_LAUNCH(tm, "chessboard_cols", s,
                hipLaunchKernelGGL(k_linf_cols, dim3((unsigned)blocks), dim3(256), lds, s, c0, c01, D, H,
-                                  W, TW));
+                                  W, TW, vec));
     return hipSuccess;
 }
 
