@@ -1,4 +1,4 @@
-"""The transforms inside a HIP graph (GPU).
+"""The transforms inside a HIP graph (GPU): EDT 2-D and 3-D, taxicab 3-D, chessboard 2-D.
 
 With outputs and workspace passed in, a call only launches kernels on the
 caller's stream (no allocation, no memset, no synchronisation), so a caller
@@ -11,7 +11,7 @@ import pytest
 
 pytestmark = pytest.mark.gpu
 
-KINDS = ["edt2d", "edt3d", "taxicab3d"]
+KINDS = ["edt2d", "edt3d", "taxicab3d", "chessboard2d"]
 
 
 @pytest.fixture(scope="module")
@@ -30,9 +30,9 @@ def _say(msg):
 @pytest.mark.parametrize("kind", KINDS)
 def test_graph_replay(torch_dev, kind):
     torch, dev = torch_dev
-    from exact_euclidean_distance_amd import api, edt2d, edt3d, taxicab
+    from exact_euclidean_distance_amd import api, chessboard, edt2d, edt3d, taxicab
     rng = np.random.default_rng([42, 6001 + KINDS.index(kind)])
-    if kind == "edt2d":
+    if kind in ("edt2d", "chessboard2d"):
         shape, sampling = (3, 300, 517), None   # unit spacing: squared distances too
         ws_bytes = api.workspace_size_2d_batched(*shape)
     else:
@@ -47,6 +47,8 @@ def test_graph_replay(torch_dev, kind):
             return edt2d(m, sampling, return_sqdist=True, return_indices=True, **out)
         if kind == "edt3d":
             return edt3d(m, sampling, return_indices=True, **out)
+        if kind == "chessboard2d":
+            return chessboard(m, return_indices=True, **out)
         return taxicab(m, return_indices=True, **out)
 
     def fields(r):
