@@ -419,7 +419,10 @@ __device__ inline int linf_search(const Val* lv, int stride, int q, int L, const
 }
 
 // LPB lines of L values per block (L <= kLinfStage: LPB = kLinfStage / L,
-// else 1); threads take consecutive positions of the block's lines.
+// else 1).  The lines are staged as g (16 bits, kNone16 for no source: g <=
+// 65534 on every accepted shape); threads take consecutive positions of the
+// block's lines, and the winner's source value is read back from the input
+// for its index.
 template <class Geo>
 __global__ __launch_bounds__(256) void k_linf_rows(const typename Geo::Val* __restrict__ in, int L,
                                                    int64_t nlines, int LPB, int vec, Geo geo,
@@ -427,59 +430,79 @@ __global__ __launch_bounds__(256) void k_linf_rows(const typename Geo::Val* __re
                                                    int32_t* __restrict__ indices) {
     using Val = typename Geo::Val;
     extern __shared__ __align__(16) unsigned char smem[];
-    Val* sv = reinterpret_cast<Val*>(smem);                                       // [LPB][L]
-    int* any = reinterpret_cast<int*>(smem + linf_flags_offset((size_t)LPB * L * sizeof(Val)));
+    uint16_t* sg = reinterpret_cast<uint16_t*>(smem);                              // [LPB][L]
+    int* any = reinterpret_cast<int*>(smem + linf_flags_offset((size_t)LPB * L * 2));   // [LPB]
+    unsigned* ctx = reinterpret_cast<unsigned*>(any + LPB);                          // [LPB]
     const int tid = threadIdx.x, nt = blockDim.x;
     const int64_t line0 = (int64_t)blockIdx.x * LPB;
     const int nl = (int)min<int64_t>(LPB, nlines - line0);
     const int total = nl * L;
-    for (int l = tid; l < LPB; l += nt) any[l] = 0;
+    for (int l = tid; l < LPB; l += nt) {
+        any[l] = 0;
+        ctx[l] = geo.ctx(line0 + (l < nl ? l : 0));
+    }
     __syncthreads();
     const Val* src = in + line0 * (int64_t)L;
+    auto gval = [&](Val v, unsigned c) -> uint16_t {
+        return Geo::valid(v) ? (uint16_t)geo.g(c, v) : kNone16;
+    };
     if (vec) {   // 16-byte pieces, each within one line (L * sizeof(Val) % 16 == 0)
         constexpr int VN = 16 / (int)sizeof(Val);
         const int npc = total / VN;
 #pragma unroll 4
         for (int i = tid; i < npc; i += nt) {
             const uint4 w = reinterpret_cast<const uint4*>(src)[i];
-            reinterpret_cast<uint4*>(sv)[i] = w;
+            const int l = (i * VN) / L;
+            const unsigned c = ctx[l];
             const Val* pv = reinterpret_cast<const Val*>(&w);
+            uint16_t gs[VN];
             bool ok = false;
 #pragma unroll
-            for (int k = 0; k < VN; ++k) ok |= Geo::valid(pv[k]);
-            if (ok) any[(i * VN) / L] = 1;   // every writer stores the same 1
+            for (int k = 0; k < VN; ++k) {
+                gs[k] = gval(pv[k], c);
+                ok |= gs[k] != kNone16;
+            }
+            if constexpr (VN == 8) {
+                reinterpret_cast<uint4*>(sg)[i] =
+                    make_uint4(gs[0] | ((uint32_t)gs[1] << 16), gs[2] | ((uint32_t)gs[3] << 16),
+                               gs[4] | ((uint32_t)gs[5] << 16), gs[6] | ((uint32_t)gs[7] << 16));
+            } else {
+                reinterpret_cast<uint2*>(sg)[i] =
+                    make_uint2(gs[0] | ((uint32_t)gs[1] << 16), gs[2] | ((uint32_t)gs[3] << 16));
+            }
+            if (ok) any[l] = 1;   // every writer stores the same 1
         }
     } else {
 #pragma unroll 4
         for (int e = tid; e < total; e += nt) {
-            const Val v = src[e];
-            sv[e] = v;
-            if (Geo::valid(v)) any[e / L] = 1;
+            const int l = e / L;
+            const uint16_t gv = gval(src[e], ctx[l]);
+            sg[e] = gv;
+            if (gv != kNone16) any[l] = 1;
         }
     }
     __syncthreads();
+    auto gof = [](uint16_t gv) { return gv != kNone16 ? (int)gv : -1; };
     for (int e = tid; e < total; e += nt) {
         const int l = e / L, q = e - l * L;
         const int64_t ln = line0 + l;
-        const unsigned c = geo.ctx(ln);
+        const unsigned c = ctx[l];
         int best;
         int32_t ix;
         if (!any[l]) {   // no source on the line: only in an image without background
             best = geo.virt(c, q);
             ix = geo.virt_index();
         } else {
-            const Val* lv = sv + l * L;
             int bj;
-            auto gof = [&](Val v) { return Geo::valid(v) ? geo.g(c, v) : -1; };
-            best = linf_search(lv, 1, q, L, gof, bj);
-            ix = geo.index(c, lv[bj], bj);
+            best = linf_search(sg + l * L, 1, q, L, gof, bj);
+            ix = geo.index(c, src[(int64_t)l * L + bj], bj);
         }
         if (dist) dist[ln * (int64_t)L + q] = best;
         if (indices) indices[ln * (int64_t)L + q] = ix;
     }
 }
 
-// Middle axis of B volumes: a block stages TW neighbouring columns (w0 ..
+// Middle axis of B volumes: a block stages g of TW neighbouring columns (w0 ..
 // w0 + TW - 1) of one plane (volume, d), all H rows, as sv[y][x]; thread x of
 // row group yg answers rows yg, yg + 256 / TW, ... of column x.  Output: the
 // packed (axis0 << 16 | axis1) owner, kNone32 for a column without a source.
@@ -499,38 +522,47 @@ __global__ __launch_bounds__(256) void k_linf_cols(const uint16_t* __restrict__ 
     uint32_t* dst = out + plane * (int64_t)H * W + w0;
     for (int x = tid; x < TW; x += 256) any[x] = 0;
     __syncthreads();
+    // staged as g = |d - axis0| (kNone16: no source)
+    auto gval = [&](uint16_t v) -> uint16_t {
+        return v != kNone16 ? (uint16_t)(d > (int)v ? d - (int)v : (int)v - d) : kNone16;
+    };
     if (vec && tw == TW) {   // rows of the tile in 16-byte pieces of 8 columns
         const int pr = TW / 8;   // pieces per row
 #pragma unroll 4
         for (int i = tid; i < H * pr; i += 256) {
             const int y = i / pr, k = i - y * pr;
             const uint4 w = *reinterpret_cast<const uint4*>(src + (int64_t)y * W + 8 * k);
-            reinterpret_cast<uint4*>(sv + y * TW)[k] = w;
             const uint16_t* pv = reinterpret_cast<const uint16_t*>(&w);
+            uint16_t gs[8];
 #pragma unroll
-            for (int c = 0; c < 8; ++c)
-                if (pv[c] != kNone16) any[8 * k + c] = 1;   // every writer stores the same 1
+            for (int c = 0; c < 8; ++c) {
+                gs[c] = gval(pv[c]);
+                if (gs[c] != kNone16) any[8 * k + c] = 1;   // every writer stores the same 1
+            }
+            reinterpret_cast<uint4*>(sv + y * TW)[k] =
+                make_uint4(gs[0] | ((uint32_t)gs[1] << 16), gs[2] | ((uint32_t)gs[3] << 16),
+                           gs[4] | ((uint32_t)gs[5] << 16), gs[6] | ((uint32_t)gs[7] << 16));
         }
     } else {
 #pragma unroll 4
         for (int e = tid; e < H * TW; e += 256) {
             const int y = e / TW, x = e - y * TW;
-            const uint16_t v = x < tw ? src[(int64_t)y * W + x] : kNone16;
-            sv[e] = v;
-            if (v != kNone16) any[x] = 1;
+            const uint16_t gv = x < tw ? gval(src[(int64_t)y * W + x]) : kNone16;
+            sv[e] = gv;
+            if (gv != kNone16) any[x] = 1;
         }
     }
     __syncthreads();
     const int x = tid % TW, yg = tid / TW, ys = 256 / TW;
     if (x >= tw || yg >= ys) return;   // no barrier follows
     const bool has = any[x] != 0;
-    auto gof = [&](uint16_t v) { return v != kNone16 ? (d > (int)v ? d - (int)v : (int)v - d) : -1; };
+    auto gof = [](uint16_t gv) { return gv != kNone16 ? (int)gv : -1; };
     for (int y = yg; y < H; y += ys) {
         uint32_t o = kNone32;
         if (has) {
             int bj;
             linf_search(sv + x, TW, y, H, gof, bj);
-            o = ((uint32_t)sv[bj * TW + x] << 16) | (uint32_t)bj;
+            o = ((uint32_t)src[(int64_t)bj * W + x] << 16) | (uint32_t)bj;
         }
         dst[(int64_t)y * W + x] = o;
     }
@@ -603,7 +635,7 @@ hipError_t launch_linf_rows_t(const typename Geo::Val* in, int L, int64_t nlines
         attr = true;
     }
     const int LPB = L <= kLinfStage ? kLinfStage / L : 1;
-    const size_t lds = linf_flags_offset((size_t)LPB * L * sizeof(Val)) + (size_t)LPB * 4;
+    const size_t lds = linf_flags_offset((size_t)LPB * L * 2) + (size_t)LPB * 8;
     const int64_t blocks = (nlines + LPB - 1) / LPB;
     if (blocks > INT32_MAX || lds > 160 * 1024) return hipErrorInvalidValue;
     const int vec = ((size_t)L * sizeof(Val) % 16 == 0 && ((uintptr_t)in & 15) == 0) ? 1 : 0;
