@@ -386,6 +386,7 @@ struct LinfRows3D {
 };
 
 constexpr int kLinfStage = 2048;   // lines up to this length share a block
+constexpr int kLinfThreads = 512;  // threads per block of either search pass
 
 __host__ __device__ inline size_t linf_flags_offset(size_t bytes) { return (bytes + 15) & ~size_t(15); }
 
@@ -424,7 +425,7 @@ __device__ inline int linf_search(const Val* lv, int stride, int q, int L, const
 // block's lines, and the winner's source value is read back from the input
 // for its index.
 template <class Geo>
-__global__ __launch_bounds__(256) void k_linf_rows(const typename Geo::Val* __restrict__ in, int L,
+__global__ __launch_bounds__(kLinfThreads) void k_linf_rows(const typename Geo::Val* __restrict__ in, int L,
                                                    int64_t nlines, int LPB, int vec, Geo geo,
                                                    int32_t* __restrict__ dist,
                                                    int32_t* __restrict__ indices) {
@@ -504,9 +505,9 @@ __global__ __launch_bounds__(256) void k_linf_rows(const typename Geo::Val* __re
 
 // Middle axis of B volumes: a block stages g of TW neighbouring columns (w0 ..
 // w0 + TW - 1) of one plane (volume, d), all H rows, as sv[y][x]; thread x of
-// row group yg answers rows yg, yg + 256 / TW, ... of column x.  Output: the
+// row group yg answers rows yg, yg + kLinfThreads / TW, ... of column x.  Output: the
 // packed (axis0 << 16 | axis1) owner, kNone32 for a column without a source.
-__global__ __launch_bounds__(256) void k_linf_cols(const uint16_t* __restrict__ c0,
+__global__ __launch_bounds__(kLinfThreads) void k_linf_cols(const uint16_t* __restrict__ c0,
                                                    uint32_t* __restrict__ out, int D, int H, int W,
                                                    int TW, int vec) {
     extern __shared__ __align__(16) unsigned char smem[];
@@ -520,7 +521,7 @@ __global__ __launch_bounds__(256) void k_linf_cols(const uint16_t* __restrict__ 
     const int tw = min(TW, W - w0);                    // columns of this tile
     const uint16_t* src = c0 + plane * (int64_t)H * W + w0;
     uint32_t* dst = out + plane * (int64_t)H * W + w0;
-    for (int x = tid; x < TW; x += 256) any[x] = 0;
+    for (int x = tid; x < TW; x += kLinfThreads) any[x] = 0;
     __syncthreads();
     // staged as g = |d - axis0| (kNone16: no source)
     auto gval = [&](uint16_t v) -> uint16_t {
@@ -529,7 +530,7 @@ __global__ __launch_bounds__(256) void k_linf_cols(const uint16_t* __restrict__ 
     if (vec && tw == TW) {   // rows of the tile in 16-byte pieces of 8 columns
         const int pr = TW / 8;   // pieces per row
 #pragma unroll 4
-        for (int i = tid; i < H * pr; i += 256) {
+        for (int i = tid; i < H * pr; i += kLinfThreads) {
             const int y = i / pr, k = i - y * pr;
             const uint4 w = *reinterpret_cast<const uint4*>(src + (int64_t)y * W + 8 * k);
             const uint16_t* pv = reinterpret_cast<const uint16_t*>(&w);
@@ -545,7 +546,7 @@ __global__ __launch_bounds__(256) void k_linf_cols(const uint16_t* __restrict__ 
         }
     } else {
 #pragma unroll 4
-        for (int e = tid; e < H * TW; e += 256) {
+        for (int e = tid; e < H * TW; e += kLinfThreads) {
             const int y = e / TW, x = e - y * TW;
             const uint16_t gv = x < tw ? gval(src[(int64_t)y * W + x]) : kNone16;
             sv[e] = gv;
@@ -553,7 +554,7 @@ __global__ __launch_bounds__(256) void k_linf_cols(const uint16_t* __restrict__ 
         }
     }
     __syncthreads();
-    const int x = tid % TW, yg = tid / TW, ys = 256 / TW;
+    const int x = tid % TW, yg = tid / TW, ys = kLinfThreads / TW;
     if (x >= tw || yg >= ys) return;   // no barrier follows
     const bool has = any[x] != 0;
     auto gof = [](uint16_t gv) { return gv != kNone16 ? (int)gv : -1; };
@@ -640,7 +641,7 @@ hipError_t launch_linf_rows_t(const typename Geo::Val* in, int L, int64_t nlines
     if (blocks > INT32_MAX || lds > 160 * 1024) return hipErrorInvalidValue;
     const int vec = ((size_t)L * sizeof(Val) % 16 == 0 && ((uintptr_t)in & 15) == 0) ? 1 : 0;
     EDT_LAUNCH(tm, "chessboard_rows", s,
-               hipLaunchKernelGGL(k_linf_rows<Geo>, dim3((unsigned)blocks), dim3(256), lds, s, in, L,
+               hipLaunchKernelGGL(k_linf_rows<Geo>, dim3((unsigned)blocks), dim3(kLinfThreads), lds, s, in, L,
                                   nlines, LPB, vec, geo, dist, indices));
     return hipSuccess;
 }
@@ -669,7 +670,7 @@ hipError_t launch_linf_cols_3d(const uint16_t* c0, int B, int D, int H, int W, u
     // 16-byte pieces: rows 16-byte aligned and tiles of whole pieces
     const int vec = (W % 8 == 0 && TW % 8 == 0 && ((uintptr_t)c0 & 15) == 0) ? 1 : 0;
     EDT_LAUNCH(tm, "chessboard_cols", s,
-               hipLaunchKernelGGL(k_linf_cols, dim3((unsigned)blocks), dim3(256), lds, s, c0, c01, D, H,
+               hipLaunchKernelGGL(k_linf_cols, dim3((unsigned)blocks), dim3(kLinfThreads), lds, s, c0, c01, D, H,
                                   W, TW, vec));
     return hipSuccess;
 }
