@@ -509,10 +509,11 @@ def test_taxicab(torch_dev):
     torch, dev = torch_dev
     from exact_euclidean_distance_amd import taxicab
     rng = np.random.default_rng([42, 5012])
-    # rows of 1, 2, 4 and 8 tiles of 256, of one wave and of several
+    # rows of 1, 2, 4 and 8 tiles of 256, of one wave and of several; middle
+    # axes up to 32768
     cases = [(1, 1), (1, 70), (37, 1), (64, 64), (4, 300), (33, 517), (3, 1100), (5, 20000),
              (3, 40, 70), (2, 13, 17, 30), (3, 9, 40, 64), (2, 3, 5, 400), (1, 5, 1100, 33),
-             (1, 2, 3, 2000)]
+             (1, 2, 3, 2000), (2, 1, 4100, 3), (2, 1, 32768, 2)]
     for shape in cases:
         # (dense backgrounds only on small cases: the oracle is a brute force)
         for p in ((0.003, 0.1, 0.6) if np.prod(shape) <= 20000 else (0.002,)):
@@ -589,7 +590,7 @@ def test_chessboard(torch_dev):
     rng = np.random.default_rng([42, 5014])
     cases = [(1, 1), (1, 70), (37, 1), (64, 64), (4, 300), (33, 517), (3, 1100), (5, 20000),
              (3, 40, 70), (2, 13, 17, 30), (3, 9, 40, 64), (2, 3, 5, 400), (1, 5, 1100, 33),
-             (1, 2, 3, 2000), (1, 3, 700, 9)]
+             (1, 2, 3, 2000), (1, 3, 700, 9), (2, 1, 4100, 3), (2, 1, 32768, 2)]
     for shape in cases:
         for p in ((0.003, 0.1, 0.6) if np.prod(shape) <= 20000 else (0.002,)):
             m = (rng.random(shape) >= p).astype(np.uint8)
