@@ -621,20 +621,13 @@ hipError_t launch_l1_rows_3d(const uint32_t* c01, int B, int D, int H, int W, in
 
 namespace {
 
-void linf_allow_lds(const void* fn) {
-    if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) != hipSuccess)
-        (void)hipGetLastError();
-}
-
 template <class Geo>
 hipError_t launch_linf_rows_t(const typename Geo::Val* in, int L, int64_t nlines, const Geo& geo,
                               int32_t* dist, int32_t* indices, hipStream_t s, KernelTimer* tm) {
     using Val = typename Geo::Val;
-    static bool attr = false;
-    if (!attr) {
-        linf_allow_lds((const void*)k_linf_rows<Geo>);
-        attr = true;
-    }
+    static unsigned long long lds_done = 0;
+    hipError_t le = large_lds_once((const void*)k_linf_rows<Geo>, &lds_done);
+    if (le != hipSuccess) return le;
     const int LPB = L <= kLinfStage ? kLinfStage / L : 1;
     const size_t lds = linf_flags_offset((size_t)LPB * L * 2) + (size_t)LPB * 8;
     const int64_t blocks = (nlines + LPB - 1) / LPB;
@@ -655,11 +648,9 @@ hipError_t launch_linf_rows_2d(const uint16_t* c0, int B, int H, int W, int32_t*
 
 hipError_t launch_linf_cols_3d(const uint16_t* c0, int B, int D, int H, int W, uint32_t* c01,
                                hipStream_t s, KernelTimer* tm) {
-    static bool attr = false;
-    if (!attr) {
-        linf_allow_lds((const void*)k_linf_cols);
-        attr = true;
-    }
+    static unsigned long long lds_done = 0;
+    hipError_t le = large_lds_once((const void*)k_linf_cols, &lds_done);
+    if (le != hipSuccess) return le;
     int TW = 32;   // columns per block: their H rows of 2-byte values within 32 KB (64 KB
                    // for one column of the longest lines), several blocks per CU
     while (TW > 1 && (size_t)H * TW * 2 > 32 * 1024) TW >>= 1;

@@ -89,6 +89,12 @@ hipError_t launch_linf_cols_3d(const uint16_t* c0, int B, int D, int H, int W, u
 hipError_t launch_linf_rows_3d(const uint32_t* c01, int B, int D, int H, int W, int32_t* dist,
                                int32_t* indices, hipStream_t s, KernelTimer* tm);
 
+// Raise a kernel's dynamic-LDS ceiling to the gfx950 LDS size on the current
+// device, once per device (done[] holds one bit per device id, set
+// atomically; devices past 63 set it on every call).  A failure is not fatal
+// here: a launch that really needs more LDS fails on its own.
+hipError_t large_lds_once(const void* fn, unsigned long long* done);
+
 // Dynamic LDS each envelope launch needs (0 if the line is too long).
 size_t rows_lds_bytes(int L, int value_bytes);
 size_t cols_lds_bytes(int H);

@@ -34,11 +34,16 @@ namespace edt {
 
 __host__ __device__ inline size_t align16(size_t x) { return (x + 15) & ~size_t(15); }
 
-// Raise the dynamic-LDS ceiling of a kernel to the gfx950 LDS size.  A failure
-// is not fatal here: a launch that really needs more LDS fails on its own.
-static void allow_large_lds(const void* fn) {
+hipError_t large_lds_once(const void* fn, unsigned long long* done) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const unsigned long long bit = dev < 64 ? 1ull << dev : 0ull;
+    if (bit && (__atomic_load_n(done, __ATOMIC_ACQUIRE) & bit)) return hipSuccess;
     if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) != hipSuccess)
         (void)hipGetLastError();
+    if (bit) __atomic_fetch_or(done, bit, __ATOMIC_RELEASE);
+    return hipSuccess;
 }
 
 hipError_t KernelTimer::begin(const char* kname, hipStream_t s) {
@@ -1286,11 +1291,9 @@ template <class Geo, int K, int VW, class Ix>
 static hipError_t launch_rows_t(const typename Geo::Val* in, int L, int64_t nlines, const RowPlan& p,
                                 const Geo& geo, int32_t* sqdist, float* dist, Ix* indices,
                                 hipStream_t s, KernelTimer* tm, const char* kname) {
-    static bool attr_done = false;
-    if (!attr_done) {
-        allow_large_lds((const void*)k_envelope_rows<Geo, K, VW, Ix>);
-        attr_done = true;
-    }
+    static unsigned long long lds_done = 0;
+    hipError_t le = large_lds_once((const void*)k_envelope_rows<Geo, K, VW, Ix>, &lds_done);
+    if (le != hipSuccess) return le;
     const int64_t nblocks = (nlines + p.LPW - 1) / p.LPW;
     const bool aligned16 = (((uintptr_t)sqdist | (uintptr_t)dist | (uintptr_t)indices) & 15) == 0;
     const int vec_out = (L % 4 == 0 && aligned16) ? 1 : 0;
@@ -1488,11 +1491,9 @@ template <int K, int TW>
 static hipError_t launch_cols_t(const uint16_t* c0, int B, int D, int H, int W, double s2_0,
                                 double s2_1, uint32_t* c01, const ColPlan& p, hipStream_t s,
                                 KernelTimer* tm) {
-    static bool attr = false;
-    if (!attr) {
-        allow_large_lds((const void*)k_envelope_cols<K, TW>);
-        attr = true;
-    }
+    static unsigned long long lds_done = 0;
+    hipError_t le = large_lds_once((const void*)k_envelope_cols<K, TW>, &lds_done);
+    if (le != hipSuccess) return le;
     const int tiles = (W + TW - 1) / TW;
     const int64_t nblocks = (int64_t)B * D * tiles;
     EDT_LAUNCH(tm, "envelope_cols_3d", s,
