@@ -1,6 +1,6 @@
-// chamfer.hip -- the city-block (taxicab, L1) distance transform, one of the
-// chamfer transforms TorchMorph ships beside its EDT (the pages name them
-// without defining them; read as the L1 metric, SciPy's `taxicab`).
+// chamfer.hip -- the chamfer transforms TorchMorph ships beside its EDT (the
+// pages name them without defining them; read as the L1 and L-infinity
+// metrics, SciPy's `taxicab` and `chessboard`).
 //
 // The L1 distance is a sum of per-axis terms, so it separates like the EDT:
 // after the axis-0 pass (the nearest background row of each column is the
@@ -8,8 +8,9 @@
 //   h(q) = min_j ( |q - j| + g(j) )
 //        = min( q + min_{j <= q} (g(j) - j),  -q + min_{j >= q} (g(j) + j) ),
 // a prefix minimum and a suffix minimum -- no envelope is needed.  Minima are
-// taken over packed 64-bit keys ((value + offset) << 32 | j), so that one
-// integer minimum gives both the value and its (smallest) position.
+// taken over packed 64-bit keys (value first, then position, and in the row
+// pass the source value too), so that one integer minimum gives the value and
+// its (smallest) position.
 //
 //   k_l1_rows   last axis + outputs: a wave takes tiles of 256 positions of a
 //               line, four consecutive positions per lane (coalesced loads
@@ -32,12 +33,13 @@
 // at most one, so the lanes of a wave stay together.  Lines without any
 // source are flagged while they are staged and never searched.
 //
-//   k_linf_cols  middle axis of a volume: a block stages TW neighbouring
-//                columns of one plane (all rows) and writes packed
-//                (axis0 << 16 | axis1) owners.
-//   k_linf_rows  last axis + outputs: a block stages whole lines (several
-//                short ones or one long one) and writes int32 distances and
-//                flat indices.
+//   k_linf_cols  middle axis of a volume: a block stages g of TW
+//                neighbouring columns of one plane (all rows, 16 bits each)
+//                and writes packed (axis0 << 16 | axis1) owners.
+//   k_linf_rows  last axis + outputs: a block stages g of whole lines
+//                (several short ones or one long one) and writes int32
+//                distances and flat indices; the winner's source value is
+//                read back from the input for its index.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
