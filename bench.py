@@ -399,8 +399,8 @@ def main(argv=None):
         return summarize_traffic(*args.summarize_traffic, args.config)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build measures one GPU only (the transform of one "
-              "workload runs on a single MI355X); run with --gpus 1", file=sys.stderr)
+        print("bench.py: measures one GPU only (the transform of one workload runs "
+              "on a single MI355X); run with --gpus 1", file=sys.stderr)
         return 2
 
     if args.probe_copy:
