@@ -1395,19 +1395,23 @@ struct ColPlan {
     size_t lds;
 };
 
-// H <= 512: chunks of 32 and 64 / Gp lines per block (at least 8); longer
-// lines: chunks of 64 and 512 / Gp lines per block (32 lines up to H = 1024,
+// H <= 128: chunks of 16 (16 x 128^3: 0.28 -> 0.26 ms against chunks of 32;
+// at H = 512 they cost 0.48 -> 0.65 ms); H <= 512: chunks of 32.  Both with
+// 64 / Gp lines per block (at least 8).  Longer lines: chunks of 64 and 512 /
+// Gp lines per block (32 lines up to H = 1024,
 // one line at H = 32768), so that a block's 512 slots of values and marks
 // stay within the LDS (narrower tiles mean smaller blocks, more of them
 // resident per CU).
 static ColPlan plan_cols(int H) {
     ColPlan p{};
-    p.K = H <= 512 ? 32 : 64;
+    p.K = H <= 128 ? 16 : H <= 512 ? 32 : 64;
     p.Gp = 1;
     while (p.Gp * p.K < H) p.Gp <<= 1;
     // the narrowest tile that still fills one wave (8 lines at the least)
     p.TW = p.K == 64 ? (512 / p.Gp > 0 ? 512 / p.Gp : 0) : (64 / p.Gp > 8 ? 64 / p.Gp : 8);
-    p.lds = p.K == 32 ? Slots<uint16_t, 32>::bytes(p.Gp * p.TW, p.Gp) : Slots<uint16_t, 64>::bytes(p.Gp * p.TW, p.Gp);
+    const int n = p.Gp * p.TW;
+    p.lds = p.K == 16 ? Slots<uint16_t, 16>::bytes(n, p.Gp)
+            : p.K == 32 ? Slots<uint16_t, 32>::bytes(n, p.Gp) : Slots<uint16_t, 64>::bytes(n, p.Gp);
     return p;
 }
 
@@ -1514,6 +1518,14 @@ hipError_t launch_cols_3d(const uint16_t* c0, int B, int D, int H, int W, double
             case 2: return launch_cols_t<64, 2>(c0, B, D, H, W, s2_0, s2_1, c01, p, s, tm);
             case 1: return launch_cols_t<64, 1>(c0, B, D, H, W, s2_0, s2_1, c01, p, s, tm);
             default: return hipErrorInvalidValue;
+        }
+    }
+    if (p.K == 16) {
+        switch (p.TW) {
+            case 8: return launch_cols_t<16, 8>(c0, B, D, H, W, s2_0, s2_1, c01, p, s, tm);
+            case 16: return launch_cols_t<16, 16>(c0, B, D, H, W, s2_0, s2_1, c01, p, s, tm);
+            case 32: return launch_cols_t<16, 32>(c0, B, D, H, W, s2_0, s2_1, c01, p, s, tm);
+            default: return launch_cols_t<16, 64>(c0, B, D, H, W, s2_0, s2_1, c01, p, s, tm);
         }
     }
     switch (p.TW) {
