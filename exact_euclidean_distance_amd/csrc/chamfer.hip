@@ -30,8 +30,10 @@
 // itself over its line staged in LDS (r = 0, 1, 2, ...): a source r away adds
 // at least r, so the search ends once r reaches the best value found.  The
 // work per position is its own distance along the axis; neighbours differ by
-// at most one, so the lanes of a wave stay together.  Lines without any
-// source are flagged while they are staged and never searched.
+// at most one, so the lanes of a wave stay together.  Sources are counted
+// while a line is staged: a line without any is never searched, and one with
+// at most kLinfList of them lists them and takes the minimum over the list
+// (a line with one far source would otherwise walk all the way to it).
 //
 //   k_linf_cols  middle axis of a volume: a block stages g of TW
 //                neighbouring columns of one plane (all rows, 16 bits each)
@@ -389,6 +391,7 @@ struct LinfRows3D {
 
 constexpr int kLinfStage = 2048;   // lines up to this length share a block
 constexpr int kLinfThreads = 512;  // threads per block of either search pass
+constexpr int kLinfList = 32;      // lines with at most this many sources scan them as a list
 
 __host__ __device__ inline size_t linf_flags_offset(size_t bytes) { return (bytes + 15) & ~size_t(15); }
 
@@ -421,6 +424,25 @@ __device__ inline int linf_search(const Val* lv, int stride, int q, int L, const
     return best;
 }
 
+// The same minimum over a line's n sources listed by position (any order):
+// for lines with few sources, whose outward search would walk far.
+template <class GAt>
+__device__ inline int linf_list(const uint16_t* lst, int n, int q, const GAt& gat, int& bj) {
+    int best = INT32_MAX, bd = INT32_MAX;
+    bj = -1;
+    for (int i = 0; i < n; ++i) {
+        const int j = lst[i];
+        const int dj = q > j ? q - j : j - q;
+        const int v = max(gat(j), dj);
+        if (v < best || (v == best && (dj < bd || (dj == bd && j < bj)))) {
+            best = v;
+            bd = dj;
+            bj = j;
+        }
+    }
+    return best;
+}
+
 // LPB lines of L values per block (L <= kLinfStage: LPB = kLinfStage / L,
 // else 1).  The lines are staged as g (16 bits, kNone16 for no source: g <=
 // 65534 on every accepted shape); threads take consecutive positions of the
@@ -434,14 +456,18 @@ __global__ __launch_bounds__(kLinfThreads) void k_linf_rows(const typename Geo::
     using Val = typename Geo::Val;
     extern __shared__ __align__(16) unsigned char smem[];
     uint16_t* sg = reinterpret_cast<uint16_t*>(smem);                              // [LPB][L]
-    int* any = reinterpret_cast<int*>(smem + linf_flags_offset((size_t)LPB * L * 2));   // [LPB]
-    unsigned* ctx = reinterpret_cast<unsigned*>(any + LPB);                          // [LPB]
+    int* cnt = reinterpret_cast<int*>(smem + linf_flags_offset((size_t)LPB * L * 2));   // [LPB] sources
+    int* fill = cnt + LPB;                                                          // [LPB]
+    unsigned* ctx = reinterpret_cast<unsigned*>(fill + LPB);                        // [LPB]
+    uint16_t* lst = reinterpret_cast<uint16_t*>(ctx + LPB);                         // [LPB][kLinfList]
+    const bool lists = LPB <= kLinfList;   // (lines shorter than that search little anyway)
     const int tid = threadIdx.x, nt = blockDim.x;
     const int64_t line0 = (int64_t)blockIdx.x * LPB;
     const int nl = (int)min<int64_t>(LPB, nlines - line0);
     const int total = nl * L;
     for (int l = tid; l < LPB; l += nt) {
-        any[l] = 0;
+        cnt[l] = 0;
+        fill[l] = 0;
         ctx[l] = geo.ctx(line0 + (l < nl ? l : 0));
     }
     __syncthreads();
@@ -459,11 +485,11 @@ __global__ __launch_bounds__(kLinfThreads) void k_linf_rows(const typename Geo::
             const unsigned c = ctx[l];
             const Val* pv = reinterpret_cast<const Val*>(&w);
             uint16_t gs[VN];
-            bool ok = false;
+            int nv = 0;
 #pragma unroll
             for (int k = 0; k < VN; ++k) {
                 gs[k] = gval(pv[k], c);
-                ok |= gs[k] != kNone16;
+                nv += gs[k] != kNone16;
             }
             if constexpr (VN == 8) {
                 reinterpret_cast<uint4*>(sg)[i] =
@@ -473,7 +499,7 @@ __global__ __launch_bounds__(kLinfThreads) void k_linf_rows(const typename Geo::
                 reinterpret_cast<uint2*>(sg)[i] =
                     make_uint2(gs[0] | ((uint32_t)gs[1] << 16), gs[2] | ((uint32_t)gs[3] << 16));
             }
-            if (ok) any[l] = 1;   // every writer stores the same 1
+            if (nv) atomicAdd(&cnt[l], nv);
         }
     } else {
 #pragma unroll 4
@@ -481,23 +507,38 @@ __global__ __launch_bounds__(kLinfThreads) void k_linf_rows(const typename Geo::
             const int l = e / L;
             const uint16_t gv = gval(src[e], ctx[l]);
             sg[e] = gv;
-            if (gv != kNone16) any[l] = 1;
+            if (gv != kNone16) atomicAdd(&cnt[l], 1);
         }
     }
     __syncthreads();
+    if (lists) {   // the sources of lines with few of them, in any order
+        for (int e = tid; e < total; e += nt) {
+            const int l = e / L;
+            if (cnt[l] <= kLinfList && sg[e] != kNone16) {
+                const int slot = atomicAdd(&fill[l], 1);   // < cnt[l]
+                lst[l * kLinfList + slot] = (uint16_t)(e - l * L);
+            }
+        }
+        __syncthreads();
+    }
     auto gof = [](uint16_t gv) { return gv != kNone16 ? (int)gv : -1; };
     for (int e = tid; e < total; e += nt) {
         const int l = e / L, q = e - l * L;
         const int64_t ln = line0 + l;
         const unsigned c = ctx[l];
+        const int n = cnt[l];
         int best;
         int32_t ix;
-        if (!any[l]) {   // no source on the line: only in an image without background
+        if (n == 0) {   // no source on the line: only in an image without background
             best = geo.virt(c, q);
             ix = geo.virt_index();
         } else {
+            const uint16_t* lg = sg + l * L;
             int bj;
-            best = linf_search(sg + l * L, 1, q, L, gof, bj);
+            if (lists && n <= kLinfList)
+                best = linf_list(lst + l * kLinfList, n, q, [&](int j) { return (int)lg[j]; }, bj);
+            else
+                best = linf_search(lg, 1, q, L, gof, bj);
             ix = geo.index(c, src[(int64_t)l * L + bj], bj);
         }
         if (dist) dist[ln * (int64_t)L + q] = best;
@@ -514,7 +555,9 @@ __global__ __launch_bounds__(kLinfThreads) void k_linf_cols(const uint16_t* __re
                                                    int TW, int vec) {
     extern __shared__ __align__(16) unsigned char smem[];
     uint16_t* sv = reinterpret_cast<uint16_t*>(smem);                              // [H][TW]
-    int* any = reinterpret_cast<int*>(smem + linf_flags_offset((size_t)H * TW * 2));   // [TW]
+    int* cnt = reinterpret_cast<int*>(smem + linf_flags_offset((size_t)H * TW * 2));   // [TW] sources
+    int* fill = cnt + TW;                                                           // [TW]
+    uint16_t* lst = reinterpret_cast<uint16_t*>(fill + TW);                         // [TW][kLinfList]
     const int tid = threadIdx.x;
     const int tiles = (W + TW - 1) / TW;
     const int64_t plane = blockIdx.x / tiles;          // volume * D + d
@@ -523,7 +566,10 @@ __global__ __launch_bounds__(kLinfThreads) void k_linf_cols(const uint16_t* __re
     const int tw = min(TW, W - w0);                    // columns of this tile
     const uint16_t* src = c0 + plane * (int64_t)H * W + w0;
     uint32_t* dst = out + plane * (int64_t)H * W + w0;
-    for (int x = tid; x < TW; x += kLinfThreads) any[x] = 0;
+    for (int x = tid; x < TW; x += kLinfThreads) {
+        cnt[x] = 0;
+        fill[x] = 0;
+    }
     __syncthreads();
     // staged as g = |d - axis0| (kNone16: no source)
     auto gval = [&](uint16_t v) -> uint16_t {
@@ -540,7 +586,7 @@ __global__ __launch_bounds__(kLinfThreads) void k_linf_cols(const uint16_t* __re
 #pragma unroll
             for (int c = 0; c < 8; ++c) {
                 gs[c] = gval(pv[c]);
-                if (gs[c] != kNone16) any[8 * k + c] = 1;   // every writer stores the same 1
+                if (gs[c] != kNone16) atomicAdd(&cnt[8 * k + c], 1);
             }
             reinterpret_cast<uint4*>(sv + y * TW)[k] =
                 make_uint4(gs[0] | ((uint32_t)gs[1] << 16), gs[2] | ((uint32_t)gs[3] << 16),
@@ -552,19 +598,30 @@ __global__ __launch_bounds__(kLinfThreads) void k_linf_cols(const uint16_t* __re
             const int y = e / TW, x = e - y * TW;
             const uint16_t gv = x < tw ? gval(src[(int64_t)y * W + x]) : kNone16;
             sv[e] = gv;
-            if (gv != kNone16) any[x] = 1;
+            if (gv != kNone16) atomicAdd(&cnt[x], 1);
+        }
+    }
+    __syncthreads();
+    for (int e = tid; e < H * TW; e += kLinfThreads) {   // the sources of columns with few of them
+        const int y = e / TW, x = e - y * TW;
+        if (cnt[x] <= kLinfList && sv[e] != kNone16) {
+            const int slot = atomicAdd(&fill[x], 1);   // < cnt[x]
+            lst[x * kLinfList + slot] = (uint16_t)y;
         }
     }
     __syncthreads();
     const int x = tid % TW, yg = tid / TW, ys = kLinfThreads / TW;
     if (x >= tw || yg >= ys) return;   // no barrier follows
-    const bool has = any[x] != 0;
+    const int n = cnt[x];
     auto gof = [](uint16_t gv) { return gv != kNone16 ? (int)gv : -1; };
     for (int y = yg; y < H; y += ys) {
         uint32_t o = kNone32;
-        if (has) {
+        if (n > 0) {
             int bj;
-            linf_search(sv + x, TW, y, H, gof, bj);
+            if (n <= kLinfList)
+                linf_list(lst + x * kLinfList, n, y, [&](int j) { return (int)sv[j * TW + x]; }, bj);
+            else
+                linf_search(sv + x, TW, y, H, gof, bj);
             o = ((uint32_t)src[(int64_t)bj * W + x] << 16) | (uint32_t)bj;
         }
         dst[(int64_t)y * W + x] = o;
@@ -631,7 +688,8 @@ hipError_t launch_linf_rows_t(const typename Geo::Val* in, int L, int64_t nlines
     hipError_t le = large_lds_once((const void*)k_linf_rows<Geo>, &lds_done);
     if (le != hipSuccess) return le;
     const int LPB = L <= kLinfStage ? kLinfStage / L : 1;
-    const size_t lds = linf_flags_offset((size_t)LPB * L * 2) + (size_t)LPB * 8;
+    const size_t lds = linf_flags_offset((size_t)LPB * L * 2) + (size_t)LPB * 12 +
+                       (LPB <= kLinfList ? (size_t)LPB * kLinfList * 2 : 0);
     const int64_t blocks = (nlines + LPB - 1) / LPB;
     if (blocks > INT32_MAX || lds > 160 * 1024) return hipErrorInvalidValue;
     const int vec = ((size_t)L * sizeof(Val) % 16 == 0 && ((uintptr_t)in & 15) == 0) ? 1 : 0;
@@ -657,7 +715,7 @@ hipError_t launch_linf_cols_3d(const uint16_t* c0, int B, int D, int H, int W, u
                    // for one column of the longest lines), several blocks per CU
     while (TW > 1 && (size_t)H * TW * 2 > 32 * 1024) TW >>= 1;
     if ((size_t)H * TW * 2 > 64 * 1024) return hipErrorInvalidValue;
-    const size_t lds = linf_flags_offset((size_t)H * TW * 2) + (size_t)TW * 4;
+    const size_t lds = linf_flags_offset((size_t)H * TW * 2) + (size_t)TW * (8 + 2 * kLinfList);
     const int64_t blocks = (int64_t)B * D * ((W + TW - 1) / TW);
     if (blocks > INT32_MAX) return hipErrorInvalidValue;
     // 16-byte pieces: rows 16-byte aligned and tiles of whole pieces

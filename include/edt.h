@@ -171,7 +171,8 @@ edt_status edt3d_taxicab_u8_batched(const uint8_t* mask, int32_t B, int32_t D, i
    element (ties: any).  Layouts, the virtual element (distance
    max(p0 + 1, p1, ...)), buffers, workspace, limits and errors exactly as for
    the taxicab entry points above.  The work per element grows with its own
-   distance (each element searches outward along each axis). */
+   distance (each element searches outward along each axis), except on lines
+   with at most 32 sources, which are scanned as a list. */
 edt_status edt2d_chessboard_u8_batched(const uint8_t* mask, int32_t B, int32_t H, int32_t W,
                                        int32_t* dist, int32_t* indices,
                                        void* workspace, size_t workspace_bytes, hipStream_t stream);

@@ -539,7 +539,7 @@ def test_taxicab(torch_dev):
                     assert (mm.reshape(-1)[i1.reshape(-1)] == 0).all()
 
 
-@pytest.mark.parametrize("name", ["b2d", "c5", "c3"])
+@pytest.mark.parametrize("name", ["b2d", "c5", "c3", "c2b"])
 def test_taxicab_full_size(torch_dev, name):
     """City-block transform at the full sizes that bench.py --taxicab times, in
     the same launch shapes: over the whole output, every index names a
@@ -615,7 +615,7 @@ def test_chessboard(torch_dev):
                     assert (mm.reshape(-1)[i1.reshape(-1)] == 0).all()
 
 
-@pytest.mark.parametrize("name", ["b2d", "c5", "c3"])
+@pytest.mark.parametrize("name", ["b2d", "c5", "c3", "c2b"])
 def test_chessboard_full_size(torch_dev, name):
     """Chessboard transform at the full sizes that bench.py --chessboard times:
     over the whole output, every index names a background element of its
