@@ -392,6 +392,10 @@ struct LinfRows3D {
 constexpr int kLinfStage = 2048;   // lines up to this length share a block
 constexpr int kLinfThreads = 512;  // threads per block of either search pass
 constexpr int kLinfList = 32;      // lines with at most this many sources scan them as a list
+constexpr int kLinfBT = 128;       // bucket width = the g threshold of the bucket lists
+constexpr int kLinfBC = 16;        // sources per bucket list
+constexpr int kLinfBLine = 2048;   // lines this long or longer use the bucket lists (shorter
+                                   // ones measured faster without their bookkeeping)
 
 __host__ __device__ inline size_t linf_flags_offset(size_t bytes) { return (bytes + 15) & ~size_t(15); }
 
@@ -448,7 +452,7 @@ __device__ inline int linf_list(const uint16_t* lst, int n, int q, const GAt& ga
 // 65534 on every accepted shape); threads take consecutive positions of the
 // block's lines, and the winner's source value is read back from the input
 // for its index.
-template <class Geo>
+template <class Geo, bool BUCKETS>
 __global__ __launch_bounds__(kLinfThreads) void k_linf_rows(const typename Geo::Val* __restrict__ in, int L,
                                                    int64_t nlines, int LPB, int vec, Geo geo,
                                                    int32_t* __restrict__ dist,
@@ -459,8 +463,13 @@ __global__ __launch_bounds__(kLinfThreads) void k_linf_rows(const typename Geo::
     int* cnt = reinterpret_cast<int*>(smem + linf_flags_offset((size_t)LPB * L * 2));   // [LPB] sources
     int* fill = cnt + LPB;                                                          // [LPB]
     unsigned* ctx = reinterpret_cast<unsigned*>(fill + LPB);                        // [LPB]
-    uint16_t* lst = reinterpret_cast<uint16_t*>(ctx + LPB);                         // [LPB][kLinfList]
+    int* small = reinterpret_cast<int*>(ctx + LPB);                                 // [LPB] g <= kLinfBT
+    const int nbk = (L + kLinfBT - 1) / kLinfBT;                                    // buckets per line
+    int* bcnt = small + LPB;                                                        // [LPB][nbk]
+    uint16_t* blst = reinterpret_cast<uint16_t*>(bcnt + (L >= kLinfBLine ? LPB * nbk : 0));  // [LPB][nbk][kLinfBC]
+    uint16_t* lst = blst + (L >= kLinfBLine ? LPB * nbk * kLinfBC : 0);              // [LPB][kLinfList]
     const bool lists = LPB <= kLinfList;   // (lines shorter than that search little anyway)
+    constexpr bool buckets = BUCKETS;   // launched with L >= kLinfBLine
     const int tid = threadIdx.x, nt = blockDim.x;
     const int64_t line0 = (int64_t)blockIdx.x * LPB;
     const int nl = (int)min<int64_t>(LPB, nlines - line0);
@@ -468,8 +477,11 @@ __global__ __launch_bounds__(kLinfThreads) void k_linf_rows(const typename Geo::
     for (int l = tid; l < LPB; l += nt) {
         cnt[l] = 0;
         fill[l] = 0;
+        small[l] = 0;
         ctx[l] = geo.ctx(line0 + (l < nl ? l : 0));
     }
+    if (buckets)
+        for (int i = tid; i < LPB * nbk; i += nt) bcnt[i] = 0;
     __syncthreads();
     const Val* src = in + line0 * (int64_t)L;
     auto gval = [&](Val v, unsigned c) -> uint16_t {
@@ -485,11 +497,12 @@ __global__ __launch_bounds__(kLinfThreads) void k_linf_rows(const typename Geo::
             const unsigned c = ctx[l];
             const Val* pv = reinterpret_cast<const Val*>(&w);
             uint16_t gs[VN];
-            int nv = 0;
+            int nv = 0, ns = 0;
 #pragma unroll
             for (int k = 0; k < VN; ++k) {
                 gs[k] = gval(pv[k], c);
                 nv += gs[k] != kNone16;
+                ns += gs[k] <= kLinfBT;   // (kNone16 > kLinfBT)
             }
             if constexpr (VN == 8) {
                 reinterpret_cast<uint4*>(sg)[i] =
@@ -500,6 +513,7 @@ __global__ __launch_bounds__(kLinfThreads) void k_linf_rows(const typename Geo::
                     make_uint2(gs[0] | ((uint32_t)gs[1] << 16), gs[2] | ((uint32_t)gs[3] << 16));
             }
             if (nv) atomicAdd(&cnt[l], nv);
+            if (buckets && ns) atomicAdd(&small[l], ns);
         }
     } else {
 #pragma unroll 4
@@ -508,15 +522,25 @@ __global__ __launch_bounds__(kLinfThreads) void k_linf_rows(const typename Geo::
             const uint16_t gv = gval(src[e], ctx[l]);
             sg[e] = gv;
             if (gv != kNone16) atomicAdd(&cnt[l], 1);
+            if (buckets && gv <= kLinfBT) atomicAdd(&small[l], 1);
         }
     }
     __syncthreads();
-    if (lists) {   // the sources of lines with few of them, in any order
+    // Lines with few sources list them all (any order).  Lines whose sources
+    // of g <= kLinfBT are sparse enough list those per bucket of kLinfBT
+    // positions (a bucket past kLinfBC of them is marked full by its count).
+    auto bucketed = [&](int l) { return buckets && cnt[l] > kLinfList && small[l] <= (kLinfBC / 2) * nbk; };
+    if (lists || buckets) {
         for (int e = tid; e < total; e += nt) {
-            const int l = e / L;
-            if (cnt[l] <= kLinfList && sg[e] != kNone16) {
+            const int l = e / L, q = e - l * L;
+            if (sg[e] == kNone16) continue;
+            if (lists && cnt[l] <= kLinfList) {
                 const int slot = atomicAdd(&fill[l], 1);   // < cnt[l]
-                lst[l * kLinfList + slot] = (uint16_t)(e - l * L);
+                lst[l * kLinfList + slot] = (uint16_t)q;
+            } else if (bucketed(l) && sg[e] <= kLinfBT) {
+                const int bk = l * nbk + q / kLinfBT;
+                const int slot = atomicAdd(&bcnt[bk], 1);
+                if (slot < kLinfBC) blst[bk * kLinfBC + slot] = (uint16_t)q;
             }
         }
         __syncthreads();
@@ -535,10 +559,37 @@ __global__ __launch_bounds__(kLinfThreads) void k_linf_rows(const typename Geo::
         } else {
             const uint16_t* lg = sg + l * L;
             int bj;
-            if (lists && n <= kLinfList)
-                best = linf_list(lst + l * kLinfList, n, q, [&](int j) { return (int)lg[j]; }, bj);
-            else
-                best = linf_search(lg, 1, q, L, gof, bj);
+            auto gat = [&](int j) { return (int)lg[j]; };
+            if (lists && n <= kLinfList) {
+                best = linf_list(lst + l * kLinfList, n, q, gat, bj);
+            } else {
+                // buckets b - 1 .. b + 1 hold every source of g <= kLinfBT within
+                // kLinfBT of q; a best found there that is <= kLinfBT is the
+                // minimum (any other source is farther or has a larger g)
+                best = INT32_MAX;
+                if (buckets && bucketed(l)) {
+                    const int b = q / kLinfBT;
+                    bool full = false;
+                    int bd = INT32_MAX;
+                    for (int bb = max(b - 1, 0); bb <= min(b + 1, nbk - 1); ++bb) {
+                        const int bk = l * nbk + bb;
+                        const int m = bcnt[bk];
+                        if (m > kLinfBC) { full = true; break; }
+                        int j1, d1;
+                        const int v = linf_list(blst + bk * kLinfBC, m, q, gat, j1);
+                        if (j1 >= 0) {
+                            d1 = q > j1 ? q - j1 : j1 - q;
+                            if (v < best || (v == best && (d1 < bd || (d1 == bd && j1 < bj)))) {
+                                best = v;
+                                bd = d1;
+                                bj = j1;
+                            }
+                        }
+                    }
+                    if (full || best > kLinfBT) best = INT32_MAX;
+                }
+                if (best == INT32_MAX) best = linf_search(lg, 1, q, L, gof, bj);
+            }
             ix = geo.index(c, src[(int64_t)l * L + bj], bj);
         }
         if (dist) dist[ln * (int64_t)L + q] = best;
@@ -684,18 +735,27 @@ template <class Geo>
 hipError_t launch_linf_rows_t(const typename Geo::Val* in, int L, int64_t nlines, const Geo& geo,
                               int32_t* dist, int32_t* indices, hipStream_t s, KernelTimer* tm) {
     using Val = typename Geo::Val;
-    static unsigned long long lds_done = 0;
-    hipError_t le = large_lds_once((const void*)k_linf_rows<Geo>, &lds_done);
+    static unsigned long long lds_done[2] = {0, 0};
+    hipError_t le = large_lds_once((const void*)k_linf_rows<Geo, false>, &lds_done[0]);
+    if (le == hipSuccess) le = large_lds_once((const void*)k_linf_rows<Geo, true>, &lds_done[1]);
     if (le != hipSuccess) return le;
     const int LPB = L <= kLinfStage ? kLinfStage / L : 1;
-    const size_t lds = linf_flags_offset((size_t)LPB * L * 2) + (size_t)LPB * 12 +
+    const int nbk = (L + kLinfBT - 1) / kLinfBT;
+    const size_t lds = linf_flags_offset((size_t)LPB * L * 2) + (size_t)LPB * 16 +
+                       (L >= kLinfBLine ? (size_t)LPB * nbk * (4 + 2 * kLinfBC) : 0) +
                        (LPB <= kLinfList ? (size_t)LPB * kLinfList * 2 : 0);
     const int64_t blocks = (nlines + LPB - 1) / LPB;
     if (blocks > INT32_MAX || lds > 160 * 1024) return hipErrorInvalidValue;
     const int vec = ((size_t)L * sizeof(Val) % 16 == 0 && ((uintptr_t)in & 15) == 0) ? 1 : 0;
-    EDT_LAUNCH(tm, "chessboard_rows", s,
-               hipLaunchKernelGGL(k_linf_rows<Geo>, dim3((unsigned)blocks), dim3(kLinfThreads), lds, s, in, L,
-                                  nlines, LPB, vec, geo, dist, indices));
+    if (L >= kLinfBLine) {
+        EDT_LAUNCH(tm, "chessboard_rows", s,
+                   hipLaunchKernelGGL((k_linf_rows<Geo, true>), dim3((unsigned)blocks), dim3(kLinfThreads), lds,
+                                      s, in, L, nlines, LPB, vec, geo, dist, indices));
+    } else {
+        EDT_LAUNCH(tm, "chessboard_rows", s,
+                   hipLaunchKernelGGL((k_linf_rows<Geo, false>), dim3((unsigned)blocks), dim3(kLinfThreads), lds,
+                                      s, in, L, nlines, LPB, vec, geo, dist, indices));
+    }
     return hipSuccess;
 }
 
