@@ -43,6 +43,7 @@ sys.path.insert(0, ROOT)
 METRIC = "EDT Gpixel/s at 1 GPU + achieved HBM GB/s fraction of peak"
 HBM_PEAK_GBS = 8000.0   # MI355X HBM3E peak, GB/s
 DEFAULT_CONFIG = "c5"
+SECOND_CONFIG = "c3"   # the other workload with an HBM target, timed beside the default
 COPY_PROBE_BYTES = 1 << 30   # float32 elements read (and as many written) by the copy probe
 KERNEL_SOURCES = ("exact_euclidean_distance_amd/csrc/kernels.hip",
                   "exact_euclidean_distance_amd/csrc/envelope.h",
@@ -268,7 +269,7 @@ def cpu_baseline(name, mask, sampling, budget_s=15.0):
     n = sample.size
     return {"value": n / dt / 1e9, "unit": "Gpixel/s", "cores": 1, "kind": "oracle",
             "sample": desc + (", with indices" if want_idx else ""), "seconds": round(dt, 3),
-            "cpu": platform.processor() or platform.machine()}
+            "cpu": host_info()["cpu_model"], "host_cpus": host_info()["usable_cpus"]}
 
 
 FP64_PEAK_TFLOPS = 78.6   # MI355X vector fp64
@@ -382,6 +383,8 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default=DEFAULT_CONFIG, choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-second", action="store_true",
+                    help="with the default workload, skip the 16384^2 sub-record")
     ap.add_argument("--check", action="store_true", help="also compare with the oracle")
     ap.add_argument("--brute", action="store_true",
                     help="time the device brute-force transform (the exactness check) instead")
@@ -407,9 +410,6 @@ def main(argv=None):
         return probe_copy()
 
     import torch
-    from exact_euclidean_distance_amd import alloc_workspace, edt2d, edt3d, workspace_size_2d_batched, \
-        workspace_size_3d
-    from workloads import make_config
 
     if args.brute:
         return bench_brute(args)
@@ -422,7 +422,91 @@ def main(argv=None):
         print("bench.py: no HIP device", file=sys.stderr)
         return 1
     dev = torch.device("cuda:0")
-    name = args.config
+    copy_gbs = measure_copy_bandwidth(dev)
+    rec = bench_workload(args.config, args, dev, copy_gbs)
+    line = {
+        "metric": METRIC,
+        "value": rec["value"],
+        "unit": "Gpixel/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": rec["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": rec["dtype"],
+        "data": "synthetic",
+        "config": rec["config"],
+        "roofline": rec["roofline"],
+        "gpu_ms": rec["gpu_ms"],
+        "path": rec["path"],
+        "kernels": rec["kernels"],
+        "cpu_baseline": rec["cpu_baseline"],
+        "copy_GBps": round(copy_gbs, 1),
+        "host": host_info(),
+    }
+    # the other configuration the HBM target is set on, timed in the same run
+    if args.config == DEFAULT_CONFIG and not args.no_second:
+        sub = bench_workload(SECOND_CONFIG, args, dev, copy_gbs)
+        line[SECOND_CONFIG] = {k: sub[k] for k in ("value", "ms_per_step", "gpu_ms", "config",
+                                                   "roofline", "path", "kernels", "cpu_baseline",
+                                                   "dtype")}
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def host_info():
+    """CPU model and core counts of the host the oracle baseline ran on."""
+    model = platform.processor() or platform.machine()
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for ln in fh:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:   # pragma: no cover
+        usable = os.cpu_count()
+    return {"cpu_model": model, "logical_cpus": os.cpu_count(), "usable_cpus": usable}
+
+
+def measure_copy_bandwidth(dev, nbytes=1 << 31, reps=10):
+    """Device-to-device copy rate (GB/s, bytes read + written) of a plain
+    elementwise copy of `nbytes`: the practical ceiling the HBM fraction is
+    also reported against."""
+    import torch
+    a = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del a, b
+    torch.cuda.empty_cache()
+    return 2 * nbytes / (ms * 1e-3) / 1e9
+
+
+def bench_workload(name, args, dev, copy_gbs):
+    """Time K transforms of one workload resident in HBM (after W warm-ups):
+    the whole-path rate, per-step median and minimum, per-kernel durations
+    from HIP events on the launch stream, the dominant kernel's roofline, and
+    the oracle baseline on the host."""
+    import torch
+    from exact_euclidean_distance_amd import alloc_workspace, edt2d, edt3d, workspace_size_2d_batched, \
+        workspace_size_3d
+    from workloads import make_config
+
     print(f"[bench] generating {name}", file=sys.stderr, flush=True)
     mask_np, sampling, _ = make_config(name)
     shape = mask_np.shape
@@ -444,7 +528,7 @@ def main(argv=None):
         return fn(mask, sampling, sqdist=sq, dist=ds, indices=ix, return_distances=ds is not None,
                   workspace=ws, stream=s, timed=timed)
 
-    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    print(f"[bench] {name}: warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -458,19 +542,19 @@ def main(argv=None):
         graph.replay()
         torch.cuda.synchronize()
 
-    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
+    print(f"[bench] {name}: timing {args.steps} steps", file=sys.stderr, flush=True)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
-    e0.record(stream)
-    for _ in range(args.steps):
+    ev[0].record(stream)
+    for i in range(args.steps):
         if graph is not None:
             graph.replay()
         else:
             step()
-    e1.record(stream)
+        ev[i + 1].record(stream)
     torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / max(1, args.steps)
+    per_step = [ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]
+    ms = ev[0].elapsed_time(ev[-1]) / max(1, args.steps)
 
     # per-kernel durations: HIP events recorded by the library around each
     # launch, on the stream the kernels run on
@@ -484,8 +568,8 @@ def main(argv=None):
     for k, ts in per.items():
         avg = float(np.mean(ts))
         b = algorithmic_bytes(k, shape, n_out)
-        kernels.append({"name": k, "ms": round(avg, 4), "alg_bytes": b,
-                        "GBps": round(b / (avg * 1e-3) / 1e9, 1)})
+        kernels.append({"name": k, "ms": round(avg, 4), "ms_min": round(float(np.min(ts)), 4),
+                        "alg_bytes": b, "GBps": round(b / (avg * 1e-3) / 1e9, 1)})
     dom = max(kernels, key=lambda r: r["ms"])
     achieved = dom["alg_bytes"] / (dom["ms"] * 1e-3) / 1e9
 
@@ -493,7 +577,7 @@ def main(argv=None):
         import oracle
         sys.path.insert(0, os.path.join(ROOT, "tests"))
         from gpu_check import compare
-        print("[bench] parity check against the oracle", file=sys.stderr, flush=True)
+        print(f"[bench] {name}: parity check against the oracle", file=sys.stderr, flush=True)
         if len(shape) == 2:
             ref, _ = oracle.edt(mask_np, sampling, features=False)
         else:
@@ -505,36 +589,36 @@ def main(argv=None):
 
     cpu = None
     if not args.no_cpu_baseline:
-        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        print(f"[bench] {name}: cpu baseline (oracle)", file=sys.stderr, flush=True)
         cpu = cpu_baseline(name, mask_np, sampling)
 
-    total_bytes = sum(k["alg_bytes"] for k in kernels)
+    model_b = sum(k["alg_bytes"] for k in kernels)
+    model_a = n * (1 + 4 * n_out)
+    path_b = model_b / (ms * 1e-3) / 1e9
+    path_a = model_a / (ms * 1e-3) / 1e9
     traffic = measured_traffic(name, dom["name"])
-    line = {
-        "metric": METRIC,
+    del mask, sq, ds, ix, ws
+    torch.cuda.empty_cache()
+    return {
         "value": round(n / (ms * 1e-3) / 1e9, 3),
-        "unit": "Gpixel/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
+        "gpu_ms": {"mean": round(ms, 4), "median": round(float(np.median(per_step)), 4),
+                   "min": round(float(np.min(per_step)), 4)},
         "dtype": "f64",
-        "data": "synthetic",
         "config": {"workload": f"{name}: {WORKLOADS[name]}", "shape": list(shape),
                    "sampling": list(sampling) if sampling else None, "outputs": list(want),
                    "launch": "graph" if graph is not None else "stream"},
         "roofline": {"bound": "hbm", "kernel": dom["name"], "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic},
-        "path_GBps": round(total_bytes / (ms * 1e-3) / 1e9, 1),
+        "path": {"model_B_bytes": model_b, "model_B_GBps": round(path_b, 1),
+                 "model_B_frac": round(path_b / HBM_PEAK_GBS, 4),
+                 "model_B_frac_of_copy": round(path_b / copy_gbs, 4),
+                 "model_A_bytes": model_a, "model_A_GBps": round(path_a, 1),
+                 "model_A_frac": round(path_a / HBM_PEAK_GBS, 4)},
         "kernels": kernels,
         "cpu_baseline": cpu,
     }
-    print(json.dumps(line), flush=True)
-    return 0
 
 
 if __name__ == "__main__":

@@ -8,7 +8,9 @@ SciPy-compatible distance-transform interface (``sampling``,
 
 from __future__ import annotations
 
+import contextlib
 import ctypes
+import functools
 from dataclasses import dataclass
 from typing import Optional, Sequence
 
@@ -23,6 +25,20 @@ class EDTResult:
     sqdist: Optional[torch.Tensor]   # int32, exact squared distances
     dist: Optional[torch.Tensor]     # float32 distances
     indices: Optional[torch.Tensor]  # flat index of the nearest background (per image), int32 or int64
+
+
+def _on_stream(fn):
+    """Run ``fn`` with its ``stream`` argument (when given) as the current
+    stream, so that every tensor it allocates (workspace and outputs) belongs
+    to the stream the kernels are enqueued on: the caching allocator then
+    hands a freed workspace out again only after that stream's work."""
+    @functools.wraps(fn)
+    def wrapper(*args, **kwargs):
+        s = kwargs.get("stream")
+        ctx = torch.cuda.stream(s) if s is not None else contextlib.nullcontext()
+        with ctx:
+            return fn(*args, **kwargs)
+    return wrapper
 
 
 def workspace_size_2d(H: int, W: int) -> int:
@@ -93,6 +109,7 @@ def _timed_call(fn, name, args):
     return [(names[i].decode(), ms[i]) for i in range(cnt.value)]
 
 
+@_on_stream
 def edt2d(mask: torch.Tensor, sampling=None, *, return_distances: bool = True,
           return_sqdist: bool = False, return_indices: bool = False,
           dist=None, sqdist=None, indices=None, workspace=None, stream=None,
@@ -132,6 +149,7 @@ def edt2d(mask: torch.Tensor, sampling=None, *, return_distances: bool = True,
     return EDTResult(sq, ds, ix), _timed_call(tfn, name + "_timed", args)
 
 
+@_on_stream
 def edt1d(mask: torch.Tensor, sampling=None, *, return_distances: bool = True,
           return_sqdist: bool = False, return_indices: bool = False,
           dist=None, sqdist=None, indices=None, workspace=None, stream=None):
@@ -158,6 +176,7 @@ def edt1d(mask: torch.Tensor, sampling=None, *, return_distances: bool = True,
     return EDTResult(sq, ds, ix)
 
 
+@_on_stream
 def unravel_indices(indices: torch.Tensor, image_shape: Sequence[int], *, out=None, stream=None):
     """Per-axis coordinates of flat indices returned by the transforms:
     (*batch, *image_shape) int32 -> (*batch, ndim, *image_shape), the layout of
@@ -184,6 +203,7 @@ def unravel_indices(indices: torch.Tensor, image_shape: Sequence[int], *, out=No
     return coords
 
 
+@_on_stream
 def edt_brute(mask: torch.Tensor, sampling=None, *, batched: bool = False,
               return_distances: bool = True, return_sqdist: bool = False,
               return_indices: bool = False, dist=None, sqdist=None, indices=None,
@@ -242,6 +262,7 @@ def _chamfer(metric: str, mask: torch.Tensor, return_indices: bool, dist, indice
     return EDTResult(None, ds, ix)
 
 
+@_on_stream
 def taxicab(mask: torch.Tensor, *, return_indices: bool = False, dist=None, indices=None,
             workspace=None, stream=None):
     """City-block (L1) distance transform: int32 distances (and flat indices)
@@ -250,6 +271,7 @@ def taxicab(mask: torch.Tensor, *, return_indices: bool = False, dist=None, indi
     return _chamfer("taxicab", mask, return_indices, dist, indices, workspace, stream)
 
 
+@_on_stream
 def chessboard(mask: torch.Tensor, *, return_indices: bool = False, dist=None, indices=None,
                workspace=None, stream=None):
     """Chessboard (L-infinity) distance transform: int32 distances (and flat
@@ -258,6 +280,7 @@ def chessboard(mask: torch.Tensor, *, return_indices: bool = False, dist=None, i
     return _chamfer("chessboard", mask, return_indices, dist, indices, workspace, stream)
 
 
+@_on_stream
 def edt3d(mask: torch.Tensor, sampling=None, *, return_distances: bool = True,
           return_sqdist: bool = False, return_indices: bool = False,
           dist=None, sqdist=None, indices=None, workspace=None, stream=None,

@@ -651,3 +651,69 @@ def test_chessboard_full_size(torch_dev, name):
         pts = np.concatenate([rng.integers(0, per, ns // min(nb, 2)), [0, per - 1]])
         ref = oracle.chessboard_at(mask[k] if mask.ndim >= 3 else mask, pts)
         assert (dh[k][pts] == ref).all(), f"sampled distance mismatch in image {k}"
+
+
+def _bucket_rows_2d(mask, bt=128, bc=16, lst=32):
+    """For each row of a 2-D mask: whether the chessboard row pass takes its
+    bucket lists (more than `lst` sources on the row, at most bc / 2 per
+    bucket of `bt` positions on average with g <= bt, g being the distance
+    along axis 0 to the nearest background of the column), and whether some
+    bucket then holds more than `bc` such sources (a full bucket)."""
+    H, W = mask.shape
+    g = np.full((H, W), np.iinfo(np.int64).max, np.int64)
+    rows = np.arange(H)[:, None]
+    for c in range(W):
+        b = np.flatnonzero(mask[:, c] == 0)
+        if len(b):
+            g[:, c] = np.abs(rows - b[None, :]).min(1)
+    valid = g != np.iinfo(np.int64).max
+    small = valid & (g <= bt)
+    nbk = (W + bt - 1) // bt
+    bucketed = (valid.sum(1) > lst) & (small.sum(1) <= (bc // 2) * nbk)
+    per_bucket = np.add.reduceat(small, np.arange(0, W, bt), axis=1)
+    full = bucketed & (per_bucket > bc).any(1)
+    return bucketed, full
+
+
+def test_chessboard_bucket_lists(torch_dev):
+    """The chessboard row pass on rows of 2048 and more: rows that take the
+    per-bucket lists of sources with g <= 128 (many sources, most of them far
+    along axis 0), including a bucket with more than 16 such sources (the
+    outward search takes over there) and positions whose best in-bucket value
+    exceeds 128 (likewise), against the definition over the whole output."""
+    torch, dev = torch_dev
+    from exact_euclidean_distance_amd import chessboard
+    rng = np.random.default_rng([42, 5016])
+    for W in (2048, 2300):   # (2300: a ragged last bucket)
+        m = np.ones((260, W), np.uint8)
+        far = rng.random(W) < 0.4
+        m[0, far] = 0                               # sources at g = r on every row
+        pts = rng.integers(0, [260, W], size=(W // 80, 2))
+        m[pts[:, 0], pts[:, 1]] = 0                 # a few near sources (g <= 128)
+        m[150, 520:540] = 0                         # 20 near sources in one bucket: a full bucket
+        bucketed, full = _bucket_rows_2d(m)
+        assert bucketed.sum() > 50 and full.any(), "the mask must drive the bucket lists"
+        _say(f"chessboard bucket lists 260 x {W}: {bucketed.sum()} bucketed rows, "
+             f"{full.sum()} with a full bucket")
+        r = chessboard(torch.from_numpy(m).to(dev), return_indices=True)
+        torch.cuda.synchronize()
+        ref, _ = oracle.chessboard_brute(m)
+        d = r.dist.cpu().numpy()
+        ix = r.indices.cpu().numpy()
+        assert (d == ref).all(), "chessboard distance mismatch on bucketed rows"
+        assert (oracle.chessboard_to(ix, m.shape) == ref).all()
+        assert (m.reshape(-1)[ix.reshape(-1)] == 0).all()
+        # positions whose best value exceeds 128: the fallback search decides there
+        assert (ref[bucketed] > 128).any()
+    # rows of 2048 in a volume: g comes from the middle-axis pass
+    v = np.ones((1, 2, 180, 2048), np.uint8)
+    v[0, 0, 0, rng.random(2048) < 0.4] = 0
+    pts = rng.integers(0, [2, 180, 2048], size=(30, 3))
+    v[0, pts[:, 0], pts[:, 1], pts[:, 2]] = 0
+    v[0, 1, 150, 700:720] = 0
+    _say("chessboard bucket lists 1 x 2 x 180 x 2048")
+    r = chessboard(torch.from_numpy(v).to(dev), return_indices=True)
+    torch.cuda.synchronize()
+    ref, _ = oracle.chessboard_brute(v[0])
+    assert (r.dist.cpu().numpy()[0] == ref).all(), "chessboard distance mismatch (volume rows)"
+    assert (oracle.chessboard_to(r.indices.cpu().numpy()[0], v.shape[1:]) == ref).all()
