@@ -28,6 +28,7 @@ EXPORTS = (
     "edt_brute_workspace_size", "edt_brute_u8", "edt3d_u8_batched_idx64",
     "edt2d_taxicab_u8_batched", "edt3d_taxicab_u8_batched",
     "edt2d_chessboard_u8_batched", "edt3d_chessboard_u8_batched",
+    "edt2d_u8_batched_noalloc", "edt2d_noalloc_max_workspace",
 )
 
 _lib = None
@@ -95,6 +96,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.edt2d_chessboard_u8_batched.argtypes = [vp, i32, i32, i32, vp, vp, vp, sz, vp]
     lib.edt3d_chessboard_u8_batched.restype = ctypes.c_int
     lib.edt3d_chessboard_u8_batched.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, sz, vp]
+    lib.edt2d_u8_batched_noalloc.restype = ctypes.c_int
+    lib.edt2d_u8_batched_noalloc.argtypes = [vp, i32, i32, i32, fp, vp, vp, vp, vp]
+    lib.edt2d_noalloc_max_workspace.restype = sz
+    lib.edt2d_noalloc_max_workspace.argtypes = []
     lib.edt_status_string.restype = ctypes.c_char_p
     lib.edt_status_string.argtypes = [ctypes.c_int]
     lib.edt_version.restype = ctypes.c_char_p

@@ -12,6 +12,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/edt.h"
 #include "kernels.h"
 
@@ -95,16 +97,22 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
 }
 
 // Common checks on outputs and workspace; n = total element count.
-// indices: int32 (idx_bytes 4) or int64 (idx_bytes 8) per element
+// indices: int32 (idx_bytes 4) or int64 (idx_bytes 8) per element.
+// check_ws false: the workspace is the library's own scratch, not checked here.
 edt_status check_buffers(const uint8_t* mask, size_t n, int32_t* sqdist, float* dist,
                          void* indices, void* ws, size_t ws_bytes, size_t ws_need,
-                         size_t idx_bytes = 4) {
+                         size_t idx_bytes = 4, bool check_ws = true) {
     if (!mask) return EDT_ERR_INVALID_ARGUMENT;
     if (!sqdist && !dist && !indices) return EDT_ERR_INVALID_ARGUMENT;
     if (((uintptr_t)sqdist & 3) || ((uintptr_t)dist & 3) || ((uintptr_t)indices & (idx_bytes - 1)))
         return EDT_ERR_INVALID_ARGUMENT;
-    if (!ws || ((uintptr_t)ws & (kAlign - 1))) return EDT_ERR_INVALID_ARGUMENT;
-    if (ws_bytes < ws_need) return EDT_ERR_WORKSPACE_TOO_SMALL;
+    if (!check_ws) {
+        ws = nullptr;
+        ws_need = 0;
+    } else {
+        if (!ws || ((uintptr_t)ws & (kAlign - 1))) return EDT_ERR_INVALID_ARGUMENT;
+        if (ws_bytes < ws_need) return EDT_ERR_WORKSPACE_TOO_SMALL;
+    }
     const void* bufs[5] = {mask, sqdist, dist, indices, ws};
     const size_t sizes[5] = {n, sqdist ? n * 4 : 0, dist ? n * 4 : 0, indices ? n * idx_bytes : 0, ws_need};
     for (int i = 0; i < 5; ++i)
@@ -113,9 +121,38 @@ edt_status check_buffers(const uint8_t* mask, size_t n, int32_t* sqdist, float* 
     return EDT_OK;
 }
 
+// Workspace of edt2d_u8_batched_noalloc, for callers that cannot allocate:
+// one copy per device, held from the first use until the process ends.  In
+// host code `scratch` only names the symbol; its device address comes from
+// hipGetSymbolAddress, once per device, and only that address is passed on.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's scratch address (nullptr on a HIP error).
+void* scratch_address() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+            (void)hipGetLastError();
+            return nullptr;
+        }
+        g_scratch_ptr[dev] = p;
+    }
+    return g_scratch_ptr[dev];
+}
+
+// use_scratch: the workspace is this device's copy of `scratch` (ws and
+// ws_bytes are ignored); it is looked up only after every argument check.
 edt_status run2d(const uint8_t* mask, int32_t B, int32_t H, int32_t W, const float* sampling,
                  int32_t* sqdist, float* dist, int32_t* indices, void* ws, size_t ws_bytes,
-                 hipStream_t stream, edt::KernelTimer* tm) {
+                 hipStream_t stream, edt::KernelTimer* tm, bool use_scratch = false) {
     if (B < 1 || H < 1 || W < 1) return EDT_ERR_INVALID_ARGUMENT;
     if (!shape2d_ok(B, H, W)) return EDT_ERR_UNSUPPORTED_SHAPE;
     double s2[2];
@@ -125,8 +162,14 @@ edt_status run2d(const uint8_t* mask, int32_t B, int32_t H, int32_t W, const flo
     if (sqdist && !unit) return EDT_ERR_INVALID_ARGUMENT;
     if (sqdist && (double)H * H + (double)W * W > (double)INT32_MAX) return EDT_ERR_UNSUPPORTED_SHAPE;
     const Layout L = layout2d(B, H, W);
-    st = check_buffers(mask, (size_t)B * H * W, sqdist, dist, indices, ws, ws_bytes, L.total);
+    if (use_scratch && L.total > kScratchBytes) return EDT_ERR_WORKSPACE_TOO_SMALL;
+    st = check_buffers(mask, (size_t)B * H * W, sqdist, dist, indices, ws, ws_bytes, L.total, 4,
+                       !use_scratch);
     if (st != EDT_OK) return st;
+    if (use_scratch) {   // the first HIP calls of this entry point
+        ws = scratch_address();
+        if (!ws) return EDT_ERR_HIP;
+    }
 
     char* base = static_cast<char*>(ws);
     uint16_t* c0 = reinterpret_cast<uint16_t*>(base + L.c0);
@@ -244,6 +287,14 @@ edt_status edt2d_u8_batched(const uint8_t* mask, int32_t B, int32_t H, int32_t W
                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
     return run2d(mask, B, H, W, sampling, sqdist, dist, indices, workspace, workspace_bytes, stream,
                  nullptr);
+}
+
+size_t edt2d_noalloc_max_workspace(void) { return kScratchBytes; }
+
+edt_status edt2d_u8_batched_noalloc(const uint8_t* mask, int32_t B, int32_t H, int32_t W,
+                                    const float* sampling, int32_t* sqdist, float* dist,
+                                    int32_t* indices, hipStream_t stream) {
+    return run2d(mask, B, H, W, sampling, sqdist, dist, indices, nullptr, 0, stream, nullptr, true);
 }
 
 edt_status edt1d_u8_batched(const uint8_t* mask, int32_t B, int32_t N, const float* sampling,

@@ -42,6 +42,8 @@
  *
  * Ownership and threading.  The library allocates no device memory and keeps
  * no state between calls; concurrent calls with distinct buffers are safe.
+ * The one exception is edt2d_u8_batched_noalloc, whose workspace is a device
+ * array of the library's own (one per device, see its declaration).
  *
  * Errors.  Argument errors are detected on the host before any HIP call and
  * return without touching any buffer.  EDT_ERR_HIP means a kernel launch was
@@ -102,6 +104,28 @@ edt_status edt2d_u8_batched(const uint8_t* mask, int32_t B, int32_t H, int32_t W
                             const float* sampling,
                             int32_t* sqdist, float* dist, int32_t* indices,
                             void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* edt2d_u8_batched for callers that cannot allocate device memory (code
+   under HIP graph capture, tight serving loops, harnesses that forbid
+   hipMalloc): the same transform, but the workspace is the library's own
+   device array of edt2d_noalloc_max_workspace() bytes (64 MiB; one copy per
+   device, held from the first call on that device until the process ends).
+   The call allocates nothing; the caller still passes the mask and outputs,
+   with the conventions of edt2d_u8_batched.  A shape whose workspace
+   (edt2d_batched_workspace_size) exceeds the array returns
+   EDT_ERR_WORKSPACE_TOO_SMALL before any HIP call.  Every call on one device
+   shares that device's array: calls that overlap in time on one device (two
+   streams, or two threads) race on it and must be serialized by the caller;
+   the array keeps the last call's contents, and nothing in it needs to be
+   cleared between calls.  EDT_ERR_HIP also covers a failure to look up the
+   array's device address on the first call on a device. */
+edt_status edt2d_u8_batched_noalloc(const uint8_t* mask, int32_t B, int32_t H, int32_t W,
+                                    const float* sampling,
+                                    int32_t* sqdist, float* dist, int32_t* indices,
+                                    hipStream_t stream);
+
+/* Size in bytes of the device array edt2d_u8_batched_noalloc works in. */
+size_t edt2d_noalloc_max_workspace(void);
 
 /* Bytes of workspace edt1d_u8_batched needs for B lines of N elements. */
 size_t edt1d_workspace_size(int32_t B, int32_t N);
