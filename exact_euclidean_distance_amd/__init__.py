@@ -13,6 +13,7 @@ from .api import (  # noqa: F401
     alloc_workspace,
     edt1d,
     edt2d,
+    edt,
     edt3d,
     edt_brute,
     chessboard,
@@ -23,6 +24,6 @@ from .api import (  # noqa: F401
     workspace_size_3d,
 )
 
-__all__ = ["chessboard", "edt1d", "edt2d", "edt3d", "edt_brute", "taxicab", "unravel_indices", "EDTResult", "EDTError",
+__all__ = ["chessboard", "edt", "edt1d", "edt2d", "edt3d", "edt_brute", "taxicab", "unravel_indices", "EDTResult", "EDTError",
            "workspace_size_2d", "workspace_size_2d_batched", "workspace_size_3d",
            "alloc_workspace"]

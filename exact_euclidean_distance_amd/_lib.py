@@ -29,6 +29,7 @@ EXPORTS = (
     "edt2d_taxicab_u8_batched", "edt3d_taxicab_u8_batched",
     "edt2d_chessboard_u8_batched", "edt3d_chessboard_u8_batched",
     "edt2d_u8_batched_noalloc", "edt2d_noalloc_max_workspace",
+    "edt_nd_workspace_size", "edt_nd_u8", "edt_unravel_indices_nd",
 )
 
 _lib = None
@@ -100,6 +101,13 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.edt2d_u8_batched_noalloc.argtypes = [vp, i32, i32, i32, fp, vp, vp, vp, vp]
     lib.edt2d_noalloc_max_workspace.restype = sz
     lib.edt2d_noalloc_max_workspace.argtypes = []
+    i64p = ctypes.POINTER(ctypes.c_int64)
+    lib.edt_nd_workspace_size.restype = sz
+    lib.edt_nd_workspace_size.argtypes = [i32, i32, i64p, i64p, i32]
+    lib.edt_nd_u8.restype = ctypes.c_int
+    lib.edt_nd_u8.argtypes = [vp, i32, i32, i64p, i64p, fp, vp, vp, vp, i32, vp, sz, vp]
+    lib.edt_unravel_indices_nd.restype = ctypes.c_int
+    lib.edt_unravel_indices_nd.argtypes = [vp, i32, ctypes.c_int64, i32, i64p, vp, vp]
     lib.edt_status_string.restype = ctypes.c_char_p
     lib.edt_status_string.argtypes = [ctypes.c_int]
     lib.edt_version.restype = ctypes.c_char_p

@@ -179,10 +179,11 @@ def edt1d(mask: torch.Tensor, sampling=None, *, return_distances: bool = True,
 @_on_stream
 def unravel_indices(indices: torch.Tensor, image_shape: Sequence[int], *, out=None, stream=None):
     """Per-axis coordinates of flat indices returned by the transforms:
-    (*batch, *image_shape) int32 -> (*batch, ndim, *image_shape), the layout of
-    SciPy's feature transform (virtual index -> (-1, 0, ...))."""
-    if not isinstance(indices, torch.Tensor) or indices.dtype != torch.int32:
-        raise TypeError("indices must be an int32 torch.Tensor")
+    (*batch, *image_shape) int32 or int64 -> (*batch, ndim, *image_shape) of the
+    same type, the layout of SciPy's feature transform (virtual index ->
+    (-1, 0, ...)); images of 1 to 8 axes."""
+    if not isinstance(indices, torch.Tensor) or indices.dtype not in (torch.int32, torch.int64):
+        raise TypeError("indices must be an int32 or int64 torch.Tensor")
     if not indices.is_cuda or not indices.is_contiguous():
         raise ValueError("indices must be a contiguous device tensor")
     img = tuple(int(s) for s in image_shape)
@@ -194,12 +195,19 @@ def unravel_indices(indices: torch.Tensor, image_shape: Sequence[int], *, out=No
     for b in batch:
         images *= int(b)
     shape = batch + (nd,) + img
-    coords = _out(out, shape, torch.int32, indices.device, True)
-    shp = (ctypes.c_int32 * nd)(*img)
-    st = _lib.load().edt_unravel_indices(_ptr(indices), images, nd, shp, _ptr(coords),
-                                         _stream(stream))
+    coords = _out(out, shape, indices.dtype, indices.device, True)
+    if indices.dtype == torch.int32 and nd <= 3:
+        shp = (ctypes.c_int32 * nd)(*img)
+        st = _lib.load().edt_unravel_indices(_ptr(indices), images, nd, shp, _ptr(coords),
+                                             _stream(stream))
+        if st != 0:
+            raise EDTError(st, "edt_unravel_indices")
+        return coords
+    ib = 8 if indices.dtype == torch.int64 else 4
+    st = _lib.load().edt_unravel_indices_nd(_ptr(indices), ib, images, nd, _i64(img), _ptr(coords),
+                                            _stream(stream))
     if st != 0:
-        raise EDTError(st, "edt_unravel_indices")
+        raise EDTError(st, "edt_unravel_indices_nd")
     return coords
 
 
@@ -320,3 +328,53 @@ def edt3d(mask: torch.Tensor, sampling=None, *, return_distances: bool = True,
         return EDTResult(sq, ds, ix)
     return EDTResult(sq, ds, ix), _timed_call(lib.edt3d_u8_batched_timed, "edt3d_u8_batched_timed",
                                               args)
+
+
+def _i64(vals):
+    vals = [int(v) for v in vals]
+    return (ctypes.c_int64 * max(1, len(vals)))(*vals)
+
+
+@_on_stream
+def edt(mask: torch.Tensor, sampling=None, *, batch_dims: int = 0, return_distances: bool = True,
+        return_sqdist: bool = False, return_indices: bool = False, index_dtype=torch.int32,
+        dist=None, sqdist=None, indices=None, workspace=None, stream=None):
+    """Exact EDT of a uint8 mask of any spatial rank (1..8) after
+    ``batch_dims`` leading batch axes, e.g. (B, C, D, H, W, T) with
+    ``batch_dims=2``.  The mask may be a strided view (slices, transposes);
+    outputs are contiguous with the mask's shape.  Indices are flat within each
+    image, int32 or int64 (``index_dtype``).  Shapes the LDS kernels take run
+    there; the rest (rank 4+, strided masks, long rows, extents over 65535)
+    run the workspace path of the same method."""
+    if not isinstance(mask, torch.Tensor):
+        raise TypeError("mask must be a torch.Tensor")
+    if mask.dtype != torch.uint8:
+        raise TypeError("mask must be uint8 (0 = background)")
+    if not mask.is_cuda:
+        raise ValueError("mask must be a device (HIP) tensor")
+    if index_dtype not in (torch.int32, torch.int64):
+        raise ValueError("index_dtype must be torch.int32 or torch.int64")
+    ndim = mask.dim() - int(batch_dims)
+    if batch_dims < 0 or not 1 <= ndim <= 8:
+        raise ValueError("need 1 to 8 spatial axes after the batch axes")
+    shape = tuple(mask.shape)
+    dev = mask.device
+    sq = _out(sqdist, shape, torch.int32, dev, return_sqdist)
+    ds = _out(dist, shape, torch.float32, dev, return_distances)
+    ix = _out(indices, shape, index_dtype, dev, return_indices)
+    ib = 8 if index_dtype == torch.int64 else 4
+    lib = _lib.load()
+    shp = _i64(shape)
+    strd = _i64(mask.stride())
+    need = int(lib.edt_nd_workspace_size(int(batch_dims), ndim, shp, strd, ib))
+    if need == 0:
+        raise EDTError(1, "edt_nd_workspace_size")
+    if workspace is None:
+        workspace = alloc_workspace(need, dev)
+    samp = _sampling(sampling, ndim)
+    st = lib.edt_nd_u8(_ptr(mask), int(batch_dims), ndim, shp, strd, samp, _ptr(sq), _ptr(ds), _ptr(ix),
+                       ib, _ptr(workspace), workspace.numel() * workspace.element_size(),
+                       _stream(stream))
+    if st != 0:
+        raise EDTError(st, "edt_nd_u8")
+    return EDTResult(sq, ds, ix)

@@ -418,6 +418,197 @@ edt_status edt_brute_u8(const uint8_t* mask, int32_t B, int32_t ndim, const int3
     return EDT_OK;
 }
 
+}  // extern "C"
+
+namespace {
+// ---------------------------------------------------------------- any rank
+
+constexpr int kMaxSpatial = 8;
+constexpr int kMaxBatchAxes = 8;
+
+// How edt_nd_u8 runs a shape: the LDS kernels for C-contiguous 1-, 2- and 3-D
+// images within their limits, the workspace path of nd.hip otherwise.
+enum class NdRoute { kEmpty, k1D, k2D, k3D, kGeneric };
+
+struct NdPlan {
+    NdRoute route = NdRoute::kGeneric;
+    edt::NdDesc d{};
+    int64_t total = 0;          // elements over all images
+    int64_t mask_span = 0;      // bytes from the mask pointer to its last element + 1
+    int32_t fB = 0, fD = 0, fH = 0, fW = 0;   // the fast path's shape
+    size_t ws = 0;
+};
+
+// Shape checks and routing (no buffer is looked at).  idx_bytes: 4 or 8.
+edt_status plan_nd(int32_t nbatch, int32_t ndim, const int64_t* shape, const int64_t* strides,
+                   int idx_bytes, NdPlan* out) {
+    if (!shape || ndim < 1 || ndim > kMaxSpatial || nbatch < 0 || nbatch > kMaxBatchAxes)
+        return EDT_ERR_INVALID_ARGUMENT;
+    if (idx_bytes != 4 && idx_bytes != 8) return EDT_ERR_INVALID_ARGUMENT;
+    NdPlan P;
+    P.d.nb = nbatch;
+    P.d.nd = ndim;
+    const int na = nbatch + ndim;
+    int64_t B = 1, N = 1;
+    bool contiguous = true;
+    int64_t expect = 1;
+    for (int a = na - 1; a >= 0; --a) {
+        const int64_t n = shape[a];
+        if (n < 0) return EDT_ERR_INVALID_ARGUMENT;
+        const int64_t st = strides ? strides[a] : expect;
+        if (st < 0) return EDT_ERR_INVALID_ARGUMENT;
+        if (n > 1 && st != expect) contiguous = false;
+        if (n > 0 && expect > ((int64_t)1 << 62) / n) return EDT_ERR_UNSUPPORTED_SHAPE;
+        expect *= n > 0 ? n : 1;
+        P.d.ext[a] = n;
+        P.d.mstride[a] = st;
+    }
+    for (int a = 0; a < nbatch; ++a) B *= shape[a];
+    for (int a = nbatch; a < na; ++a) N *= shape[a];
+    P.d.B = B;
+    P.d.N = N;
+    P.total = B * N;
+    if (P.total == 0) {
+        P.route = NdRoute::kEmpty;
+        *out = P;
+        return EDT_OK;
+    }
+    int64_t span = 1;
+    for (int a = 0; a < na; ++a) {
+        const int64_t reach = (shape[a] - 1) * P.d.mstride[a];
+        if (P.d.mstride[a] > 0 && shape[a] - 1 > (((int64_t)1 << 62) - span) / P.d.mstride[a])
+            return EDT_ERR_UNSUPPORTED_SHAPE;
+        span += reach;
+    }
+    P.mask_span = span;
+    // the LDS kernels: C-contiguous, at most 65535 images, int32 indices
+    // (int64 for volumes), shapes within their limits
+    if (contiguous && B <= kMaxExtent) {
+        const int32_t b32 = (int32_t)B;
+        auto fits = [](int64_t x) { return x >= 1 && x <= kMaxExtent; };
+        if (ndim == 1 && fits(shape[nbatch]) && idx_bytes == 4 && shape2d_ok(b32, (int32_t)shape[nbatch], 1)) {
+            P.route = NdRoute::k1D;
+            P.fB = b32;
+            P.fH = (int32_t)shape[nbatch];
+            P.fW = 1;
+            P.ws = layout2d(b32, P.fH, 1).total;
+        } else if (ndim == 2 && fits(shape[nbatch]) && fits(shape[nbatch + 1]) && idx_bytes == 4 &&
+                   shape2d_ok(b32, (int32_t)shape[nbatch], (int32_t)shape[nbatch + 1])) {
+            P.route = NdRoute::k2D;
+            P.fB = b32;
+            P.fH = (int32_t)shape[nbatch];
+            P.fW = (int32_t)shape[nbatch + 1];
+            P.ws = layout2d(b32, P.fH, P.fW).total;
+        } else if (ndim == 3 && fits(shape[nbatch]) && fits(shape[nbatch + 1]) && fits(shape[nbatch + 2]) &&
+                   shape3d_ok(b32, (int32_t)shape[nbatch], (int32_t)shape[nbatch + 1], (int32_t)shape[nbatch + 2]) &&
+                   (idx_bytes == 8 || N <= INT32_MAX)) {
+            P.route = NdRoute::k3D;
+            P.fB = b32;
+            P.fD = (int32_t)shape[nbatch];
+            P.fH = (int32_t)shape[nbatch + 1];
+            P.fW = (int32_t)shape[nbatch + 2];
+            P.ws = layout3d(b32, P.fD, P.fH, P.fW).total;
+        }
+    }
+    if (P.route == NdRoute::kGeneric) P.ws = edt::nd_workspace_bytes(P.total);
+    *out = P;
+    return EDT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+size_t edt_nd_workspace_size(int32_t nbatch, int32_t ndim, const int64_t* shape,
+                             const int64_t* strides, int32_t index_bytes) {
+    NdPlan P;
+    if (plan_nd(nbatch, ndim, shape, strides, index_bytes == 8 ? 8 : 4, &P) != EDT_OK) return 0;
+    return P.ws > 0 ? P.ws : 256;
+}
+
+edt_status edt_nd_u8(const uint8_t* mask, int32_t nbatch, int32_t ndim, const int64_t* shape,
+                     const int64_t* strides, const float* sampling, int32_t* sqdist, float* dist,
+                     void* indices, int32_t index_bytes, void* workspace, size_t workspace_bytes,
+                     hipStream_t stream) {
+    if (indices && index_bytes != 4 && index_bytes != 8) return EDT_ERR_INVALID_ARGUMENT;
+    const int ib = indices ? index_bytes : 4;
+    NdPlan P;
+    edt_status st = plan_nd(nbatch, ndim, shape, strides, ib, &P);
+    if (st != EDT_OK) return st;
+    double s2[kMaxSpatial];
+    bool unit;
+    st = read_sampling(sampling, ndim, s2, &unit);
+    if (st != EDT_OK) return st;
+    if (!mask) return EDT_ERR_INVALID_ARGUMENT;
+    if (!sqdist && !dist && !indices) return EDT_ERR_INVALID_ARGUMENT;
+    if (sqdist) {
+        if (!unit) return EDT_ERR_INVALID_ARGUMENT;
+        double mx = 0.0;
+        for (int k = 0; k < ndim; ++k) mx += (double)shape[nbatch + k] * (double)shape[nbatch + k];
+        if (mx > (double)INT32_MAX) return EDT_ERR_UNSUPPORTED_SHAPE;
+    }
+    if (indices && ib == 4 && P.d.N > INT32_MAX) return EDT_ERR_UNSUPPORTED_SHAPE;
+    // outputs, mask span and workspace: alignment and overlap
+    if (((uintptr_t)sqdist & 3) || ((uintptr_t)dist & 3) || ((uintptr_t)indices & (ib - 1)))
+        return EDT_ERR_INVALID_ARGUMENT;
+    if (P.route == NdRoute::kEmpty) return EDT_OK;
+    if (!workspace || ((uintptr_t)workspace & (kAlign - 1))) return EDT_ERR_INVALID_ARGUMENT;
+    if (workspace_bytes < P.ws) return EDT_ERR_WORKSPACE_TOO_SMALL;
+    const size_t n = (size_t)P.total;
+    const void* bufs[5] = {mask, sqdist, dist, indices, workspace};
+    const size_t sizes[5] = {(size_t)P.mask_span, sqdist ? n * 4 : 0, dist ? n * 4 : 0,
+                             indices ? n * (size_t)ib : 0, P.ws};
+    for (int i = 0; i < 5; ++i)
+        for (int j = i + 1; j < 5; ++j)
+            if (overlap(bufs[i], sizes[i], bufs[j], sizes[j])) return EDT_ERR_INVALID_ARGUMENT;
+    float samp[kMaxSpatial];
+    for (int k = 0; k < ndim; ++k) samp[k] = sampling ? sampling[k] : 1.0f;
+    switch (P.route) {
+        case NdRoute::k1D: {
+            const float s1[2] = {samp[0], 1.0f};
+            return run2d(mask, P.fB, P.fH, 1, s1, sqdist, dist, static_cast<int32_t*>(indices), workspace,
+                         workspace_bytes, stream, nullptr);
+        }
+        case NdRoute::k2D:
+            return run2d(mask, P.fB, P.fH, P.fW, samp, sqdist, dist, static_cast<int32_t*>(indices),
+                         workspace, workspace_bytes, stream, nullptr);
+        case NdRoute::k3D:
+            if (ib == 8)
+                return run3d(mask, P.fB, P.fD, P.fH, P.fW, samp, sqdist, dist, nullptr, workspace,
+                             workspace_bytes, stream, nullptr, static_cast<int64_t*>(indices));
+            return run3d(mask, P.fB, P.fD, P.fH, P.fW, samp, sqdist, dist, static_cast<int32_t*>(indices),
+                         workspace, workspace_bytes, stream, nullptr);
+        default:
+            break;
+    }
+    for (int k = 0; k < ndim; ++k) P.d.s2[k] = s2[k];
+    if (edt::launch_nd(mask, P.d, workspace, sqdist, dist, indices, ib, stream) != hipSuccess)
+        return EDT_ERR_HIP;
+    return EDT_OK;
+}
+
+edt_status edt_unravel_indices_nd(const void* indices, int32_t index_bytes, int64_t images,
+                                  int32_t ndim, const int64_t* shape, void* coords,
+                                  hipStream_t stream) {
+    if (!indices || !coords || !shape || images < 0 || ndim < 1 || ndim > kMaxSpatial)
+        return EDT_ERR_INVALID_ARGUMENT;
+    if (index_bytes != 4 && index_bytes != 8) return EDT_ERR_INVALID_ARGUMENT;
+    if (((uintptr_t)indices & (index_bytes - 1)) || ((uintptr_t)coords & (index_bytes - 1)))
+        return EDT_ERR_INVALID_ARGUMENT;
+    int64_t per = 1;
+    for (int k = 0; k < ndim; ++k) {
+        if (shape[k] < 1) return EDT_ERR_INVALID_ARGUMENT;
+        if (per > ((int64_t)1 << 62) / shape[k]) return EDT_ERR_UNSUPPORTED_SHAPE;
+        per *= shape[k];
+    }
+    if (index_bytes == 4 && per > INT32_MAX) return EDT_ERR_UNSUPPORTED_SHAPE;
+    if (images > 0 && per > (((int64_t)1 << 62) / ndim) / images) return EDT_ERR_UNSUPPORTED_SHAPE;
+    const size_t nin = (size_t)images * (size_t)per * (size_t)index_bytes;
+    if (overlap(indices, nin, coords, nin * (size_t)ndim)) return EDT_ERR_INVALID_ARGUMENT;
+    if (edt::launch_unravel_nd(indices, index_bytes, images, ndim, shape, coords, stream) != hipSuccess)
+        return EDT_ERR_HIP;
+    return EDT_OK;
+}
+
 namespace {
 
 enum class Chamfer { kTaxicab, kChessboard };

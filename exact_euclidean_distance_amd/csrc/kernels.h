@@ -89,6 +89,25 @@ hipError_t launch_linf_cols_3d(const uint16_t* c0, int B, int D, int H, int W, u
 hipError_t launch_linf_rows_3d(const uint32_t* c01, int B, int D, int H, int W, int32_t* dist,
                                int32_t* indices, hipStream_t s, KernelTimer* tm);
 
+// The transform for any spatial rank (nd.hip): nb leading batch axes and nd
+// (1..8) spatial axes; ext[] the extents (batch first), mstride[] the mask's
+// element strides, s2[] the squared spacings of the spatial axes; B the
+// number of images, N the elements per image.  Outputs C-contiguous.
+struct NdDesc {
+    int nb, nd;
+    int64_t ext[16];
+    int64_t mstride[16];
+    double s2[8];
+    int64_t B, N;
+};
+size_t nd_workspace_bytes(int64_t total);
+hipError_t launch_nd(const uint8_t* mask, const NdDesc& d, void* ws, int32_t* sqdist, float* dist,
+                     void* indices, int idx_bytes, hipStream_t s);
+// Flat per-image indices (int32 or int64) of `images` images of shape
+// ext[0..nd) -> per-axis coordinates of the same type, coords[b][k][i].
+hipError_t launch_unravel_nd(const void* flat, int idx_bytes, int64_t images, int nd,
+                             const int64_t* ext, void* coords, hipStream_t s);
+
 // Raise a kernel's dynamic-LDS ceiling to the gfx950 LDS size on the current
 // device, once per device (done[] holds one bit per device id, set
 // atomically; devices past 63 set it on every call).  A failure is not fatal

@@ -49,7 +49,8 @@
  * return without touching any buffer.  EDT_ERR_HIP means a kernel launch was
  * rejected (hipGetLastError after the launch); outputs are then unspecified.
  *
- * Limits.  Every extent and every batch size B in [1, 65535]; elements per
+ * Limits (of the entry points with int32 extents; edt_nd_u8 below lifts
+ * them).  Every extent and every batch size B in [1, 65535]; elements per
  * image <= 2^31-1, and per volume too when indices are requested (a volume of
  * more elements, which HBM holds easily, is transformed when only sqdist
  * and/or dist are asked for);
@@ -252,6 +253,51 @@ edt_status edt3d_u8_batched_timed(const uint8_t* mask, int32_t B, int32_t D, int
                                   hipStream_t stream, float* kernel_ms,
                                   const char** kernel_names, int32_t capacity,
                                   int32_t* count);
+
+/* Bytes of workspace edt_nd_u8 needs for the given shape and mask strides
+   (NULL: C-contiguous) and index width (4 or 8); 0 if the arguments are
+   invalid.  The size depends on the path the shape takes (see edt_nd_u8). */
+size_t edt_nd_workspace_size(int32_t nbatch, int32_t ndim, const int64_t* shape,
+                             const int64_t* strides, int32_t index_bytes);
+
+/* The transform for any spatial rank: TorchMorph's batched (B, C, Spatial...)
+   tensors with a spatial rank from 1 to 8 (the separable method applies one
+   pass per axis, whatever the rank).
+     shape    HOST int64 [nbatch + ndim]: nbatch leading batch axes (0..8; each
+              image is transformed on its own), then ndim (1..8) spatial axes.
+              Extents >= 0 (any extent 0: nothing to do, EDT_OK).
+     strides  HOST int64 [nbatch + ndim] element strides of the mask (>= 0;
+              views such as slices and transposes), or NULL for C-contiguous.
+     sampling HOST float [ndim] (spatial axes) or NULL.
+     outputs  C-contiguous over the full shape: sqdist int32 / dist float32 as
+              for the entry points above; indices int32 (index_bytes 4) or
+              int64 (8), flat within each image (row-major over the spatial
+              axes), the virtual element -(n1 * ... * n_{ndim-1}).
+   C-contiguous 1-, 2- and 3-D images within the limits of edt1d_u8_batched,
+   edt2d_u8_batched and edt3d_u8_batched (int64 indices: 3-D only) run those
+   kernels.  Every other shape -- rank 4 and above, strided masks, rows longer
+   than the LDS envelope holds (2-D W > 32768, 3-D W > 16384 or H > 32768),
+   extents over 65535, more than 65535 images -- runs the workspace path: the
+   envelope of each line in the caller's workspace instead of LDS (TorchMorph's
+   fallback for long lines), 40 bytes of workspace per element.  Limits:
+   elements of all images < 2^62; int32 indices need elements per image
+   <= 2^31-1; sqdist needs unit spacing and sum of extent^2 <= 2^31-1.  Errors
+   as above; the mask's span (from its pointer to its last element) must not
+   overlap the outputs or the workspace. */
+edt_status edt_nd_u8(const uint8_t* mask, int32_t nbatch, int32_t ndim, const int64_t* shape,
+                     const int64_t* strides, const float* sampling,
+                     int32_t* sqdist, float* dist, void* indices, int32_t index_bytes,
+                     void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Per-axis coordinates of flat indices of any rank (1..8) and width:
+   indices int32 (index_bytes 4) or int64 (8), [images][n]; coords of the same
+   type, [images][ndim][n] (the layout of edt_unravel_indices); shape HOST
+   int64 [ndim].  The virtual index becomes (-1, 0, ..., 0).  Buffers
+   caller-owned, aligned to the index width, not overlapping; asynchronous on
+   stream; argument errors return before any HIP call. */
+edt_status edt_unravel_indices_nd(const void* indices, int32_t index_bytes, int64_t images,
+                                  int32_t ndim, const int64_t* shape, void* coords,
+                                  hipStream_t stream);
 
 /* Human-readable name of a status code (static string). */
 const char* edt_status_string(edt_status status);

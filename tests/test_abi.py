@@ -6,6 +6,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 from exact_euclidean_distance_amd import _lib
@@ -262,3 +263,73 @@ def test_chamfer_argument_errors(lib, metric):
     assert c3(W=20000) == SHAPE
     assert c3(B=1, D=2100, H=1024, W=1000) == SHAPE      # int32 indices of > 2^31 elements
     assert c3(ws_bytes=lib.edt3d_workspace_size(2, 8, 8, 8) - 1) == SMALL
+
+
+def _i64(vals):
+    return (ctypes.c_int64 * max(1, len(vals)))(*vals)
+
+
+def callnd(lib, shape=(4, 5, 6, 7), nbatch=0, strides=None, sampling=None, sq=SQ, dist=DIST,
+           idx=IDX, ib=4, ws=WS, ws_bytes=BIG, mask=MASK):
+    ndim = len(shape) - nbatch
+    samp = None if sampling is None else (ctypes.c_float * len(sampling))(*sampling)
+    strd = None if strides is None else _i64(strides)
+    return lib.edt_nd_u8(mask, nbatch, ndim, _i64(shape), strd, samp, sq, dist, idx, ib, ws, ws_bytes,
+                         None)
+
+
+def test_nd_workspace_sizes(lib):
+    ws = lambda shape, nb=0, strides=None, ib=4: lib.edt_nd_workspace_size(   # noqa: E731
+        nb, len(shape) - nb, _i64(shape), None if strides is None else _i64(strides), ib)
+    # C-contiguous 2-D / 3-D shapes within the LDS limits take those kernels' workspace
+    assert ws((512, 512)) == lib.edt2d_workspace_size(512, 512)
+    assert ws((16, 128, 128, 128), nb=1) == lib.edt3d_workspace_size(16, 128, 128, 128)
+    assert ws((3, 5, 7, 9), nb=2) == lib.edt2d_batched_workspace_size(15, 7, 9)
+    # rank 4, long rows, big extents, strided masks, int64 2-D indices: 40 bytes per element
+    for shape, kw in (((4, 5, 6, 7), {}), ((40, 40000), {}), ((70000, 3), {}),
+                      ((64, 64), {"strides": (128, 1)}), ((64, 64), {"ib": 8}),
+                      ((2, 3, 20000), {})):
+        n = int(np.prod(shape))
+        assert ws(shape, **kw) >= 40 * n, (shape, kw)
+    assert ws((4, 5), nb=-1) == 0
+    assert ws((4,) * 9) == 0
+    assert ws((4, 5), ib=3) == lib.edt_nd_workspace_size(0, 2, _i64((4, 5)), None, 4)
+    assert ws((4, -5)) == 0
+
+
+@fake_pointers
+def test_nd_argument_errors(lib):
+    assert callnd(lib, mask=None) == INVALID
+    assert callnd(lib, shape=(4,) * 9) == INVALID                 # spatial rank 9
+    assert callnd(lib, shape=(2, 3), nbatch=2) == INVALID         # no spatial axis
+    assert callnd(lib, shape=(2,) * 10, nbatch=9) == INVALID      # nine batch axes
+    assert callnd(lib, shape=(4, -1, 6)) == INVALID
+    assert callnd(lib, strides=(1, -1, 1, 1)) == INVALID
+    assert callnd(lib, ib=3) == INVALID
+    assert callnd(lib, sq=None, dist=None, idx=None) == INVALID
+    assert callnd(lib, sampling=(2.0, 1.0, 1.0, 1.0)) == INVALID  # sqdist needs unit spacing
+    assert callnd(lib, sampling=(1.0, 0.0, 1.0, 1.0), sq=None) == INVALID
+    assert callnd(lib, ws=None) == INVALID
+    assert callnd(lib, ws=WS + 8) == INVALID
+    need = lib.edt_nd_workspace_size(0, 4, _i64((4, 5, 6, 7)), None, 4)
+    assert callnd(lib, ws_bytes=need - 1) == SMALL
+    assert callnd(lib, sq=SQ + 2) == INVALID
+    assert callnd(lib, idx=IDX + 4, ib=8) == INVALID               # int64 indices 8-byte aligned
+    assert callnd(lib, dist=MASK + 100) == INVALID                 # inside the mask's span
+    assert callnd(lib, dist=WS + 256) == INVALID
+    assert callnd(lib, shape=(50000, 50000), dist=None, idx=None) == SHAPE   # sqdist range
+    assert callnd(lib, shape=(3, 1 << 31), sq=None, dist=None) == SHAPE      # int32 indices
+    # an empty shape is done before any HIP call
+    assert callnd(lib, shape=(4, 0, 6, 7)) == OK
+
+
+@fake_pointers
+def test_unravel_nd_argument_errors(lib):
+    shp = _i64((3, 4, 5, 6, 7))
+    assert lib.edt_unravel_indices_nd(None, 4, 2, 5, shp, IDX, None) == INVALID
+    assert lib.edt_unravel_indices_nd(SQ, 3, 2, 5, shp, IDX, None) == INVALID
+    assert lib.edt_unravel_indices_nd(SQ, 4, 2, 9, shp, IDX, None) == INVALID
+    assert lib.edt_unravel_indices_nd(SQ, 8, 2, 5, shp, IDX + 4, None) == INVALID
+    assert lib.edt_unravel_indices_nd(SQ, 4, 2, 5, shp, SQ + 8, None) == INVALID      # overlap
+    assert lib.edt_unravel_indices_nd(SQ, 4, 2, 2, _i64((1 << 20, 1 << 20)), IDX, None) == SHAPE
+    assert lib.edt_unravel_indices_nd(SQ, 4, 2, 2, _i64((0, 3)), IDX, None) == INVALID
