@@ -30,6 +30,8 @@ EXPORTS = (
     "edt2d_chessboard_u8_batched", "edt3d_chessboard_u8_batched",
     "edt2d_u8_batched_noalloc", "edt2d_noalloc_max_workspace",
     "edt_nd_workspace_size", "edt_nd_u8", "edt_unravel_indices_nd",
+    "edt2d_proximate_workspace_size", "edt2d_proximate_u8_batched",
+    "edt2d_proximate_u8_batched_timed",
 )
 
 _lib = None
@@ -108,6 +110,13 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.edt_nd_u8.argtypes = [vp, i32, i32, i64p, i64p, fp, vp, vp, vp, i32, vp, sz, vp]
     lib.edt_unravel_indices_nd.restype = ctypes.c_int
     lib.edt_unravel_indices_nd.argtypes = [vp, i32, ctypes.c_int64, i32, i64p, vp, vp]
+    lib.edt2d_proximate_workspace_size.restype = sz
+    lib.edt2d_proximate_workspace_size.argtypes = [i32, i32, i32]
+    lib.edt2d_proximate_u8_batched.restype = ctypes.c_int
+    lib.edt2d_proximate_u8_batched.argtypes = [vp, i32, i32, i32, fp, vp, vp, vp, vp, sz, vp]
+    lib.edt2d_proximate_u8_batched_timed.restype = ctypes.c_int
+    lib.edt2d_proximate_u8_batched_timed.argtypes = [vp, i32, i32, i32, fp, vp, vp, vp, vp, sz, vp,
+                                                     fp, ctypes.POINTER(ctypes.c_char_p), i32, ip]
     lib.edt_status_string.restype = ctypes.c_char_p
     lib.edt_status_string.argtypes = [ctypes.c_int]
     lib.edt_version.restype = ctypes.c_char_p

@@ -113,10 +113,14 @@ def _timed_call(fn, name, args):
 def edt2d(mask: torch.Tensor, sampling=None, *, return_distances: bool = True,
           return_sqdist: bool = False, return_indices: bool = False,
           dist=None, sqdist=None, indices=None, workspace=None, stream=None,
-          timed: bool = False):
+          timed: bool = False, method: str = "separable"):
     """Exact EDT of one (H, W) uint8 mask, or of a batch (B, H, W) or
     (B, C, H, W) of independent images (indices flat within each image).
+    ``method="proximate"`` runs PR-EDT's row-recursive proximate-point row
+    pass instead of the separable envelope (same result; W <= 16384).
     Returns :class:`EDTResult` (and the per-kernel times in ms when ``timed``)."""
+    if method not in ("separable", "proximate"):
+        raise ValueError("method must be 'separable' or 'proximate'")
     _check_mask(mask, (2, 3, 4))
     m3 = mask if mask.dim() == 3 else (mask.unsqueeze(0) if mask.dim() == 2 else mask.flatten(0, 1))
     B, H, W = m3.shape
@@ -126,12 +130,24 @@ def edt2d(mask: torch.Tensor, sampling=None, *, return_distances: bool = True,
     ds = _out(dist, shape, torch.float32, dev, return_distances)
     ix = _out(indices, shape, torch.int32, dev, return_indices)
     lib = _lib.load()
-    need = int(lib.edt2d_batched_workspace_size(B, H, W))
+    if method == "proximate":
+        need = int(lib.edt2d_proximate_workspace_size(B, H, W))
+        if need == 0:
+            raise EDTError(2, "edt2d_proximate_workspace_size")
+    else:
+        need = int(lib.edt2d_batched_workspace_size(B, H, W))
     if workspace is None:
         workspace = alloc_workspace(need, dev)
     samp = _sampling(sampling, 2)
     wsb = workspace.numel() * workspace.element_size()
-    if mask.dim() == 2:
+    if method == "proximate":
+        if B > 65535:
+            raise ValueError("at most 65535 images per call")
+        args = [_ptr(mask), B, H, W, samp, _ptr(sq), _ptr(ds), _ptr(ix), _ptr(workspace), wsb,
+                _stream(stream)]
+        fn, tfn, name = (lib.edt2d_proximate_u8_batched, lib.edt2d_proximate_u8_batched_timed,
+                         "edt2d_proximate_u8_batched")
+    elif mask.dim() == 2:
         args = [_ptr(mask), H, W, samp, _ptr(sq), _ptr(ds), _ptr(ix), _ptr(workspace), wsb,
                 _stream(stream)]
         fn, tfn, name = lib.edt2d_u8, lib.edt2d_u8_timed, "edt2d_u8"

@@ -182,6 +182,56 @@ edt_status run2d(const uint8_t* mask, int32_t B, int32_t H, int32_t W, const flo
     return EDT_OK;
 }
 
+// PR-EDT's row-recursive pass: the axis-0 summaries, then the proximate-point
+// sets of each 64-row sub-block; workspace = summaries + each pixel's upper
+// answer (float64 + int32).
+bool prox_shape_ok(int32_t B, int32_t H, int32_t W) {
+    if (B < 1 || H < 1 || W < 1 || B > kMaxExtent || H > kMaxExtent) return false;
+    if (W > edt::prox_max_width()) return false;
+    return (int64_t)H * W <= INT32_MAX;
+}
+
+size_t prox_workspace(int32_t B, int32_t H, int32_t W, size_t* off_f, size_t* off_i) {
+    const Layout L = layout2d(B, H, W);
+    const size_t n = (size_t)B * H * W;
+    const size_t summ = L.total - L.first;   // first, last, bits (no c0)
+    *off_f = round_up(summ);
+    *off_i = *off_f + round_up(n * 8);
+    return *off_i + round_up(n * 4);
+}
+
+edt_status run_prox2d(const uint8_t* mask, int32_t B, int32_t H, int32_t W, const float* sampling,
+                      int32_t* sqdist, float* dist, int32_t* indices, void* ws, size_t ws_bytes,
+                      hipStream_t stream, edt::KernelTimer* tm) {
+    if (B < 1 || H < 1 || W < 1) return EDT_ERR_INVALID_ARGUMENT;
+    if (!prox_shape_ok(B, H, W)) return EDT_ERR_UNSUPPORTED_SHAPE;
+    double s2[2];
+    bool unit;
+    edt_status st = read_sampling(sampling, 2, s2, &unit);
+    if (st != EDT_OK) return st;
+    if (sqdist && !unit) return EDT_ERR_INVALID_ARGUMENT;
+    if (sqdist && (double)H * H + (double)W * W > (double)INT32_MAX) return EDT_ERR_UNSUPPORTED_SHAPE;
+    size_t off_f, off_i;
+    const size_t need = prox_workspace(B, H, W, &off_f, &off_i);
+    st = check_buffers(mask, (size_t)B * H * W, sqdist, dist, indices, ws, ws_bytes, need);
+    if (st != EDT_OK) return st;
+    const Layout L = layout2d(B, H, W);
+    char* base = static_cast<char*>(ws);
+    // the summaries at the front of the workspace (the same relative layout
+    // as the separable path's, without its per-pixel coordinates)
+    uint16_t* first = reinterpret_cast<uint16_t*>(base);
+    uint16_t* last = reinterpret_cast<uint16_t*>(base + (L.last - L.first));
+    uint64_t* bits = reinterpret_cast<uint64_t*>(base + (L.bits - L.first));
+    if (edt::launch_axis0(mask, B, H, W, first, last, bits, nullptr, stream, tm) != hipSuccess)
+        return EDT_ERR_HIP;
+    if (edt::launch_prox_rows_2d(last, first, bits, B, H, W, s2[0], s2[1],
+                                 reinterpret_cast<double*>(base + off_f),
+                                 reinterpret_cast<int32_t*>(base + off_i), sqdist, dist, indices, stream,
+                                 tm) != hipSuccess)
+        return EDT_ERR_HIP;
+    return EDT_OK;
+}
+
 edt_status run3d(const uint8_t* mask, int32_t B, int32_t D, int32_t H, int32_t W,
                  const float* sampling, int32_t* sqdist, float* dist, int32_t* indices,
                  void* ws, size_t ws_bytes, hipStream_t stream, edt::KernelTimer* tm,
@@ -290,6 +340,34 @@ edt_status edt2d_u8_batched(const uint8_t* mask, int32_t B, int32_t H, int32_t W
 }
 
 size_t edt2d_noalloc_max_workspace(void) { return kScratchBytes; }
+
+size_t edt2d_proximate_workspace_size(int32_t B, int32_t H, int32_t W) {
+    if (!prox_shape_ok(B, H, W)) return 0;
+    size_t a, b;
+    return prox_workspace(B, H, W, &a, &b);
+}
+
+edt_status edt2d_proximate_u8_batched(const uint8_t* mask, int32_t B, int32_t H, int32_t W,
+                                      const float* sampling, int32_t* sqdist, float* dist,
+                                      int32_t* indices, void* workspace, size_t workspace_bytes,
+                                      hipStream_t stream) {
+    return run_prox2d(mask, B, H, W, sampling, sqdist, dist, indices, workspace, workspace_bytes,
+                      stream, nullptr);
+}
+
+edt_status edt2d_proximate_u8_batched_timed(const uint8_t* mask, int32_t B, int32_t H, int32_t W,
+                                            const float* sampling, int32_t* sqdist, float* dist,
+                                            int32_t* indices, void* workspace,
+                                            size_t workspace_bytes, hipStream_t stream,
+                                            float* kernel_ms, const char** kernel_names,
+                                            int32_t capacity, int32_t* count) {
+    if (!kernel_ms || capacity < 1) return EDT_ERR_INVALID_ARGUMENT;
+    edt::KernelTimer tm;
+    tm.capacity = capacity;
+    edt_status st = run_prox2d(mask, B, H, W, sampling, sqdist, dist, indices, workspace,
+                               workspace_bytes, stream, &tm);
+    return finish_timed(st, tm, stream, kernel_ms, kernel_names, count);
+}
 
 edt_status edt2d_u8_batched_noalloc(const uint8_t* mask, int32_t B, int32_t H, int32_t W,
                                     const float* sampling, int32_t* sqdist, float* dist,

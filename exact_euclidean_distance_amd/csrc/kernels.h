@@ -37,7 +37,9 @@ struct KernelTimer {
 // Axis-0 pass: for every line along axis 0 (B images of n0 x M elements), the
 // axis-0 coordinate of the nearest background element on that line (kNone16 if
 // the line has none).  first/last: workspace of B * nseg * M uint16 each;
-// bits: B * nseg * M uint64 (nseg = ceil(n0 / kSegRows)).
+// bits: B * nseg * M uint64 (nseg = ceil(n0 / kSegRows)).  With c0 null only
+// the summaries are made (first / last then hold the nearest background row
+// strictly below / above each segment when nseg > 1).
 hipError_t launch_axis0(const uint8_t* mask, int B, int n0, int64_t M,
                         uint16_t* first, uint16_t* last, uint64_t* bits, uint16_t* c0,
                         hipStream_t s, KernelTimer* tm);
@@ -107,6 +109,17 @@ hipError_t launch_nd(const uint8_t* mask, const NdDesc& d, void* ws, int32_t* sq
 // ext[0..nd) -> per-axis coordinates of the same type, coords[b][k][i].
 hipError_t launch_unravel_nd(const void* flat, int idx_bytes, int64_t images, int nd,
                              const int64_t* ext, void* coords, hipStream_t s);
+
+// PR-EDT's row-recursive proximate-point row pass (prox.hip) for B images
+// H x W (W <= prox_max_width()), from the axis-0 summary: above / below the
+// nearest background row strictly above / below each 64-row segment, bits
+// its background rows; tmpF / tmpI: workspace of B * H * W float64 / int32.
+hipError_t launch_prox_rows_2d(const uint16_t* above, const uint16_t* below, const uint64_t* bits,
+                               int B, int H, int W, double s2r, double s2c, double* tmpF,
+                               int32_t* tmpI, int32_t* sqdist, float* dist, int32_t* indices,
+                               hipStream_t s, KernelTimer* tm);
+size_t prox_lds_bytes();
+int prox_max_width();
 
 // Raise a kernel's dynamic-LDS ceiling to the gfx950 LDS size on the current
 // device, once per device (done[] holds one bit per device id, set

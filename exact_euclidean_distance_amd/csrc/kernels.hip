@@ -348,6 +348,7 @@ hipError_t launch_axis0(const uint8_t* mask, int B, int n0, int64_t M, uint16_t*
             EDT_LAUNCH(tm, "axis0_scan", s, hipLaunchKernelGGL(k_axis0_scan<16>, sgrid, dim3(64, 16), 0, s, first, last, nseg, M));
         }
     }
+    if (!c0) return hipSuccess;   // the summaries alone were asked for
     // the resolve keeps per-column state in registers: 4 columns per lane
     if (vec >= 4) {
         EDT_LAUNCH(tm, "axis0_resolve", s, hipLaunchKernelGGL(k_axis0_resolve<4>, grid_for(4), block, 0, s, bits, n0, M, nseg, last, first, c0));

@@ -128,6 +128,35 @@ edt_status edt2d_u8_batched_noalloc(const uint8_t* mask, int32_t B, int32_t H, i
 /* Size in bytes of the device array edt2d_u8_batched_noalloc works in. */
 size_t edt2d_noalloc_max_workspace(void);
 
+/* Bytes of workspace edt2d_proximate_u8_batched needs for B images of H x W
+   (0 outside its limits: B, H <= 65535, W <= 16384, H * W <= 2^31-1). */
+size_t edt2d_proximate_workspace_size(int32_t B, int32_t H, int32_t W);
+
+/* The same 2-D transform as edt2d_u8_batched, by the row pass of "GPU-Based
+   Parallel Euclidean Distance Transform Algorithm" instead of the separable
+   envelope: sub-blocks of 64 rows, each row's upper and lower proximate-point
+   sets built by Algorithm 1 for the sub-block's first row and updated row by
+   row by Algorithms 2-3 (masked points removed, the row's background pixels
+   merged in, prefix-sum compaction), every pixel answered from both sets
+   (§3.3-§3.4).  A second implementation of the same result, kept for
+   comparison with the page's own method: arguments, outputs, indices and the
+   virtual element exactly as edt2d_u8_batched; any nearest background
+   element may be returned where several are equally near. */
+edt_status edt2d_proximate_u8_batched(const uint8_t* mask, int32_t B, int32_t H, int32_t W,
+                                      const float* sampling,
+                                      int32_t* sqdist, float* dist, int32_t* indices,
+                                      void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* edt2d_proximate_u8_batched with per-kernel HIP event timings, as
+   edt2d_u8_timed. */
+edt_status edt2d_proximate_u8_batched_timed(const uint8_t* mask, int32_t B, int32_t H, int32_t W,
+                                            const float* sampling,
+                                            int32_t* sqdist, float* dist, int32_t* indices,
+                                            void* workspace, size_t workspace_bytes,
+                                            hipStream_t stream, float* kernel_ms,
+                                            const char** kernel_names, int32_t capacity,
+                                            int32_t* count);
+
 /* Bytes of workspace edt1d_u8_batched needs for B lines of N elements. */
 size_t edt1d_workspace_size(int32_t B, int32_t N);
 
