@@ -113,6 +113,10 @@ def algorithmic_bytes(kernel: str, shape, n_out: int) -> int:
         return 2 * n + 4 * n
     if kernel == "envelope_rows_3d":
         return 4 * n + 4 * n * n_out
+    if kernel == "proximate_rows_2d":
+        # summaries and row bits read, outputs written, and each pixel's
+        # upper answer (float64 + int32) written and read back
+        return summ // 2 + rows + 4 * n * n_out + 2 * 12 * n
     raise KeyError(kernel)
 
 
@@ -392,6 +396,9 @@ def main(argv=None):
                     help="time the city-block (L1) transform on the workload instead")
     ap.add_argument("--chessboard", action="store_true",
                     help="time the chessboard (L-infinity) transform on the workload instead")
+    ap.add_argument("--method", default="separable", choices=("separable", "proximate"),
+                    help="2-D row pass: the separable envelope (default) or PR-EDT's "
+                         "row-recursive proximate-point sets")
     ap.add_argument("--graph", action="store_true",
                     help="time replays of a HIP graph holding one transform (launch gaps removed)")
     ap.add_argument("--probe-copy", action="store_true")
@@ -516,9 +523,15 @@ def bench_workload(name, args, dev, copy_gbs):
     sq = torch.empty(shape, dtype=torch.int32, device=dev) if "sqdist" in want else None
     ds = torch.empty(shape, dtype=torch.float32, device=dev) if "dist" in want else None
     ix = torch.empty(shape, dtype=torch.int32, device=dev) if "indices" in want else None
+    method = getattr(args, "method", "separable")
     if len(shape) in (2, 3):
-        ws = alloc_workspace(workspace_size_2d_batched(*((1,) + shape)[-3:]), dev)
-        fn = edt2d
+        if method == "proximate":
+            from exact_euclidean_distance_amd import _lib
+            ws = alloc_workspace(int(_lib.load().edt2d_proximate_workspace_size(*((1,) + shape)[-3:])), dev)
+            fn = lambda *a, **k: edt2d(*a, method="proximate", **k)   # noqa: E731
+        else:
+            ws = alloc_workspace(workspace_size_2d_batched(*((1,) + shape)[-3:]), dev)
+            fn = edt2d
     else:
         ws = alloc_workspace(workspace_size_3d(*shape), dev)
         fn = edt3d
@@ -607,7 +620,8 @@ def bench_workload(name, args, dev, copy_gbs):
         "dtype": "f64",
         "config": {"workload": f"{name}: {WORKLOADS[name]}", "shape": list(shape),
                    "sampling": list(sampling) if sampling else None, "outputs": list(want),
-                   "launch": "graph" if graph is not None else "stream"},
+                   "launch": "graph" if graph is not None else "stream",
+                   "row_pass": method if len(shape) in (2, 3) else "separable"},
         "roofline": {"bound": "hbm", "kernel": dom["name"], "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic},

@@ -27,11 +27,12 @@
 // The lower sets follow from the bottom row of the sub-block upwards, and each
 // pixel keeps the nearer of its upper and lower answers (§3.4).
 //
-// Differences from the page: sub-blocks are the 64-row segments of the axis-0
-// summary kernels, whose nearest background above / below each segment and
-// per-segment background-row bits stand in for the full candidate matrices of
-// §3.2 (the rows in between need only the bits); the first row's sweep runs on
-// one thread of the work-group.
+// Differences from the page: sub-blocks are 16 or 64 rows (the page uses 20),
+// four or one to each 64-row segment of the axis-0 summary kernels, whose nearest
+// background above / below each segment and per-segment background-row bits
+// stand in for the full candidate matrices of §3.2 (a sub-block's first row
+// takes its candidates from them, the rows after it need only the bits); the
+// first row's sweep runs on one thread of the work-group.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -43,6 +44,12 @@ namespace edt {
 namespace {
 
 constexpr int kProxThreads = 1024;
+// Rows per sub-block: 16 (a quarter of a 64-row summary segment) for rows
+// of up to 4096 pixels, a whole segment beyond: Algorithm 1's sweep costs the
+// row's width once per sub-block, which for wide rows outweighs the
+// parallelism of more sub-blocks (16384^2: 24.5 ms with 16 rows, 11.0 with
+// 64; 1024^2: 0.88 against 1.77 ms).
+int sub_rows(int W) { return W <= 4096 ? 16 : kSegRows; }
 constexpr int kProxMaxW = 16384;
 constexpr int kProxPer = kProxMaxW / kProxThreads;   // array entries per thread at most
 constexpr uint32_t kNoCand = 0xFFFFFFFFu;
@@ -209,15 +216,15 @@ struct ProxOut {
     int32_t* indices;
 };
 
-// One sub-block (rows [r0, r1) of image b): the upper sets from r0 down, then
-// the lower sets from r1 - 1 up.  above / below: per (image, segment, column)
+// One sub-block (rows [rs, re) of image b): the upper sets from rs down, then
+// the lower sets from re - 1 up.  above / below: per (image, segment, column)
 // the nearest background row strictly above / below the segment (kNone16:
 // none); bits: the segment's background rows per column.  tmpF / tmpI hold
 // each pixel's upper answer until the lower pass.
 __global__ __launch_bounds__(kProxThreads) void k_prox_rows(
     const uint16_t* __restrict__ above, const uint16_t* __restrict__ below,
     const uint64_t* __restrict__ bits, int H, int W, int nseg, double s2r, double s2c,
-    double* __restrict__ tmpF, int32_t* __restrict__ tmpI, ProxOut out) {
+    double* __restrict__ tmpF, int32_t* __restrict__ tmpI, ProxOut out, int kSub) {
     extern __shared__ __align__(16) unsigned char smem[];
     uint32_t* Q = reinterpret_cast<uint32_t*>(smem);              // [W]
     uint32_t* dense = Q + kProxMaxW;                              // [W]
@@ -227,12 +234,15 @@ __global__ __launch_bounds__(kProxThreads) void k_prox_rows(
     int* nset = flag + 1;
 
     const int tid = threadIdx.x;
-    const int s = blockIdx.x;
+    const int rs = blockIdx.x * kSub;       // the sub-block's rows [rs, re)
+    if (rs >= H) return;                    // (the whole work-group: no barrier reached)
+    const int re = min(rs + kSub, H);
+    const int s = rs / kSegRows;            // its summary segment, rows [r0, ...)
     const int64_t b = blockIdx.y;
-    const int r0 = s * kSegRows, r1 = min(r0 + kSegRows, H);
+    const int r0 = s * kSegRows;
     const int64_t so = (b * nseg + s) * (int64_t)W;
     const int64_t img = b * (int64_t)H * W;
-    RowMetric M{s2r, s2c, r0};
+    RowMetric M{s2r, s2c, rs};
     // the sub-block's background-row bits of the thread's columns
     // j = tid + kProxThreads * u
     uint64_t cb[kProxPer];
@@ -243,17 +253,21 @@ __global__ __launch_bounds__(kProxThreads) void k_prox_rows(
     }
 
     for (int pass = 0; pass < 2; ++pass) {   // 0: upper sets, top-down; 1: lower sets, bottom-up
-        const int first = pass == 0 ? r0 : r1 - 1;
-        // the first row's candidates: its own background pixel, else the
-        // nearest background beyond the sub-block
+        const int first = pass == 0 ? rs : re - 1;
+        // the first row's candidates: the nearest background of the column at
+        // or above it (at or below, bottom-up) -- within the segment from its
+        // row bits, else beyond the segment
+        const int fb = first - r0;
 #pragma unroll
         for (int u = 0; u < kProxPer; ++u) {
             const int j = tid + kProxThreads * u;
             if (j >= W) break;
             int r = -1;
-            if ((cb[u] >> (first - r0)) & 1ull) {
-                r = first;
-            } else {   // nearest background beyond the sub-block (none for a single segment)
+            const uint64_t near = pass == 0 ? (fb == 63 ? cb[u] : cb[u] & ((2ull << fb) - 1ull))
+                                            : cb[u] & ~((1ull << fb) - 1ull);
+            if (near) {
+                r = r0 + (pass == 0 ? 63 - __builtin_clzll(near) : __builtin_ctzll(near));
+            } else {   // beyond the segment (nothing for an image of a single segment)
                 const uint16_t* beyond = pass == 0 ? above : below;
                 const uint16_t c = beyond ? beyond[so + j] : kNone16;
                 if (c != kNone16) r = c;
@@ -268,7 +282,7 @@ __global__ __launch_bounds__(kProxThreads) void k_prox_rows(
         n = *nset;
         for (int step = 0;; ++step) {
             const int row = pass == 0 ? first + step : first - step;
-            if (row < r0 || row >= r1) break;
+            if (row < rs || row >= re) break;
             M.row = row;
             if (step > 0) {
                 // Algorithm 3: masked points at the new row leave; the row's
@@ -341,12 +355,14 @@ hipError_t launch_prox_rows_2d(const uint16_t* above, const uint16_t* below, con
     hipError_t le = large_lds_once((const void*)k_prox_rows, &lds_done);
     if (le != hipSuccess) return le;
     const int nseg = (H + kSegRows - 1) / kSegRows;
+    const int kSub = sub_rows(W);
+    const int nsub = (H + kSub - 1) / kSub;
     ProxOut out{sqdist, dist, indices};
     if (nseg == 1) above = below = nullptr;   // (the axis-0 scan did not run)
     EDT_LAUNCH(tm, "proximate_rows_2d", s,
-               hipLaunchKernelGGL(k_prox_rows, dim3((unsigned)nseg, (unsigned)B), dim3(kProxThreads),
+               hipLaunchKernelGGL(k_prox_rows, dim3((unsigned)nsub, (unsigned)B), dim3(kProxThreads),
                                   prox_lds_bytes(), s, above, below, bits, H, W, nseg, s2r, s2c, tmpF,
-                                  tmpI, out));
+                                  tmpI, out, kSub));
     return hipSuccess;
 }
 
