@@ -25,7 +25,7 @@ EXPORTS = (
     "edt2d_u8_timed", "edt3d_u8_batched_timed", "edt_status_string", "edt_version",
     "edt2d_batched_workspace_size", "edt2d_u8_batched", "edt2d_u8_batched_timed",
     "edt1d_workspace_size", "edt1d_u8_batched", "edt_unravel_indices",
-    "edt_brute_workspace_size", "edt_brute_u8", "edt3d_u8_batched_idx64",
+    "edt_brute_workspace_size", "edt_brute_u8", "edt_brute_metric_u8", "edt3d_u8_batched_idx64",
     "edt2d_taxicab_u8_batched", "edt3d_taxicab_u8_batched",
     "edt2d_chessboard_u8_batched", "edt3d_chessboard_u8_batched",
     "edt2d_u8_batched_noalloc", "edt2d_noalloc_max_workspace",
@@ -89,6 +89,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.edt_brute_workspace_size.argtypes = [i32, i32, ip]
     lib.edt_brute_u8.restype = ctypes.c_int
     lib.edt_brute_u8.argtypes = [vp, i32, i32, ip, fp, vp, vp, vp, vp, sz, vp]
+    lib.edt_brute_metric_u8.restype = ctypes.c_int
+    lib.edt_brute_metric_u8.argtypes = [vp, i32, i32, ip, i32, vp, vp, vp, sz, vp]
     lib.edt3d_u8_batched_idx64.restype = ctypes.c_int
     lib.edt3d_u8_batched_idx64.argtypes = [vp, i32, i32, i32, i32, fp, vp, vp, vp, vp, sz, vp]
     lib.edt2d_taxicab_u8_batched.restype = ctypes.c_int

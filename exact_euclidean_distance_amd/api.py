@@ -231,29 +231,44 @@ def unravel_indices(indices: torch.Tensor, image_shape: Sequence[int], *, out=No
 def edt_brute(mask: torch.Tensor, sampling=None, *, batched: bool = False,
               return_distances: bool = True, return_sqdist: bool = False,
               return_indices: bool = False, dist=None, sqdist=None, indices=None,
-              workspace=None, stream=None):
+              workspace=None, stream=None, metric: str = "euclidean"):
     """The transform by its definition on the device (every element against
-    every background element): an exactness check for small images.  mask is
-    one image of 1-3 axes, or a batch of them (leading axis) when ``batched``."""
+    every background element): an exactness check.  mask is one image of 1-3
+    axes, or a batch of them (leading axis) when ``batched``.  ``metric``
+    "taxicab" or "chessboard" gives those transforms instead (int32
+    distances in ``dist``, no spacing, no sqdist)."""
     _check_mask(mask, (1, 2, 3, 4))
     img = tuple(mask.shape[1:]) if batched else tuple(mask.shape)
     B = int(mask.shape[0]) if batched else 1
     if not 1 <= len(img) <= 3:
         raise ValueError("images must have 1 to 3 axes")
+    if metric not in ("euclidean", "taxicab", "chessboard"):
+        raise ValueError("metric must be 'euclidean', 'taxicab' or 'chessboard'")
     shape = tuple(mask.shape)
     dev = mask.device
-    sq = _out(sqdist, shape, torch.int32, dev, return_sqdist)
-    ds = _out(dist, shape, torch.float32, dev, return_distances)
-    ix = _out(indices, shape, torch.int32, dev, return_indices)
     lib = _lib.load()
     shp = (ctypes.c_int32 * len(img))(*img)
     need = int(lib.edt_brute_workspace_size(B, len(img), shp))
     if workspace is None:
         workspace = alloc_workspace(need, dev)
+    wsb = workspace.numel() * workspace.element_size()
+    if metric != "euclidean":
+        if sampling is not None or return_sqdist or sqdist is not None:
+            raise ValueError("the chamfer metrics take no spacing and give no sqdist")
+        ds = _out(dist, shape, torch.int32, dev, return_distances)
+        ix = _out(indices, shape, torch.int32, dev, return_indices)
+        code = 1 if metric == "taxicab" else 2
+        st = lib.edt_brute_metric_u8(_ptr(mask), B, len(img), shp, code, _ptr(ds), _ptr(ix),
+                                     _ptr(workspace), wsb, _stream(stream))
+        if st != 0:
+            raise EDTError(st, "edt_brute_metric_u8")
+        return EDTResult(None, ds, ix)
+    sq = _out(sqdist, shape, torch.int32, dev, return_sqdist)
+    ds = _out(dist, shape, torch.float32, dev, return_distances)
+    ix = _out(indices, shape, torch.int32, dev, return_indices)
     samp = _sampling(sampling, len(img))
     st = lib.edt_brute_u8(_ptr(mask), B, len(img), shp, samp, _ptr(sq), _ptr(ds), _ptr(ix),
-                          _ptr(workspace), workspace.numel() * workspace.element_size(),
-                          _stream(stream))
+                          _ptr(workspace), wsb, _stream(stream))
     if st != 0:
         raise EDTError(st, "edt_brute_u8")
     return EDTResult(sq, ds, ix)

@@ -282,6 +282,20 @@ bool brute_shape_ok(int32_t B, int32_t ndim, const int32_t* shape, int64_t* per)
     return true;
 }
 
+// Workspace of the brute force: the background list, the per-image counts
+// and the per-block offsets of the list kernels.
+struct BruteLayout {
+    size_t list, counts, block_off, total;
+};
+BruteLayout brute_layout(int32_t B, int64_t per) {
+    BruteLayout L{};
+    L.list = 0;
+    L.counts = round_up((size_t)B * (size_t)per * 4);
+    L.block_off = L.counts + round_up((size_t)B * 4);
+    L.total = L.block_off + round_up((size_t)B * edt::brute_list_block_count(per) * 4);
+    return L;
+}
+
 edt_status finish_timed(edt_status st, edt::KernelTimer& tm, hipStream_t stream, float* kernel_ms,
                         const char** kernel_names, int32_t* count) {
     if (st == EDT_OK && hipStreamSynchronize(stream) != hipSuccess) st = EDT_ERR_HIP;
@@ -461,7 +475,7 @@ edt_status edt3d_u8_batched_timed(const uint8_t* mask, int32_t B, int32_t D, int
 size_t edt_brute_workspace_size(int32_t B, int32_t ndim, const int32_t* shape) {
     int64_t per = 0;
     if (!brute_shape_ok(B, ndim, shape, &per)) return 0;
-    return round_up((size_t)B * (size_t)per * 4) + round_up((size_t)B * 4);
+    return brute_layout(B, per).total;
 }
 
 edt_status edt_brute_u8(const uint8_t* mask, int32_t B, int32_t ndim, const int32_t* shape,
@@ -482,16 +496,43 @@ edt_status edt_brute_u8(const uint8_t* mask, int32_t B, int32_t ndim, const int3
         for (int k = 0; k < ndim; ++k) mx += (double)shape[k] * shape[k];
         if (mx > (double)INT32_MAX) return EDT_ERR_UNSUPPORTED_SHAPE;
     }
-    const size_t list_bytes = round_up((size_t)B * (size_t)per * 4);
-    const size_t need = list_bytes + round_up((size_t)B * 4);
-    st = check_buffers(mask, (size_t)B * per, sqdist, dist, indices, workspace, workspace_bytes, need);
+    const BruteLayout L = brute_layout(B, per);
+    st = check_buffers(mask, (size_t)B * per, sqdist, dist, indices, workspace, workspace_bytes, L.total);
     if (st != EDT_OK) return st;
     char* base = static_cast<char*>(workspace);
     int n[3];
     for (int k = 0; k < ndim; ++k) n[k] = shape[k];
-    if (edt::launch_brute(mask, B, ndim, n, s2, reinterpret_cast<int32_t*>(base),
-                          reinterpret_cast<int32_t*>(base + list_bytes), sqdist, dist, indices,
+    if (edt::launch_brute(mask, B, ndim, n, s2, reinterpret_cast<int32_t*>(base + L.list),
+                          reinterpret_cast<int32_t*>(base + L.counts),
+                          reinterpret_cast<int32_t*>(base + L.block_off), sqdist, dist, indices,
                           stream) != hipSuccess)
+        return EDT_ERR_HIP;
+    return EDT_OK;
+}
+
+edt_status edt_brute_metric_u8(const uint8_t* mask, int32_t B, int32_t ndim, const int32_t* shape,
+                               int32_t metric, int32_t* dist, int32_t* indices, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream) {
+    if (!shape || ndim < 1 || ndim > 3 || B < 1) return EDT_ERR_INVALID_ARGUMENT;
+    if (metric != EDT_METRIC_TAXICAB && metric != EDT_METRIC_CHESSBOARD) return EDT_ERR_INVALID_ARGUMENT;
+    for (int k = 0; k < ndim; ++k)
+        if (shape[k] < 1) return EDT_ERR_INVALID_ARGUMENT;
+    int64_t per = 0;
+    if (!brute_shape_ok(B, ndim, shape, &per)) return EDT_ERR_UNSUPPORTED_SHAPE;
+    const BruteLayout L = brute_layout(B, per);
+    // the int32 distance buffer goes in the sqdist slot of the common check
+    edt_status st = check_buffers(mask, (size_t)B * per, dist, nullptr, indices, workspace,
+                                  workspace_bytes, L.total);
+    if (st != EDT_OK) return st;
+    char* base = static_cast<char*>(workspace);
+    int n[3];
+    for (int k = 0; k < ndim; ++k) n[k] = shape[k];
+    if (edt::launch_brute_metric(mask, B, ndim, n,
+                                 metric == EDT_METRIC_TAXICAB ? edt::kBruteTaxicab : edt::kBruteChessboard,
+                                 reinterpret_cast<int32_t*>(base + L.list),
+                                 reinterpret_cast<int32_t*>(base + L.counts),
+                                 reinterpret_cast<int32_t*>(base + L.block_off), dist, indices,
+                                 stream) != hipSuccess)
         return EDT_ERR_HIP;
     return EDT_OK;
 }

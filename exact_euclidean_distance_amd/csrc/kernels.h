@@ -69,10 +69,20 @@ hipError_t launch_unravel(const int32_t* flat, int64_t images, int64_t per_image
                           int n2, int32_t* coords, hipStream_t s);
 
 // The transform by its definition (brute force), B images of ndim (1..3)
-// extents n[]: list / counts are workspace (B * elements and B int32).
+// extents n[]: list / counts / block_off are workspace (B * elements,
+// B and B * brute_list_block_count(elements) int32).
+size_t brute_list_block_count(int64_t per);
 hipError_t launch_brute(const uint8_t* mask, int B, int ndim, const int* n, const double* s2,
-                        int32_t* list, int32_t* counts, int32_t* sqdist, float* dist,
-                        int32_t* indices, hipStream_t s);
+                        int32_t* list, int32_t* counts, int32_t* block_off, int32_t* sqdist,
+                        float* dist, int32_t* indices, hipStream_t s);
+// Integer metrics of the brute force (the squared one is launch_brute's at
+// unit spacing); launch_brute_metric takes the city block or the chessboard.
+constexpr int kBruteSquared = 0;
+constexpr int kBruteTaxicab = 1;
+constexpr int kBruteChessboard = 2;
+hipError_t launch_brute_metric(const uint8_t* mask, int B, int ndim, const int* n, int metric,
+                               int32_t* list, int32_t* counts, int32_t* block_off, int32_t* dist,
+                               int32_t* indices, hipStream_t s);
 
 // City-block (taxicab) transform (chamfer.hip): last-axis pass with int32
 // distances / indices for B images or volumes, and the middle-axis pass of

@@ -200,6 +200,26 @@ edt_status edt_brute_u8(const uint8_t* mask, int32_t B, int32_t ndim, const int3
                         int32_t* sqdist, float* dist, int32_t* indices,
                         void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Metric codes of edt_brute_metric_u8. */
+#define EDT_METRIC_TAXICAB 1
+#define EDT_METRIC_CHESSBOARD 2
+
+/* The chamfer transforms by their definition, the checker beside the taxicab
+   and chessboard entry points below (TorchMorph ships both chamfer transforms
+   and a brute-force oracle beside its EDT): for every element the minimum
+   over the background elements of its image of sum_k |p_k - b_k|
+   (EDT_METRIC_TAXICAB) or max_k |p_k - b_k| (EDT_METRIC_CHESSBOARD), as
+   int32, and the smallest flat index attaining it.  B images of ndim = 1..3
+   axes, extents shape[0..ndim) (HOST pointer), mask [B][...]; dist and/or
+   indices (int32, device, 4-byte aligned, [B][...]); the virtual element for
+   images without background as for the taxicab and chessboard entry points;
+   workspace of edt_brute_workspace_size(B, ndim, shape) bytes.  Limits as
+   for edt_brute_u8; an unknown metric is EDT_ERR_INVALID_ARGUMENT.  Cost
+   O(elements x background elements). */
+edt_status edt_brute_metric_u8(const uint8_t* mask, int32_t B, int32_t ndim, const int32_t* shape,
+                               int32_t metric, int32_t* dist, int32_t* indices,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* City-block (taxicab, L1) distance transform, one of the chamfer
    transforms TorchMorph ships beside its EDT (read as the L1 metric, like
    SciPy's "taxicab"): for every element, min over background elements of

@@ -225,6 +225,27 @@ def test_brute_argument_errors(lib):
 
 
 @fake_pointers
+def test_brute_metric_argument_errors(lib):
+    shp = (ctypes.c_int32 * 2)(40, 50)
+    need = lib.edt_brute_workspace_size(3, 2, shp)
+    assert need >= 3 * 40 * 50 * 4
+
+    def call(mask=MASK, B=3, ndim=2, shape=shp, metric=1, dist=SQ, idx=IDX, ws=WS, ws_bytes=BIG):
+        return lib.edt_brute_metric_u8(mask, B, ndim, shape, metric, dist, idx, ws, ws_bytes, None)
+
+    assert call(mask=None) == INVALID
+    assert call(metric=0) == INVALID
+    assert call(metric=3) == INVALID
+    assert call(ndim=4) == INVALID
+    assert call(shape=(ctypes.c_int32 * 2)(40, 0)) == INVALID
+    assert call(shape=(ctypes.c_int32 * 2)(40, 70000)) == SHAPE
+    assert call(ws_bytes=need - 1) == SMALL
+    assert call(dist=None, idx=None) == INVALID
+    assert call(dist=SQ + 2) == INVALID
+    assert call(ws=WS + 8) == INVALID
+
+
+@fake_pointers
 def test_idx64_argument_errors(lib):
     def call(idx=IDX, **kw):
         a = dict(mask=MASK, B=2, D=8, H=8, W=8, samp=None, sq=SQ, dist=DIST, ws=WS, ws_bytes=BIG)

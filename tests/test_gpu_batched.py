@@ -274,6 +274,47 @@ def test_brute_force_transform(torch_dev):
     assert torch.equal(e.sqdist, f.sqdist)
 
 
+def test_brute_force_metrics(torch_dev):
+    """The device brute force of the city-block and chessboard metrics (and
+    the integer squared Euclidean one at unit spacing) against the oracle's
+    brute forces: distances and the smallest-index minimiser equal, on 1-3
+    axes, batches with an image without background, and ragged tile tails."""
+    torch, dev = torch_dev
+    from exact_euclidean_distance_amd import edt_brute
+    rng = np.random.default_rng([42, 5020])
+    shapes = [(1,), (37,), (1, 1), (23, 57), (64, 65), (9, 13, 17), (5, 31, 2), (1, 300, 3)]
+    for shape in shapes:
+        for p in (0.003, 0.05, 0.5, 1.0):
+            mask = (rng.random(shape) >= p).astype(np.uint8)
+            mask.reshape(-1)[rng.integers(mask.size)] = 0
+            t = torch.from_numpy(mask).to(dev)
+            for metric, fn in (("taxicab", oracle.taxicab_brute), ("chessboard", oracle.chessboard_brute)):
+                _say(f"brute {metric} {shape} p={p}")
+                r = edt_brute(t, metric=metric, return_indices=True)
+                torch.cuda.synchronize()
+                ref, who = fn(mask)
+                assert (_np(r.dist) == ref).all(), f"{metric} distance mismatch"
+                assert (_np(r.indices) == who).all(), f"{metric} minimiser is not the smallest index"
+            r = edt_brute(t, return_sqdist=True, return_indices=True)
+            torch.cuda.synchronize()
+            ref, feat = oracle.edt_brute(mask, None, features=True)
+            assert (_np(r.sqdist) == ref).all()
+            assert (_np(r.indices) == oracle.flat_index(feat, mask.shape)).all()
+    masks = (rng.random((4, 30, 70)) >= 0.02).astype(np.uint8)
+    masks[1] = 1
+    masks[3] = 0
+    t = torch.from_numpy(masks).to(dev)
+    for metric, fn in (("taxicab", oracle.taxicab_brute), ("chessboard", oracle.chessboard_brute)):
+        _say(f"brute {metric} batch with an image without background")
+        r = edt_brute(t, batched=True, metric=metric, return_indices=True)
+        torch.cuda.synchronize()
+        for b in range(4):
+            ref, who = fn(masks[b])
+            assert (_np(r.dist)[b] == ref).all() and (_np(r.indices)[b] == who).all()
+    with pytest.raises(ValueError):
+        edt_brute(t, (2.0, 1.0), batched=True, metric="taxicab")
+
+
 def test_randomized_sweep(torch_dev):
     """Seeded random cases across every entry point: shapes (ragged, tiny,
     lines of one), densities, dyadic spacings (exact in float64), images
@@ -578,6 +619,21 @@ def test_taxicab_full_size(torch_dev, name):
         pts = np.concatenate([rng.integers(0, per, ns // min(nb, 2)), [0, per - 1]])
         ref = oracle.taxicab_at(mask[k] if mask.ndim >= 3 else mask, pts)
         assert (dh[k][pts] == ref).all(), f"sampled distance mismatch in image {k}"
+    _brute_cross_check(torch, m, name, r.dist, "taxicab")
+
+
+def _brute_cross_check(torch, m, name, dist, metric):
+    """Every distance of a full-size chamfer output against the device brute
+    force (the definition, itself checked against the oracle's brute force on
+    small inputs) where it finishes in seconds: the 2-D workloads, not the
+    512^3 volume (1.3e8 elements x 1.7e7 background elements)."""
+    if m.dim() > 3:
+        return
+    from exact_euclidean_distance_amd import edt_brute
+    _say(f"{metric} full size {name}: device brute force over the whole output")
+    rb = edt_brute(m, metric=metric, batched=m.dim() == 3)
+    torch.cuda.synchronize()
+    assert torch.equal(rb.dist, dist), f"{metric} distance differs from the definition"
 
 
 def test_chessboard(torch_dev):
@@ -651,6 +707,7 @@ def test_chessboard_full_size(torch_dev, name):
         pts = np.concatenate([rng.integers(0, per, ns // min(nb, 2)), [0, per - 1]])
         ref = oracle.chessboard_at(mask[k] if mask.ndim >= 3 else mask, pts)
         assert (dh[k][pts] == ref).all(), f"sampled distance mismatch in image {k}"
+    _brute_cross_check(torch, m, name, r.dist, "chessboard")
 
 
 def _bucket_rows_2d(mask, bt=128, bc=16, lst=32):

@@ -33,11 +33,13 @@ def _say(msg):
     sys.stdout.flush()
 
 
-def run_gpu(torch_dev, mask, sampling=None, want=("sqdist", "dist", "indices"), offset=0):
+def run_gpu(torch_dev, mask, sampling=None, want=("sqdist", "dist", "indices"), offset=0, poison=0xFF):
     """Run the transform on ``mask`` (2-D, or 4-D batch of volumes); returns
-    numpy outputs.  ``offset`` > 0 places the mask at a misaligned address."""
+    numpy outputs.  ``offset`` > 0 places the mask at a misaligned address.
+    The workspace is filled with ``poison`` first (its contents on entry must
+    not matter)."""
     torch, dev = torch_dev
-    from exact_euclidean_distance_amd import edt2d, edt3d
+    from exact_euclidean_distance_amd import _lib, edt2d, edt3d
     flat = torch.from_numpy(np.ascontiguousarray(mask).reshape(-1))
     if offset:
         buf = torch.empty(flat.numel() + offset, dtype=torch.uint8, device=dev)
@@ -49,8 +51,11 @@ def run_gpu(torch_dev, mask, sampling=None, want=("sqdist", "dist", "indices"), 
     sq = torch.full(shape, -7, dtype=torch.int32, device=dev) if "sqdist" in want else None
     ds = torch.full(shape, float("nan"), dtype=torch.float32, device=dev) if "dist" in want else None
     ix = torch.full(shape, -7, dtype=torch.int32, device=dev) if "indices" in want else None
+    lib = _lib.load()
+    need = (lib.edt2d_workspace_size(*shape) if mask.ndim == 2 else lib.edt3d_workspace_size(*shape))
+    ws = torch.full((max(1, int(need)),), poison, dtype=torch.uint8, device=dev)
     fn = edt2d if mask.ndim == 2 else edt3d
-    fn(m, sampling, sqdist=sq, dist=ds, indices=ix, return_distances=ds is not None)
+    fn(m, sampling, sqdist=sq, dist=ds, indices=ix, return_distances=ds is not None, workspace=ws)
     torch.cuda.synchronize()
     out = {}
     for k, t in (("sqdist", sq), ("dist", ds), ("indices", ix)):
@@ -256,11 +261,16 @@ def test_background_runs(torch_dev):
         check(torch_dev, mask, samp)
 
 
-def test_repeat_is_bit_identical(torch_dev):
+@pytest.mark.parametrize("name", ["c1", "c3", "c5"])
+def test_repeat_is_bit_identical(torch_dev, name):
+    """Two calls on the same input, the workspace poisoned differently each
+    time, give the same bits (ties resolved the same way every time)."""
     from workloads import make_config
-    mask, _, _ = make_config("c1")
-    a = run_gpu(torch_dev, mask)
-    b = run_gpu(torch_dev, mask)
+    mask, sampling, _ = make_config(name)
+    want = ("sqdist", "dist", "indices") if sampling is None else ("dist", "indices")
+    _say(f"repeat {name}")
+    a = run_gpu(torch_dev, mask, sampling, want, poison=0xFF)
+    b = run_gpu(torch_dev, mask, sampling, want, poison=0x00)
     for k in a:
         np.testing.assert_array_equal(a[k], b[k])
 
