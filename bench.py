@@ -157,10 +157,12 @@ def _pmc_per_dispatch(run_dir: str, counter: str):
     return {k: float(np.mean(v)) for k, v in acc.items()}
 
 
-def summarize_traffic(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, config):
+def summarize_traffic(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, config, check=None):
     """Write profiles/traffic_<config>.json: per-kernel HBM bytes per dispatch
     from FETCH_SIZE / WRITE_SIZE (KiB), each scaled by the same counter's
-    reading for the copy probe divided by the bytes it is known to move."""
+    reading for the copy probe divided by the bytes it is known to move.
+    check: (fetch dir, write dir, bytes) of a second copy probe of another
+    size, whose scale factors are recorded beside the first ones."""
     fetch = _pmc_per_dispatch(fetch_dir, "FETCH_SIZE")
     write = _pmc_per_dispatch(write_dir, "WRITE_SIZE")
     cf = _pmc_per_dispatch(copy_fetch_dir, "FETCH_SIZE")
@@ -187,11 +189,73 @@ def summarize_traffic(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, conf
            "copy_probe_WRITE_SIZE_KiB": round(copy_write_kib, 1),
            "scale_fetch": round(f_fetch, 5), "scale_write": round(f_write, 5),
            "kernels": kernels}
+    if check:
+        nb = int(check[2])
+        out["copy_probe_check"] = {
+            "bytes_each_way": nb,
+            "scale_fetch": round(max(_pmc_per_dispatch(check[0], "FETCH_SIZE").values()) * 1024.0 / nb, 5),
+            "scale_write": round(max(_pmc_per_dispatch(check[1], "WRITE_SIZE").values()) * 1024.0 / nb, 5)}
     path = os.path.join(ROOT, "profiles", f"traffic_{config}.json")
     with open(path, "w") as fh:
         json.dump(out, fh, indent=1)
         fh.write("\n")
     print(json.dumps(out, indent=1))
+    return 0
+
+
+COUNTER_PASSES = (
+    "SQ_WAVES SQ_INSTS_VALU SQ_INSTS_SALU SQ_INSTS_LDS SQ_INSTS_VMEM_RD SQ_INSTS_VMEM_WR "
+    "SQ_INSTS_VALU_CVT SQ_INSTS_VALU_FMA_F64",
+    "SQ_ACTIVE_INST_LDS SQ_LDS_IDX_ACTIVE SQ_WAIT_INST_LDS SQ_WAIT_ANY SQ_WAVE_CYCLES "
+    "SQ_BUSY_CYCLES SQ_INSTS_VALU_MUL_F64 SQ_INSTS_VALU_INT32",
+    "VALUBusy VALUUtilization LDSBankConflict OccupancyPercent",
+    "MeanOccupancyPerCU",
+)
+
+
+def summarize_counters(dirs, config):
+    """Markdown table of rocprofv3 --pmc counters (one directory per pass of
+    COUNTER_PASSES), per envelope kernel, averaged over its dispatches, with
+    per-element figures (instructions per element are wave instructions x 64
+    lanes / elements of the dispatch)."""
+    from workloads import make_config
+    mask, _, _ = make_config(config)
+    n = int(np.prod(mask.shape))
+    acc = {}
+    for d in dirs:
+        files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        if not files:
+            raise FileNotFoundError(f"no counter_collection.csv under {d}")
+        for path in files:
+            with open(path) as fh:
+                for r in csv.DictReader(fh):
+                    key = _kernel_key(r["Kernel_Name"])
+                    if key is None:
+                        continue
+                    acc.setdefault(key, {}).setdefault(r["Counter_Name"], []).append(
+                        float(r["Counter_Value"]))
+    lines = [f"kernel | VALU/elem | SALU/elem | LDS/elem | VMEM rd+wr/elem | cvt/elem | "
+             f"f64 fma+mul/elem | int32/elem | VALUBusy % | VALUUtil % | LDSBankConflict % | "
+             f"LDS bank-conflict cycles / LDS active cycles | Occupancy % | MeanOccupancyPerCU (waves)"]
+    lines.append(" | ".join(["---"] * 14))
+    for key in ("axis0_summary", "axis0_scan", "axis0_resolve", "envelope_cols_3d",
+                "envelope_rows_3d", "envelope_rows_2d"):
+        c = acc.get(key)
+        if not c:
+            continue
+        m = {k: float(np.mean(v)) for k, v in c.items()}
+        g = lambda k: m.get(k, float("nan"))  # noqa: E731
+        per = lambda k: 64.0 * g(k) / n  # noqa: E731
+        conflict = g("SQ_LDS_BANK_CONFLICT")
+        lds_active = g("SQ_LDS_IDX_ACTIVE")
+        lines.append(" | ".join([
+            key, f"{per('SQ_INSTS_VALU'):.1f}", f"{per('SQ_INSTS_SALU'):.1f}", f"{per('SQ_INSTS_LDS'):.1f}",
+            f"{per('SQ_INSTS_VMEM_RD') + per('SQ_INSTS_VMEM_WR'):.2f}", f"{per('SQ_INSTS_VALU_CVT'):.1f}",
+            f"{per('SQ_INSTS_VALU_FMA_F64') + per('SQ_INSTS_VALU_MUL_F64'):.1f}",
+            f"{per('SQ_INSTS_VALU_INT32'):.1f}", f"{g('VALUBusy'):.1f}", f"{g('VALUUtilization'):.1f}",
+            f"{g('LDSBankConflict'):.2f}", f"{conflict / lds_active:.3f}" if lds_active == lds_active and lds_active else "n/a",
+            f"{g('OccupancyPercent'):.1f}", f"{g('MeanOccupancyPerCU'):.2f}"]))
+    print("\n".join(lines))
     return 0
 
 
@@ -208,12 +272,12 @@ def measured_traffic(config: str, kernel: str):
     return None if k is None else k.get("hbm_bytes")
 
 
-def probe_copy():
-    """A plain elementwise kernel of known size (reads and writes
-    COPY_PROBE_BYTES each) for calibrating FETCH_SIZE / WRITE_SIZE."""
+def probe_copy(nbytes: int = COPY_PROBE_BYTES):
+    """A plain elementwise kernel of known size (reads and writes nbytes
+    each) for calibrating FETCH_SIZE / WRITE_SIZE."""
     import torch
     dev = torch.device("cuda:0")
-    a = torch.ones(COPY_PROBE_BYTES // 4, dtype=torch.float32, device=dev)
+    a = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
     b = torch.empty_like(a)
     for _ in range(3):
         torch.neg(a, out=b)
@@ -402,11 +466,19 @@ def main(argv=None):
     ap.add_argument("--graph", action="store_true",
                     help="time replays of a HIP graph holding one transform (launch gaps removed)")
     ap.add_argument("--probe-copy", action="store_true")
+    ap.add_argument("--probe-bytes", type=int, default=COPY_PROBE_BYTES,
+                    help="bytes read (and written) by --probe-copy")
     ap.add_argument("--summarize-traffic", nargs=4, metavar="DIR")
+    ap.add_argument("--copy-check", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "BYTES"),
+                    help="with --summarize-traffic: a second copy probe of another size")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="DIR",
+                    help="rocprofv3 --pmc directories (the COUNTER_PASSES) -> markdown table")
     args = ap.parse_args(argv)
 
     if args.summarize_traffic:
-        return summarize_traffic(*args.summarize_traffic, args.config)
+        return summarize_traffic(*args.summarize_traffic, args.config, args.copy_check)
+    if args.summarize_counters:
+        return summarize_counters(args.summarize_counters, args.config)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: measures one GPU only (the transform of one workload runs "
@@ -414,7 +486,7 @@ def main(argv=None):
         return 2
 
     if args.probe_copy:
-        return probe_copy()
+        return probe_copy(args.probe_bytes)
 
     import torch
 

@@ -763,8 +763,10 @@ struct Geo2D {          // rows of B images of H x W; value = axis-0 coordinate
     static constexpr Val kNoneVal = kNone16;
     // Rows of an image follow the nearest background of one column each, so
     // their F varies freely along the row and many chunks see more reaching
-    // members than the per-chunk lists hold: whole lines in rounds are faster.
+    // members than the per-chunk lists hold: whole lines in rounds are faster
+    // (16384^2: 0.90 against 1.07 ms; 4096^2 disks: 0.21 against 0.46 ms).
     static constexpr bool kPerChunk = false;
+    static bool per_chunk(int) { return false; }
     double s2a, s2l;    // squared spacing of axis 0 and along the row
     int W;
     int H;              // rows per image: line ln is row ln % H of image ln / H
@@ -789,7 +791,11 @@ struct Geo2D {          // rows of B images of H x W; value = axis-0 coordinate
 };
 
 struct Geo3D {          // rows along W of B x D x H x W volumes; value = packed (axis0, axis1)
+    // Per-chunk resolution for rows longer than 128 (512^3: 0.66 ms against
+    // 0.71 ms in whole-line rounds); rows of 128 or fewer go faster in rounds
+    // (16 x 128^3: 0.288 against 0.310 ms).
     static constexpr bool kPerChunk = true;
+    static bool per_chunk(int L) { return L > 128; }
     using Val = uint32_t;
     static constexpr Val kNoneVal = kNone32;
     double s2a, s2b, s2l;
@@ -808,7 +814,9 @@ struct Geo3D {          // rows along W of B x D x H x W volumes; value = packed
         return s2a * t0 * t0 + s2b * t1 * t1;
     }
     __device__ int32_t index(const Line&, uint32_t v, int pos) const {
-        const unsigned dh = __umul24(v >> 16, (unsigned)H) + (v & 0xFFFFu);   // axis 0 < 2^16, H <= 1024
+        // both factors are below 2^24, and d * H + h < 2^31 whenever int32
+        // indices are asked for (D * H * W < 2^31)
+        const unsigned dh = __umul24(v >> 16, (unsigned)H) + (v & 0xFFFFu);
         return (int32_t)(dh24 ? __umul24(dh, (unsigned)W) : dh * (unsigned)W) + pos;
     }
     __device__ double virt_f(const Line& l) const {
@@ -862,7 +870,7 @@ __device__ inline void load_row_line(const Val* __restrict__ src, int L, int g, 
     }
 }
 
-template <class Geo, int K, int VW, class Ix = int32_t>
+template <class Geo, int K, int VW, class Ix = int32_t, bool PerChunk = Geo::kPerChunk>
 __global__ __launch_bounds__(1024) void k_envelope_rows(const typename Geo::Val* __restrict__ in,
                                                         int L, int64_t nlines, int Gp, int LPW,
                                                         Geo geo, int32_t* __restrict__ sqdist,
@@ -895,7 +903,7 @@ __global__ __launch_bounds__(1024) void k_envelope_rows(const typename Geo::Val*
     LineView<Val, K, decltype(fof), 1> view{sa.val, sa.mask, sa.occ + (size_t)r * ((Gp + 63) / 64),
                                             sa.own, slot0, geo.s2l, fof};
     uint16_t* mymarks = sa.mark + __umul24(tid, CM);
-    resolve_line<K, Geo::kPerChunk>(view, sa, sa.val + __umul24(tid, CS), mymarks, g, Gp, L, active, tid, r,
+    resolve_line<K, PerChunk>(view, sa, sa.val + __umul24(tid, CS), mymarks, g, Gp, L, active, tid, r,
                     [](Val v) { return Geo::valid(v); }, fof);
 
     // 5. outputs.  mk is owner + 1 of position q (0: the line has no
@@ -1288,18 +1296,18 @@ size_t rows_lds_bytes(int L, int value_bytes) {
     return p.lds;
 }
 
-template <class Geo, int K, int VW, class Ix>
+template <class Geo, int K, int VW, class Ix, bool PerChunk>
 static hipError_t launch_rows_t(const typename Geo::Val* in, int L, int64_t nlines, const RowPlan& p,
                                 const Geo& geo, int32_t* sqdist, float* dist, Ix* indices,
                                 hipStream_t s, KernelTimer* tm, const char* kname) {
     static unsigned long long lds_done = 0;
-    hipError_t le = large_lds_once((const void*)k_envelope_rows<Geo, K, VW, Ix>, &lds_done);
+    hipError_t le = large_lds_once((const void*)k_envelope_rows<Geo, K, VW, Ix, PerChunk>, &lds_done);
     if (le != hipSuccess) return le;
     const int64_t nblocks = (nlines + p.LPW - 1) / p.LPW;
     const bool aligned16 = (((uintptr_t)sqdist | (uintptr_t)dist | (uintptr_t)indices) & 15) == 0;
     const int vec_out = (L % 4 == 0 && aligned16) ? 1 : 0;
     EDT_LAUNCH(tm, kname, s,
-               hipLaunchKernelGGL((k_envelope_rows<Geo, K, VW, Ix>), dim3((unsigned)nblocks),
+               hipLaunchKernelGGL((k_envelope_rows<Geo, K, VW, Ix, PerChunk>), dim3((unsigned)nblocks),
                                   dim3(p.Gp * p.LPW), p.lds, s, in, L, nlines, p.Gp, p.LPW, geo,
                                   sqdist, dist, indices, vec_out));
     return hipSuccess;
@@ -1312,8 +1320,14 @@ static hipError_t launch_rows_any(const typename Geo::Val* in, int L, int64_t nl
     constexpr int VB = (int)sizeof(typename Geo::Val);
     constexpr int V16 = 16 / VB;
     const RowPlan p = plan_rows(L, VB);
-    if (p.VW == V16) return launch_rows_t<Geo, K, V16>(in, L, nlines, p, geo, sqdist, dist, indices, s, tm, kname);
-    return launch_rows_t<Geo, K, 1>(in, L, nlines, p, geo, sqdist, dist, indices, s, tm, kname);
+    if (Geo::kPerChunk && !Geo::per_chunk(L)) {   // (only Geo3D takes both)
+        if (p.VW == V16)
+            return launch_rows_t<Geo, K, V16, Ix, false>(in, L, nlines, p, geo, sqdist, dist, indices, s, tm, kname);
+        return launch_rows_t<Geo, K, 1, Ix, false>(in, L, nlines, p, geo, sqdist, dist, indices, s, tm, kname);
+    }
+    if (p.VW == V16)
+        return launch_rows_t<Geo, K, V16, Ix, Geo::kPerChunk>(in, L, nlines, p, geo, sqdist, dist, indices, s, tm, kname);
+    return launch_rows_t<Geo, K, 1, Ix, Geo::kPerChunk>(in, L, nlines, p, geo, sqdist, dist, indices, s, tm, kname);
 }
 
 hipError_t launch_rows_2d(const uint16_t* c0, int B, int H, int W, double s2_0, double s2_1,
