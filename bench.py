@@ -236,8 +236,9 @@ def summarize_counters(dirs, config):
                         float(r["Counter_Value"]))
     lines = [f"kernel | VALU/elem | SALU/elem | LDS/elem | VMEM rd+wr/elem | cvt/elem | "
              f"f64 fma+mul/elem | int32/elem | VALUBusy % | VALUUtil % | LDSBankConflict % | "
-             f"LDS bank-conflict cycles / LDS active cycles | Occupancy % | MeanOccupancyPerCU (waves)"]
-    lines.append(" | ".join(["---"] * 14))
+             f"LDS-issue wait / wave cycles | any wait / wave cycles | Occupancy % | "
+             f"MeanOccupancyPerCU (waves)"]
+    lines.append(" | ".join(["---"] * 15))
     for key in ("axis0_summary", "axis0_scan", "axis0_resolve", "envelope_cols_3d",
                 "envelope_rows_3d", "envelope_rows_2d"):
         c = acc.get(key)
@@ -246,14 +247,13 @@ def summarize_counters(dirs, config):
         m = {k: float(np.mean(v)) for k, v in c.items()}
         g = lambda k: m.get(k, float("nan"))  # noqa: E731
         per = lambda k: 64.0 * g(k) / n  # noqa: E731
-        conflict = g("SQ_LDS_BANK_CONFLICT")
-        lds_active = g("SQ_LDS_IDX_ACTIVE")
+        wc = g("SQ_WAVE_CYCLES")
         lines.append(" | ".join([
             key, f"{per('SQ_INSTS_VALU'):.1f}", f"{per('SQ_INSTS_SALU'):.1f}", f"{per('SQ_INSTS_LDS'):.1f}",
             f"{per('SQ_INSTS_VMEM_RD') + per('SQ_INSTS_VMEM_WR'):.2f}", f"{per('SQ_INSTS_VALU_CVT'):.1f}",
             f"{per('SQ_INSTS_VALU_FMA_F64') + per('SQ_INSTS_VALU_MUL_F64'):.1f}",
             f"{per('SQ_INSTS_VALU_INT32'):.1f}", f"{g('VALUBusy'):.1f}", f"{g('VALUUtilization'):.1f}",
-            f"{g('LDSBankConflict'):.2f}", f"{conflict / lds_active:.3f}" if lds_active == lds_active and lds_active else "n/a",
+            f"{g('LDSBankConflict'):.2f}", f"{g('SQ_WAIT_INST_LDS') / wc:.3f}", f"{g('SQ_WAIT_ANY') / wc:.3f}",
             f"{g('OccupancyPercent'):.1f}", f"{g('MeanOccupancyPerCU'):.2f}"]))
     print("\n".join(lines))
     return 0
