@@ -343,10 +343,18 @@ def cpu_baseline(name, mask, sampling, budget_s=15.0):
 FP64_PEAK_TFLOPS = 78.6   # MI355X vector fp64
 
 
+# 32-bit integer VALU operations per second: 256 CUs x 4 SIMDs x 16 lanes x
+# 2.4 GHz (a wave64 instruction takes four cycles on a 16-lane SIMD)
+INT32_VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
+
+
 def bench_brute(args):
     """Time the device brute force (every element against every background
-    element of its image) on a workload; ALU-bound: 3 fp64 flops per axis and
-    (element, background element) pair, against the fp64 vector peak."""
+    element of its image) on a workload; ALU-bound.  At unit spacing the
+    integer kernel runs: per pair 2 integer operations per axis (|difference|,
+    multiply-add) and 3 for the running minimum (compare, two selects),
+    against the int32 VALU peak; otherwise 3 fp64 flops per axis and pair,
+    against the fp64 vector peak."""
     import torch
     from exact_euclidean_distance_amd import edt_brute
     from workloads import make_config
@@ -373,17 +381,24 @@ def bench_brute(args):
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / max(1, args.steps)
-    tflops = pairs * 3 * ndim / (ms * 1e-3) / 1e12
+    integer = sampling is None or all(float(x) == 1.0 for x in sampling)
+    if integer:
+        rate = pairs * (2 * ndim + 3) / (ms * 1e-3) / 1e12
+        roof = {"bound": "alu", "achieved": round(rate, 3), "peak": round(INT32_VALU_PEAK_TOPS, 2),
+                "unit": "TOP/s (int32 VALU)", "frac": round(rate / INT32_VALU_PEAK_TOPS, 4), "traffic": None}
+    else:
+        rate = pairs * 3 * ndim / (ms * 1e-3) / 1e12
+        roof = {"bound": "alu", "achieved": round(rate, 3), "peak": FP64_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(rate / FP64_PEAK_TFLOPS, 4), "traffic": None}
     line = {
         "metric": METRIC + " (device brute-force check, not the transform's path)",
         "value": round(mask_np.size / (ms * 1e-3) / 1e9, 4), "unit": "Gpixel/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f64",
-        "data": "synthetic",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "int32" if integer else "f64", "data": "synthetic",
         "config": {"workload": f"{name}: {WORKLOADS[name]}", "shape": list(mask_np.shape),
                    "path": "brute force", "pairs": pairs},
-        "roofline": {"bound": "alu", "achieved": round(tflops, 3), "peak": FP64_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(tflops / FP64_PEAK_TFLOPS, 4), "traffic": None},
+        "roofline": roof,
         "Gpairs_per_s": round(pairs / (ms * 1e-3) / 1e9, 2),
         "cpu_baseline": None,
     }

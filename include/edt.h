@@ -246,7 +246,9 @@ edt_status edt3d_taxicab_u8_batched(const uint8_t* mask, int32_t B, int32_t D, i
    max(p0 + 1, p1, ...)), buffers, workspace, limits and errors exactly as for
    the taxicab entry points above.  The work per element grows with its own
    distance (each element searches outward along each axis), except on lines
-   with at most 32 sources, which are scanned as a list. */
+   with at most 32 sources, which are scanned as a list, and on lines of 2048
+   or more, where each element first scans per-bucket lists of the nearby
+   sources with small axis-0 distance. */
 edt_status edt2d_chessboard_u8_batched(const uint8_t* mask, int32_t B, int32_t H, int32_t W,
                                        int32_t* dist, int32_t* indices,
                                        void* workspace, size_t workspace_bytes, hipStream_t stream);
