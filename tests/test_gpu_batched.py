@@ -733,44 +733,56 @@ def _bucket_rows_2d(mask, bt=128, bc=16, lst=32):
 
 
 def test_chessboard_bucket_lists(torch_dev):
-    """The chessboard row pass on rows of 2048 and more: rows that take the
+    """The chessboard row pass on rows longer than 4096 (the outward-search
+    kernel; shorter rows take the range-minimum kernel): rows that take the
     per-bucket lists of sources with g <= 128 (many sources, most of them far
     along axis 0), including a bucket with more than 16 such sources (the
     outward search takes over there) and positions whose best in-bucket value
-    exceeds 128 (likewise), against the definition over the whole output."""
+    exceeds 128 (likewise).  The whole output is compared with the device
+    brute force (itself checked against the oracle's), and sampled positions
+    of the bucketed rows with the oracle's definition."""
     torch, dev = torch_dev
-    from exact_euclidean_distance_amd import chessboard
+    from exact_euclidean_distance_amd import chessboard, edt_brute
     rng = np.random.default_rng([42, 5016])
-    for W in (2048, 2300):   # (2300: a ragged last bucket)
-        m = np.ones((260, W), np.uint8)
+    for W in (4160, 4397):   # (4397: a ragged last bucket)
+        m = np.ones((200, W), np.uint8)
         far = rng.random(W) < 0.4
         m[0, far] = 0                               # sources at g = r on every row
-        pts = rng.integers(0, [260, W], size=(W // 80, 2))
+        pts = rng.integers(0, [200, W], size=(W // 160, 2))
         m[pts[:, 0], pts[:, 1]] = 0                 # a few near sources (g <= 128)
         m[150, 520:540] = 0                         # 20 near sources in one bucket: a full bucket
         bucketed, full = _bucket_rows_2d(m)
         assert bucketed.sum() > 50 and full.any(), "the mask must drive the bucket lists"
-        _say(f"chessboard bucket lists 260 x {W}: {bucketed.sum()} bucketed rows, "
+        _say(f"chessboard bucket lists 200 x {W}: {bucketed.sum()} bucketed rows, "
              f"{full.sum()} with a full bucket")
-        r = chessboard(torch.from_numpy(m).to(dev), return_indices=True)
+        t = torch.from_numpy(m).to(dev)
+        r = chessboard(t, return_indices=True)
+        ref = edt_brute(t, metric="chessboard").dist
         torch.cuda.synchronize()
-        ref, _ = oracle.chessboard_brute(m)
+        assert torch.equal(r.dist, ref), "chessboard distance mismatch"
         d = r.dist.cpu().numpy()
         ix = r.indices.cpu().numpy()
-        assert (d == ref).all(), "chessboard distance mismatch on bucketed rows"
-        assert (oracle.chessboard_to(ix, m.shape) == ref).all()
+        assert (oracle.chessboard_to(ix, m.shape) == d).all()
         assert (m.reshape(-1)[ix.reshape(-1)] == 0).all()
+        rows = np.flatnonzero(bucketed)
+        sel = rng.choice(rows, 8, replace=False)
+        pts = (sel[:, None] * W + rng.integers(0, W, (8, 40))).reshape(-1)
+        pts = np.concatenate([pts, [150 * W + 530, 150 * W + 525]])   # the full bucket
+        assert (d.reshape(-1)[pts] == oracle.chessboard_at(m, pts)).all(), "sampled oracle mismatch"
         # positions whose best value exceeds 128: the fallback search decides there
-        assert (ref[bucketed] > 128).any()
-    # rows of 2048 in a volume: g comes from the middle-axis pass
-    v = np.ones((1, 2, 180, 2048), np.uint8)
-    v[0, 0, 0, rng.random(2048) < 0.4] = 0
-    pts = rng.integers(0, [2, 180, 2048], size=(30, 3))
+        assert (d[bucketed] > 128).any()
+    # rows of 4160 in a volume: g comes from the middle-axis pass
+    v = np.ones((1, 2, 200, 4160), np.uint8)
+    v[0, 0, 0, rng.random(4160) < 0.4] = 0
+    pts = rng.integers(0, [2, 200, 4160], size=(30, 3))
     v[0, pts[:, 0], pts[:, 1], pts[:, 2]] = 0
     v[0, 1, 150, 700:720] = 0
-    _say("chessboard bucket lists 1 x 2 x 180 x 2048")
-    r = chessboard(torch.from_numpy(v).to(dev), return_indices=True)
+    _say("chessboard bucket lists 1 x 2 x 200 x 4160")
+    t = torch.from_numpy(v).to(dev)
+    r = chessboard(t, return_indices=True)
+    ref = edt_brute(t, metric="chessboard", batched=True).dist
     torch.cuda.synchronize()
-    ref, _ = oracle.chessboard_brute(v[0])
-    assert (r.dist.cpu().numpy()[0] == ref).all(), "chessboard distance mismatch (volume rows)"
-    assert (oracle.chessboard_to(r.indices.cpu().numpy()[0], v.shape[1:]) == ref).all()
+    assert torch.equal(r.dist, ref), "chessboard distance mismatch (volume rows)"
+    assert (oracle.chessboard_to(r.indices.cpu().numpy()[0], v.shape[1:]) == r.dist.cpu().numpy()[0]).all()
+    pts = rng.integers(0, v[0].size, 200)
+    assert (r.dist.cpu().numpy()[0].reshape(-1)[pts] == oracle.chessboard_at(v[0], pts)).all()
