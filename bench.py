@@ -65,6 +65,10 @@ WORKLOADS = {
     "b2d": "batched 2D: 32 images of 1024x1024 uint8, background i.i.d. Bernoulli(0.01) "
            "per image, isotropic; outputs sqdist + dist + index (flat per image)",
 }
+WORKLOADS["nd4"] = ("4D 80^4 uint8 (any-rank path), background i.i.d. Bernoulli(1e-3), "
+                    "sampling (2.5,1,1,1); outputs float32 dist + int32 index")
+WORKLOADS["w40k"] = ("2D 256x40000 uint8 (rows past the LDS kernels, any-rank path), background "
+                     "i.i.d. Bernoulli(1e-3), isotropic; outputs sqdist + dist + int32 index")
 WORKLOADS["v2048"] = ("3D 64x2048x2048 uint8 (a stack of 2048^2 slices), background i.i.d. "
                       "Bernoulli(1e-3), isotropic; output float32 dist")
 for _n in (1024, 2048, 4096, 8192):
@@ -83,6 +87,9 @@ OUTPUTS = {
 }
 OUTPUTS.update({k: ("dist",) for k in WORKLOADS if k.startswith("p1_")})
 OUTPUTS["v2048"] = ("dist",)
+OUTPUTS["nd4"] = ("dist", "indices")
+OUTPUTS["w40k"] = ("sqdist", "dist", "indices")
+ND_CONFIGS = ("nd4", "w40k")   # timed through edt_nd_u8 (the workspace path)
 
 
 def algorithmic_bytes(kernel: str, shape, n_out: int) -> int:
@@ -406,6 +413,98 @@ def bench_brute(args):
     return 0
 
 
+def bench_nd(args):
+    """Time the any-rank entry point (edt_nd_u8, Python ``edt``) on a shape
+    that takes its workspace path.  Bytes: model A (mask in, outputs out) and
+    the path's own model (per spatial axis the float64 distance and int64
+    feature read and written once, 32 bytes per element, plus the mask and
+    the outputs)."""
+    import torch
+    from exact_euclidean_distance_amd import alloc_workspace, edt
+    from exact_euclidean_distance_amd import _lib
+    from workloads import make_config
+    name = args.config
+    mask_np, sampling, _ = make_config(name)
+    dev = torch.device("cuda:0")
+    mask = torch.from_numpy(mask_np).to(dev)
+    shape = tuple(mask.shape)
+    n = int(np.prod(shape))
+    want = OUTPUTS[name]
+    idx_dt = torch.int32
+    sq = torch.empty(shape, dtype=torch.int32, device=dev) if "sqdist" in want else None
+    ds = torch.empty(shape, dtype=torch.float32, device=dev) if "dist" in want else None
+    ix = torch.empty(shape, dtype=idx_dt, device=dev) if "indices" in want else None
+    import ctypes
+    shp = (ctypes.c_int64 * len(shape))(*shape)
+    strd = (ctypes.c_int64 * len(shape))(*mask.stride())
+    ib = 8 if idx_dt == torch.int64 else 4
+    ws = alloc_workspace(int(_lib.load().edt_nd_workspace_size(0, len(shape), shp, strd, ib)), dev)
+
+    def step():
+        edt(mask, sampling, sqdist=sq, dist=ds, indices=ix, return_distances=ds is not None,
+            index_dtype=idx_dt, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    stream = torch.cuda.current_stream()
+    ev[0].record(stream)
+    for i in range(args.steps):
+        step()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per_step = [ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]
+    ms = ev[0].elapsed_time(ev[-1]) / max(1, args.steps)
+    out_bytes = sum(4 if k != "indices" else ib for k in want)
+    model_a = n * (1 + out_bytes)
+    model_path = n * (1 + 32 * len(shape) + out_bytes)
+    if args.check:
+        import oracle
+        sys.path.insert(0, os.path.join(ROOT, "tests"))
+        from gpu_check import compare
+        print(f"[bench] {name}: parity check against the oracle", file=sys.stderr, flush=True)
+        ref, _ = oracle.edt(mask_np, sampling, features=False)
+        compare(mask_np, sampling, ref, None if sq is None else sq.cpu().numpy(),
+                None if ds is None else ds.cpu().numpy(),
+                None if ix is None else ix.cpu().numpy())
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        # the oracle on leading slabs of the array (each its own image)
+        take = 1
+        while True:
+            sample = np.ascontiguousarray(mask_np[:take])
+            if not (sample == 0).any():
+                sample.reshape(-1)[0] = 0
+            t0 = time.perf_counter()
+            oracle.edt(sample, sampling, features="indices" in want)
+            dt = time.perf_counter() - t0
+            if dt > 10.0 or take >= shape[0]:
+                break
+            take = min(shape[0], take * 2)
+        cpu = {"value": sample.size / dt / 1e9, "unit": "Gpixel/s", "cores": 1, "kind": "oracle",
+               "sample": f"oracle on the leading {take} of {shape[0]} slabs along axis 0 (as its own array)",
+               "seconds": round(dt, 2), "cpu": host_info()["cpu_model"], "host_cpus": host_info()["usable_cpus"]}
+    line = {
+        "metric": METRIC + " (any-rank path)", "value": round(n / (ms * 1e-3) / 1e9, 3), "unit": "Gpixel/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f64", "data": "synthetic",
+        "config": {"workload": f"{name}: {WORKLOADS[name]}", "shape": list(shape),
+                   "sampling": list(sampling) if sampling else None, "outputs": list(want), "path": "edt_nd_u8"},
+        "gpu_ms": {"mean": round(ms, 4), "median": round(float(np.median(per_step)), 4),
+                   "min": round(float(np.min(per_step)), 4)},
+        "roofline": {"bound": "hbm", "kernel": "whole path", "achieved": round(model_path / (ms * 1e-3) / 1e9, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(model_path / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "traffic": None},
+        "path": {"model_A_bytes": model_a, "model_A_GBps": round(model_a / (ms * 1e-3) / 1e9, 1),
+                 "path_model_bytes": model_path},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def bench_chamfer(args, metric):
     """Time a chamfer transform, city-block ("taxicab") or chessboard (int32
     distances, plus indices when the workload times them), on a 2-D, batched
@@ -507,6 +606,8 @@ def main(argv=None):
 
     if args.brute:
         return bench_brute(args)
+    if args.config in ND_CONFIGS:
+        return bench_nd(args)
     if args.taxicab:
         return bench_chamfer(args, "taxicab")
     if args.chessboard:

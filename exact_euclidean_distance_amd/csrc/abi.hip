@@ -546,16 +546,23 @@ constexpr int kMaxSpatial = 8;
 constexpr int kMaxBatchAxes = 8;
 
 // How edt_nd_u8 runs a shape: the LDS kernels for C-contiguous 1-, 2- and 3-D
-// images within their limits, the workspace path of nd.hip otherwise.
-enum class NdRoute { kEmpty, k1D, k2D, k3D, kGeneric };
+// images within their limits; otherwise, for 1-, 2- and 3-D images whose
+// spatial axes in some order fit those kernels, a reordered run (the mask
+// gathered into the workspace in that order, the outputs put back); the
+// workspace path of nd.hip for the rest.
+enum class NdRoute { kEmpty, k1D, k2D, k3D, kPermuted, kGeneric };
 
 struct NdPlan {
     NdRoute route = NdRoute::kGeneric;
     edt::NdDesc d{};
     int64_t total = 0;          // elements over all images
     int64_t mask_span = 0;      // bytes from the mask pointer to its last element + 1
-    int32_t fB = 0, fD = 0, fH = 0, fW = 0;   // the fast path's shape
+    int32_t fB = 0, fD = 0, fH = 0, fW = 0;   // the fast path's shape (permuted order for kPermuted)
+    int perm[3] = {0, 1, 2};    // kPermuted: permuted axis k is spatial axis perm[k]
     size_t ws = 0;
+    // kPermuted workspace: gathered mask, permuted int32 index / sqdist /
+    // dist, then the LDS kernels' own workspace
+    size_t off_idx = 0, off_sq = 0, off_dist = 0, off_inner = 0;
 };
 
 // Shape checks and routing (no buffer is looked at).  idx_bytes: 4 or 8.
@@ -629,6 +636,46 @@ edt_status plan_nd(int32_t nbatch, int32_t ndim, const int64_t* shape, const int
             P.ws = layout3d(b32, P.fD, P.fH, P.fW).total;
         }
     }
+    // a reordered run: the first order of the spatial axes (identity first)
+    // whose shape the LDS kernels take; int32 indices inside
+    if (P.route == NdRoute::kGeneric && ndim <= 3 && B <= kMaxExtent && N <= INT32_MAX) {
+        static const int kPerms2[2][3] = {{0, 1, 2}, {1, 0, 2}};
+        static const int kPerms3[6][3] = {{0, 1, 2}, {0, 2, 1}, {1, 0, 2}, {1, 2, 0}, {2, 0, 1}, {2, 1, 0}};
+        const int np = ndim == 1 ? 1 : ndim == 2 ? 2 : 6;
+        bool fitsall = true;
+        for (int k = 0; k < ndim; ++k) fitsall = fitsall && shape[nbatch + k] >= 1 && shape[nbatch + k] <= kMaxExtent;
+        const int32_t b32 = (int32_t)B;
+        for (int pi = 0; fitsall && pi < np && P.route == NdRoute::kGeneric; ++pi) {
+            const int* pm = ndim == 3 ? kPerms3[pi] : kPerms2[pi];
+            int32_t e[3] = {1, 1, 1};
+            for (int k = 0; k < ndim; ++k) e[k] = (int32_t)shape[nbatch + pm[k]];
+            size_t inner = 0;
+            bool ok = false;
+            if (ndim == 1) {
+                ok = shape2d_ok(b32, e[0], 1);
+                if (ok) inner = layout2d(b32, e[0], 1).total;
+            } else if (ndim == 2) {
+                ok = shape2d_ok(b32, e[0], e[1]);
+                if (ok) inner = layout2d(b32, e[0], e[1]).total;
+            } else {
+                ok = shape3d_ok(b32, e[0], e[1], e[2]);
+                if (ok) inner = layout3d(b32, e[0], e[1], e[2]).total;
+            }
+            if (!ok) continue;
+            P.route = NdRoute::kPermuted;
+            for (int k = 0; k < 3; ++k) P.perm[k] = k < ndim ? pm[k] : k;
+            P.fB = b32;
+            P.fD = e[0];
+            P.fH = e[1];
+            P.fW = e[2];
+            const size_t n = (size_t)P.total;
+            P.off_idx = round_up(n);
+            P.off_sq = P.off_idx + round_up(n * 4);
+            P.off_dist = P.off_sq + round_up(n * 4);
+            P.off_inner = P.off_dist + round_up(n * 4);
+            P.ws = P.off_inner + inner;
+        }
+    }
     if (P.route == NdRoute::kGeneric) P.ws = edt::nd_workspace_bytes(P.total);
     *out = P;
     return EDT_OK;
@@ -696,6 +743,34 @@ edt_status edt_nd_u8(const uint8_t* mask, int32_t nbatch, int32_t ndim, const in
                              workspace_bytes, stream, nullptr, static_cast<int64_t*>(indices));
             return run3d(mask, P.fB, P.fD, P.fH, P.fW, samp, sqdist, dist, static_cast<int32_t*>(indices),
                          workspace, workspace_bytes, stream, nullptr);
+        case NdRoute::kPermuted: {
+            char* base = static_cast<char*>(workspace);
+            uint8_t* pm = reinterpret_cast<uint8_t*>(base);
+            int32_t* pidx = reinterpret_cast<int32_t*>(base + P.off_idx);
+            int32_t* psq = sqdist ? reinterpret_cast<int32_t*>(base + P.off_sq) : nullptr;
+            float* pdist = dist ? reinterpret_cast<float*>(base + P.off_dist) : nullptr;
+            void* inner = base + P.off_inner;
+            const size_t inner_bytes = workspace_bytes - P.off_inner;
+            for (int k = 0; k < ndim; ++k) P.d.s2[k] = s2[k];
+            if (edt::launch_nd_gather(mask, P.d, P.perm, pm, stream) != hipSuccess) return EDT_ERR_HIP;
+            float ps[3] = {1.0f, 1.0f, 1.0f};
+            for (int k = 0; k < ndim; ++k) ps[k] = samp[P.perm[k]];
+            edt_status rs;
+            if (ndim == 1) {
+                const float s1[2] = {ps[0], 1.0f};
+                rs = run2d(pm, P.fB, P.fD, 1, s1, psq, pdist, pidx, inner, inner_bytes, stream, nullptr);
+            } else if (ndim == 2) {
+                rs = run2d(pm, P.fB, P.fD, P.fH, ps, psq, pdist, pidx, inner, inner_bytes, stream, nullptr);
+            } else {
+                rs = run3d(pm, P.fB, P.fD, P.fH, P.fW, ps, psq, pdist, pidx, inner, inner_bytes, stream,
+                           nullptr);
+            }
+            if (rs != EDT_OK) return rs;
+            if (edt::launch_nd_unpermute(P.d, P.perm, pidx, psq, pdist, sqdist, dist, indices, ib, stream) !=
+                hipSuccess)
+                return EDT_ERR_HIP;
+            return EDT_OK;
+        }
         default:
             break;
     }

@@ -115,6 +115,15 @@ struct NdDesc {
 size_t nd_workspace_bytes(int64_t total);
 hipError_t launch_nd(const uint8_t* mask, const NdDesc& d, void* ws, int32_t* sqdist, float* dist,
                      void* indices, int idx_bytes, hipStream_t s);
+// Reordered runs (nd.hip): gather the mask of d (1..3 spatial axes) into a
+// contiguous [B][permuted image] buffer (permuted axis k = original axis
+// perm[k]); put the permuted run's outputs back in the original order
+// (pidx: its int32 indices, always; psq / pdist when sqdist / dist are asked
+// for; images without background get the original frame's virtual element).
+hipError_t launch_nd_gather(const uint8_t* mask, const NdDesc& d, const int* perm, uint8_t* dst, hipStream_t s);
+hipError_t launch_nd_unpermute(const NdDesc& d, const int* perm, const int32_t* pidx, const int32_t* psq,
+                               const float* pdist, int32_t* sqdist, float* dist, void* indices, int idx_bytes,
+                               hipStream_t s);
 // Flat per-image indices (int32 or int64) of `images` images of shape
 // ext[0..nd) -> per-axis coordinates of the same type, coords[b][k][i].
 hipError_t launch_unravel_nd(const void* flat, int idx_bytes, int64_t images, int nd,

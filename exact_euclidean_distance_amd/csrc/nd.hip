@@ -258,6 +258,125 @@ hipError_t launch_unravel_nd(const void* flat, int idx_bytes, int64_t images, in
 
 // workspace: F (2 x float64) and features (2 x int64) per element for the
 // ping-pong between passes, and the members' positions (int64) per element
+// ---------------------------------------------------------------------------
+// Reordered runs of the LDS kernels.  The transform is separable, so its
+// result does not depend on the order in which the axes are taken: a 1-, 2- or
+// 3-D image the LDS kernels refuse as laid out (a strided mask, rows too long
+// for them) is gathered into a contiguous buffer with its spatial axes in
+// another order (perm: permuted axis k is original axis perm[k]), transformed
+// there with the spacings reordered alike, and the outputs are put back in
+// the original order.  An image without background used the virtual element
+// (-1, 0, ...) of the permuted axis 0, so its outputs are recomputed in the
+// original frame (the virtual element on the original axis 0).
+// ---------------------------------------------------------------------------
+
+namespace {
+
+struct PermDesc {
+    int nd;
+    int perm[3];
+    int64_t pext[3];   // extents in permuted order
+};
+
+// original coordinates of the element with flat index r of one image (row-major)
+__device__ __forceinline__ void unravel3(const NdDesc& d, int64_t r, int64_t oc[3]) {
+    for (int a = d.nd - 1; a >= 0; --a) {
+        const int64_t n = d.ext[d.nb + a];
+        oc[a] = r % n;
+        r /= n;
+    }
+}
+
+}  // namespace
+
+// dst[b][permuted image] = mask at the original coordinates; one thread per element
+__global__ __launch_bounds__(256) void k_nd_gather(const uint8_t* __restrict__ mask, NdDesc d, PermDesc pd,
+                                                   uint8_t* __restrict__ dst) {
+    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (e >= d.B * d.N) return;
+    const int64_t b = e / d.N;
+    int64_t r = e - b * d.N;
+    int64_t oc[3] = {0, 0, 0};
+    for (int k = pd.nd - 1; k >= 0; --k) {   // permuted coordinates -> original axes
+        oc[pd.perm[k]] = r % pd.pext[k];
+        r /= pd.pext[k];
+    }
+    int64_t off = 0, bb = b;
+    for (int a = d.nb - 1; a >= 0; --a) {
+        off += (bb % d.ext[a]) * d.mstride[a];
+        bb /= d.ext[a];
+    }
+    for (int a = 0; a < pd.nd; ++a) off += oc[a] * d.mstride[d.nb + a];
+    dst[e] = mask[off];
+}
+
+// Outputs in the original order from the permuted run's int32 index (always)
+// and sqdist / dist (when asked for); one thread per output element.
+__global__ __launch_bounds__(256) void k_nd_unpermute(NdDesc d, PermDesc pd, const int32_t* __restrict__ pidx,
+                                                      const int32_t* __restrict__ psq,
+                                                      const float* __restrict__ pdist,
+                                                      int32_t* __restrict__ sqdist, float* __restrict__ dist,
+                                                      void* __restrict__ indices, int idx_bytes) {
+    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (e >= d.B * d.N) return;
+    const int64_t b = e / d.N, r = e - b * d.N;
+    int64_t oc[3] = {0, 0, 0};
+    unravel3(d, r, oc);
+    int64_t pr = 0;   // flat index of the same element in the permuted image
+    for (int k = 0; k < pd.nd; ++k) pr = pr * pd.pext[k] + oc[pd.perm[k]];
+    const int64_t pe = b * d.N + pr;
+    const int32_t pi = pidx[pe];
+    if (pi < 0) {   // no background in the image: the virtual element of the original axis 0
+        double f;
+        int64_t ft;
+        virtual_at(d, r, &f, &ft);
+        write_out(e, f, ft, sqdist, dist, indices, idx_bytes);
+        return;
+    }
+    if (sqdist) sqdist[e] = psq[pe];
+    if (dist) dist[e] = pdist[pe];
+    if (indices) {
+        int64_t q = pi, pc[3] = {0, 0, 0};
+        for (int k = pd.nd - 1; k >= 0; --k) {
+            pc[k] = q % pd.pext[k];
+            q /= pd.pext[k];
+        }
+        int64_t oo[3] = {0, 0, 0};
+        for (int k = 0; k < pd.nd; ++k) oo[pd.perm[k]] = pc[k];
+        int64_t flat = 0;
+        for (int a = 0; a < pd.nd; ++a) flat = flat * d.ext[d.nb + a] + oo[a];
+        if (idx_bytes == 8) reinterpret_cast<int64_t*>(indices)[e] = flat;
+        else reinterpret_cast<int32_t*>(indices)[e] = (int32_t)flat;
+    }
+}
+
+hipError_t launch_nd_gather(const uint8_t* mask, const NdDesc& d, const int* perm, uint8_t* dst, hipStream_t s) {
+    PermDesc pd{};
+    pd.nd = d.nd;
+    for (int k = 0; k < d.nd; ++k) {
+        pd.perm[k] = perm[k];
+        pd.pext[k] = d.ext[d.nb + perm[k]];
+    }
+    const int64_t total = d.B * d.N;
+    hipLaunchKernelGGL(k_nd_gather, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, mask, d, pd, dst);
+    return hipGetLastError();
+}
+
+hipError_t launch_nd_unpermute(const NdDesc& d, const int* perm, const int32_t* pidx, const int32_t* psq,
+                               const float* pdist, int32_t* sqdist, float* dist, void* indices, int idx_bytes,
+                               hipStream_t s) {
+    PermDesc pd{};
+    pd.nd = d.nd;
+    for (int k = 0; k < d.nd; ++k) {
+        pd.perm[k] = perm[k];
+        pd.pext[k] = d.ext[d.nb + perm[k]];
+    }
+    const int64_t total = d.B * d.N;
+    hipLaunchKernelGGL(k_nd_unpermute, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, d, pd, pidx, psq,
+                       pdist, sqdist, dist, indices, idx_bytes);
+    return hipGetLastError();
+}
+
 size_t nd_workspace_bytes(int64_t total) {
     auto al = [](size_t x) { return (x + 255) & ~size_t(255); };
     return 2 * al((size_t)total * 8) + 2 * al((size_t)total * 8) + al((size_t)total * 8);

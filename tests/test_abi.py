@@ -306,12 +306,21 @@ def test_nd_workspace_sizes(lib):
     assert ws((512, 512)) == lib.edt2d_workspace_size(512, 512)
     assert ws((16, 128, 128, 128), nb=1) == lib.edt3d_workspace_size(16, 128, 128, 128)
     assert ws((3, 5, 7, 9), nb=2) == lib.edt2d_batched_workspace_size(15, 7, 9)
-    # rank 4, long rows, big extents, strided masks, int64 2-D indices: 40 bytes per element
-    for shape, kw in (((4, 5, 6, 7), {}), ((40, 40000), {}), ((70000, 3), {}),
-                      ((64, 64), {"strides": (128, 1)}), ((64, 64), {"ib": 8}),
-                      ((2, 3, 20000), {})):
+    # rank 4 and extents over 65535 take the workspace path: 40 bytes per element
+    for shape, kw in (((4, 5, 6, 7), {}), ((70000, 3), {})):
         n = int(np.prod(shape))
         assert ws(shape, **kw) >= 40 * n, (shape, kw)
+    # strided masks, int64 2-D indices and rows past the LDS kernels take a
+    # reordered run: the gathered mask, the permuted int32 index, sqdist and
+    # dist (13 bytes per element, each part rounded to 256 bytes), then the
+    # LDS kernels' workspace for the shape in the order they take it
+    rup = lambda x: (x + 255) // 256 * 256   # noqa: E731
+    for shape, kw, inner in (((64, 64), {"strides": (128, 1)}, lib.edt2d_workspace_size(64, 64)),
+                             ((64, 64), {"ib": 8}, lib.edt2d_workspace_size(64, 64)),
+                             ((40, 40000), {}, lib.edt2d_workspace_size(40000, 40)),
+                             ((2, 3, 20000), {}, lib.edt3d_workspace_size(1, 2, 20000, 3))):
+        n = int(np.prod(shape))
+        assert ws(shape, **kw) == rup(n) + 3 * rup(4 * n) + inner, (shape, kw)
     assert ws((4, 5), nb=-1) == 0
     assert ws((4,) * 9) == 0
     assert ws((4, 5), ib=3) == lib.edt_nd_workspace_size(0, 2, _i64((4, 5)), None, 4)

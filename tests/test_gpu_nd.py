@@ -182,3 +182,39 @@ def test_unravel_nd(env):
             assert (c[:, k] == ref).all()
         assert (c[:, 0] == f).all()
         assert (c[0, :, 0, 0, 0, 0, 0] == np.array([-1, 0, 0, 0, 0])).all()
+
+
+def test_reordered_runs(env):
+    """Shapes whose axes are reordered for the LDS kernels (rows past their
+    limits, strided masks, int64 indices of 2-D images), with images without
+    background among them: the virtual element stays (-1, 0, ...) of the
+    original axis 0."""
+    torch, dev = env
+    rng = np.random.default_rng([42, 9106])
+    cases = [((3, 60, 40000), 1, None), ((2, 3, 5, 20000), 1, (2.5, 1.0, 0.5)),
+             ((2, 20000, 5, 3), 1, None), ((4, 70, 33000), 1, (1.0, 2.5))]
+    for shape, nb, samp in cases:
+        m = (rng.random(shape) >= 0.002).astype(np.uint8)
+        m[1] = 1                                   # an image without background
+        m.reshape(shape[0], -1)[0, -1] = 0
+        _say(f"reordered run {shape} batch_dims={nb} sampling={samp}")
+        want = ("sqdist", "dist", "indices") if samp is None else ("dist", "indices")
+        mt = torch.from_numpy(m).to(dev)
+        out = run_nd(env, mt, samp, batch_dims=nb, want=want)
+        check_images(m, out, samp, nb)
+        img = shape[nb:]
+        assert (out["indices"][1] == -int(np.prod(img[1:]))).all()
+        out64 = run_nd(env, mt, samp, batch_dims=nb, index_dtype=torch.int64, want=("indices",))
+        check_images(m, out64, samp, nb)
+    # a strided 2-D view with int64 indices, and a transposed 3-D view
+    base = torch.from_numpy((rng.random((2, 300, 500)) >= 0.003).astype(np.uint8)).to(dev)
+    base[1] = 1
+    for v in (base[:, ::2, 1:400], base.permute(0, 2, 1)):
+        vn = np.ascontiguousarray(v.cpu().numpy())
+        _say(f"reordered strided view {tuple(v.shape)} strides {v.stride()}")
+        out = run_nd(env, v, None, batch_dims=1, index_dtype=torch.int64)
+        check_images(vn, out, None, 1)
+    v3 = base.reshape(2, 300, 20, 25).permute(0, 3, 1, 2)
+    vn = np.ascontiguousarray(v3.cpu().numpy())
+    _say(f"reordered strided view {tuple(v3.shape)}")
+    check_images(vn, run_nd(env, v3, (1.5, 1.0, 2.0), batch_dims=1, want=("dist", "indices")), (1.5, 1.0, 2.0), 1)

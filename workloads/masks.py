@@ -43,6 +43,10 @@ CONFIGS = {
     "b2d": dict(shape=(32, 1024, 1024), sampling=None, outputs=("sqdist", "dist", "indices")),
     # a stack of 2048^2 slices (middle axis longer than 1024)
     "v2048": dict(shape=(1, 64, 2048, 2048), sampling=None, outputs=("dist",)),
+    # shapes for the any-rank path: a 4-D array, and rows longer than the
+    # LDS kernels take
+    "nd4": dict(shape=(80, 80, 80, 80), sampling=(2.5, 1.0, 1.0, 1.0), outputs=("dist", "indices")),
+    "w40k": dict(shape=(256, 40000), sampling=None, outputs=("sqdist", "dist", "indices")),
 }
 # PR-EDT's own workloads (its §4.1 and Table 1): random square images, seed 42,
 # background ratio 1 % or 99 %; distances timed
@@ -51,7 +55,7 @@ for _n in (1024, 2048, 4096, 8192):
         CONFIGS[f"p1_{_n}_{_pct}"] = dict(shape=(_n, _n), sampling=None, outputs=("dist",))
 
 _CFG_ID = {"c1": 1, "c2a": 2, "c2b": 2, "c3": 3, "c4": 4, "c5": 5, "stress_row": 6, "b2d": 7,
-           "v2048": 8}
+           "v2048": 8, "nd4": 9, "w40k": 10}
 _CFG_ID.update({f"p1_{n}_{pct}": 100 + 10 * i + pct % 10
                 for i, n in enumerate((1024, 2048, 4096, 8192)) for pct in (1, 99)})
 _SUB_ID = {"c2a": 0, "c2b": 1}
@@ -203,6 +207,15 @@ def make_config(name: str, scale: int = 1):
         _, n, pct = name.split("_")
         n = int(n) // scale
         return bernoulli_2d(rng_for(name), n, n, int(pct) / 100.0), None, {}
+    if name == "nd4":
+        n = max(2, 80 // scale)
+        rng = rng_for(name)
+        m = np.empty((n, n, n, n), np.uint8)
+        for i in range(n):   # one 3-D slab at a time
+            m[i] = (rng.random((n, n, n), dtype=np.float32) >= 1e-3).astype(np.uint8)
+        return _ensure_background(m, rng), (2.5, 1.0, 1.0, 1.0), {}
+    if name == "w40k":
+        return bernoulli_2d(rng_for(name), max(1, 256 // scale), max(1, 40000 // scale), 1e-3), None, {}
     if name == "stress_row":
         n = 4096 // scale
         m, r0 = full_row_2d(rng_for(name), n, n)
