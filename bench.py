@@ -45,10 +45,11 @@ HBM_PEAK_GBS = 8000.0   # MI355X HBM3E peak, GB/s
 DEFAULT_CONFIG = "c5"
 SECOND_CONFIG = "c3"   # the other workload with an HBM target, timed beside the default
 COPY_PROBE_BYTES = 1 << 30   # float32 elements read (and as many written) by the copy probe
+# the sources of the EDT kernels and their launches (the counter summaries in
+# profiles/ are keyed by their hash)
 KERNEL_SOURCES = ("exact_euclidean_distance_amd/csrc/kernels.hip",
                   "exact_euclidean_distance_amd/csrc/envelope.h",
-                  "exact_euclidean_distance_amd/csrc/kernels.h",
-                  "exact_euclidean_distance_amd/csrc/abi.hip")
+                  "exact_euclidean_distance_amd/csrc/kernels.h")
 
 WORKLOADS = {
     "c1": "2D 512x512 uint8, background i.i.d. Bernoulli(0.01), isotropic; "
