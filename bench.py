@@ -70,6 +70,8 @@ WORKLOADS["nd4"] = ("4D 80^4 uint8 (any-rank path), background i.i.d. Bernoulli(
                     "sampling (2.5,1,1,1); outputs float32 dist + int32 index")
 WORKLOADS["w40k"] = ("2D 256x40000 uint8 (rows past the LDS kernels, any-rank path), background "
                      "i.i.d. Bernoulli(1e-3), isotropic; outputs sqdist + dist + int32 index")
+WORKLOADS["l4m"] = ("1D signal of 2^22 uint8 samples (one line longer than 65535, any-rank path), "
+                    "background i.i.d. Bernoulli(1e-4); outputs float32 dist + int32 index")
 WORKLOADS["v2048"] = ("3D 64x2048x2048 uint8 (a stack of 2048^2 slices), background i.i.d. "
                       "Bernoulli(1e-3), isotropic; output float32 dist")
 for _n in (1024, 2048, 4096, 8192):
@@ -90,7 +92,8 @@ OUTPUTS.update({k: ("dist",) for k in WORKLOADS if k.startswith("p1_")})
 OUTPUTS["v2048"] = ("dist",)
 OUTPUTS["nd4"] = ("dist", "indices")
 OUTPUTS["w40k"] = ("sqdist", "dist", "indices")
-ND_CONFIGS = ("nd4", "w40k")   # timed through edt_nd_u8 (the workspace path)
+OUTPUTS["l4m"] = ("dist", "indices")
+ND_CONFIGS = ("nd4", "w40k", "l4m")   # timed through edt_nd_u8 (any-rank entry point)
 
 
 def algorithmic_bytes(kernel: str, shape, n_out: int) -> int:

@@ -124,6 +124,138 @@ __global__ __launch_bounds__(256) void k_nd_axis0(const uint8_t* __restrict__ ma
     }
 }
 
+// The same pass for few long lines, in segments of kNdSeg positions so that
+// the GPU has work (few lines of at least 4 segments: fewer than 16384 lines):
+// per (segment, line) the first and last background in the
+// segment; per line, over its segments, the last background strictly before
+// and the first strictly after each segment; then each segment resolved from
+// those carries.  Thread u takes line u % lines of segment u / lines.
+constexpr int64_t kNdSeg = 64;
+
+__global__ __launch_bounds__(256) void k_nd_axis0_seg_summary(const uint8_t* __restrict__ mask, NdDesc d,
+                                                              int64_t nseg, int64_t* __restrict__ sfirst,
+                                                              int64_t* __restrict__ slast) {
+    const int64_t n0 = d.ext[d.nb];
+    const int64_t S0 = d.N / n0, lines = d.B * S0;
+    const int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (u >= lines * nseg) return;
+    const int64_t t = u % lines, sg = u / lines;
+    const int64_t b = t / S0, i = t - b * S0;
+    const uint8_t* m = mask + mask_line_offset(d, b, i);
+    const int64_t st = d.mstride[d.nb];
+    const int64_t j0 = sg * kNdSeg, j1 = min(n0, j0 + kNdSeg);
+    int64_t f = -1, l = -1;
+    for (int64_t j = j0; j < j1; ++j) {
+        if (m[j * st] == 0) {
+            if (f < 0) f = j;
+            l = j;
+        }
+    }
+    sfirst[u] = f;
+    slast[u] = l;
+}
+
+// per line (one block of kNdScanThreads each): above[sg * lines + t] = the
+// last background before segment sg, below[...] = the first after it (-1:
+// none), written in place of slast / sfirst.  Each thread takes a run of
+// consecutive segments; the block scans the runs' totals (prefix maximum of
+// the last, suffix minimum of the first), then each thread sweeps its run.
+constexpr int kNdScanThreads = 1024;
+constexpr int64_t kNdNoFirst = INT64_MAX;
+
+__global__ __launch_bounds__(kNdScanThreads) void k_nd_axis0_seg_scan(NdDesc d, int64_t nseg,
+                                                                       int64_t* __restrict__ sfirst,
+                                                                       int64_t* __restrict__ slast) {
+    __shared__ int64_t pmax[kNdScanThreads];
+    __shared__ int64_t smin[kNdScanThreads];
+    const int64_t lines = d.B * (d.N / d.ext[d.nb]);
+    const int64_t t = blockIdx.x;
+    const int k = threadIdx.x;
+    const int64_t run = (nseg + kNdScanThreads - 1) / kNdScanThreads;
+    const int64_t s0 = min(nseg, (int64_t)k * run), s1 = min(nseg, s0 + run);
+    int64_t lmax = -1, fmin = kNdNoFirst;
+    for (int64_t sg = s0; sg < s1; ++sg) {
+        const int64_t l = slast[sg * lines + t], f = sfirst[sg * lines + t];
+        if (l > lmax) lmax = l;
+        if (f >= 0 && f < fmin) fmin = f;
+    }
+    pmax[k] = lmax;
+    smin[k] = fmin;
+    __syncthreads();
+    for (int o = 1; o < kNdScanThreads; o <<= 1) {   // inclusive scans over the runs
+        const int64_t a = k >= o ? pmax[k - o] : -1;
+        const int64_t b = k + o < kNdScanThreads ? smin[k + o] : kNdNoFirst;
+        __syncthreads();
+        if (a > pmax[k]) pmax[k] = a;
+        if (b < smin[k]) smin[k] = b;
+        __syncthreads();
+    }
+    int64_t above = k > 0 ? pmax[k - 1] : -1;   // from the runs before / after this one
+    int64_t below = k + 1 < kNdScanThreads ? smin[k + 1] : kNdNoFirst;
+    for (int64_t sg = s0; sg < s1; ++sg) {
+        const int64_t l = slast[sg * lines + t];
+        slast[sg * lines + t] = above;
+        if (l >= 0) above = l;
+    }
+    for (int64_t sg = s1 - 1; sg >= s0; --sg) {
+        const int64_t f = sfirst[sg * lines + t];
+        sfirst[sg * lines + t] = below == kNdNoFirst ? -1 : below;
+        if (f >= 0) below = f;
+    }
+}
+
+__global__ __launch_bounds__(256) void k_nd_axis0_seg_resolve(const uint8_t* __restrict__ mask, NdDesc d,
+                                                              int64_t nseg, const int64_t* __restrict__ below,
+                                                              const int64_t* __restrict__ above,
+                                                              double* __restrict__ F, int64_t* __restrict__ feat,
+                                                              int final_pass, int32_t* __restrict__ sqdist,
+                                                              float* __restrict__ dist, void* __restrict__ indices,
+                                                              int idx_bytes) {
+    const int64_t n0 = d.ext[d.nb];
+    const int64_t S0 = d.N / n0, lines = d.B * S0;
+    const int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (u >= lines * nseg) return;
+    const int64_t t = u % lines, sg = u / lines;
+    const int64_t b = t / S0, i = t - b * S0;
+    const uint8_t* m = mask + mask_line_offset(d, b, i);
+    const int64_t st = d.mstride[d.nb];
+    const int64_t e0 = b * d.N + i;
+    const int64_t j0 = sg * kNdSeg, j1 = min(n0, j0 + kNdSeg);
+    int64_t last = above[u];   // forward: the last background at or above j
+    for (int64_t j = j0; j < j1; ++j) {
+        if (m[j * st] == 0) last = j;
+        feat[e0 + j * S0] = last;
+    }
+    int64_t next = below[u];   // backward: the first background at or below j
+    const double s2 = d.s2[0];
+    for (int64_t j = j1 - 1; j >= j0; --j) {
+        const int64_t e = e0 + j * S0;
+        const int64_t up = feat[e];
+        if (up == j) next = j;
+        int64_t c;
+        if (up < 0) c = next;
+        else if (next < 0) c = up;
+        else c = (j - up <= next - j) ? up : next;
+        double f;
+        int64_t ft;
+        if (c < 0) {
+            f = kInfF;
+            ft = -1;
+        } else {
+            const double dd = (double)(j - c);
+            f = s2 * dd * dd;
+            ft = c * S0 + i;
+        }
+        if (final_pass) {
+            if (c < 0) virtual_at(d, e - b * d.N, &f, &ft);
+            write_out(e, f, ft, sqdist, dist, indices, idx_bytes);
+        } else {
+            F[e] = f;
+            feat[e] = ft;
+        }
+    }
+}
+
 // b between a and c leaves the envelope (equality included)
 __device__ __forceinline__ bool nd_dominated(int64_t a, double Ya, int64_t b, double Yb, int64_t c, double Yc) {
     return (Yb - Ya) * (double)(c - b) >= (Yc - Yb) * (double)(b - a);
@@ -394,9 +526,29 @@ hipError_t launch_nd(const uint8_t* mask, const NdDesc& d, void* ws, int32_t* sq
     p += 2 * al((size_t)total * 8);
     int64_t* stk = reinterpret_cast<int64_t*>(p);
     const int64_t S0 = d.N / d.ext[d.nb];
-    hipLaunchKernelGGL(k_nd_axis0, dim3(blocks_for(d.B * S0)), dim3(256), 0, s, mask, d, F[0], feat[0],
-                       d.nd == 1 ? 1 : 0, sqdist, dist, indices, idx_bytes);
-    hipError_t e = hipGetLastError();
+    const int64_t lines0 = d.B * S0, n0 = d.ext[d.nb];
+    hipError_t e;
+    if (lines0 < 16384 && n0 >= 4 * kNdSeg) {
+        // few long lines: segments; the summaries use the stack region, idle
+        // until the envelope passes (4 * nseg * lines0 <= total words)
+        const int64_t nseg = (n0 + kNdSeg - 1) / kNdSeg;
+        int64_t* sfirst = stk;
+        int64_t* slast = stk + nseg * lines0;
+        hipLaunchKernelGGL(k_nd_axis0_seg_summary, dim3(blocks_for(nseg * lines0)), dim3(256), 0, s, mask, d, nseg,
+                           sfirst, slast);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(k_nd_axis0_seg_scan, dim3((unsigned)lines0), dim3(kNdScanThreads), 0, s, d, nseg, sfirst,
+                           slast);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(k_nd_axis0_seg_resolve, dim3(blocks_for(nseg * lines0)), dim3(256), 0, s, mask, d, nseg,
+                           sfirst, slast, F[0], feat[0], d.nd == 1 ? 1 : 0, sqdist, dist, indices, idx_bytes);
+    } else {
+        hipLaunchKernelGGL(k_nd_axis0, dim3(blocks_for(d.B * S0)), dim3(256), 0, s, mask, d, F[0], feat[0],
+                           d.nd == 1 ? 1 : 0, sqdist, dist, indices, idx_bytes);
+    }
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
     int cur = 0;
     for (int k = 1; k < d.nd; ++k) {

@@ -218,3 +218,28 @@ def test_reordered_runs(env):
     vn = np.ascontiguousarray(v3.cpu().numpy())
     _say(f"reordered strided view {tuple(v3.shape)}")
     check_images(vn, run_nd(env, v3, (1.5, 1.0, 2.0), batch_dims=1, want=("dist", "indices")), (1.5, 1.0, 2.0), 1)
+
+
+def test_long_lines_in_segments(env):
+    """Few long lines along axis 0 run in segments of 64 (per-segment
+    summaries, carries across segments): a 1-D signal of 2^20 with sparse
+    background, one whose only background is at the start (a carry across
+    every segment), ties at segment edges, and a tall 2-D image."""
+    torch, dev = env
+    rng = np.random.default_rng([42, 9107])
+    n = 1 << 20
+    sig = (rng.random(n) >= 2e-4).astype(np.uint8)
+    sig[-1] = 0
+    edge = np.ones(4096, np.uint8)
+    edge[[255, 769, 1024, 3000]] = 0          # midpoints fall on segment edges
+    first = np.ones(300000, np.uint8)
+    first[0] = 0
+    tall = (rng.random((90000, 5)) >= 0.001).astype(np.uint8)
+    tall[-1] = 0
+    for name, m, samp in (("signal 2^20", sig, None), ("background at the start", first, (0.5,)),
+                          ("ties at segment edges", edge, None), ("tall 90000 x 5", tall, (2.5, 1.0))):
+        _say(f"segmented axis 0: {name} {m.shape}")
+        fits = sum(k * k for k in m.shape) <= 2**31 - 1
+        want = ("sqdist", "dist", "indices") if samp is None and fits else ("dist", "indices")
+        out = run_nd(env, torch.from_numpy(m).to(dev), samp, want=want)
+        check_images(m, out, samp, 0)

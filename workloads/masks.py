@@ -47,6 +47,8 @@ CONFIGS = {
     # LDS kernels take
     "nd4": dict(shape=(80, 80, 80, 80), sampling=(2.5, 1.0, 1.0, 1.0), outputs=("dist", "indices")),
     "w40k": dict(shape=(256, 40000), sampling=None, outputs=("sqdist", "dist", "indices")),
+    # one 1-D signal of 2^22 samples (a single long line)
+    "l4m": dict(shape=(1 << 22,), sampling=None, outputs=("dist", "indices")),
 }
 # PR-EDT's own workloads (its §4.1 and Table 1): random square images, seed 42,
 # background ratio 1 % or 99 %; distances timed
@@ -55,7 +57,7 @@ for _n in (1024, 2048, 4096, 8192):
         CONFIGS[f"p1_{_n}_{_pct}"] = dict(shape=(_n, _n), sampling=None, outputs=("dist",))
 
 _CFG_ID = {"c1": 1, "c2a": 2, "c2b": 2, "c3": 3, "c4": 4, "c5": 5, "stress_row": 6, "b2d": 7,
-           "v2048": 8, "nd4": 9, "w40k": 10}
+           "v2048": 8, "nd4": 9, "w40k": 10, "l4m": 11}
 _CFG_ID.update({f"p1_{n}_{pct}": 100 + 10 * i + pct % 10
                 for i, n in enumerate((1024, 2048, 4096, 8192)) for pct in (1, 99)})
 _SUB_ID = {"c2a": 0, "c2b": 1}
@@ -216,6 +218,10 @@ def make_config(name: str, scale: int = 1):
         return _ensure_background(m, rng), (2.5, 1.0, 1.0, 1.0), {}
     if name == "w40k":
         return bernoulli_2d(rng_for(name), max(1, 256 // scale), max(1, 40000 // scale), 1e-3), None, {}
+    if name == "l4m":
+        rng = rng_for(name)
+        return _ensure_background((rng.random(max(1, (1 << 22) // scale), dtype=np.float32) >= 1e-4)
+                                  .astype(np.uint8), rng), None, {}
     if name == "stress_row":
         n = 4096 // scale
         m, r0 = full_row_2d(rng_for(name), n, n)
