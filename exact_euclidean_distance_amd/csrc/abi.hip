@@ -550,7 +550,7 @@ constexpr int kMaxBatchAxes = 8;
 // spatial axes in some order fit those kernels, a reordered run (the mask
 // gathered into the workspace in that order, the outputs put back); the
 // workspace path of nd.hip for the rest.
-enum class NdRoute { kEmpty, k1D, k2D, k3D, kPermuted, kGeneric };
+enum class NdRoute { kEmpty, k1D, k2D, k3D, kPermuted, kGenericPermuted, kGeneric };
 
 struct NdPlan {
     NdRoute route = NdRoute::kGeneric;
@@ -676,6 +676,26 @@ edt_status plan_nd(int32_t nbatch, int32_t ndim, const int64_t* shape, const int
             P.ws = P.off_inner + inner;
         }
     }
+    // the workspace path gives each line one thread on every axis but the
+    // first (which runs in segments when its lines are few): a longest axis
+    // with few lines goes first, in a reordered run of the workspace path
+    if (P.route == NdRoute::kGeneric && (ndim == 2 || ndim == 3) && N <= INT32_MAX) {
+        int amax = 0;
+        for (int k = 1; k < ndim; ++k)
+            if (shape[nbatch + k] > shape[nbatch + amax]) amax = k;
+        if (amax != 0 && B * (N / shape[nbatch + amax]) < 16384) {
+            P.route = NdRoute::kGenericPermuted;
+            P.perm[0] = amax;
+            for (int k = 0, o = 1; k < ndim; ++k)
+                if (k != amax) P.perm[o++] = k;
+            const size_t n = (size_t)P.total;
+            P.off_idx = round_up(n);
+            P.off_sq = P.off_idx + round_up(n * 4);
+            P.off_dist = P.off_sq + round_up(n * 4);
+            P.off_inner = P.off_dist + round_up(n * 4);
+            P.ws = P.off_inner + edt::nd_workspace_bytes(P.total);
+        }
+    }
     if (P.route == NdRoute::kGeneric) P.ws = edt::nd_workspace_bytes(P.total);
     *out = P;
     return EDT_OK;
@@ -766,6 +786,31 @@ edt_status edt_nd_u8(const uint8_t* mask, int32_t nbatch, int32_t ndim, const in
                            nullptr);
             }
             if (rs != EDT_OK) return rs;
+            if (edt::launch_nd_unpermute(P.d, P.perm, pidx, psq, pdist, sqdist, dist, indices, ib, stream) !=
+                hipSuccess)
+                return EDT_ERR_HIP;
+            return EDT_OK;
+        }
+        case NdRoute::kGenericPermuted: {
+            char* base = static_cast<char*>(workspace);
+            uint8_t* pm = reinterpret_cast<uint8_t*>(base);
+            int32_t* pidx = reinterpret_cast<int32_t*>(base + P.off_idx);
+            int32_t* psq = sqdist ? reinterpret_cast<int32_t*>(base + P.off_sq) : nullptr;
+            float* pdist = dist ? reinterpret_cast<float*>(base + P.off_dist) : nullptr;
+            for (int k = 0; k < ndim; ++k) P.d.s2[k] = s2[k];
+            if (edt::launch_nd_gather(mask, P.d, P.perm, pm, stream) != hipSuccess) return EDT_ERR_HIP;
+            edt::NdDesc q = P.d;   // the gathered array: C-contiguous, spatial axes permuted
+            for (int k = 0; k < ndim; ++k) {
+                q.ext[nbatch + k] = P.d.ext[nbatch + P.perm[k]];
+                q.s2[k] = s2[P.perm[k]];
+            }
+            int64_t st = 1;
+            for (int a = nbatch + ndim - 1; a >= 0; --a) {
+                q.mstride[a] = st;
+                st *= q.ext[a];
+            }
+            if (edt::launch_nd(pm, q, base + P.off_inner, psq, pdist, pidx, 4, stream) != hipSuccess)
+                return EDT_ERR_HIP;
             if (edt::launch_nd_unpermute(P.d, P.perm, pidx, psq, pdist, sqdist, dist, indices, ib, stream) !=
                 hipSuccess)
                 return EDT_ERR_HIP;

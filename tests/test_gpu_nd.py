@@ -124,12 +124,14 @@ def test_strided_views(env):
 
 def test_long_rows_and_big_extents(env):
     """Rows beyond the LDS envelope (2-D W > 32768, 3-D W > 16384, 3-D H >
-    32768) and extents over 65535 take the workspace path."""
+    32768) take reordered runs of the LDS kernels; extents over 65535 the
+    workspace path (its longest axis first when that axis has few lines)."""
     torch, dev = env
     rng = np.random.default_rng([42, 9103])
     cases = [((40, 40000), 0.0005, None), ((3, 4, 20000), 0.001, (2.5, 1.0, 1.0)),
              ((2, 40000, 3), 0.0005, None), ((70000, 3), 0.0002, None), ((100000,), 0.0001, None),
-             ((3, 70000), 0.0003, (1.0, 0.5))]
+             ((3, 70000), 0.0003, (1.0, 0.5)), ((4, 5, 70000), 0.0005, (1.0, 2.0, 0.5)),
+             ((2, 90000, 3), 0.0005, None)]
     for shape, p, samp in cases:
         m = (rng.random(shape) >= p).astype(np.uint8)
         m.reshape(-1)[-1] = 0
