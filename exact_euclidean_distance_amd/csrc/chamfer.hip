@@ -566,7 +566,7 @@ __global__ __launch_bounds__(kLinfThreads) void k_linf_rows(const typename Geo::
             ix = geo.virt_index();
         } else {
             const uint16_t* lg = sg + l * L;
-            int bj;
+            int bj = -1;
             auto gat = [&](int j) { return (int)lg[j]; };
             if (lists && n <= kLinfList) {
                 best = linf_list(lst + l * kLinfList, n, q, gat, bj);
