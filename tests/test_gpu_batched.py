@@ -732,6 +732,36 @@ def _bucket_rows_2d(mask, bt=128, bc=16, lst=32):
     return bucketed, full
 
 
+def test_chessboard_large_values(torch_dev):
+    """The range-minimum chessboard kernels with large axis-0 distances (g up
+    to 40000 in the keys g << 16 | j, wide bisection bounds): a tall image
+    with a few background pixels, and a volume whose middle axis carries
+    them; full output against the device brute force, sampled points and
+    the corners against the oracle."""
+    torch, dev = torch_dev
+    from exact_euclidean_distance_amd import chessboard, edt_brute
+    rng = np.random.default_rng([42, 5017])
+    m = np.ones((40000, 120), np.uint8)
+    m[rng.integers(0, 40000, 6), rng.integers(0, 120, 6)] = 0
+    v = np.ones((2, 3000, 900, 3), np.uint8)
+    v[0, 0, 0, 0] = 0
+    v[1, rng.integers(0, 3000, 4), rng.integers(0, 900, 4), rng.integers(0, 3, 4)] = 0
+    for name, arr, batched in (("40000 x 120", m, False), ("2 x 3000 x 900 x 3", v, True)):
+        _say(f"chessboard large values {name}")
+        t = torch.from_numpy(arr).to(dev)
+        r = chessboard(t, return_indices=True)
+        ref = edt_brute(t, metric="chessboard", batched=batched).dist
+        torch.cuda.synchronize()
+        assert torch.equal(r.dist, ref), "chessboard distance differs from the definition"
+        d = r.dist.cpu().numpy()
+        ix = r.indices.cpu().numpy()
+        imgs = [(arr, d, ix)] if not batched else list(zip(arr, d, ix))
+        for a, dd, ii in imgs:
+            assert (oracle.chessboard_to(ii, a.shape) == dd).all()
+            pts = np.concatenate([rng.integers(0, a.size, 60), [0, a.size - 1]])
+            assert (dd.reshape(-1)[pts] == oracle.chessboard_at(a, pts)).all()
+
+
 def test_chessboard_bucket_lists(torch_dev):
     """The chessboard row pass on rows longer than 4096 (the outward-search
     kernel; shorter rows take the range-minimum kernel): rows that take the
