@@ -869,7 +869,7 @@ edt_status chamfer2d(Chamfer metric, const uint8_t* mask, int32_t B, int32_t H, 
         return EDT_ERR_HIP;
     const hipError_t e = metric == Chamfer::kTaxicab
                              ? edt::launch_l1_rows_2d(c0, B, H, W, dist, indices, stream, nullptr)
-                             : edt::launch_linf_rows_2d(c0, B, H, W, dist, indices, stream, nullptr);
+                             : edt::launch_rows_linf_2d(c0, B, H, W, dist, indices, stream, nullptr);
     return e == hipSuccess ? EDT_OK : EDT_ERR_HIP;
 }
 
@@ -892,10 +892,10 @@ edt_status chamfer3d(Chamfer metric, const uint8_t* mask, int32_t B, int32_t D, 
         return EDT_ERR_HIP;
     const bool l1 = metric == Chamfer::kTaxicab;
     if ((l1 ? edt::launch_l1_cols_3d(c0, B, D, H, W, c01, stream, nullptr)
-            : edt::launch_linf_cols_3d(c0, B, D, H, W, c01, stream, nullptr)) != hipSuccess)
+            : edt::launch_cols_linf_3d(c0, B, D, H, W, c01, stream, nullptr)) != hipSuccess)
         return EDT_ERR_HIP;
     if ((l1 ? edt::launch_l1_rows_3d(c01, B, D, H, W, dist, indices, stream, nullptr)
-            : edt::launch_linf_rows_3d(c01, B, D, H, W, dist, indices, stream, nullptr)) != hipSuccess)
+            : edt::launch_rows_linf_3d(c01, B, D, H, W, dist, indices, stream, nullptr)) != hipSuccess)
         return EDT_ERR_HIP;
     return EDT_OK;
 }

@@ -12,10 +12,16 @@
 // x(a,b) = (Y_b - Y_a) / (2 s^2 (b - a)), where the bisector of their background
 // elements meets the line.  pi_b(q) < pi_a(q) exactly when
 // Y_b - Y_a < 2 s^2 q (b - a).
+//
+// The same machinery serves the chessboard step of TorchMorph's chamfer
+// transforms (read as the L-infinity metric), f_j(q) = max(g_j, |q - j|): see
+// the metrics below.
 #pragma once
 
 #include <math.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #if defined(__HIPCC__)
 #define EDT_HD __host__ __device__
@@ -64,8 +70,9 @@ EDT_HD inline bool dominated(int a, double Ya, int b, double Yb, int c, double Y
 
 // One round for chunk c of a line of G chunks with member mask m: the bits of
 // its first and last members that the dominance test removes, against the
-// line as it stands at the start of the round.  View: mask(c), Y(pos),
-// last_nonempty / first_nonempty over a half-open chunk range (-1 if none).
+// line as it stands at the start of the round.  View: mask(c), Y(pos), mt (the
+// metric), last_nonempty / first_nonempty over a half-open chunk range (-1 if
+// none).
 template <int K, class View, class Mask>
 EDT_HD inline Mask boundary_dead(View& v, int c, int G, Mask m) {
     if (!m) return 0;
@@ -79,14 +86,58 @@ EDT_HD inline Mask boundary_dead(View& v, int c, int G, Mask m) {
         const int p = base + tf;
         const Mask above = m & bits_above<Mask>(tf);
         const int pn = above ? base + low_bit(above) : nf;
-        if (pl >= 0 && pn >= 0 && dominated(pl, v.Y(pl), p, v.Y(p), pn, v.Y(pn))) dead |= Mask(1) << tf;
+        if (pl >= 0 && pn >= 0 && v.mt.dominated(pl, v.Y(pl), p, v.Y(p), pn, v.Y(pn))) dead |= Mask(1) << tf;
     }
     if (tl != tf) {
         const int p = base + tl;
         const int pp = base + high_bit(m & bits_below<Mask>(tl));
-        if (nf >= 0 && dominated(pp, v.Y(pp), p, v.Y(p), nf, v.Y(nf))) dead |= Mask(1) << tl;
+        if (nf >= 0 && v.mt.dominated(pp, v.Y(pp), p, v.Y(p), nf, v.Y(nf))) dead |= Mask(1) << tl;
     }
     return dead;
+}
+
+// Cascade steps of the whole-line rounds.  back_cascade: the trailing members
+// of chunk c (member mask m) leave one after another while the last one is
+// dominated by its predecessor in the chunk and w, the first member of the
+// next non-empty chunk (w >= 0); the chunk's first member always stays.  In a
+// step where every chunk does only this, every first member stays, so w is
+// present at each removal and the removals are justified one by one (unlike
+// boundary_dead, where neighbours may leave together).  front_cascade is the
+// mirror image: leading members leave against their successor and w, the
+// last member of the previous non-empty chunk; the chunk's last member stays.
+// A chunk whose interior members only the far side can dominate then empties
+// down to one member in one step instead of one member per round.
+template <int K, class View, class Mask>
+EDT_HD inline Mask back_cascade(View& v, int c, Mask m, int w) {
+    const int base = c * K;
+    const auto Yw = v.Y(w);
+    int tl = high_bit(m);
+    auto Yl = v.Y(base + tl);
+    while (m & (m - 1)) {
+        const int pp = high_bit(m & bits_below<Mask>(tl));
+        const auto Yp = v.Y(base + pp);
+        if (!v.mt.dominated(base + pp, Yp, base + tl, Yl, w, Yw)) break;
+        m &= ~(Mask(1) << tl);
+        tl = pp;
+        Yl = Yp;
+    }
+    return m;
+}
+template <int K, class View, class Mask>
+EDT_HD inline Mask front_cascade(View& v, int c, Mask m, int w) {
+    const int base = c * K;
+    const auto Yw = v.Y(w);
+    int tf = low_bit(m);
+    auto Yf = v.Y(base + tf);
+    while (m & (m - 1)) {
+        const int nn = low_bit(m & bits_above<Mask>(tf));
+        const auto Yn = v.Y(base + nn);
+        if (!v.mt.dominated(w, Yw, base + tf, Yf, base + nn, Yn)) break;
+        m &= ~(Mask(1) << tf);
+        tf = nn;
+        Yf = Yn;
+    }
+    return m;
 }
 
 // Non-empty chunk search over an occupancy bit set (bit c of word c / 64 set
@@ -119,18 +170,19 @@ EDT_HD inline int occ_first(const Words& occ, int lo, int hi) {  // smallest set
 // Local envelope of one chunk by the insertion sweep, over the candidate
 // positions base + t for the set bits t of cand (increasing order); returns the
 // member mask.  val_at(t) reads the stored value of position base + t and
-// height(v, p) is its lifted height Y_p.
-template <class Mask, class ValAt, class HeightOf>
-EDT_HD inline Mask build_chunk(int base, Mask cand, ValAt val_at, HeightOf height) {
+// height(v, p) is its height Y_p under the metric mt.
+template <class Mask, class Mt, class ValAt, class HeightOf>
+EDT_HD inline Mask build_chunk(const Mt& mt, int base, Mask cand, ValAt val_at, HeightOf height) {
+    using H = typename Mt::Val;
     Mask m = 0;
     int top = -1, sec = -1;
-    double Ytop = 0.0, Ysec = 0.0;
+    H Ytop = H(0), Ysec = H(0);
     while (cand) {
         const int t = low_bit(cand);
         cand &= cand - 1;
         const int p = base + t;
-        const double Y = height(val_at(t), p);
-        while (sec >= 0 && dominated(sec, Ysec, top, Ytop, p, Y)) {
+        const H Y = height(val_at(t), p);
+        while (sec >= 0 && mt.dominated(sec, Ysec, top, Ytop, p, Y)) {
             m &= ~(Mask(1) << (top - base));
             top = sec; Ytop = Ysec;
             const Mask below = m & bits_below<Mask>(top - base);
@@ -151,17 +203,19 @@ EDT_HD inline Mask build_chunk(int base, Mask cand, ValAt val_at, HeightOf heigh
 // The same sweep with the heights of the chunk's K positions at hand (Yr[t] is
 // Y of position base + t; unrolled over t, so that Yr can live in registers);
 // y_at(p) gives the height of an earlier position that a removal uncovers.
-template <int K, class Mask, class YAt>
-EDT_HD inline Mask build_chunk_unrolled(int base, Mask cand, const double (&Yr)[K], YAt y_at) {
+template <int K, class Mask, class Mt, class YAt>
+EDT_HD inline Mask build_chunk_unrolled(const Mt& mt, int base, Mask cand,
+                                        const typename Mt::Val (&Yr)[K], YAt y_at) {
+    using H = typename Mt::Val;
     Mask m = 0;
     int top = -1, sec = -1;
-    double Ytop = 0.0, Ysec = 0.0;
+    H Ytop = H(0), Ysec = H(0);
 #pragma unroll
     for (int t = 0; t < K; ++t) {
         if (!((cand >> t) & Mask(1))) continue;
         const int p = base + t;
-        const double Y = Yr[t];
-        while (sec >= 0 && dominated(sec, Ysec, top, Ytop, p, Y)) {
+        const H Y = Yr[t];
+        while (sec >= 0 && mt.dominated(sec, Ysec, top, Ytop, p, Y)) {
             m &= ~(Mask(1) << (top - base));
             top = sec; Ytop = Ysec;
             const Mask below = m & bits_below<Mask>(top - base);
@@ -229,6 +283,86 @@ EDT_HD inline int first_index_beating(double A, double B, int cap) {
     return c;
 }
 
+// --------------------------------------------------------------------------
+// Metrics.  The envelope steps need only this of the per-candidate functions
+// f_j along a line: for j < k, the positions where f_k is strictly below f_j,
+// and those where it is at most f_j, are right half-lines.  Then two
+// neighbouring members of an envelope hand over at one position, a candidate
+// that neither of two others around it lets win is never needed, a chain in
+// which no member is beaten by its two neighbours is the lower envelope, and a
+// candidate that loses to a nearer one at a chunk's first position loses on the
+// whole chunk.  Both families below have it:
+//   L2Metric    f_j(q) = F_j + s^2 (q - j)^2   (the Euclidean step)
+//   LinfMetric  f_j(q) = max(g_j, |q - j|)    (the chessboard step; for j < k,
+//               f_k - f_j is k - j far to the left and j - k far to the right,
+//               and once f_k <= f_j (or <) holds it holds further right)
+// A metric gives the candidate value type (Val) and the height its tests
+// compare, dist(d) and combine(v, dist(d)) (a candidate of value v at signed
+// offset d), the dominance test, cross (the first position, clipped to [0, cap], where
+// the later of two candidates is strictly below the earlier), the chunk bound,
+// and the 32-bit form in which chunk minima and bounds are kept.
+// --------------------------------------------------------------------------
+struct L2Metric {
+    using Val = double;
+    static constexpr double kInf = __builtin_huge_val();   // no source
+    static constexpr double kMaxFinite = __DBL_MAX__;
+    double s2;   // squared spacing along the line
+    EDT_HD Val height(Val f, int p) const { return f + s2 * (double)p * (double)p; }
+    EDT_HD Val dist(int d) const { return s2 * (double)d * (double)d; }
+    EDT_HD static Val combine(Val f, Val dd) { return f + dd; }
+    EDT_HD static bool dominated(int a, Val Ya, int b, Val Yb, int c, Val Yc) {
+        return edt::dominated(a, Ya, b, Yb, c, Yc);
+    }
+    EDT_HD int cross(int a, Val Ya, int b, Val Yb, int cap) const {
+        return first_index_beating(Yb - Ya, 2.0 * s2 * (double)(b - a), cap);
+    }
+    // chunk minima and bounds as float32 bits rounded up; a lower bound of
+    // the exact minimum is one float32 step below
+    EDT_HD static uint32_t min_bits(Val f) { return __builtin_bit_cast(uint32_t, round_up_float(f)); }
+    EDT_HD static Val from_bits(uint32_t b) { return (double)__builtin_bit_cast(float, b); }
+    EDT_HD static Val lower_from_bits(uint32_t b) { return from_bits(b) * (1.0 - 0x1p-22); }
+    EDT_HD uint32_t bound_bits(Val self, Val prev, Val next, int K) const {
+        return __builtin_bit_cast(uint32_t, round_up_float(chunk_bound(self, prev, next, s2, K)));
+    }
+};
+
+struct LinfMetric {
+    using Val = int;
+    static constexpr int kInf = 0x3FFFFFFF;   // no source (sums with positions stay in int32)
+    static constexpr int kMaxFinite = kInf - 1;
+    EDT_HD static Val height(Val g, int) { return g; }
+    EDT_HD static Val dist(int d) { return d < 0 ? -d : d; }
+    EDT_HD static Val combine(Val g, Val dd) { return g > dd ? g : dd; }
+    // First position q where candidate k is strictly below candidate j (j < k).
+    // If g_k >= g_j, f_k can only be below where f_j = q - j > g_k and q is
+    // nearer k than j; otherwise already where |q - k| < g_j inside j's flat
+    // part, or, past it, where q is nearer k.
+    EDT_HD static int first_below(int j, int gj, int k, int gk) {
+        const int mid = (j + k) >> 1;
+        const int x = gk >= gj ? (j + gk > mid ? j + gk : mid) : (k - gj < mid ? k - gj : mid);
+        return x + 1;
+    }
+    EDT_HD static bool dominated(int a, Val ga, int b, Val gb, int c, Val gc) {
+        return first_below(a, ga, b, gb) >= first_below(b, gb, c, gc);
+    }
+    EDT_HD static int cross(int a, Val ga, int b, Val gb, int cap) {
+        const int x = first_below(a, ga, b, gb);
+        return x < 0 ? 0 : x > cap ? cap : x;
+    }
+    EDT_HD static uint32_t min_bits(Val g) { return (uint32_t)g; }
+    EDT_HD static Val from_bits(uint32_t b) { return (int)b; }
+    EDT_HD static Val lower_from_bits(uint32_t b) { return (int)b; }
+    // every position of chunk c lies within K - 1 of its own chunk's
+    // minimiser and within 2K - 1 of a neighbour's (as chunk_bound)
+    EDT_HD static uint32_t bound_bits(Val self, Val prev, Val next, int K) {
+        const int a = self > K - 1 ? self : K - 1;
+        const int b = prev > 2 * K - 1 ? prev : 2 * K - 1;
+        const int c = next > 2 * K - 1 ? next : 2 * K - 1;
+        const int m = a < b ? a : b;
+        return (uint32_t)(m < c ? m : c);
+    }
+};
+
 template <bool Narrow> struct SeqBits { using T = uint64_t; };
 template <> struct SeqBits<true> { using T = uint32_t; };
 
@@ -256,11 +390,13 @@ struct Packed8 {
 // M and the members of other chunks that reach into it, with no merging of
 // whole lines.
 //
-// A member m < b can own a position of the chunk only if it is strictly nearer
-// at b than every member between m and b: for m < x, pi_m - pi_x grows with q,
-// so losing at b means losing on the whole chunk.  Scanning leftwards from b,
-// such members are kept while s^2 (b - m)^2 stays below the best value at b so
-// far (beyond that no member can beat it).  Symmetrically on the right at e.
+// A member m < b is needed for the chunk only if it is strictly nearer at b
+// than every member between m and b: for m < x, once x is at least as near as
+// m it stays so further right (the metric's half-line property), so not
+// winning at b means not being needed on the whole chunk.  Scanning leftwards
+// from b, such members are kept while their distance term alone, dist(b - m),
+// stays below the best value at b so far (beyond that no member can beat it).
+// Symmetrically on the right at e.
 // The reaching members (at most CAP per side) and the chunk's members form a
 // short sorted sequence whose lower envelope, on [b, e], is the line's.  Its
 // members then get their owned intervals; mark(t, owner) is called at chunk
@@ -268,9 +404,9 @@ struct Packed8 {
 // is passed over when a lower bound of its F plus the squared distance to its
 // nearest position is no better than the best value so far.  Returns false
 // without marking if more than CAP members reach in from one side.
-// View: Y(pos), f(pos), s2l, mask(c), last_nonempty / first_nonempty (as for
-// boundary_dead), fmin_lb(c) (a lower bound of F over chunk c).  Needs
-// 2 CAP + K <= 64.
+// View: Y(pos), f(pos), mt (the metric), mask(c), last_nonempty /
+// first_nonempty (as for boundary_dead), fmin_lb(c) (a lower bound of the
+// values of chunk c).  Needs 2 CAP + K <= 64.
 template <int K, int CAP, class View, class Mask, class Mark>
 EDT_HD inline bool chunk_owner_marks(View& v, int c, int G, int L, Mask M, Mark mark) {
     static_assert(2 * CAP + K <= 64, "sequence index space must fit 64 bits");
@@ -280,32 +416,30 @@ EDT_HD inline bool chunk_owner_marks(View& v, int c, int G, int L, Mask M, Mark 
     const int b = c * K;
     const int n = L - b < K ? L - b : K;
     const int e = b + n - 1;
-    const double s2 = v.s2l;
+    const auto& mt = v.mt;
+    using H = typename std::remove_reference_t<decltype(mt)>::Val;
 
     // members reaching in from the left (Lp[0] nearest) and from the right
     Packed8 Lp, Rp;
     int nL = 0, nR = 0;
-    double best = __builtin_huge_val();
+    H best = mt.kInf;
     if (M) {
         const int x = b + low_bit(M);
-        const double d = (double)(x - b);
-        best = v.f(x) + s2 * d * d;
+        best = mt.combine(v.f(x), mt.dist(x - b));
     }
     for (int cc = v.last_nonempty(0, c); cc >= 0; cc = v.last_nonempty(0, cc)) {
-        const double dn = (double)(b - (cc * K + K - 1));   // to the chunk's nearest position
-        const double ddn = s2 * dn * dn;
+        const H ddn = mt.dist(b - (cc * K + K - 1));   // to the chunk's nearest position
         if (!(ddn < best)) break;
-        if (!(v.fmin_lb(cc) + ddn < best)) continue;         // no member of it can win
+        if (!(mt.combine(v.fmin_lb(cc), ddn) < best)) continue;   // no member of it can win
         Mask mk = v.mask(cc);
         bool stop = false;
         do {
             const int t = high_bit(mk);
             mk ^= Mask(1) << t;
             const int m = cc * K + t;
-            const double d = (double)(b - m);
-            const double dd = s2 * d * d;
+            const H dd = mt.dist(b - m);
             if (!(dd < best)) { stop = true; break; }
-            const double p = v.f(m) + dd;
+            const H p = mt.combine(v.f(m), dd);
             if (p < best) {
                 if (nL == CAP) return false;
                 Lp.set(nL, m);
@@ -315,27 +449,24 @@ EDT_HD inline bool chunk_owner_marks(View& v, int c, int G, int L, Mask M, Mark 
         } while (mk);
         if (stop) break;
     }
-    best = __builtin_huge_val();
+    best = mt.kInf;
     if (M) {
         const int x = b + high_bit(M);
-        const double d = (double)(e - x);
-        best = v.f(x) + s2 * d * d;
+        best = mt.combine(v.f(x), mt.dist(e - x));
     }
     for (int cc = v.first_nonempty(c + 1, G); cc >= 0; cc = v.first_nonempty(cc + 1, G)) {
-        const double dn = (double)(cc * K - e);
-        const double ddn = s2 * dn * dn;
+        const H ddn = mt.dist(cc * K - e);
         if (!(ddn < best)) break;
-        if (!(v.fmin_lb(cc) + ddn < best)) continue;
+        if (!(mt.combine(v.fmin_lb(cc), ddn) < best)) continue;
         Mask mk = v.mask(cc);
         bool stop = false;
         do {
             const int t = low_bit(mk);
             mk &= mk - 1;
             const int m = cc * K + t;
-            const double d = (double)(m - e);
-            const double dd = s2 * d * d;
+            const H dd = mt.dist(m - e);
             if (!(dd < best)) { stop = true; break; }
-            const double p = v.f(m) + dd;
+            const H p = mt.combine(v.f(m), dd);
             if (p < best) {
                 if (nR == CAP) return false;
                 Rp.set(nR, m);
@@ -361,10 +492,10 @@ EDT_HD inline bool chunk_owner_marks(View& v, int c, int G, int L, Mask M, Mark 
     // lead the stack)
     Seq alive = 0;
     int top = -1, sec = -1, ptop = 0, psec = 0;
-    double Ytop = 0.0, Ysec = 0.0;
+    H Ytop = H(0), Ysec = H(0);
     auto insert = [&](int i, int p) {
-        const double Y = v.Y(p);
-        while (sec >= 0 && dominated(psec, Ysec, ptop, Ytop, p, Y)) {
+        const H Y = v.Y(p);
+        while (sec >= 0 && mt.dominated(psec, Ysec, ptop, Ytop, p, Y)) {
             alive &= ~(Seq(1) << top);
             top = sec;
             ptop = psec;
@@ -418,18 +549,18 @@ EDT_HD inline bool chunk_owner_marks(View& v, int c, int G, int L, Mask M, Mark 
     if (!alive) return true;
     int i = low_bit(alive);
     int pi = pos_of(i);
-    double Yi = v.Y(pi);
+    H Yi = v.Y(pi);
     int st = b;
     for (;;) {
         const Seq after = i + 1 < (int)(8 * sizeof(Seq)) ? alive & ~((Seq(2) << i) - 1) : Seq(0);
         int en = e + 1;
         int j = -1, pj = 0;
-        double Yj = 0.0;
+        H Yj = H(0);
         if (after) {
             j = low_bit(after);
             pj = pos_of(j);
             Yj = v.Y(pj);
-            en = first_index_beating(Yj - Yi, 2.0 * s2 * (double)(pj - pi), e + 1);
+            en = mt.cross(pi, Yi, pj, Yj, e + 1);
         }
         const int lo = st > b ? st : b;
         if (lo < en) mark(lo - b, pi);

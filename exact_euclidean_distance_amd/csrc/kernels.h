@@ -93,13 +93,17 @@ hipError_t launch_l1_cols_3d(const uint16_t* c0, int B, int D, int H, int W, uin
                              hipStream_t s, KernelTimer* tm);
 hipError_t launch_l1_rows_3d(const uint32_t* c01, int B, int D, int H, int W, int32_t* dist,
                              int32_t* indices, hipStream_t s, KernelTimer* tm);
-// chessboard (L-infinity) transform: last axis with outputs, and the middle axis of volumes
-hipError_t launch_linf_rows_2d(const uint16_t* c0, int B, int H, int W, int32_t* dist,
+// Chessboard (L-infinity) transform (kernels.hip, the envelope kernels under
+// the chessboard metric): last axis with int32 distances / indices for B
+// images or volumes, and the middle axis of volumes (packed owners, as
+// launch_cols_3d).  Lines must fit the kernels' LDS (rows_lds_bytes /
+// cols_lds_bytes non-zero).
+hipError_t launch_rows_linf_2d(const uint16_t* c0, int B, int H, int W, int32_t* dist,
                                int32_t* indices, hipStream_t s, KernelTimer* tm);
-hipError_t launch_linf_cols_3d(const uint16_t* c0, int B, int D, int H, int W, uint32_t* c01,
+hipError_t launch_rows_linf_3d(const uint32_t* c01, int B, int D, int H, int W, int32_t* dist,
+                               int32_t* indices, hipStream_t s, KernelTimer* tm);
+hipError_t launch_cols_linf_3d(const uint16_t* c0, int B, int D, int H, int W, uint32_t* c01,
                                hipStream_t s, KernelTimer* tm);
-hipError_t launch_linf_rows_3d(const uint32_t* c01, int B, int D, int H, int W, int32_t* dist,
-                               int32_t* indices, hipStream_t s, KernelTimer* tm);
 
 // The transform for any spatial rank (nd.hip): nb leading batch axes and nd
 // (1..8) spatial axes; ext[] the extents (batch first), mstride[] the mask's

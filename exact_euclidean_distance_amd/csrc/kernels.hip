@@ -372,7 +372,8 @@ hipError_t launch_axis0(const uint8_t* mask, int B, int n0, int64_t M, uint16_t*
 //
 // Phases of one line (all lanes of the line together):
 //   1. chunk minima of F and the line's candidate bound U (see chunk_bound),
-//      then the candidates a nearest chunk minimiser pair dominates are dropped;
+//      then the candidates that a pair of chunk minimisers dominates are
+//      dropped (on each side the minimiser best at the chunk's nearer end);
 //   2. local envelope of every chunk's remaining candidates;
 //   3. each lane resolves its chunk alone from its own envelope and the few
 //      members of other chunks that reach into it (chunk_owner_marks), writing
@@ -403,6 +404,8 @@ struct Slots {
 constexpr uint16_t kNoFirst = 0xFFFFu;   // "no member" in the first-member scan
 constexpr int kReach = 8;                // reaching members kept per chunk side
 constexpr int kSparseCand = 12;          // above: a wave tests every position of its chunks
+constexpr int kWitnessScan = 16;         // chunks scanned per side for the filter's witnesses
+constexpr int kCascadeFrom = 2;          // first whole-line round with cascade steps
 
 // LDS carve-up shared by both layouts.
 template <class Val, int K>
@@ -441,25 +444,26 @@ struct SlotArrays {
 };
 
 // One line as seen by the envelope helpers: chunk c of the line lives in slot
-// slot0 + c * gs; occ points at the line's occupancy words.  (LDS offsets are
-// products of small slot indices and strides: 24-bit multiplies suffice.)
-template <class Val, int K, class FOf, int GS>
+// slot0 + c * gs; occ points at the line's occupancy words; mt is the metric
+// (L2Metric or LinfMetric), fof maps a stored value to the candidate's value.
+// (LDS offsets are products of small slot indices and strides: 24-bit
+// multiplies suffice.)
+template <class Val, int K, class FOf, int GS, class Mt = L2Metric>
 struct LineView {
     using Mask = typename MaskOf<K>::T;
+    using Metric = Mt;
+    using F = typename Mt::Val;
     static constexpr int CS = Slots<Val, K>::CS;
     const Val* vals;
     Mask* masks;
     uint64_t* occ;
-    const int* own;   // chunk minima of F as float32 bits, rounded up
+    const int* own;   // chunk minima in the metric's 32-bit form
     int slot0;
     static constexpr int gs = GS;   // slot step between neighbouring chunks
-    double s2l;
+    Mt mt;
     FOf fof;
-    // a lower bound of F over chunk c: its float32 minimum is within one float32
-    // step above the exact one
-    __device__ double fmin_lb(int c) const {
-        return (double)__int_as_float(own[slot(c)]) * (1.0 - 0x1p-22);
-    }
+    // a lower bound of the values of chunk c
+    __device__ F fmin_lb(int c) const { return Mt::lower_from_bits((uint32_t)own[slot(c)]); }
     __device__ int last_nonempty(int lo, int hi) const {
         return occ_last([&](int w) { return occ[w]; }, lo, hi);
     }
@@ -471,8 +475,8 @@ struct LineView {
     __device__ Val val(int pos) const {
         return vals[__umul24((unsigned)slot((unsigned)pos / K), CS) + ((unsigned)pos % K)];
     }
-    __device__ double f(int pos) const { return fof(val(pos)); }
-    __device__ double Y(int pos) const { return f(pos) + s2l * (double)pos * (double)pos; }
+    __device__ F f(int pos) const { return fof(val(pos)); }
+    __device__ F Y(int pos) const { return mt.height(f(pos), pos); }
     __device__ Mask mask(int c) const { return masks[slot(c)]; }
     __device__ void set_mask(int c, Mask m) { masks[slot(c)] = m; }
 };
@@ -537,7 +541,9 @@ __device__ void resolve_line(View& view, SlotArrays<Val, K>& sa, const Val* mych
     const int base = g * K;
     const int n = active ? min(K, L - base) : 0;
     const int G = (L + K - 1) / K;
-    const double s2l = view.s2l;
+    using Mt = typename View::Metric;
+    using F = typename Mt::Val;
+    const Mt& mt = view.mt;
 
     // 1. chunk minimum of F and its first minimiser, then the line's
     //    candidate bound.  The minimiser (+1, 0: none) is published in the mask
@@ -545,8 +551,8 @@ __device__ void resolve_line(View& view, SlotArrays<Val, K>& sa, const Val* mych
     //    F of the chunk's positions stays in registers for the candidate pass
     //    when the chunk is short enough (+inf: no candidate there).
     constexpr bool kKeepF = K <= 32;
-    double Fr[kKeepF ? K : 1];
-    double fmin = __builtin_huge_val();
+    F Fr[kKeepF ? K : 1];
+    F fmin = Mt::kInf;
     int amin = -1;
     bool allzero = true;   // every position is background itself (F = 0)
     if constexpr (kKeepF) {
@@ -554,75 +560,101 @@ __device__ void resolve_line(View& view, SlotArrays<Val, K>& sa, const Val* mych
         for (int t = 0; t < K; ++t) {
             const Val v = mychunk[t];   // positions past the line hold "no background"
             const bool here = valid(v);
-            Fr[t] = here ? fval(v) : __builtin_huge_val();
-            if (Fr[t] != 0.0) allzero = false;
+            Fr[t] = here ? fval(v) : F(Mt::kInf);
+            if (Fr[t] != F(0)) allzero = false;
             if (Fr[t] < fmin) { fmin = Fr[t]; amin = t; }
         }
     } else {
 #pragma unroll 8
         for (int t = 0; t < n; ++t) {
             const Val v = mychunk[t];
-            const double f = fval(v);
-            if (!valid(v) || f != 0.0) allzero = false;
+            const F f = fval(v);
+            if (!valid(v) || f != F(0)) allzero = false;
             if (valid(v) && f < fmin) { fmin = f; amin = t; }
         }
     }
     // A chunk of background positions owns itself: F_q = 0 there, and any other
     // candidate j is s^2 (q - j)^2 > 0 away.
     const bool selfowned = n > 0 && allzero;
-    const float fmin_up = round_up_float(fmin);
-    sa.own[myslot] = __float_as_int(fmin_up);
+    const uint32_t fmin_bits = Mt::min_bits(fmin);
+    sa.own[myslot] = (int)fmin_bits;
     sa.mask[myslot] = (Mask)(amin < 0 ? 0 : base + amin + 1);
     if (g == 0) sa.bound[lslot] = 0u;
     if ((g & 63) == 0) view.occ[g >> 6] = 0ull;
     if (myslot == 0) { sa.flag[0] = 0u; sa.flag[1] = 0u; }
     __syncthreads();
+    // Witnesses for the filter of step 2: on each side, the chunk minimiser
+    // with the smallest value at the chunk's nearer end, found by scanning
+    // chunk minima outward until the distance term alone is no better, over
+    // at most kWitnessScan chunks (lines far from their background -- large
+    // objects -- have their useful witnesses many chunks away, often past
+    // chunks without candidates).  Only on the whole-line route: the per-chunk
+    // route looks
+    // past neighbouring chunks by itself (chunk_owner_marks), and there the
+    // nearest chunk minimisers serve as witnesses.
+    constexpr int kScan = (PerChunk && 2 * kReach + K <= 64) ? 1 : kWitnessScan;
     int aprev = -1, anext = -1;
     if (n > 0) {
-        const double prev = g > 0 ? (double)__int_as_float(sa.own[myslot - gs]) : __builtin_huge_val();
-        const double next = g + 1 < G ? (double)__int_as_float(sa.own[myslot + gs]) : __builtin_huge_val();
-        const float b = round_up_float(chunk_bound((double)fmin_up, prev, next, s2l, K));
-        atomicMax(&sa.bound[lslot], __float_as_uint(b));
-        if (g > 0) aprev = (int)sa.mask[myslot - gs] - 1;
-        if (g + 1 < G) anext = (int)sa.mask[myslot + gs] - 1;
+        const F prev = g > 0 ? Mt::from_bits((uint32_t)sa.own[myslot - gs]) : F(Mt::kInf);
+        const F next = g + 1 < G ? Mt::from_bits((uint32_t)sa.own[myslot + gs]) : F(Mt::kInf);
+        atomicMax(&sa.bound[lslot], mt.bound_bits(Mt::from_bits(fmin_bits), prev, next, K));
+        F best = F(Mt::kInf);
+        for (int c2 = g - 1, sl = myslot - gs; c2 >= 0 && c2 >= g - kScan; --c2, sl -= gs) {
+            if (!(mt.dist(base - (c2 * K + K - 1)) < best)) break;
+            const int k = (int)sa.mask[sl] - 1;
+            if (k < 0) continue;
+            const F v = mt.combine(Mt::from_bits((uint32_t)sa.own[sl]), mt.dist(base - k));
+            if (v < best) { best = v; aprev = k; }
+        }
+        best = F(Mt::kInf);
+        const int e = base + n - 1;
+        for (int c2 = g + 1, sl = myslot + gs; c2 < G && c2 <= g + kScan; ++c2, sl += gs) {
+            if (!(mt.dist(c2 * K - e) < best)) break;
+            const int k = (int)sa.mask[sl] - 1;
+            if (k < 0) continue;
+            const F v = mt.combine(Mt::from_bits((uint32_t)sa.own[sl]), mt.dist(k - e));
+            if (v < best) { best = v; anext = k; }
+        }
     }
     __syncthreads();
-    const double U = (double)__uint_as_float(sa.bound[lslot]);
+    const F U = Mt::from_bits(sa.bound[lslot]);
 
     // 2. local envelope of the chunk's candidates that can still own a
-    //    position: F <= U, and not dominated by the nearest chunk minimisers on
-    //    either side (both are candidates, so a dominated candidate is no
-    //    vertex of the envelope).
+    //    position: F <= U, and not dominated by a chunk minimiser on either
+    //    side (the chunk's own where it lies on that side, else the witness;
+    //    a candidate that two others dominate never attains the minimum, and
+    //    a witness that attains it somewhere passes F <= U there).
     const int acur = amin < 0 ? -1 : base + amin;
-    const double Yprev = aprev >= 0 ? view.Y(aprev) : 0.0;
-    const double Ycur = acur >= 0 ? view.Y(acur) : 0.0;
-    const double Ynext = anext >= 0 ? view.Y(anext) : 0.0;
+    const F Yprev = aprev >= 0 ? view.Y(aprev) : F(0);
+    const F Ycur = acur >= 0 ? view.Y(acur) : F(0);
+    const F Ynext = anext >= 0 ? view.Y(anext) : F(0);
     Mask m;
     if (selfowned) {
         m = n >= (int)(8 * sizeof(Mask)) ? ~Mask(0) : (Mask(1) << n) - Mask(1);   // positions 0 .. n-1
     } else {
         Mask cand = 0;
         // (U may be +inf when a chunk and both its neighbours hold no candidate)
-        auto consider = [&](int t, double Yp, bool here) {
+        auto consider = [&](int t, F Yp, bool here) {
             const int p = base + t;
             const int lo = acur >= 0 && acur < p ? acur : aprev;
-            const double Ylo = acur >= 0 && acur < p ? Ycur : Yprev;
+            const F Ylo = acur >= 0 && acur < p ? Ycur : Yprev;
             const int hi = acur > p ? acur : anext;
-            const double Yhi = acur > p ? Ycur : Ynext;
+            const F Yhi = acur > p ? Ycur : Ynext;
             // (no short-circuit: the test is cheap, and a branch here keeps one
             // lane mask per position alive until the loop ends)
-            const bool gone = (lo >= 0) & (hi >= 0) & dominated(lo, Ylo, p, Yp, hi, Yhi);
+            const bool gone = (lo >= 0) & (hi >= 0) & mt.dominated(lo, Ylo, p, Yp, hi, Yhi);
             cand |= (Mask)(here & !gone) << t;
         };
-        auto height = [&](Val v, int p) { return fval(v) + s2l * (double)p * (double)p; };
+        auto height = [&](Val v, int p) { return mt.height(fval(v), p); };
         if constexpr (kKeepF) {
             // Most positions of a line far from the background fail F <= U, so
             // the dominance test runs only on those that pass -- one at a time
             // unless some lane of the wave has many of them; then every
             // position's height comes from the registers of phase 1.
-            // (F is +inf exactly where a position has no background; U itself
-            // may be +inf, so the test runs against the largest finite value)
-            const double Ufin = U < __DBL_MAX__ ? U : __DBL_MAX__;
+            // (F is the metric's kInf exactly where a position has no
+            // background; U itself may be kInf, so the test runs against the
+            // largest finite value)
+            const F Ufin = U < Mt::kMaxFinite ? U : F(Mt::kMaxFinite);
             Mask pass = 0;
 #pragma unroll
             for (int t = 0; t < K; ++t)
@@ -630,28 +662,28 @@ __device__ void resolve_line(View& view, SlotArrays<Val, K>& sa, const Val* mych
             if (__any(__builtin_popcount(pass) > kSparseCand)) {
 #pragma unroll
                 for (int t = 0; t < K; ++t) {
-                    Fr[t] += s2l * (double)(base + t) * (double)(base + t);   // now Y
+                    Fr[t] = mt.height(Fr[t], base + t);   // now Y
                     consider(t, Fr[t], (pass >> t) & 1);
                 }
                 if constexpr (K <= 16)   // (for longer chunks the registers run out)
-                    m = build_chunk_unrolled<K>(base, cand, Fr, [&](int p) { return view.Y(p); });
+                    m = build_chunk_unrolled<K>(mt, base, cand, Fr, [&](int p) { return view.Y(p); });
                 else
-                    m = build_chunk<Mask>(base, cand, [&](int t) { return mychunk[t]; }, height);
+                    m = build_chunk<Mask>(mt, base, cand, [&](int t) { return mychunk[t]; }, height);
             } else {
                 for (Mask rest = pass; rest; rest &= rest - 1) {
                     const int t = low_bit(rest);
                     consider(t, height(mychunk[t], base + t), true);
                 }
-                m = build_chunk<Mask>(base, cand, [&](int t) { return mychunk[t]; }, height);
+                m = build_chunk<Mask>(mt, base, cand, [&](int t) { return mychunk[t]; }, height);
             }
         } else {
 #pragma unroll 8
             for (int t = 0; t < n; ++t) {
                 const Val v = mychunk[t];
-                const double f = fval(v);
+                const F f = fval(v);
                 consider(t, height(v, base + t), valid(v) && f <= U);
             }
-            m = build_chunk<Mask>(base, cand, [&](int t) { return mychunk[t]; }, height);
+            m = build_chunk<Mask>(mt, base, cand, [&](int t) { return mychunk[t]; }, height);
         }
     }
     sa.mask[myslot] = m;
@@ -682,6 +714,11 @@ __device__ void resolve_line(View& view, SlotArrays<Val, K>& sa, const Val* mych
     //    (boundary_dead: every chunk's first and last members tested against
     //    the nearest members around them, dominated ones removed together,
     //    until a round removes nothing), then marks from every member.
+    //    From round kCascadeFrom on, a round that removed something goes on
+    //    with a back and a front cascade step (back_cascade, front_cascade),
+    //    which empty a chunk down to one member at once where only a far
+    //    neighbour dominates its interior members (large objects); a round
+    //    whose boundary step removes nothing leaves nothing to cascade.
     //    flag[1] was cleared with flag[0]; each round clears the other one.
     for (int r = 0;; ++r) {
         m = sa.mask[myslot];
@@ -696,6 +733,30 @@ __device__ void resolve_line(View& view, SlotArrays<Val, K>& sa, const Val* mych
         }
         __syncthreads();
         if (sa.flag[1 + (r & 1)] == 0u) break;
+        if (r >= kCascadeFrom) {
+            if (m & (m - 1)) {   // (inactive lanes hold no members)
+                const int cn = view.first_nonempty(g + 1, G);
+                if (cn >= 0) {
+                    const Mask m2 = back_cascade<K>(view, g, m, cn * K + low_bit(view.mask(cn)));
+                    if (m2 != m) {
+                        m = m2;
+                        sa.mask[myslot] = m;
+                    }
+                }
+            }
+            __syncthreads();
+            if (m & (m - 1)) {
+                const int cp = view.last_nonempty(0, g);
+                if (cp >= 0) {
+                    const Mask m2 = front_cascade<K>(view, g, m, cp * K + high_bit(view.mask(cp)));
+                    if (m2 != m) {
+                        m = m2;
+                        sa.mask[myslot] = m;
+                    }
+                }
+            }
+            __syncthreads();
+        }
     }
 
     // last member up to each chunk, first member from each chunk on; clear marks
@@ -714,9 +775,9 @@ __device__ void resolve_line(View& view, SlotArrays<Val, K>& sa, const Val* mych
         const int u = g > 0 ? (int)sa.last[myslot - gs] - 1 : -1;
         int v = base + low_bit(mm);
         mm &= mm - 1;
-        double Yv = view.Y(v);
+        F Yv = view.Y(v);
         int st = 0;
-        if (u >= 0) st = first_index_beating(Yv - view.Y(u), 2.0 * s2l * (double)(v - u), L);
+        if (u >= 0) st = mt.cross(u, view.Y(u), v, Yv, L);
         for (;;) {
             int w;
             if (mm) {
@@ -726,10 +787,10 @@ __device__ void resolve_line(View& view, SlotArrays<Val, K>& sa, const Val* mych
                 w = nf == kNoFirst ? -1 : (int)nf;
             }
             int en = L;
-            double Yw = 0.0;
+            F Yw = F(0);
             if (w >= 0) {
                 Yw = view.Y(w);
-                en = first_index_beating(Yw - Yv, 2.0 * s2l * (double)(w - v), L);
+                en = mt.cross(v, Yv, w, Yw, L);
             }
             if (st < en) {   // st < L follows from en <= L
                 const int cs = (unsigned)st / K;
@@ -767,9 +828,12 @@ struct Geo2D {          // rows of B images of H x W; value = axis-0 coordinate
     // (16384^2: 0.90 against 1.07 ms; 4096^2 disks: 0.21 against 0.46 ms).
     static constexpr bool kPerChunk = false;
     static bool per_chunk(int) { return false; }
+    using Metric = L2Metric;
+    static constexpr bool kRootOut = true;   // float32 distances beside the squared ones
     double s2a, s2l;    // squared spacing of axis 0 and along the row
     int W;
     int H;              // rows per image: line ln is row ln % H of image ln / H
+    __device__ Metric metric() const { return L2Metric{s2l}; }
     struct Line { int row; };
     __device__ Line line(int64_t ln) const {
         return Line{ln < 0x100000000ll ? (int)((unsigned)ln % (unsigned)H) : (int)(ln % H)};
@@ -798,9 +862,12 @@ struct Geo3D {          // rows along W of B x D x H x W volumes; value = packed
     static bool per_chunk(int L) { return L > 128; }
     using Val = uint32_t;
     static constexpr Val kNoneVal = kNone32;
+    using Metric = L2Metric;
+    static constexpr bool kRootOut = true;
     double s2a, s2b, s2l;
     int D, H, W;
     bool dh24;          // D * H < 2^24: the flat index needs only 24-bit products
+    __device__ Metric metric() const { return L2Metric{s2l}; }
     struct Line { int d, h; };
     __device__ Line line(int64_t ln) const {
         const unsigned DH = (unsigned)D * (unsigned)H;   // D * H * W < 2^31
@@ -825,6 +892,66 @@ struct Geo3D {          // rows along W of B x D x H x W volumes; value = packed
     }
     __device__ int32_t virt_index() const { return -(H * W); }
     // the same flat index for volumes over 2^31 - 1 elements
+    __device__ int64_t index64(const Line&, uint32_t v, int pos) const {
+        return ((int64_t)(v >> 16) * H + (v & 0xFFFFu)) * (int64_t)W + pos;
+    }
+};
+
+// The chessboard (L-infinity) row passes (TorchMorph's chamfer transforms):
+// the same lines and values, the candidate value g = the L-infinity distance
+// over the earlier axes, f_j(q) = max(g_j, |q - j|), and int32 distances out
+// (through the sqdist output).  The virtual element of an image without
+// background sits one row before its first row, in column 0, as for the
+// Euclidean transform.
+struct GeoLinf2D {
+    using Val = uint16_t;
+    static constexpr Val kNoneVal = kNone16;
+    static constexpr bool kPerChunk = false;
+    static bool per_chunk(int) { return false; }
+    using Metric = LinfMetric;
+    static constexpr bool kRootOut = false;
+    int W;
+    int H;
+    __device__ Metric metric() const { return LinfMetric{}; }
+    struct Line { int row; };
+    __device__ Line line(int64_t ln) const {
+        return Line{ln < 0x100000000ll ? (int)((unsigned)ln % (unsigned)H) : (int)(ln % H)};
+    }
+    __device__ static bool valid(uint16_t v) { return v != kNone16; }
+    __device__ int f(const Line& l, uint16_t v) const { return abs(l.row - (int)v); }
+    __device__ int32_t index(const Line&, uint16_t v, int pos) const {
+        return (int32_t)__umul24((unsigned)v, (unsigned)W) + pos;
+    }
+    __device__ int virt_f(const Line& l) const { return l.row + 1; }
+    __device__ int32_t virt_index() const { return -W; }
+};
+
+struct GeoLinf3D {
+    using Val = uint32_t;
+    static constexpr Val kNoneVal = kNone32;
+    static constexpr bool kPerChunk = true;
+    static bool per_chunk(int L) { return L > 128; }
+    using Metric = LinfMetric;
+    static constexpr bool kRootOut = false;
+    int D, H, W;
+    bool dh24;
+    __device__ Metric metric() const { return LinfMetric{}; }
+    struct Line { int d, h; };
+    __device__ Line line(int64_t ln) const {
+        const unsigned DH = (unsigned)D * (unsigned)H;
+        const unsigned dh = ln < 0x100000000ll ? (unsigned)ln % DH : (unsigned)(ln % DH);
+        return Line{(int)(dh / (unsigned)H), (int)(dh % (unsigned)H)};
+    }
+    __device__ static bool valid(uint32_t v) { return v != kNone32; }
+    __device__ int f(const Line& l, uint32_t v) const {
+        return max(abs(l.d - (int)(v >> 16)), abs(l.h - (int)(v & 0xFFFFu)));
+    }
+    __device__ int32_t index(const Line&, uint32_t v, int pos) const {
+        const unsigned dh = __umul24(v >> 16, (unsigned)H) + (v & 0xFFFFu);
+        return (int32_t)(dh24 ? __umul24(dh, (unsigned)W) : dh * (unsigned)W) + pos;
+    }
+    __device__ int virt_f(const Line& l) const { return max(l.d + 1, l.h); }
+    __device__ int32_t virt_index() const { return -(H * W); }
     __device__ int64_t index64(const Line&, uint32_t v, int pos) const {
         return ((int64_t)(v >> 16) * H + (v & 0xFFFFu)) * (int64_t)W + pos;
     }
@@ -900,8 +1027,9 @@ __global__ __launch_bounds__(1024) void k_envelope_rows(const typename Geo::Val*
 
     const typename Geo::Line gl = geo.line(active ? line : 0);
     auto fof = [&](Val v) { return geo.f(gl, v); };
-    LineView<Val, K, decltype(fof), 1> view{sa.val, sa.mask, sa.occ + (size_t)r * ((Gp + 63) / 64),
-                                            sa.own, slot0, geo.s2l, fof};
+    using Mt = typename Geo::Metric;
+    LineView<Val, K, decltype(fof), 1, Mt> view{sa.val, sa.mask, sa.occ + (size_t)r * ((Gp + 63) / 64),
+                                                sa.own, slot0, geo.metric(), fof};
     uint16_t* mymarks = sa.mark + __umul24(tid, CM);
     resolve_line<K, PerChunk>(view, sa, sa.val + __umul24(tid, CS), mymarks, g, Gp, L, active, tid, r,
                     [](Val v) { return Geo::valid(v); }, fof);
@@ -909,17 +1037,17 @@ __global__ __launch_bounds__(1024) void k_envelope_rows(const typename Geo::Val*
     // 5. outputs.  mk is owner + 1 of position q (0: the line has no
     //    background, the owner is the virtual element).
     const int n = active ? min(K, L - g * K) : 0;
-    const double s2l = geo.s2l;
-    const double fvirt = geo.virt_f(gl);
+    const Mt mt = geo.metric();
+    const typename Mt::Val fvirt = geo.virt_f(gl);
     const int32_t ivirt = geo.virt_index();
     auto one = [&](int q, int mk, int32_t& osq, float& od, Ix& oix) {
         const int ow = mk - 1;
         const int oq = ow < 0 ? 0 : ow;   // the virtual element acts as one at position 0
         const Val vo = view.val(oq);
-        const double dq = (double)(q - oq);
-        const double F = (ow < 0 ? fvirt : fof(vo)) + s2l * dq * dq;
+        const typename Mt::Val F = mt.combine(ow < 0 ? fvirt : fof(vo), mt.dist(q - oq));
         osq = sqdist ? (int32_t)F : 0;
-        od = __builtin_amdgcn_sqrtf((float)F);
+        if constexpr (Geo::kRootOut) od = __builtin_amdgcn_sqrtf((float)F);
+        else od = 0.0f;
         if constexpr (sizeof(Ix) == 8) oix = ow < 0 ? (Ix)ivirt : (Ix)geo.index64(gl, vo, ow);
         else oix = ow < 0 ? ivirt : geo.index(gl, vo, ow);
     };
@@ -1398,6 +1526,21 @@ hipError_t launch_rows_3d(const uint32_t* c01, int B, int D, int H, int W, doubl
     return launch_rows_any<Geo3D, 16>(c01, W, nlines, geo, sqdist, dist, indices, s, tm, "envelope_rows_3d");
 }
 
+// Chessboard row passes on the envelope kernel (lines that fit its LDS).
+hipError_t launch_rows_linf_2d(const uint16_t* c0, int B, int H, int W, int32_t* dist,
+                               int32_t* indices, hipStream_t s, KernelTimer* tm) {
+    const GeoLinf2D geo{W, H};
+    return launch_rows_any<GeoLinf2D, 32>(c0, W, (int64_t)B * H, geo, dist, (float*)nullptr, indices, s, tm,
+                                          "chessboard_rows");
+}
+
+hipError_t launch_rows_linf_3d(const uint32_t* c01, int B, int D, int H, int W, int32_t* dist,
+                               int32_t* indices, hipStream_t s, KernelTimer* tm) {
+    const GeoLinf3D geo{D, H, W, (int64_t)D * H < (1 << 24)};
+    return launch_rows_any<GeoLinf3D, 16>(c01, W, (int64_t)B * D * H, geo, dist, (float*)nullptr, indices, s,
+                                          tm, "chessboard_rows");
+}
+
 // --------------------------------------------------------------------------
 // Column layout: the middle axis of a volume, lines strided by W.  A
 // work-group takes TW neighbouring lines (lane x = line) and Gp chunk groups
@@ -1435,10 +1578,28 @@ size_t cols_lds_bytes(int H) {
     return (p.TW < 1 || p.Gp * p.TW > 1024 || p.lds > 160 * 1024) ? 0 : p.lds;
 }
 
-template <int K, int TW>
+// Candidate values of the middle-axis pass from the axis-0 coordinate v at
+// plane d: the Euclidean one (s2a (d - v)^2, lines of squared spacing s2l) and
+// the chessboard one (|d - v|).
+struct ColL2 {
+    using Metric = L2Metric;
+    double s2a, s2l;
+    __device__ Metric metric() const { return L2Metric{s2l}; }
+    __device__ double f(int d, uint16_t v) const {
+        const double t = (double)(d - (int)v);
+        return s2a * t * t;
+    }
+};
+struct ColLinf {
+    using Metric = LinfMetric;
+    __device__ Metric metric() const { return LinfMetric{}; }
+    __device__ int f(int d, uint16_t v) const { return abs(d - (int)v); }
+};
+
+template <int K, int TW, class CG>
 __global__ __launch_bounds__(1024) void k_envelope_cols(const uint16_t* __restrict__ c0,
                                                         uint32_t* __restrict__ out, int D, int H,
-                                                        int W, int Gp, double s2a, double s2l) {
+                                                        int W, int Gp, CG cg) {
     constexpr int CS = Slots<uint16_t, K>::CS;
     constexpr int CM = Slots<uint16_t, K>::CM;
     extern __shared__ __align__(16) unsigned char smem[];
@@ -1484,11 +1645,9 @@ __global__ __launch_bounds__(1024) void k_envelope_cols(const uint16_t* __restri
         for (int t = 0; t < K; t += 2) *reinterpret_cast<uint32_t*>(mine + t) = kNone16 | (kNone16 << 16);
     }
 
-    auto fof = [&](uint16_t v) {
-        const double t = (double)(d - (int)v);
-        return s2a * t * t;
-    };
-    LineView<uint16_t, K, decltype(fof), TW> view{sa.val, sa.mask, sa.occ + x, sa.own, x, s2l, fof};
+    auto fof = [&](uint16_t v) { return cg.f(d, v); };
+    LineView<uint16_t, K, decltype(fof), TW, typename CG::Metric> view{sa.val, sa.mask, sa.occ + x, sa.own,
+                                                                       x, cg.metric(), fof};
     uint16_t* mymarks = sa.mark + __umul24(tid, CM);
     resolve_line<K, true>(view, sa, mine, mymarks, g, Gp, H, active, tid, x,
                     [](uint16_t v) { return v != kNone16; }, fof);
@@ -1506,49 +1665,60 @@ __global__ __launch_bounds__(1024) void k_envelope_cols(const uint16_t* __restri
     }
 }
 
-template <int K, int TW>
-static hipError_t launch_cols_t(const uint16_t* c0, int B, int D, int H, int W, double s2_0,
-                                double s2_1, uint32_t* c01, const ColPlan& p, hipStream_t s,
-                                KernelTimer* tm) {
+template <int K, int TW, class CG>
+static hipError_t launch_cols_t(const uint16_t* c0, int B, int D, int H, int W, const CG& cg,
+                                uint32_t* c01, const ColPlan& p, hipStream_t s, KernelTimer* tm,
+                                const char* kname) {
     static unsigned long long lds_done = 0;
-    hipError_t le = large_lds_once((const void*)k_envelope_cols<K, TW>, &lds_done);
+    hipError_t le = large_lds_once((const void*)k_envelope_cols<K, TW, CG>, &lds_done);
     if (le != hipSuccess) return le;
     const int tiles = (W + TW - 1) / TW;
     const int64_t nblocks = (int64_t)B * D * tiles;
-    EDT_LAUNCH(tm, "envelope_cols_3d", s,
-               hipLaunchKernelGGL((k_envelope_cols<K, TW>), dim3((unsigned)nblocks), dim3(TW, p.Gp),
-                                  p.lds, s, c0, c01, D, H, W, p.Gp, s2_0, s2_1));
+    EDT_LAUNCH(tm, kname, s,
+               hipLaunchKernelGGL((k_envelope_cols<K, TW, CG>), dim3((unsigned)nblocks), dim3(TW, p.Gp),
+                                  p.lds, s, c0, c01, D, H, W, p.Gp, cg));
     return hipSuccess;
 }
 
-hipError_t launch_cols_3d(const uint16_t* c0, int B, int D, int H, int W, double s2_0,
-                          double s2_1, uint32_t* c01, hipStream_t s, KernelTimer* tm) {
+template <class CG>
+static hipError_t launch_cols_any(const uint16_t* c0, int B, int D, int H, int W, const CG& cg,
+                                  uint32_t* c01, hipStream_t s, KernelTimer* tm, const char* kname) {
     const ColPlan p = plan_cols(H);
     if (p.K == 64) {
         switch (p.TW) {
-            case 32: return launch_cols_t<64, 32>(c0, B, D, H, W, s2_0, s2_1, c01, p, s, tm);
-            case 16: return launch_cols_t<64, 16>(c0, B, D, H, W, s2_0, s2_1, c01, p, s, tm);
-            case 8: return launch_cols_t<64, 8>(c0, B, D, H, W, s2_0, s2_1, c01, p, s, tm);
-            case 4: return launch_cols_t<64, 4>(c0, B, D, H, W, s2_0, s2_1, c01, p, s, tm);
-            case 2: return launch_cols_t<64, 2>(c0, B, D, H, W, s2_0, s2_1, c01, p, s, tm);
-            case 1: return launch_cols_t<64, 1>(c0, B, D, H, W, s2_0, s2_1, c01, p, s, tm);
+            case 32: return launch_cols_t<64, 32>(c0, B, D, H, W, cg, c01, p, s, tm, kname);
+            case 16: return launch_cols_t<64, 16>(c0, B, D, H, W, cg, c01, p, s, tm, kname);
+            case 8: return launch_cols_t<64, 8>(c0, B, D, H, W, cg, c01, p, s, tm, kname);
+            case 4: return launch_cols_t<64, 4>(c0, B, D, H, W, cg, c01, p, s, tm, kname);
+            case 2: return launch_cols_t<64, 2>(c0, B, D, H, W, cg, c01, p, s, tm, kname);
+            case 1: return launch_cols_t<64, 1>(c0, B, D, H, W, cg, c01, p, s, tm, kname);
             default: return hipErrorInvalidValue;
         }
     }
     if (p.K == 16) {
         switch (p.TW) {
-            case 8: return launch_cols_t<16, 8>(c0, B, D, H, W, s2_0, s2_1, c01, p, s, tm);
-            case 16: return launch_cols_t<16, 16>(c0, B, D, H, W, s2_0, s2_1, c01, p, s, tm);
-            case 32: return launch_cols_t<16, 32>(c0, B, D, H, W, s2_0, s2_1, c01, p, s, tm);
-            default: return launch_cols_t<16, 64>(c0, B, D, H, W, s2_0, s2_1, c01, p, s, tm);
+            case 8: return launch_cols_t<16, 8>(c0, B, D, H, W, cg, c01, p, s, tm, kname);
+            case 16: return launch_cols_t<16, 16>(c0, B, D, H, W, cg, c01, p, s, tm, kname);
+            case 32: return launch_cols_t<16, 32>(c0, B, D, H, W, cg, c01, p, s, tm, kname);
+            default: return launch_cols_t<16, 64>(c0, B, D, H, W, cg, c01, p, s, tm, kname);
         }
     }
     switch (p.TW) {
-        case 8: return launch_cols_t<32, 8>(c0, B, D, H, W, s2_0, s2_1, c01, p, s, tm);
-        case 16: return launch_cols_t<32, 16>(c0, B, D, H, W, s2_0, s2_1, c01, p, s, tm);
-        case 32: return launch_cols_t<32, 32>(c0, B, D, H, W, s2_0, s2_1, c01, p, s, tm);
-        default: return launch_cols_t<32, 64>(c0, B, D, H, W, s2_0, s2_1, c01, p, s, tm);
+        case 8: return launch_cols_t<32, 8>(c0, B, D, H, W, cg, c01, p, s, tm, kname);
+        case 16: return launch_cols_t<32, 16>(c0, B, D, H, W, cg, c01, p, s, tm, kname);
+        case 32: return launch_cols_t<32, 32>(c0, B, D, H, W, cg, c01, p, s, tm, kname);
+        default: return launch_cols_t<32, 64>(c0, B, D, H, W, cg, c01, p, s, tm, kname);
     }
+}
+
+hipError_t launch_cols_3d(const uint16_t* c0, int B, int D, int H, int W, double s2_0,
+                          double s2_1, uint32_t* c01, hipStream_t s, KernelTimer* tm) {
+    return launch_cols_any(c0, B, D, H, W, ColL2{s2_0, s2_1}, c01, s, tm, "envelope_cols_3d");
+}
+
+hipError_t launch_cols_linf_3d(const uint16_t* c0, int B, int D, int H, int W, uint32_t* c01,
+                               hipStream_t s, KernelTimer* tm) {
+    return launch_cols_any(c0, B, D, H, W, ColLinf{}, c01, s, tm, "chessboard_cols");
 }
 
 }  // namespace edt

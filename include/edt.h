@@ -244,12 +244,9 @@ edt_status edt3d_taxicab_u8_batched(const uint8_t* mask, int32_t B, int32_t D, i
    max_k |p_k - b_k|, as int32, and optionally the flat index of such an
    element (ties: any).  Layouts, the virtual element (distance
    max(p0 + 1, p1, ...)), buffers, workspace, limits and errors exactly as for
-   the taxicab entry points above.  Lines of up to 4096 elements cost
-   amortised constant work per element (a range-minimum structure in LDS);
-   along longer lines each element searches outward, its work growing with
-   its own distance, except on lines with at most 32 sources (scanned as a
-   list) and where per-bucket lists of the nearby sources with small axis-0
-   distance settle it. */
+   the taxicab entry points above.  Computed as the EDT is, one lower
+   envelope per line and axis (the functions max(g_j, |q - j|) change places
+   once, as parabolas do), with exact integer crossings. */
 edt_status edt2d_chessboard_u8_batched(const uint8_t* mask, int32_t B, int32_t H, int32_t W,
                                        int32_t* dist, int32_t* indices,
                                        void* workspace, size_t workspace_bytes, hipStream_t stream);

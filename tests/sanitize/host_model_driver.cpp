@@ -2,11 +2,13 @@
 // (tests/host_model/host_model.cpp) under AddressSanitizer and
 // UndefinedBehaviorSanitizer (test-only; built by tests/test_sanitize.py).
 // Random lines of candidate values, every chunk layout and reach the kernels
-// use: each owner must attain the minimum over all candidates.  Exit status 0
-// when every line agrees.
+// use, under both metrics (squared Euclidean and chessboard): each owner must
+// attain the minimum over all candidates.  Exit status 0 when every line
+// agrees.
 #include <math.h>
 #include <stdint.h>
 #include <stdio.h>
+#include <stdlib.h>
 
 #include <vector>
 
@@ -46,6 +48,41 @@ int main() {
                         const int o = own[q];
                         const double v = o < 0 ? INFINITY : s2l * (double)(q - o) * (q - o) + f[o];
                         if (v != best) { ++bad; break; }
+                    }
+                    ++lines;
+                }
+            }
+        }
+    }
+    // the chessboard metric: g[j] < 0 is no source; owners must attain
+    // min_j max(g_j, |q - j|), and the value the model forms must equal it
+    for (int L : Ls) {
+        for (int K : Ks) {
+            for (int reach : reaches) {
+                for (int rep = 0; rep < 3; ++rep) {
+                    std::vector<int32_t> g(L);
+                    for (int i = 0; i < L; ++i) {
+                        const uint64_t r = next_u64();
+                        g[i] = (r % 5 == 0) ? -1 : (int32_t)((r >> 8) % (uint64_t)(2 * L + 1));
+                    }
+                    if (rep == 1) for (int i = 0; i < L; ++i) g[i] = (int32_t)((next_u64() >> 8) % 4);
+                    if (rep == 2) for (int i = 0; i < L; ++i) g[i] = 7;   // flat bottoms everywhere
+                    const int G = (L + K - 1) / K + (rep == 1 ? 3 : 0);
+                    std::vector<int32_t> own(L), val(L);
+                    if (model_linf_envelope_lines(g.data(), 1, L, K, G, reach, own.data(), val.data()) != 0) {
+                        ++bad;
+                        continue;
+                    }
+                    for (int q = 0; q < L; ++q) {
+                        int best = -1;
+                        for (int j = 0; j < L; ++j) {
+                            if (g[j] < 0) continue;
+                            const int v = g[j] > abs(q - j) ? g[j] : abs(q - j);
+                            if (best < 0 || v < best) best = v;
+                        }
+                        const int o = own[q];
+                        const int v = o < 0 ? -1 : (g[o] > abs(q - o) ? g[o] : abs(q - o));
+                        if (v != best || val[q] != best || (o >= 0 && g[o] < 0)) { ++bad; break; }
                     }
                     ++lines;
                 }

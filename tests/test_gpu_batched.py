@@ -671,7 +671,7 @@ def test_chessboard(torch_dev):
                     assert (mm.reshape(-1)[i1.reshape(-1)] == 0).all()
 
 
-@pytest.mark.parametrize("name", ["b2d", "c5", "c3", "c2b"])
+@pytest.mark.parametrize("name", ["b2d", "c5", "c3", "c2b", "c2a"])
 def test_chessboard_full_size(torch_dev, name):
     """Chessboard transform at the full sizes that bench.py --chessboard times:
     over the whole output, every index names a background element of its
@@ -710,34 +710,12 @@ def test_chessboard_full_size(torch_dev, name):
     _brute_cross_check(torch, m, name, r.dist, "chessboard")
 
 
-def _bucket_rows_2d(mask, bt=128, bc=16, lst=32):
-    """For each row of a 2-D mask: whether the chessboard row pass takes its
-    bucket lists (more than `lst` sources on the row, at most bc / 2 per
-    bucket of `bt` positions on average with g <= bt, g being the distance
-    along axis 0 to the nearest background of the column), and whether some
-    bucket then holds more than `bc` such sources (a full bucket)."""
-    H, W = mask.shape
-    g = np.full((H, W), np.iinfo(np.int64).max, np.int64)
-    rows = np.arange(H)[:, None]
-    for c in range(W):
-        b = np.flatnonzero(mask[:, c] == 0)
-        if len(b):
-            g[:, c] = np.abs(rows - b[None, :]).min(1)
-    valid = g != np.iinfo(np.int64).max
-    small = valid & (g <= bt)
-    nbk = (W + bt - 1) // bt
-    bucketed = (valid.sum(1) > lst) & (small.sum(1) <= (bc // 2) * nbk)
-    per_bucket = np.add.reduceat(small, np.arange(0, W, bt), axis=1)
-    full = bucketed & (per_bucket > bc).any(1)
-    return bucketed, full
-
-
 def test_chessboard_large_values(torch_dev):
-    """The range-minimum chessboard kernels with large axis-0 distances (g up
-    to 40000 in the keys g << 16 | j, wide bisection bounds): a tall image
-    with a few background pixels, and a volume whose middle axis carries
-    them; full output against the device brute force, sampled points and
-    the corners against the oracle."""
+    """The chessboard envelope kernels with large axis-0 distances (g up to
+    40000; integer crossings far from the line): a tall image with a few
+    background pixels, and a volume whose middle axis carries them; full
+    output against the device brute force, sampled points and the corners
+    against the oracle."""
     torch, dev = torch_dev
     from exact_euclidean_distance_amd import chessboard, edt_brute
     rng = np.random.default_rng([42, 5017])
@@ -762,57 +740,49 @@ def test_chessboard_large_values(torch_dev):
             assert (dd.reshape(-1)[pts] == oracle.chessboard_at(a, pts)).all()
 
 
-def test_chessboard_bucket_lists(torch_dev):
-    """The chessboard row pass on rows longer than 4096 (the outward-search
-    kernel; shorter rows take the range-minimum kernel): rows that take the
-    per-bucket lists of sources with g <= 128 (many sources, most of them far
-    along axis 0), including a bucket with more than 16 such sources (the
-    outward search takes over there) and positions whose best in-bucket value
-    exceeds 128 (likewise).  The whole output is compared with the device
-    brute force (itself checked against the oracle's), and sampled positions
-    of the bucketed rows with the oracle's definition."""
+def test_chessboard_long_rows_and_large_objects(torch_dev):
+    """The chessboard envelope kernels where whole-line rounds are long:
+    rows over 4096 with many sources far along axis 0 (dense candidates with
+    large g) and a few near ones; an image covered by large disks (interior
+    candidates are dominated only by sources many chunks away: witnesses far
+    along the line, cascade steps); the same in the rows and columns of a
+    volume.  The whole output against the device brute force (itself checked
+    against the oracle's), sampled positions against the oracle's
+    definition."""
     torch, dev = torch_dev
     from exact_euclidean_distance_amd import chessboard, edt_brute
     rng = np.random.default_rng([42, 5016])
-    for W in (4160, 4397):   # (4397: a ragged last bucket)
+    cases = []
+    for W in (4160, 4397):   # (4397: a ragged last chunk)
         m = np.ones((200, W), np.uint8)
-        far = rng.random(W) < 0.4
-        m[0, far] = 0                               # sources at g = r on every row
+        m[0, rng.random(W) < 0.4] = 0                  # sources at g = r on every row
         pts = rng.integers(0, [200, W], size=(W // 160, 2))
-        m[pts[:, 0], pts[:, 1]] = 0                 # a few near sources (g <= 128)
-        m[150, 520:540] = 0                         # 20 near sources in one bucket: a full bucket
-        bucketed, full = _bucket_rows_2d(m)
-        assert bucketed.sum() > 50 and full.any(), "the mask must drive the bucket lists"
-        _say(f"chessboard bucket lists 200 x {W}: {bucketed.sum()} bucketed rows, "
-             f"{full.sum()} with a full bucket")
-        t = torch.from_numpy(m).to(dev)
+        m[pts[:, 0], pts[:, 1]] = 0                    # a few near sources
+        m[150, 520:540] = 0
+        cases.append((f"long rows 200 x {W}", m, False))
+    yy, xx = np.mgrid[0:900, 0:1700]
+    disks = np.zeros((900, 1700), bool)
+    for cy, cx, r in ((450, 600, 420), (300, 1350, 260), (700, 1250, 180), (120, 150, 90)):
+        disks |= (yy - cy) ** 2 + (xx - cx) ** 2 <= r * r
+    m = disks.astype(np.uint8)                         # foreground disks, background elsewhere
+    m[rng.integers(0, 900, 40), rng.integers(0, 1700, 40)] = 0
+    cases.append(("large disks 900 x 1700", m, False))
+    zz, yv, xv = np.mgrid[0:3, 0:240, 0:1200]
+    v = ((yv - 120) ** 2 + (xv - 600) ** 2 <= 110 ** 2 + (zz * 40) ** 2).astype(np.uint8)[None]
+    v[0, 1, :, 0:300] = 1                              # a long run of columns without background
+    cases.append(("volume 1 x 3 x 240 x 1200", v, True))
+    for name, arr, batched in cases:
+        _say(f"chessboard {name}")
+        t = torch.from_numpy(arr).to(dev)
         r = chessboard(t, return_indices=True)
-        ref = edt_brute(t, metric="chessboard").dist
+        ref = edt_brute(t, metric="chessboard", batched=batched).dist
         torch.cuda.synchronize()
-        assert torch.equal(r.dist, ref), "chessboard distance mismatch"
+        assert torch.equal(r.dist, ref), f"chessboard distance mismatch ({name})"
         d = r.dist.cpu().numpy()
         ix = r.indices.cpu().numpy()
-        assert (oracle.chessboard_to(ix, m.shape) == d).all()
-        assert (m.reshape(-1)[ix.reshape(-1)] == 0).all()
-        rows = np.flatnonzero(bucketed)
-        sel = rng.choice(rows, 8, replace=False)
-        pts = (sel[:, None] * W + rng.integers(0, W, (8, 40))).reshape(-1)
-        pts = np.concatenate([pts, [150 * W + 530, 150 * W + 525]])   # the full bucket
-        assert (d.reshape(-1)[pts] == oracle.chessboard_at(m, pts)).all(), "sampled oracle mismatch"
-        # positions whose best value exceeds 128: the fallback search decides there
-        assert (d[bucketed] > 128).any()
-    # rows of 4160 in a volume: g comes from the middle-axis pass
-    v = np.ones((1, 2, 200, 4160), np.uint8)
-    v[0, 0, 0, rng.random(4160) < 0.4] = 0
-    pts = rng.integers(0, [2, 200, 4160], size=(30, 3))
-    v[0, pts[:, 0], pts[:, 1], pts[:, 2]] = 0
-    v[0, 1, 150, 700:720] = 0
-    _say("chessboard bucket lists 1 x 2 x 200 x 4160")
-    t = torch.from_numpy(v).to(dev)
-    r = chessboard(t, return_indices=True)
-    ref = edt_brute(t, metric="chessboard", batched=True).dist
-    torch.cuda.synchronize()
-    assert torch.equal(r.dist, ref), "chessboard distance mismatch (volume rows)"
-    assert (oracle.chessboard_to(r.indices.cpu().numpy()[0], v.shape[1:]) == r.dist.cpu().numpy()[0]).all()
-    pts = rng.integers(0, v[0].size, 200)
-    assert (r.dist.cpu().numpy()[0].reshape(-1)[pts] == oracle.chessboard_at(v[0], pts)).all()
+        imgs = [(arr, d, ix)] if not batched else list(zip(arr, d, ix))
+        for a, dd, ii in imgs:
+            assert (oracle.chessboard_to(ii, a.shape) == dd).all()
+            assert (a.reshape(-1)[ii.reshape(-1)] == 0).all()
+            pts = np.concatenate([rng.integers(0, a.size, 200), [0, a.size - 1]])
+            assert (dd.reshape(-1)[pts] == oracle.chessboard_at(a, pts)).all(), f"sampled oracle mismatch ({name})"

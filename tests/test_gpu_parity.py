@@ -261,6 +261,38 @@ def test_background_runs(torch_dev):
         check(torch_dev, mask, samp)
 
 
+def test_large_objects(torch_dev):
+    """Large foreground objects, where whole-line rounds are long: interior
+    candidates are dominated only by members many chunks away (the filter's
+    far witnesses, the rounds' cascade steps), with runs of columns without
+    background.  A 2-D image of large disks, a volume holding a wide
+    cylinder (rows of 1200: whole-line rounds; middle axis of 600: chunks of
+    64, always whole-line rounds) and a volume whose rows are 128 long
+    (whole-line rounds in the 3-D row pass)."""
+    rng = np.random.default_rng([42, 3010])
+    yy, xx = np.mgrid[0:900, 0:1700]
+    disks = np.zeros((900, 1700), bool)
+    for cy, cx, r in ((450, 600, 420), (300, 1350, 260), (700, 1250, 180), (120, 150, 90)):
+        disks |= (yy - cy) ** 2 + (xx - cx) ** 2 <= r * r
+    m = disks.astype(np.uint8)
+    m[rng.integers(0, 900, 40), rng.integers(0, 1700, 40)] = 0
+    for samp in (None, (2.5, 1.0), (1.0, 0.75)):
+        _say(f"large disks 900 x 1700 sampling {samp}")
+        check(torch_dev, m, samp)
+    zz, yv, xv = np.mgrid[0:3, 0:600, 0:1200]
+    v = ((yv - 300) ** 2 + (xv - 600) ** 2 <= 280 ** 2 - (zz * 60) ** 2).astype(np.uint8)[None]
+    v[0, 1, :, 0:300] = 1                                # columns without background
+    for samp in (None, (2.5, 1.0, 1.0)):
+        _say(f"cylinder 1 x 3 x 600 x 1200 sampling {samp}")
+        check(torch_dev, v, samp)
+    zz, yv, xv = np.mgrid[0:40, 0:64, 0:128]
+    w = ((zz - 20) ** 2 + (yv - 32) ** 2 + (xv - 64) ** 2 <= 60 ** 2).astype(np.uint8)[None]
+    w[0, 0, 0, 0] = 0
+    for samp in (None, (1.0, 2.0, 0.5)):
+        _say(f"ball 1 x 40 x 64 x 128 sampling {samp}")
+        check(torch_dev, w, samp)
+
+
 @pytest.mark.parametrize("name", ["c1", "c3", "c5"])
 def test_repeat_is_bit_identical(torch_dev, name):
     """Two calls on the same input, the workspace poisoned differently each

@@ -156,3 +156,124 @@ def test_model_transform_matches_oracle(model, K, reach):
         ref, _ = oracle.edt(mask, samp, False)
         got = _model_edt(model, mask, samp, K, reach)
         np.testing.assert_array_equal(got, ref, err_msg=f"shape {mask.shape} sampling {samp}")
+
+
+# ---------------------------------------------------------------------------
+# The same machinery under the chessboard metric, f_j(q) = max(g_j, |q - j|)
+# (TorchMorph's chamfer transforms, read as the L-infinity metric): the line
+# step against its definition, and composed transforms against the oracle's
+# brute force.
+# ---------------------------------------------------------------------------
+
+@pytest.fixture(scope="module")
+def linf_model(tmp_path_factory):
+    out = str(tmp_path_factory.mktemp("host_model_linf") / "host_model.so")
+    subprocess.run(["g++", "-O2", "-std=c++17", "-fPIC", "-shared", "-o", out, SRC], check=True)
+    lib = ctypes.CDLL(out)
+    lib.model_linf_envelope_lines.restype = ctypes.c_int
+    lib.model_linf_envelope_lines.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+                                              ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                              ctypes.c_void_p, ctypes.c_void_p]
+
+    def run(gb, K, G, reach=8):
+        gb = np.ascontiguousarray(gb, np.int32)
+        nl, L = gb.shape
+        own = np.empty((nl, L), np.int32)
+        val = np.empty((nl, L), np.int32)
+        rc = lib.model_linf_envelope_lines(gb.ctypes.data, nl, L, K, G, reach, own.ctypes.data,
+                                           val.ctypes.data)
+        assert rc == 0
+        # the value the metric forms for the owner (the kernels' output step)
+        np.testing.assert_array_equal(val, _linf_value_at(gb, own))
+        return own
+
+    return run
+
+
+def _linf_brute_lines(gb):
+    """min_j max(g_j, |q - j|) over the sources (g >= 0) of every line (-1: none)."""
+    L = gb.shape[1]
+    q = np.arange(L)
+    d = np.abs(q[:, None] - q[None, :])                       # [q][j]
+    v = np.maximum(gb[:, None, :].astype(np.int64), d[None])  # [line][q][j]
+    v = np.where(gb[:, None, :] >= 0, v, np.iinfo(np.int64).max)
+    out = v.min(-1)
+    return np.where(out == np.iinfo(np.int64).max, -1, out)
+
+
+def _linf_value_at(gb, own):
+    q = np.arange(gb.shape[1])
+    sel = np.take_along_axis(gb, np.maximum(own, 0), 1).astype(np.int64)
+    v = np.maximum(sel, np.abs(q[None, :] - own))
+    return np.where(own < 0, -1, v)
+
+
+@pytest.mark.parametrize("L", [1, 2, 31, 32, 33, 64, 100, 257, 1000, 2048])
+def test_linf_lines_match_definition(linf_model, L):
+    rng = np.random.default_rng([42, 2002, L])
+    nl = 24
+    gb = np.empty((nl, L), np.int64)
+    for i in range(nl):
+        kind = i % 7
+        if kind == 0:      # column distances, some columns without background
+            gb[i] = rng.integers(0, 2 * L + 1, L)
+            gb[i][rng.random(L) < 0.3] = -1
+        elif kind == 1:    # all equal: flat bottoms everywhere, every tie
+            gb[i] = rng.integers(0, 50)
+        elif kind == 2:    # a single source
+            gb[i] = -1
+            gb[i][rng.integers(0, L)] = rng.integers(0, 100)
+        elif kind == 3:    # no source
+            gb[i] = -1
+        elif kind == 4:    # deep dip at the end: long removal cascades at junctions
+            gb[i] = L
+            gb[i][-1] = 0
+        elif kind == 5:    # random small values (many ties)
+            gb[i] = rng.integers(0, 4, L)
+        else:              # large values near the uint16 limit, sparse
+            gb[i] = np.where(rng.random(L) < 0.05, rng.integers(60000, 65535, L), -1)
+    ref = _linf_brute_lines(gb)
+    for (K, G), reach in itertools.product(_layouts(L), (8, 1, 0)):
+        own = linf_model(gb, K, G, reach)
+        got = _linf_value_at(gb, own)
+        np.testing.assert_array_equal(got, ref, err_msg=f"L={L} K={K} G={G} reach={reach}")
+        ok = own >= 0
+        assert (ok == (gb >= 0).any(1)[:, None]).all()
+        assert (np.take_along_axis(gb, np.maximum(own, 0), 1)[ok] >= 0).all()
+
+
+def _model_chessboard(linf_model, mask, K, reach=8):
+    """Chessboard transform composed from the model: axis-0 nearest, then one
+    envelope pass per further axis (values are L-infinity distances so far)."""
+    g = _axis0_nearest(mask)
+    i = np.arange(mask.shape[0]).reshape((mask.shape[0],) + (1,) * (mask.ndim - 1))
+    D = np.where(g >= 0, np.abs(i - g), -1)
+    for ax in range(1, mask.ndim):
+        Dm = np.moveaxis(D, ax, -1)
+        shp = Dm.shape
+        gb = Dm.reshape(-1, shp[-1])
+        own = linf_model(gb, K, -(-shp[-1] // K), reach)
+        D = np.moveaxis(_linf_value_at(gb, own).reshape(shp), -1, ax)
+    return D
+
+
+@pytest.mark.parametrize("K", [8, 16, 32, 64])
+@pytest.mark.parametrize("reach", [8, 0])
+def test_linf_model_transform_matches_oracle(linf_model, K, reach):
+    rng = np.random.default_rng([42, 2003, K])
+    cases = []
+    for t in range(12):
+        shape = tuple(int(x) for x in rng.integers(1, 120, 2))
+        cases.append((rng.random(shape) >= [1e-3, 0.01, 0.2, 0.9][t % 4]).astype(np.uint8))
+    single = np.ones((90, 170), np.uint8)
+    single[3, 160] = 0
+    cases.append(single)
+    for t in range(6):
+        shape = tuple(int(x) for x in rng.integers(1, 30, 3))
+        cases.append((rng.random(shape) >= [0.001, 0.05, 0.5][t % 3]).astype(np.uint8))
+    for mask in cases:
+        if not (mask == 0).any():
+            mask.reshape(-1)[0] = 0
+        ref, _ = oracle.chessboard_brute(mask)
+        got = _model_chessboard(linf_model, mask, K, reach)
+        np.testing.assert_array_equal(got, ref, err_msg=f"shape {mask.shape}")
