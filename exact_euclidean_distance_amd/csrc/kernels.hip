@@ -1646,8 +1646,9 @@ __global__ __launch_bounds__(1024) void k_envelope_cols(const uint16_t* __restri
     }
 
     auto fof = [&](uint16_t v) { return cg.f(d, v); };
-    LineView<uint16_t, K, decltype(fof), TW, typename CG::Metric> view{sa.val, sa.mask, sa.occ + x, sa.own,
-                                                                       x, cg.metric(), fof};
+    // (line x's occupancy words follow those of lines 0 .. x - 1)
+    LineView<uint16_t, K, decltype(fof), TW, typename CG::Metric> view{
+        sa.val, sa.mask, sa.occ + (size_t)x * ((Gp + 63) / 64), sa.own, x, cg.metric(), fof};
     uint16_t* mymarks = sa.mark + __umul24(tid, CM);
     resolve_line<K, true>(view, sa, mine, mymarks, g, Gp, H, active, tid, x,
                     [](uint16_t v) { return v != kNone16; }, fof);

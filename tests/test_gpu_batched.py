@@ -519,8 +519,10 @@ def test_long_middle_axis(torch_dev):
     torch, dev = torch_dev
     from exact_euclidean_distance_amd import edt3d
     rng = np.random.default_rng([42, 5011])
-    for shape, p in (((1, 3, 2048, 40), 0.002), ((2, 2, 4100, 17), 0.001), ((1, 2, 16384, 6), 0.0005),
-                     ((1, 1, 32768, 3), 0.0003)):
+    # (middle axes over 4096 with several lines per tile: each line keeps two
+    # or more occupancy words, 4100 -> 4 lines per tile, 8200 -> 2)
+    for shape, p in (((1, 3, 2048, 40), 0.002), ((2, 2, 4100, 17), 0.001), ((1, 3, 8200, 9), 0.001),
+                     ((1, 2, 16384, 6), 0.0005), ((1, 1, 32768, 3), 0.0003)):
         vols = (rng.random(shape) >= p).astype(np.uint8)
         vols[:, 0, 0, 0] = 0
         for samp in (None, (2.5, 1.0, 1.0)):
@@ -646,7 +648,8 @@ def test_chessboard(torch_dev):
     rng = np.random.default_rng([42, 5014])
     cases = [(1, 1), (1, 70), (37, 1), (64, 64), (4, 300), (33, 517), (3, 1100), (5, 20000),
              (3, 40, 70), (2, 13, 17, 30), (3, 9, 40, 64), (2, 3, 5, 400), (1, 5, 1100, 33),
-             (1, 2, 3, 2000), (1, 3, 700, 9), (2, 1, 4100, 3), (2, 1, 32768, 2)]
+             (1, 2, 3, 2000), (1, 3, 700, 9), (2, 1, 4100, 3), (1, 3, 4100, 13), (1, 2, 8200, 7),
+             (2, 1, 32768, 2)]
     for shape in cases:
         for p in ((0.003, 0.1, 0.6) if np.prod(shape) <= 20000 else (0.002,)):
             m = (rng.random(shape) >= p).astype(np.uint8)
