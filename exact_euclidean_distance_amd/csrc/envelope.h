@@ -292,7 +292,8 @@ EDT_HD inline int first_index_beating(double A, double B, int cap) {
 // which no member is beaten by its two neighbours is the lower envelope, and a
 // candidate that loses to a nearer one at a chunk's first position loses on the
 // whole chunk.  Both families below have it:
-//   L2Metric    f_j(q) = F_j + s^2 (q - j)^2   (the Euclidean step)
+//   L2Metric    f_j(q) = F_j + s^2 (q - j)^2   (the Euclidean step; L2IntMetric
+//               the same in exact scaled integers)
 //   LinfMetric  f_j(q) = max(g_j, |q - j|)    (the chessboard step; for j < k,
 //               f_k - f_j is k - j far to the left and j - k far to the right,
 //               and once f_k <= f_j (or <) holds it holds further right)
@@ -323,6 +324,39 @@ struct L2Metric {
     EDT_HD static Val lower_from_bits(uint32_t b) { return from_bits(b) * (1.0 - 0x1p-22); }
     EDT_HD uint32_t bound_bits(Val self, Val prev, Val next, int K) const {
         return __builtin_bit_cast(uint32_t, round_up_float(chunk_bound(self, prev, next, s2, K)));
+    }
+};
+
+// The same parabolas with exact integer values: every value and height is
+// S times the real one (S a power of two with S * s^2 an integer for every
+// axis) and stays below 2^29, so values, heights, their differences and kInf
+// plus any of them fit int32 (the host checks the bound before choosing this
+// metric).  The dominance test and the crossing take float64 products of
+// int32 differences and offsets below 2^16: exact, as in L2Metric.
+struct L2IntMetric {
+    using Val = int;
+    static constexpr int kInf = 0x3FFFFFFF;   // no source
+    static constexpr int kMaxFinite = kInf - 1;
+    int s2;   // S x squared spacing along the line
+    EDT_HD Val height(Val f, int p) const { return f + s2 * p * p; }
+    EDT_HD Val dist(int d) const { return s2 * d * d; }
+    EDT_HD static Val combine(Val f, Val dd) { return f + dd; }
+    EDT_HD static bool dominated(int a, Val Ya, int b, Val Yb, int c, Val Yc) {
+        return (double)(Yb - Ya) * (double)(c - b) >= (double)(Yc - Yb) * (double)(b - a);
+    }
+    EDT_HD int cross(int a, Val Ya, int b, Val Yb, int cap) const {
+        return first_index_beating((double)(Yb - Ya), 2.0 * (double)s2 * (double)(b - a), cap);
+    }
+    EDT_HD static uint32_t min_bits(Val f) { return (uint32_t)f; }
+    EDT_HD static Val from_bits(uint32_t b) { return (int)b; }
+    EDT_HD static Val lower_from_bits(uint32_t b) { return (int)b; }
+    // chunk_bound in integers, saturated at kInf (no candidate nearby)
+    EDT_HD uint32_t bound_bits(Val self, Val prev, Val next, int K) const {
+        const int nr = s2 * (K - 1) * (K - 1), fr = s2 * (2 * K - 1) * (2 * K - 1);
+        int b = self + nr;
+        if (prev + fr < b) b = prev + fr;
+        if (next + fr < b) b = next + fr;
+        return (uint32_t)(b < kInf ? b : kInf);
     }
 };
 

@@ -22,6 +22,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <climits>
+#include <cmath>
+#include <algorithm>
+#include <type_traits>
 
 #include "envelope.h"
 #include "kernels.h"
@@ -819,7 +822,14 @@ __device__ void resolve_line(View& view, SlotArrays<Val, K>& sa, const Val* mych
 // over one cache line per lane).
 // --------------------------------------------------------------------------
 
-struct Geo2D {          // rows of B images of H x W; value = axis-0 coordinate
+// Candidate values of the Euclidean passes: T = double (L2Metric), or int
+// (L2IntMetric: every value and squared spacing times S = 2^shift, exact;
+// the outputs divide by S again, exactly).
+template <class T> struct L2Of { using type = L2Metric; };
+template <> struct L2Of<int> { using type = L2IntMetric; };
+
+template <class T>
+struct Geo2DT {         // rows of B images of H x W; value = axis-0 coordinate
     using Val = uint16_t;
     static constexpr Val kNoneVal = kNone16;
     // Rows of an image follow the nearest background of one column each, so
@@ -828,33 +838,38 @@ struct Geo2D {          // rows of B images of H x W; value = axis-0 coordinate
     // (16384^2: 0.90 against 1.07 ms; 4096^2 disks: 0.21 against 0.46 ms).
     static constexpr bool kPerChunk = false;
     static bool per_chunk(int) { return false; }
-    using Metric = L2Metric;
+    using Metric = typename L2Of<T>::type;
     static constexpr bool kRootOut = true;   // float32 distances beside the squared ones
-    double s2a, s2l;    // squared spacing of axis 0 and along the row
+    static constexpr bool kScaled = !std::is_same<T, double>::value;
+    T s2a, s2l;         // (S x) squared spacing of axis 0 and along the row
     int W;
     int H;              // rows per image: line ln is row ln % H of image ln / H
-    __device__ Metric metric() const { return L2Metric{s2l}; }
+    int shift;          // S = 2^shift (scaled values only)
+    float inv_s;        // 1 / S
+    __device__ Metric metric() const { return Metric{s2l}; }
     struct Line { int row; };
     __device__ Line line(int64_t ln) const {
         return Line{ln < 0x100000000ll ? (int)((unsigned)ln % (unsigned)H) : (int)(ln % H)};
     }
     __device__ static bool valid(uint16_t v) { return v != kNone16; }
-    __device__ double f(const Line& l, uint16_t v) const {
-        const double t = (double)(l.row - (int)v);
+    __device__ T f(const Line& l, uint16_t v) const {
+        const T t = (T)(l.row - (int)v);
         return s2a * t * t;
     }
     // v < 2^16 and W <= 32768: a 24-bit product is exact
     __device__ int32_t index(const Line&, uint16_t v, int pos) const {
         return (int32_t)__umul24((unsigned)v, (unsigned)W) + pos;
     }
-    __device__ double virt_f(const Line& l) const {
-        const double t = (double)(l.row + 1);
+    __device__ T virt_f(const Line& l) const {
+        const T t = (T)(l.row + 1);
         return s2a * t * t;
     }
     __device__ int32_t virt_index() const { return -W; }
 };
+using Geo2D = Geo2DT<double>;
 
-struct Geo3D {          // rows along W of B x D x H x W volumes; value = packed (axis0, axis1)
+template <class T>
+struct Geo3DT {         // rows along W of B x D x H x W volumes; value = packed (axis0, axis1)
     // Per-chunk resolution for rows longer than 128 (512^3: 0.66 ms against
     // 0.71 ms in whole-line rounds); rows of 128 or fewer go faster in rounds
     // (16 x 128^3: 0.288 against 0.310 ms).
@@ -862,12 +877,15 @@ struct Geo3D {          // rows along W of B x D x H x W volumes; value = packed
     static bool per_chunk(int L) { return L > 128; }
     using Val = uint32_t;
     static constexpr Val kNoneVal = kNone32;
-    using Metric = L2Metric;
+    using Metric = typename L2Of<T>::type;
     static constexpr bool kRootOut = true;
-    double s2a, s2b, s2l;
+    static constexpr bool kScaled = !std::is_same<T, double>::value;
+    T s2a, s2b, s2l;    // (S x) squared spacings
     int D, H, W;
     bool dh24;          // D * H < 2^24: the flat index needs only 24-bit products
-    __device__ Metric metric() const { return L2Metric{s2l}; }
+    int shift;          // S = 2^shift (scaled values only)
+    float inv_s;        // 1 / S
+    __device__ Metric metric() const { return Metric{s2l}; }
     struct Line { int d, h; };
     __device__ Line line(int64_t ln) const {
         const unsigned DH = (unsigned)D * (unsigned)H;   // D * H * W < 2^31
@@ -875,9 +893,9 @@ struct Geo3D {          // rows along W of B x D x H x W volumes; value = packed
         return Line{(int)(dh / (unsigned)H), (int)(dh % (unsigned)H)};
     }
     __device__ static bool valid(uint32_t v) { return v != kNone32; }
-    __device__ double f(const Line& l, uint32_t v) const {
-        const double t0 = (double)(l.d - (int)(v >> 16));
-        const double t1 = (double)(l.h - (int)(v & 0xFFFFu));
+    __device__ T f(const Line& l, uint32_t v) const {
+        const T t0 = (T)(l.d - (int)(v >> 16));
+        const T t1 = (T)(l.h - (int)(v & 0xFFFFu));
         return s2a * t0 * t0 + s2b * t1 * t1;
     }
     __device__ int32_t index(const Line&, uint32_t v, int pos) const {
@@ -886,9 +904,9 @@ struct Geo3D {          // rows along W of B x D x H x W volumes; value = packed
         const unsigned dh = __umul24(v >> 16, (unsigned)H) + (v & 0xFFFFu);
         return (int32_t)(dh24 ? __umul24(dh, (unsigned)W) : dh * (unsigned)W) + pos;
     }
-    __device__ double virt_f(const Line& l) const {
-        const double t0 = (double)(l.d + 1);
-        return s2a * t0 * t0 + s2b * (double)l.h * (double)l.h;
+    __device__ T virt_f(const Line& l) const {
+        const T t0 = (T)(l.d + 1);
+        return s2a * t0 * t0 + s2b * (T)l.h * (T)l.h;
     }
     __device__ int32_t virt_index() const { return -(H * W); }
     // the same flat index for volumes over 2^31 - 1 elements
@@ -896,6 +914,7 @@ struct Geo3D {          // rows along W of B x D x H x W volumes; value = packed
         return ((int64_t)(v >> 16) * H + (v & 0xFFFFu)) * (int64_t)W + pos;
     }
 };
+using Geo3D = Geo3DT<double>;
 
 // The chessboard (L-infinity) row passes (TorchMorph's chamfer transforms):
 // the same lines and values, the candidate value g = the L-infinity distance
@@ -910,6 +929,7 @@ struct GeoLinf2D {
     static bool per_chunk(int) { return false; }
     using Metric = LinfMetric;
     static constexpr bool kRootOut = false;
+    static constexpr bool kScaled = false;
     int W;
     int H;
     __device__ Metric metric() const { return LinfMetric{}; }
@@ -933,6 +953,7 @@ struct GeoLinf3D {
     static bool per_chunk(int L) { return L > 128; }
     using Metric = LinfMetric;
     static constexpr bool kRootOut = false;
+    static constexpr bool kScaled = false;
     int D, H, W;
     bool dh24;
     __device__ Metric metric() const { return LinfMetric{}; }
@@ -1045,9 +1066,14 @@ __global__ __launch_bounds__(1024) void k_envelope_rows(const typename Geo::Val*
         const int oq = ow < 0 ? 0 : ow;   // the virtual element acts as one at position 0
         const Val vo = view.val(oq);
         const typename Mt::Val F = mt.combine(ow < 0 ? fvirt : fof(vo), mt.dist(q - oq));
-        osq = sqdist ? (int32_t)F : 0;
-        if constexpr (Geo::kRootOut) od = __builtin_amdgcn_sqrtf((float)F);
-        else od = 0.0f;
+        if constexpr (Geo::kScaled) {   // F = S x the squared distance, S = 2^shift
+            osq = sqdist ? (int32_t)(F >> geo.shift) : 0;
+            od = __builtin_amdgcn_sqrtf((float)F * geo.inv_s);   // (exact scaling)
+        } else {
+            osq = sqdist ? (int32_t)F : 0;
+            if constexpr (Geo::kRootOut) od = __builtin_amdgcn_sqrtf((float)F);
+            else od = 0.0f;
+        }
         if constexpr (sizeof(Ix) == 8) oix = ow < 0 ? (Ix)ivirt : (Ix)geo.index64(gl, vo, ow);
         else oix = ow < 0 ? ivirt : geo.index(gl, vo, ow);
     };
@@ -1458,6 +1484,27 @@ static hipError_t launch_rows_any(const typename Geo::Val* in, int L, int64_t nl
     return launch_rows_t<Geo, K, 1, Ix, Geo::kPerChunk>(in, L, nlines, p, geo, sqdist, dist, indices, s, tm, kname);
 }
 
+// Exact integer values for a pass (L2IntMetric): the smallest S = 2^k,
+// k <= 10, with every S * s2[i] an integer (at most 2^20), provided that
+// S * sum_i s2[i] * ext[i]^2 stays below 2^29, ext[i] bounding the offsets
+// the pass forms along axis i (the virtual element's and the chunk bound's
+// included).  -1: the pass keeps double values.  (A larger S only raises the
+// sum, so the smallest one decides.)
+static int int_scale_shift(const double* s2, const double* ext, int n) {
+    for (int k = 0; k <= 10; ++k) {
+        const double S = (double)(1 << k);
+        bool whole = true;
+        double ymax = 0.0;
+        for (int i = 0; i < n; ++i) {
+            const double x = S * s2[i];
+            if (!(x >= 0.0 && x <= 1048576.0 && x == rint(x))) whole = false;   // (NaN: false)
+            ymax += x * ext[i] * ext[i];
+        }
+        if (whole) return ymax < 536870912.0 ? k : -1;
+    }
+    return -1;
+}
+
 hipError_t launch_rows_2d(const uint16_t* c0, int B, int H, int W, double s2_0, double s2_1,
                           int32_t* sqdist, float* dist, int32_t* indices, hipStream_t s,
                           KernelTimer* tm) {
@@ -1466,6 +1513,14 @@ hipError_t launch_rows_2d(const uint16_t* c0, int B, int H, int W, double s2_0, 
     hipError_t e = hipSuccess;
     if (launch_rows_wave<Geo2D>(c0, W, nlines, geo, sqdist, dist, indices, s, tm, "envelope_rows_2d", &e))
         return e;
+    const double s2[2] = {s2_0, s2_1}, ext[2] = {(double)H, (double)std::max(W - 1, 63)};
+    const int k = int_scale_shift(s2, ext, 2);
+    if (k >= 0) {
+        const int S = 1 << k;
+        const Geo2DT<int> gi{(int)(S * s2_0), (int)(S * s2_1), W, H, k, 1.0f / (float)S};
+        return launch_rows_any<Geo2DT<int>, 32>(c0, W, nlines, gi, sqdist, dist, indices, s, tm,
+                                                "envelope_rows_2d");
+    }
     return launch_rows_any<Geo2D, 32>(c0, W, nlines, geo, sqdist, dist, indices, s, tm, "envelope_rows_2d");
 }
 
@@ -1516,13 +1571,25 @@ hipError_t launch_unravel(const int32_t* flat, int64_t images, int64_t per_image
 hipError_t launch_rows_3d(const uint32_t* c01, int B, int D, int H, int W, double s2_0,
                           double s2_1, double s2_2, int32_t* sqdist, float* dist,
                           int32_t* indices, int64_t* indices64, hipStream_t s, KernelTimer* tm) {
-    Geo3D geo{s2_0, s2_1, s2_2, D, H, W, (int64_t)D * H < (1 << 24)};
+    const bool dh24 = (int64_t)D * H < (1 << 24);
+    Geo3D geo{s2_0, s2_1, s2_2, D, H, W, dh24};
     const int64_t nlines = (int64_t)B * D * H;
-    if (indices64)   // int64 indices: the chunk kernel for any number of lines
+    const double s2[3] = {s2_0, s2_1, s2_2}, ext[3] = {(double)D, (double)H, (double)std::max(W - 1, 31)};
+    const int k = int_scale_shift(s2, ext, 3);
+    const int S = 1 << (k < 0 ? 0 : k);
+    const Geo3DT<int> gi{(int)(S * s2_0), (int)(S * s2_1), (int)(S * s2_2), D, H, W, dh24, k, 1.0f / (float)S};
+    if (indices64) {   // int64 indices: the chunk kernel for any number of lines
+        if (k >= 0)
+            return launch_rows_any<Geo3DT<int>, 16>(c01, W, nlines, gi, sqdist, dist, indices64, s, tm,
+                                                    "envelope_rows_3d");
         return launch_rows_any<Geo3D, 16>(c01, W, nlines, geo, sqdist, dist, indices64, s, tm,
                                           "envelope_rows_3d");
+    }
     hipError_t e = hipSuccess;
     if (launch_rows_wave<Geo3D>(c01, W, nlines, geo, sqdist, dist, indices, s, tm, "envelope_rows_3d", &e)) return e;
+    if (k >= 0)
+        return launch_rows_any<Geo3DT<int>, 16>(c01, W, nlines, gi, sqdist, dist, indices, s, tm,
+                                                "envelope_rows_3d");
     return launch_rows_any<Geo3D, 16>(c01, W, nlines, geo, sqdist, dist, indices, s, tm, "envelope_rows_3d");
 }
 
@@ -1579,17 +1646,19 @@ size_t cols_lds_bytes(int H) {
 }
 
 // Candidate values of the middle-axis pass from the axis-0 coordinate v at
-// plane d: the Euclidean one (s2a (d - v)^2, lines of squared spacing s2l) and
-// the chessboard one (|d - v|).
-struct ColL2 {
-    using Metric = L2Metric;
-    double s2a, s2l;
-    __device__ Metric metric() const { return L2Metric{s2l}; }
-    __device__ double f(int d, uint16_t v) const {
-        const double t = (double)(d - (int)v);
+// plane d: the Euclidean one (s2a (d - v)^2, lines of squared spacing s2l; in
+// double, or scaled integers) and the chessboard one (|d - v|).
+template <class T>
+struct ColL2T {
+    using Metric = typename L2Of<T>::type;
+    T s2a, s2l;   // (S x) squared spacings
+    __device__ Metric metric() const { return Metric{s2l}; }
+    __device__ T f(int d, uint16_t v) const {
+        const T t = (T)(d - (int)v);
         return s2a * t * t;
     }
 };
+using ColL2 = ColL2T<double>;
 struct ColLinf {
     using Metric = LinfMetric;
     __device__ Metric metric() const { return LinfMetric{}; }
@@ -1714,6 +1783,13 @@ static hipError_t launch_cols_any(const uint16_t* c0, int B, int D, int H, int W
 
 hipError_t launch_cols_3d(const uint16_t* c0, int B, int D, int H, int W, double s2_0,
                           double s2_1, uint32_t* c01, hipStream_t s, KernelTimer* tm) {
+    const double s2[2] = {s2_0, s2_1}, ext[2] = {(double)D, (double)std::max(H - 1, 127)};
+    const int k = int_scale_shift(s2, ext, 2);
+    if (k >= 0) {
+        const int S = 1 << k;
+        return launch_cols_any(c0, B, D, H, W, ColL2T<int>{(int)(S * s2_0), (int)(S * s2_1)}, c01, s, tm,
+                               "envelope_cols_3d");
+    }
     return launch_cols_any(c0, B, D, H, W, ColL2{s2_0, s2_1}, c01, s, tm, "envelope_cols_3d");
 }
 

@@ -8,6 +8,18 @@ import oracle
 # float32 distances: 1e-6 relative (unit spacing) / 1e-5 relative (anisotropic)
 TOL_ISO = 1e-6
 TOL_ANISO = 1e-5
+# attaining indices under squared spacings that are not multiples of 2^-20:
+# squared distances equal up to a relative 1e-12 (float64 rounding of the sums)
+TOL_TIE = 1e-12
+
+
+def _exact_sums(sampling):
+    """True when every squared spacing is a multiple of 2^-20 (then every
+    squared distance of the tested sizes is an exact float64 sum)."""
+    if sampling is None:
+        return True
+    return all(float(s) * float(s) * 2.0 ** 20 == float(int(float(s) * float(s) * 2.0 ** 20))
+               for s in sampling)
 
 
 def compare(mask, sampling, ref_sq, sq=None, dist=None, idx=None, batch=False):
@@ -39,7 +51,14 @@ def compare(mask, sampling, ref_sq, sq=None, dist=None, idx=None, batch=False):
     if idx is not None:
         assert idx.dtype == np.int32
         d2 = oracle.sqdist_to(idx, mask.shape, sampling)
-        bad = np.flatnonzero(d2.reshape(-1) != ref_sq.reshape(-1))
+        if _exact_sums(sampling):
+            bad = np.flatnonzero(d2.reshape(-1) != ref_sq.reshape(-1))
+        else:
+            # squared spacings with no finite binary form: two background
+            # elements at one distance can differ in their float64 sums by a
+            # rounding step, and either is a correct answer
+            diff = np.abs(d2.reshape(-1) - ref_sq.reshape(-1))
+            bad = np.flatnonzero(diff > TOL_TIE * np.maximum(ref_sq.reshape(-1), 1.0))
         assert bad.size == 0, (
             f"index does not attain the minimum at {bad.size} elements; first {bad[:5]}: "
             f"d2 {d2.reshape(-1)[bad[:5]]} oracle {ref_sq.reshape(-1)[bad[:5]]}")

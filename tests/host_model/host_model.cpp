@@ -3,8 +3,8 @@
 //
 // Runs, for one line at a time, the same functions the envelope kernels run
 // (the metrics' bounds and tests, build_chunk, chunk_owner_marks,
-// boundary_dead) in the same phase order as the kernels, for both metrics
-// (squared Euclidean and chessboard), with plain arrays in place of LDS, so the CPU
+// boundary_dead) in the same phase order as the kernels, for every metric
+// (squared Euclidean in float64 and in scaled integers, chessboard), with plain arrays in place of LDS, so the CPU
 // test-suite can check the algorithm against the definition.  Not part of the
 // library.
 #include <math.h>
@@ -24,6 +24,7 @@ constexpr int kCascadeFrom = 2;    // first whole-line round with cascade steps
 template <class Mt> bool has_source(typename Mt::Val v);
 template <> bool has_source<edt::L2Metric>(double v) { return isfinite(v); }
 template <> bool has_source<edt::LinfMetric>(int v) { return v < edt::LinfMetric::kInf; }
+template <> bool has_source<edt::L2IntMetric>(int v) { return v < edt::L2IntMetric::kInf; }
 
 template <int K, class Mt>
 struct LineView {
@@ -235,6 +236,23 @@ extern "C" int model_envelope_lines(const double* fb, int64_t nlines, int L, dou
                                     int G, int reach, int32_t* owner) {
     for (int64_t i = 0; i < nlines; ++i) {
         const int rc = model_envelope_line(fb + i * L, L, s2l, K, G, reach, owner + i * L);
+        if (rc) return rc;
+    }
+    return 0;
+}
+
+// The squared Euclidean step in exact integers (L2IntMetric): fb[p] = S F_p
+// (negative: no source), s2l = S x the squared spacing along the line; every
+// line of a [nlines][L] array.
+extern "C" int model_envelope_lines_int(const int32_t* fb, int64_t nlines, int L, int s2l, int K, int G,
+                                        int reach, int32_t* owner) {
+    std::vector<int> line(L);
+    for (int64_t i = 0; i < nlines; ++i) {
+        for (int p = 0; p < L; ++p) {
+            const int32_t v = fb[i * L + p];
+            line[p] = v < 0 ? edt::L2IntMetric::kInf : v;
+        }
+        const int rc = line_any(line.data(), L, edt::L2IntMetric{s2l}, K, G, reach, owner + i * L);
         if (rc) return rc;
     }
     return 0;

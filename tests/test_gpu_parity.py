@@ -93,9 +93,10 @@ def test_random_2d(torch_dev, shape):
         if not (mask == 0).any():
             mask.reshape(-1)[rng.integers(0, mask.size)] = 0
         _say(f"2d {shape} p={p}")
-        check(torch_dev, mask)
-        check(torch_dev, mask, (2.5, 1.0))
-        check(torch_dev, mask, (1.0, 0.75))
+        check(torch_dev, mask)                  # (exact integer values)
+        check(torch_dev, mask, (2.5, 1.0))      # (integers after scaling by 4)
+        check(torch_dev, mask, (1.0, 0.75))     # (by 16)
+        check(torch_dev, mask, (1.0, 0.7))      # (no power of two makes 0.49 whole: float64 values)
 
 
 SHAPES_3D = [(1, 1, 1, 1), (2, 5, 7, 9), (1, 1, 33, 70), (1, 70, 1, 33), (1, 66, 40, 1),
@@ -114,6 +115,7 @@ def test_random_3d(torch_dev, shape):
         check(torch_dev, mask)
         check(torch_dev, mask, (2.5, 1.0, 1.0))
         check(torch_dev, mask, (1.0, 2.0, 0.5))
+        check(torch_dev, mask, (1.3, 1.0, 0.7))   # (float64 values)
 
 
 @pytest.mark.parametrize("name", golden_names())
@@ -261,6 +263,31 @@ def test_background_runs(torch_dev):
         check(torch_dev, mask, samp)
 
 
+def test_value_kinds(torch_dev):
+    """The Euclidean passes take exact integer values (every squared spacing a
+    whole number after scaling by a power of two, and the largest height
+    S * sum s2 * extent^2 below 2^29) or float64 values otherwise; both give
+    the oracle's result.  A tall image at unit spacing (integers) and with
+    doubled axis-0 spacing (4 x 16384^2 is over the bound: float64), long
+    rows, spacings that need a scale of 2^6 or 2^8, one that would need more
+    than 2^10 and ones no power of two makes whole (float64).  (16384^2 at
+    unit spacing, just under the bound, is one of the full-size tests.)"""
+    rng = np.random.default_rng([42, 3011])
+    for shape, samp in (((16384, 64), None), ((16384, 64), (2.0, 1.0)), ((64, 16384), (1.0, 1.0)),
+                        ((300, 700), (0.125, 1.0)), ((300, 700), (1.0, 1.0 / 1024)),
+                        ((300, 700), (1.0, 0.1)), ((300, 700), (3.0, 7.0))):
+        mask = (rng.random(shape) >= 0.01).astype(np.uint8)
+        mask[0, 0] = 0
+        _say(f"value kinds {shape} sampling {samp}")
+        check(torch_dev, mask, samp)
+    for shape, samp in (((1, 40, 300, 520), (2.5, 1.0, 1.0)), ((1, 40, 300, 520), (0.3, 1.0, 1.0)),
+                        ((1, 600, 600, 70), (4.0, 4.0, 1.0)), ((1, 20, 70, 600), (1.0, 1.0, 0.0625))):
+        mask = (rng.random(shape) >= 0.003).astype(np.uint8)
+        mask[0, 0, 0, 0] = 0
+        _say(f"value kinds {shape} sampling {samp}")
+        check(torch_dev, mask, samp)
+
+
 def test_large_objects(torch_dev):
     """Large foreground objects, where whole-line rounds are long: interior
     candidates are dominated only by members many chunks away (the filter's
@@ -276,13 +303,13 @@ def test_large_objects(torch_dev):
         disks |= (yy - cy) ** 2 + (xx - cx) ** 2 <= r * r
     m = disks.astype(np.uint8)
     m[rng.integers(0, 900, 40), rng.integers(0, 1700, 40)] = 0
-    for samp in (None, (2.5, 1.0), (1.0, 0.75)):
+    for samp in (None, (2.5, 1.0), (1.0, 0.75), (0.9, 1.1)):
         _say(f"large disks 900 x 1700 sampling {samp}")
         check(torch_dev, m, samp)
     zz, yv, xv = np.mgrid[0:3, 0:600, 0:1200]
     v = ((yv - 300) ** 2 + (xv - 600) ** 2 <= 280 ** 2 - (zz * 60) ** 2).astype(np.uint8)[None]
     v[0, 1, :, 0:300] = 1                                # columns without background
-    for samp in (None, (2.5, 1.0, 1.0)):
+    for samp in (None, (2.5, 1.0, 1.0), (1.3, 0.9, 1.1)):
         _say(f"cylinder 1 x 3 x 600 x 1200 sampling {samp}")
         check(torch_dev, v, samp)
     zz, yv, xv = np.mgrid[0:40, 0:64, 0:128]

@@ -158,6 +158,55 @@ def test_model_transform_matches_oracle(model, K, reach):
         np.testing.assert_array_equal(got, ref, err_msg=f"shape {mask.shape} sampling {samp}")
 
 
+@pytest.fixture(scope="module")
+def int_model(tmp_path_factory):
+    out = str(tmp_path_factory.mktemp("host_model_int") / "host_model.so")
+    subprocess.run(["g++", "-O2", "-std=c++17", "-fPIC", "-shared", "-o", out, SRC], check=True)
+    lib = ctypes.CDLL(out)
+    lib.model_envelope_lines_int.restype = ctypes.c_int
+    lib.model_envelope_lines_int.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                             ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+
+    def run(fb, s2l, K, G, reach=8):
+        fb = np.ascontiguousarray(fb, np.int32)
+        nl, L = fb.shape
+        own = np.empty((nl, L), np.int32)
+        assert lib.model_envelope_lines_int(fb.ctypes.data, nl, L, s2l, K, G, reach, own.ctypes.data) == 0
+        return own
+
+    return run
+
+
+@pytest.mark.parametrize("L", [1, 33, 257, 1000, 4096])
+def test_int_lines_match_definition(int_model, L):
+    """The squared Euclidean step in exact scaled integers (L2IntMetric, the
+    kernels' integer values): owners attain the definition's minimum, with
+    values S F up to the 2^29 bound the host allows."""
+    rng = np.random.default_rng([42, 2004, L])
+    for s2l in (1, 4, 25):
+        top = (2 ** 29 - 1) // 2 - s2l * L * L   # heights below 2^29
+        nl = 12
+        fb = np.empty((nl, L), np.int64)
+        for i in range(nl):
+            kind = i % 4
+            if kind == 0:
+                fb[i] = rng.integers(0, max(1, min(top, 4 * L * L)), L)
+                fb[i][rng.random(L) < 0.3] = -1
+            elif kind == 1:
+                fb[i] = rng.integers(0, max(1, top), L)
+            elif kind == 2:
+                fb[i] = -1
+                fb[i][rng.integers(0, L)] = rng.integers(0, max(1, top))
+            else:
+                fb[i] = rng.integers(0, 4, L)
+        ref_in = np.where(fb >= 0, fb.astype(np.float64), np.inf)
+        ref = _brute_lines(ref_in, float(s2l))
+        for (K, G), reach in itertools.product(_layouts(L), (8, 0)):
+            own = int_model(fb, s2l, K, G, reach)
+            got = _value_at(ref_in, own, float(s2l))
+            np.testing.assert_array_equal(got, ref, err_msg=f"L={L} K={K} G={G} s2={s2l} reach={reach}")
+
+
 # ---------------------------------------------------------------------------
 # The same machinery under the chessboard metric, f_j(q) = max(g_j, |q - j|)
 # (TorchMorph's chamfer transforms, read as the L-infinity metric): the line
