@@ -116,7 +116,7 @@ EDT_HD inline Mask back_cascade(View& v, int c, Mask m, int w) {
     while (m & (m - 1)) {
         const int pp = high_bit(m & bits_below<Mask>(tl));
         const auto Yp = v.Y(base + pp);
-        if (!v.mt.dominated(base + pp, Yp, base + tl, Yl, w, Yw)) break;
+        if (!v.mt.dominated_seq(base + pp, Yp, base + tl, Yl, w, Yw)) break;
         m &= ~(Mask(1) << tl);
         tl = pp;
         Yl = Yp;
@@ -132,7 +132,7 @@ EDT_HD inline Mask front_cascade(View& v, int c, Mask m, int w) {
     while (m & (m - 1)) {
         const int nn = low_bit(m & bits_above<Mask>(tf));
         const auto Yn = v.Y(base + nn);
-        if (!v.mt.dominated(w, Yw, base + tf, Yf, base + nn, Yn)) break;
+        if (!v.mt.dominated_seq(w, Yw, base + tf, Yf, base + nn, Yn)) break;
         m &= ~(Mask(1) << tf);
         tf = nn;
         Yf = Yn;
@@ -182,7 +182,7 @@ EDT_HD inline Mask build_chunk(const Mt& mt, int base, Mask cand, ValAt val_at, 
         cand &= cand - 1;
         const int p = base + t;
         const H Y = height(val_at(t), p);
-        while (sec >= 0 && mt.dominated(sec, Ysec, top, Ytop, p, Y)) {
+        while (sec >= 0 && mt.dominated_seq(sec, Ysec, top, Ytop, p, Y)) {
             m &= ~(Mask(1) << (top - base));
             top = sec; Ytop = Ysec;
             const Mask below = m & bits_below<Mask>(top - base);
@@ -215,7 +215,7 @@ EDT_HD inline Mask build_chunk_unrolled(const Mt& mt, int base, Mask cand,
         if (!((cand >> t) & Mask(1))) continue;
         const int p = base + t;
         const H Y = Yr[t];
-        while (sec >= 0 && mt.dominated(sec, Ysec, top, Ytop, p, Y)) {
+        while (sec >= 0 && mt.dominated_seq(sec, Ysec, top, Ytop, p, Y)) {
             m &= ~(Mask(1) << (top - base));
             top = sec; Ytop = Ysec;
             const Mask below = m & bits_below<Mask>(top - base);
@@ -299,7 +299,12 @@ EDT_HD inline int first_index_beating(double A, double B, int cap) {
 //               and once f_k <= f_j (or <) holds it holds further right)
 // A metric gives the candidate value type (Val) and the height its tests
 // compare, dist(d) and combine(v, dist(d)) (a candidate of value v at signed
-// offset d), the dominance test, cross (the first position, clipped to [0, cap], where
+// offset d), the dominance test (dominated: b never strictly below the
+// nearer of a and c from its own crossings on -- safe when every dominated
+// member leaves at once, as in boundary_dead and the candidate filter;
+// dominated_seq: b never strictly below both, ties included -- for the steps
+// that remove one member at a time against members still present, which
+// keeps every value and leaves no member that dominated would remove), cross (the first position, clipped to [0, cap], where
 // the later of two candidates is strictly below the earlier), the chunk bound,
 // and the 32-bit form in which chunk minima and bounds are kept.
 // --------------------------------------------------------------------------
@@ -313,6 +318,9 @@ struct L2Metric {
     EDT_HD static Val combine(Val f, Val dd) { return f + dd; }
     EDT_HD static bool dominated(int a, Val Ya, int b, Val Yb, int c, Val Yc) {
         return edt::dominated(a, Ya, b, Yb, c, Yc);
+    }
+    EDT_HD static bool dominated_seq(int a, Val Ya, int b, Val Yb, int c, Val Yc) {
+        return dominated(a, Ya, b, Yb, c, Yc);
     }
     EDT_HD int cross(int a, Val Ya, int b, Val Yb, int cap) const {
         return first_index_beating(Yb - Ya, 2.0 * s2 * (double)(b - a), cap);
@@ -343,6 +351,9 @@ struct L2IntMetric {
     EDT_HD static Val combine(Val f, Val dd) { return f + dd; }
     EDT_HD static bool dominated(int a, Val Ya, int b, Val Yb, int c, Val Yc) {
         return (double)(Yb - Ya) * (double)(c - b) >= (double)(Yc - Yb) * (double)(b - a);
+    }
+    EDT_HD static bool dominated_seq(int a, Val Ya, int b, Val Yb, int c, Val Yc) {
+        return dominated(a, Ya, b, Yb, c, Yc);
     }
     EDT_HD int cross(int a, Val Ya, int b, Val Yb, int cap) const {
         return first_index_beating((double)(Yb - Ya), 2.0 * (double)s2 * (double)(b - a), cap);
@@ -376,8 +387,22 @@ struct LinfMetric {
         const int x = gk >= gj ? (j + gk > mid ? j + gk : mid) : (k - gj < mid ? k - gj : mid);
         return x + 1;
     }
+    // First position q where candidate k is at most candidate j (j < k): the
+    // same cases with ties counted, m rounded up.
+    EDT_HD static int first_at_most(int j, int gj, int k, int gk) {
+        const int mc = (j + k + 1) >> 1;
+        return gk > gj ? (j + gk > mc ? j + gk : mc) : (k - gj < mc ? k - gj : mc);
+    }
     EDT_HD static bool dominated(int a, Val ga, int b, Val gb, int c, Val gc) {
         return first_below(a, ga, b, gb) >= first_below(b, gb, c, gc);
+    }
+    // b is strictly below both a and c nowhere: from first_below(a, b) on it
+    // is below a, from first_at_most(b, c) on c is at most b.  Flat bottoms
+    // make such ties common (a line at equal g keeps every candidate under
+    // the strict test); where removals are justified one at a time, dropping
+    // them keeps every value.
+    EDT_HD static bool dominated_seq(int a, Val ga, int b, Val gb, int c, Val gc) {
+        return first_below(a, ga, b, gb) >= first_at_most(b, gb, c, gc);
     }
     EDT_HD static int cross(int a, Val ga, int b, Val gb, int cap) {
         const int x = first_below(a, ga, b, gb);
@@ -529,7 +554,7 @@ EDT_HD inline bool chunk_owner_marks(View& v, int c, int G, int L, Mask M, Mark 
     H Ytop = H(0), Ysec = H(0);
     auto insert = [&](int i, int p) {
         const H Y = v.Y(p);
-        while (sec >= 0 && mt.dominated(psec, Ysec, ptop, Ytop, p, Y)) {
+        while (sec >= 0 && mt.dominated_seq(psec, Ysec, ptop, Ytop, p, Y)) {
             alive &= ~(Seq(1) << top);
             top = sec;
             ptop = psec;

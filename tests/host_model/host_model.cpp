@@ -241,6 +241,13 @@ extern "C" int model_envelope_lines(const double* fb, int64_t nlines, int L, dou
     return 0;
 }
 
+// LinfMetric's crossings for candidates j < k: out[0] = the first position
+// where k is strictly below j, out[1] = the first where it is at most j.
+extern "C" void model_linf_crossings(int j, int gj, int k, int gk, int32_t* out) {
+    out[0] = edt::LinfMetric::first_below(j, gj, k, gk);
+    out[1] = edt::LinfMetric::first_at_most(j, gj, k, gk);
+}
+
 // The squared Euclidean step in exact integers (L2IntMetric): fb[p] = S F_p
 // (negative: no source), s2l = S x the squared spacing along the line; every
 // line of a [nlines][L] array.

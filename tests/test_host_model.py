@@ -236,7 +236,32 @@ def linf_model(tmp_path_factory):
         np.testing.assert_array_equal(val, _linf_value_at(gb, own))
         return own
 
+    run.path = out
     return run
+
+
+def test_linf_crossings_match_definition(linf_model):
+    """LinfMetric's closed-form crossings against the definition, position by
+    position: for j < k the positions where max(g_k, |q - k|) is below (at
+    most) max(g_j, |q - j|) form a right half-line starting at first_below
+    (first_at_most)."""
+    lib = ctypes.CDLL(linf_model.path)
+    lib.model_linf_crossings.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                         ctypes.c_void_p]
+    rng = np.random.default_rng([42, 2005])
+    q = np.arange(-300, 400)
+    out = np.empty(2, np.int32)
+    for _ in range(3000):
+        j = int(rng.integers(0, 80))
+        k = int(rng.integers(j + 1, 100))
+        gj, gk = (int(x) for x in rng.integers(0, 60, 2))
+        fj = np.maximum(gj, np.abs(q - j))
+        fk = np.maximum(gk, np.abs(q - k))
+        lib.model_linf_crossings(j, gj, k, gk, out.ctypes.data)
+        for lt, x in ((fk < fj, out[0]), (fk <= fj, out[1])):
+            first = q[np.argmax(lt)]
+            assert lt[-1] and (lt[q >= first]).all() and not lt[q < first].any(), (j, gj, k, gk)
+            assert x == first, (j, gj, k, gk, x, first)
 
 
 def _linf_brute_lines(gb):
