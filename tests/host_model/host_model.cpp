@@ -19,6 +19,7 @@
 namespace {
 
 constexpr int kWitnessScan = 16;   // chunks scanned per side for the filter's witnesses
+constexpr int kWitnessScanLinf = 32;   // the same under the chessboard metric
 constexpr int kCascadeFrom = 2;    // first whole-line round with cascade steps
 
 template <class Mt> bool has_source(typename Mt::Val v);
@@ -80,14 +81,14 @@ int run_line(const typename Mt::Val* fb, int L, const Mt& mt, int G, int32_t* ow
         if (b > Ub) Ub = b;
     }
     const F U = Mt::from_bits(Ub);
-    constexpr int scan = CAP > 0 ? 1 : kWitnessScan;
+    constexpr int scan = CAP > 0 ? 1 : std::is_same<Mt, edt::LinfMetric>::value ? kWitnessScanLinf : kWitnessScan;
     // phase 1: local envelopes of the candidates with a value <= U that are
     // not dominated by a chunk minimiser on either side: the chunk's own where
     // it lies on that side, else the witness (the minimiser of an earlier /
     // later chunk best at the chunk's first / last position, scanning chunk
     // minima outward while the distance term alone is still better, at most
-    // kWitnessScan chunks; only the neighbouring chunk where the per-chunk
-    // route is tried, CAP > 0)
+    // kWitnessScan chunks (kWitnessScanLinf for the chessboard); only the
+    // neighbouring chunk where the per-chunk route is tried, CAP > 0)
     for (int g = 0; g < G; ++g) {
         const int base = g * K;
         const int n = L - base < K ? L - base : K;
